@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Multi-Token Attention forward on one MI355X.
+
+One step = one fused forward (``mta_forward``, a single kernel launch) over the
+T=4096 workload: B=2, T=4096, M=32, d=128, c_q=4, c_k=9, c_h=4, convolution after
+softmax, head mixing before softmax, GroupNorm with gate 1/sqrt(12) (bf16 tensors,
+fp32 accumulation). Inputs are seeded synthetic tensors already resident in HBM.
+
+Printed: one JSON line with tokens/s (``value``), effective TFLOP/s and the fraction
+of the bf16 MFMA peak, the roofline of the fused kernel (HIP events on its launch
+stream), the library's plain causal attention and the default placement at the same
+shape, the unfused T^2 path, and the fp64 CPU oracle timed on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mta_inputs  # noqa: E402
+
+METRIC = "MTA fwd tokens/sec + effective TFLOP/s (% bf16 MFMA peak), T=4096, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+HEADLINE = 4  # index of the T=4096 workload in mta_inputs.CONFIGS
+
+
+def flops(cfg) -> int:
+    """Algorithmic flops: causal pairs x (QK^T 2d + AV 2d + conv 2*c_q*c_k + mix 2*c_h)."""
+    n_c = cfg.T * (cfg.T + 1) // 2
+    per = 4 * cfg.d
+    if cfg.kq:
+        per += 2 * cfg.c_q * cfg.c_k
+    if cfg.mix:
+        per += 2 * cfg.c_h
+    return cfg.B * cfg.M * n_c * per
+
+
+def materialized_bytes(cfg) -> int:
+    """Map traffic of the unfused chain (fp32 T x T maps) plus q, k, v, out."""
+    maps = 1  # logits write
+    if cfg.mix:
+        maps += 2
+    if cfg.kq:
+        maps += 2
+    maps += 2  # softmax read + write
+    maps += 1  # AV read
+    elt = 2 if cfg.dtype == "bf16" else 4
+    return cfg.B * cfg.M * cfg.T * cfg.T * 4 * maps + 4 * cfg.B * cfg.T * cfg.M * cfg.d * elt
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "token_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("mta_fused") or name in ("mta_device.h", "mta_internal.h"):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "fused_variant_T4096_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def gpu_inputs(cfg, torch):
+    inp = mta_inputs.make_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(inp[n]).to("cuda").to(dt).contiguous() for n in ("q", "k", "v")}
+    for n in ("theta", "w", "gamma", "beta"):
+        d[n] = torch.from_numpy(np.ascontiguousarray(inp[n], np.float32)).to("cuda")
+    d["lam"] = inp["lam"]
+    return inp, d
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Average ms per call, HIP events recorded on the current stream (the launch stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(cfg, inp, n_rows: int):
+    from oracle import oracle  # the CPU baseline leg is the only product-side user of the oracle
+
+    rng = np.random.default_rng(2024)
+    rows = np.sort(rng.choice(cfg.T, size=min(n_rows, cfg.T), replace=False)).astype(np.int32)
+    sl = {n: inp[n][:1] for n in ("q", "k", "v")}
+    sub = dict(inp, **sl)
+    c1 = cfg.replace(B=1)
+    t0 = time.perf_counter()
+    oracle.forward_cfg(c1, sub, rows=rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": len(rows) / dt,
+        "unit": "tokens/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} seeded random query rows of batch 0, all {cfg.M} heads, T={cfg.T} "
+                  f"(fp64 C++ oracle, OpenMP); {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-materialized", action="store_true")
+    ap.add_argument("--only-fused", action="store_true", help="time the fused kernel only (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(the layer shards by batch and head group without communication)"}))
+        sys.exit(2)
+
+    import torch
+    import token_attention_amd as ta
+
+    ta.lib()  # fail loudly if the HIP library is missing
+    cfg = mta_inputs.config(HEADLINE)
+    inp, d = gpu_inputs(cfg, torch)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    out = torch.empty_like(d["q"])
+
+    def fused():
+        ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out, **kw)
+
+    ms = time_launches(fused, args.steps, args.warmup, torch)
+    F = flops(cfg)
+    tokens = cfg.B * cfg.T
+    tflops = F / (ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v rounded to bf16; theta = delta + N(0,0.05); w = I + N(0,0.05))",
+        "config": {
+            "workload": "variant_bf16: B=2 T=4096 M=32 d=128 c_q=4 c_k=9 c_h=4, key-query conv after softmax, "
+                        "head mixing before softmax, GroupNorm + gate 1/sqrt(12)",
+            "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU",
+        },
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "flops_per_step": F,
+        "roofline": {
+            "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+        },
+    }
+    if not args.only_fused:
+        def plain():
+            ta.attention_plain(d["q"], d["k"], d["v"], out=out)
+        ms_plain = time_launches(plain, args.steps, args.warmup, torch)
+        dflt = cfg.replace(kq="pre", mix="post")
+        kw2 = dict(kw, kq="pre", mix="post")
+
+        def fused_default():
+            ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out,
+                       **kw2)
+        ms_dflt = time_launches(fused_default, args.steps, args.warmup, torch)
+        result["plain_attention"] = {
+            "ms": ms_plain, "tflops": cfg.B * cfg.M * (cfg.T * (cfg.T + 1) // 2) * 4 * cfg.d / (ms_plain * 1e-3) / 1e12,
+            "mta_slowdown": ms / ms_plain,
+        }
+        result["default_placement_same_shape"] = {
+            "ms": ms_dflt, "tokens_per_s": tokens / (ms_dflt * 1e-3),
+            "tflops": flops(dflt) / (ms_dflt * 1e-3) / 1e12,
+            "pct_bf16_peak": 100.0 * flops(dflt) / (ms_dflt * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "mta_slowdown_vs_plain": ms_dflt / ms_plain,
+        }
+        if not args.no_materialized:
+            ws = torch.empty(ta.materialized_workspace_bytes(cfg.B, cfg.T, cfg.M), dtype=torch.uint8, device="cuda")
+
+            def mat():
+                ta.forward_materialized(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"],
+                                        d["lam"], out=out, workspace=ws, **kw)
+            ms_mat = time_launches(mat, max(2, args.steps // 4), 1, torch)
+            mb = materialized_bytes(cfg)
+            result["materialized"] = {
+                "ms": ms_mat, "tokens_per_s": tokens / (ms_mat * 1e-3), "bytes": mb,
+                "gbs": mb / (ms_mat * 1e-3) / 1e9, "frac_hbm_peak": mb / (ms_mat * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "workspace_gib": ws.numel() / 2 ** 30, "fused_speedup": ms_mat / ms,
+            }
+            del ws
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                        "gcn_arch": getattr(props, "gcnArchName", "")}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

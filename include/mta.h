@@ -1,0 +1,135 @@
+/*
+ * libmta: Multi-Token Attention forward layer for AMD MI355X (gfx950).
+ *
+ * The layer is the one described on the page "Multi-Token Attention | Summary"
+ * (greeksharifa.github.io): per-head logits QK^T/sqrt(d) (§2), a key-query
+ * convolution over (query, key) with a separate c_q x c_k kernel per head, either
+ * before softmax with Mask_0 before it and Mask_-inf after it, or after softmax
+ * (§3.1), a head-mixing linear map inside groups of c_h heads, before or after
+ * softmax (§3.2), the AV product (§2), and a per-head GroupNorm followed by a
+ * scalar gate (§3.3).
+ *
+ * Conventions shared by every entry point
+ *   Layout      q, k, v, out: [B, T, M, d] contiguous (token-major, heads
+ *               concatenated, hidden size D = M*d). bf16 unless MTA_FP32 is set,
+ *               then fp32. out has the input dtype.
+ *   theta_kq    [M, c_q, c_k] fp32. theta[m][a][e] weighs the map entry at
+ *               (query i-a, key j-e+h0), h0 = (c_k-1)/2: the query axis reaches only
+ *               current and past rows (§3.1), the key axis is centred. Entries
+ *               outside the T x T map count as 0.
+ *   w_mix       [M/c_h, c_h, c_h] fp32, w[g][out][in] (§3.2 mixing equations);
+ *               group g holds heads g*c_h .. g*c_h+c_h-1.
+ *   GroupNorm   per (token, head) over the d channels, biased variance, eps 1e-5:
+ *               out = lambda * (gamma[m*d+t] * (O_t - mean) / sqrt(var + eps) +
+ *               beta[m*d+t]); gn_gamma, gn_beta are [M*d] fp32. lambda is the gate
+ *               value itself (already passed through its sigmoid or depth rule).
+ *   Placement   the key-query convolution is MTA_KQ_PRE or MTA_KQ_POST (or
+ *               absent); head mixing is MTA_MIX_PRE or MTA_MIX_POST (or absent).
+ *               When both act on the same side of softmax they are applied in
+ *               sequence: mixing before the convolution on the pre side, the
+ *               convolution before mixing on the post side.
+ *   Memory      every pointer is device memory owned by the caller. Nothing is
+ *               retained after a call returns; buffers must stay alive until the
+ *               queued work completes. q, k, v, out and workspace must be 16-byte
+ *               aligned.
+ *   Streams     stream is a hipStream_t (NULL = the default stream). Calls are
+ *               asynchronous: they validate, enqueue and return. Launch errors are
+ *               reported; faults during execution surface at the caller's sync.
+ *   Errors      functions return an mta_status; they never abort or throw. A
+ *               thread-local message with details is kept for mta_last_error().
+ *   Threads     reentrant; no global mutable state besides the per-thread message.
+ */
+#ifndef MTA_H
+#define MTA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mta_status {
+  MTA_OK = 0,
+  MTA_ERR_INVALID_ARG = 1, /* sizes <= 0, M % c_h != 0, NULL/misaligned pointers,
+                              conflicting placement flags                        */
+  MTA_ERR_UNSUPPORTED = 2, /* valid but not built: d, dtype, c_q > 8, even c_k,
+                              c_k > 17, c_h not in {1, 2, 4}                      */
+  MTA_ERR_HIP = 3,         /* the HIP runtime reported an error                   */
+  MTA_ERR_WORKSPACE = 4    /* workspace missing or smaller than required          */
+} mta_status;
+
+#define MTA_KQ_PRE 0x1u   /* key-query convolution before softmax (§3.1 equation)  */
+#define MTA_KQ_POST 0x2u  /* key-query convolution after softmax, then Mask_0     */
+#define MTA_MIX_PRE 0x4u  /* head mixing of the logits, before softmax (§3.2)     */
+#define MTA_MIX_POST 0x8u /* head mixing of the softmax weights (§3.2)            */
+#define MTA_GN 0x10u      /* per-head GroupNorm and scalar gate (§3.3)            */
+#define MTA_FP32 0x20u    /* q, k, v, out are fp32 instead of bf16                */
+
+/*
+ * mta_forward: fused forward of the whole layer (§2-§3.3) in one kernel launch.
+ * Flash-style: the T x T maps are never written to memory; each workgroup owns one
+ * head group and one tile of query rows and recomputes the logits of the c_q-1
+ * preceding rows and of the key halo it needs. Allocates nothing.
+ *   q, k, v      inputs [B,T,M,d]
+ *   theta_kq     required iff a KQ flag is set (ignored otherwise)
+ *   w_mix        required iff a MIX flag is set (ignored otherwise)
+ *   gn_gamma/beta, lambda   required iff MTA_GN (ignored otherwise)
+ *   out          [B,T,M,d] output; may not alias the inputs
+ *   c_q, c_k     kernel size; ignored without a KQ flag. 1 <= c_q <= 8, c_k odd <= 17
+ *   c_h          head-group size; M % c_h == 0; c_h in {1,2,4}; ignored without MIX
+ *   flags        MTA_* bits above
+ * Supported head sizes: d in {32, 64, 96, 128} for bf16, d in {16, 32, 64} for fp32.
+ */
+int mta_forward(const void* q, const void* k, const void* v, const float* theta_kq,
+                const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
+                void* out, int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags,
+                void* stream);
+
+/*
+ * mta_forward_materialized: the same layer as mta_forward computed the unfused way,
+ * one kernel per step, with full fp32 [B, M, T, T] maps in the caller's workspace
+ * (the memory-hungry implementation style whose cost the page's complexity table,
+ * Appendix F, attributes to MTA). Same arguments as mta_forward plus:
+ *   workspace        device buffer of at least mta_materialized_workspace_bytes()
+ *   workspace_bytes  its size
+ */
+int mta_forward_materialized(const void* q, const void* k, const void* v, const float* theta_kq,
+                             const float* w_mix, const float* gn_gamma, const float* gn_beta,
+                             float lambda, void* out, int B, int T, int M, int d, int c_q, int c_k,
+                             int c_h, unsigned flags, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace needed by mta_forward_materialized: two fp32 [B, M, T, T] maps. Returns 0
+ * for invalid sizes. */
+size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags);
+
+/*
+ * mta_attention_plain: standard causal softmax attention softmax(QK^T/sqrt(d))V
+ * (§2), computed by the same fused kernel with the convolution, mixing and
+ * GroupNorm switched off. flags: 0 or MTA_FP32. Allocates nothing.
+ */
+int mta_attention_plain(const void* q, const void* k, const void* v, void* out, int B, int T,
+                        int M, int d, unsigned flags, void* stream);
+
+/*
+ * mta_check_args: the validation mta_forward performs, without touching the GPU.
+ * Pointer arguments are checked for NULL/alignment only. Returns an mta_status.
+ */
+int mta_check_args(const void* q, const void* k, const void* v, const float* theta_kq,
+                   const float* w_mix, const float* gn_gamma, const float* gn_beta, const void* out,
+                   int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags);
+
+/* Static description of a status code. */
+const char* mta_status_string(int status);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* mta_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int mta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTA_H */

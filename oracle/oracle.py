@@ -25,7 +25,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with g++ (-O3, OpenMP) into ``oracle/libmta_oracle.so``."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        cmd = ["g++", "-O3", "-march=native", "-fopenmp", "-std=c++17", "-shared", "-fPIC",
+        cmd = ["g++", "-O3", "-march=x86-64-v3", "-fopenmp", "-std=c++17", "-shared", "-fPIC",
                "-Wall", "-Wextra", "-o", tmp, _SRC]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)

@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/mta.h
+declares, its flag values match the binding, and argument validation (host-only,
+``mta_check_args``) returns the documented status codes."""
+import os
+import re
+
+import pytest
+
+import token_attention_amd as ta
+from token_attention_amd import mta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mta.h")
+
+P = 0x10000  # a 16-byte aligned, never dereferenced pointer value
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mta_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ta.lib()
+    declared = _header_functions()
+    assert set(declared) == set(mta.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_flag_values_match_header():
+    text = open(HEADER).read()
+    for name in ("KQ_PRE", "KQ_POST", "MIX_PRE", "MIX_POST", "GN", "FP32"):
+        m = re.search(r"#define MTA_%s (0x[0-9a-f]+)u" % name, text)
+        assert m, name
+        assert int(m.group(1), 16) == getattr(mta, name), name
+    for name, val in (("MTA_OK", 0), ("MTA_ERR_INVALID_ARG", 1), ("MTA_ERR_UNSUPPORTED", 2),
+                      ("MTA_ERR_HIP", 3), ("MTA_ERR_WORKSPACE", 4)):
+        assert re.search(r"%s = %d" % (name, val), text), name
+
+
+def _check(**kw):
+    a = dict(q=P, k=P, v=P, theta=P, w=P, gamma=P, beta=P, out=P + 0x100, B=1, T=64, M=4, d=128, c_q=3,
+             c_k=5, c_h=2, flags=mta.KQ_PRE | mta.MIX_POST | mta.GN)
+    a.update(kw)
+    return mta.check_args(a["q"], a["k"], a["v"], a["theta"], a["w"], a["gamma"], a["beta"], a["out"], a["B"],
+                          a["T"], a["M"], a["d"], a["c_q"], a["c_k"], a["c_h"], a["flags"])
+
+
+def test_valid_arguments_pass():
+    assert _check() == mta.OK
+    assert _check(flags=mta.KQ_POST | mta.MIX_PRE | mta.GN, c_q=4, c_k=9, c_h=4) == mta.OK
+    assert _check(flags=0, theta=0, w=0, gamma=0, beta=0) == mta.OK  # plain attention
+    assert _check(flags=mta.FP32 | mta.KQ_PRE, d=16, w=0) == mta.OK
+    assert mta.last_error() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), mta.ERR_INVALID_ARG),
+    (dict(T=-1), mta.ERR_INVALID_ARG),
+    (dict(M=6, c_h=4), mta.ERR_INVALID_ARG),
+    (dict(q=0), mta.ERR_INVALID_ARG),
+    (dict(out=P + 8), mta.ERR_INVALID_ARG),               # misaligned
+    (dict(out=P), mta.ERR_INVALID_ARG),                   # aliases q
+    (dict(theta=0), mta.ERR_INVALID_ARG),                 # KQ flag without theta
+    (dict(w=0), mta.ERR_INVALID_ARG),                     # MIX flag without w
+    (dict(gamma=0), mta.ERR_INVALID_ARG),                 # GN without gamma
+    (dict(flags=mta.KQ_PRE | mta.KQ_POST), mta.ERR_INVALID_ARG),
+    (dict(flags=mta.MIX_PRE | mta.MIX_POST), mta.ERR_INVALID_ARG),
+    (dict(flags=0x400), mta.ERR_INVALID_ARG),
+    (dict(c_k=4), mta.ERR_UNSUPPORTED),                   # even key size
+    (dict(c_q=9), mta.ERR_UNSUPPORTED),
+    (dict(c_k=19), mta.ERR_UNSUPPORTED),
+    (dict(c_h=8, M=8), mta.ERR_UNSUPPORTED),
+    (dict(d=80), mta.ERR_UNSUPPORTED),
+    (dict(d=128, flags=mta.FP32), mta.ERR_UNSUPPORTED),
+    (dict(c_q=0), mta.ERR_INVALID_ARG),
+])
+def test_invalid_arguments_are_rejected(kw, status):
+    assert _check(**kw) == status
+    assert mta.last_error() != ""
+
+
+def test_ignored_arguments_without_flags():
+    # without a KQ flag, theta/c_q/c_k are ignored; without MIX, w/c_h are ignored
+    assert _check(flags=mta.GN, theta=0, w=0, c_q=0, c_k=4, c_h=3) == mta.OK
+
+
+def test_status_strings_and_version():
+    L = ta.lib()
+    for s in range(5):
+        assert L.mta_status_string(s).decode()
+    assert L.mta_status_string(99).decode() == "unknown status"
+    assert L.mta_version() >= 100
+
+
+def test_workspace_size():
+    assert ta.materialized_workspace_bytes(2, 64, 4) == 2 * 2 * 4 * 64 * 64 * 4
+    assert ta.materialized_workspace_bytes(0, 64, 4) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ta.attention_plain(q, q.clone(), q.clone())

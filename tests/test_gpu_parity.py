@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bars (per workload): fp32 tensors max |err| <= 1e-5; bf16 tensors max |err| <= 2e-2
+and mean |err| <= 2e-3 on the outputs. Both sides get the identical bf16-rounded
+inputs. Small cases are checked on every output; the full-size workloads on
+sampled rows (tile edges, both ends, seeded random rows), which the oracle
+computes one by one.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mta_inputs
+import token_attention_amd as ta
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": (1e-5, None), "bf16": (2e-2, 2e-3)}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_inputs(cfg, inp):
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(inp[n]).to("cuda").to(dt).contiguous() for n in ("q", "k", "v")}
+    for n in ("theta", "w", "gamma", "beta"):
+        d[n] = torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to("cuda")
+    return d
+
+
+def run(path, cfg, d, lam):
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    args = (d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], lam)
+    if path == "fused":
+        out = ta.forward(*args, **kw)
+    elif path == "materialized":
+        out = ta.forward_materialized(*args, **kw)
+    else:
+        raise ValueError(path)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def compare(cfg, got, want, rows=None, what=""):
+    if rows is not None:
+        got, want = got[:, rows], want[:, rows]
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    mx, mean = float(err.max()), float(err.mean())
+    log(f"  {what}: max|err| {mx:.3e}  mean|err| {mean:.3e}")
+    tmax, tmean = TOL[cfg.dtype]
+    assert mx <= tmax, f"{what}: max abs error {mx} > {tmax}"
+    if tmean is not None:
+        assert mean <= tmean, f"{what}: mean abs error {mean} > {tmean}"
+    return mx, mean
+
+
+@functools.lru_cache(maxsize=None)
+def case(cfg):
+    inp = mta_inputs.make_inputs(cfg)
+    return inp
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_full(cfg):
+    return oracle.forward_cfg(cfg, case(cfg))
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_rows(cfg):
+    rows = mta_inputs.sample_rows(cfg.T, row_tile=61, n_random=20)
+    rows = np.unique(np.concatenate([rows, mta_inputs.sample_rows(cfg.T, row_tile=59, n_random=0),
+                                     mta_inputs.sample_rows(cfg.T, row_tile=27, n_random=0)]))
+    return rows, oracle.forward_cfg(cfg, case(cfg), rows=rows)
+
+
+def small(cfg, **kw):
+    """The workload's placement and kernel sizes at a size the oracle finishes in full."""
+    base = dict(B=2, T=150, M=8 if cfg.M >= 8 else cfg.M)
+    base.update(kw)
+    return cfg.replace(name=cfg.name + "_small", **base)
+
+
+# ---- the five workloads -------------------------------------------------------------
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+def test_tiny_fp32_workload_full(path):
+    cfg = mta_inputs.config(0)
+    log(f"[{path}] {cfg}")
+    compare(cfg, run(path, cfg, dev_inputs(cfg, case(cfg)), case(cfg)["lam"]), oracle_full(cfg), what=path)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+def test_workload_small_full_check(idx, path):
+    cfg = small(mta_inputs.config(idx))
+    log(f"[{path}] {cfg}")
+    inp = case(cfg)
+    compare(cfg, run(path, cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=path)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+def test_workload_full_size_sampled_rows(idx, path):
+    cfg = mta_inputs.config(idx)
+    log(f"[{path}] full size {cfg}")
+    rows, want = oracle_rows(cfg)
+    inp = case(cfg)
+    got = run(path, cfg, dev_inputs(cfg, inp), inp["lam"])
+    compare(cfg, got, want, rows=rows, what=f"{path} rows={len(rows)}")
+    assert np.isfinite(got).all()
+
+
+def test_degenerate_kernels_equal_plain_attention():
+    # delta kernel + identity mixing + no GroupNorm must reproduce plain causal attention
+    cfg = mta_inputs.config(2)
+    inp = case(cfg)
+    d = dev_inputs(cfg, inp)
+    mtaout = ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h,
+                        kq=cfg.kq, mix=cfg.mix, gn=False)
+    plain = ta.attention_plain(d["q"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    a = mtaout.float().cpu().numpy()
+    b = plain.float().cpu().numpy()
+    err = np.abs(a - b)
+    log(f"  mta vs plain: max {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+# ---- plain attention -----------------------------------------------------------------
+@pytest.mark.parametrize("shape,dtype", [((2, 300, 4, 128), "bf16"), ((1, 77, 3, 64), "bf16"),
+                                         ((2, 129, 2, 96), "bf16"), ((1, 64, 4, 16), "fp32"),
+                                         ((1, 50, 2, 32), "fp32")])
+def test_plain_attention(shape, dtype):
+    B, T, M, d = shape
+    cfg = mta_inputs.MTAConfig("plain", B, T, M, d, 1, 1, 1, None, None, False, dtype, 0.0, 0.0, seed=7)
+    inp = case(cfg)
+    dv = dev_inputs(cfg, inp)
+    got = ta.attention_plain(dv["q"], dv["k"], dv["v"])
+    torch.cuda.synchronize()
+    compare(cfg, got.float().cpu().numpy().astype(np.float64), oracle_full(cfg), what="plain")
+
+
+# ---- placements, kernel sizes, head sizes, ragged lengths -------------------------------
+COMBOS = [("pre", "post"), ("post", "pre"), ("pre", None), ("post", None), (None, "post"), (None, "pre"),
+          ("pre", "pre"), ("post", "post"), (None, None)]
+
+
+@pytest.mark.parametrize("kq,mix", COMBOS)
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+def test_every_placement(kq, mix, path):
+    cfg = mta_inputs.MTAConfig("combo", 2, 97, 8, 64, 3, 7, 4, kq, mix, True, "bf16", 0.2, 0.3, 1.0, 0.0,
+                               0.9, seed=11)
+    inp = case(cfg)
+    compare(cfg, run(path, cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"{path} {kq}/{mix}")
+
+
+@pytest.mark.parametrize("c_q,c_k", [(1, 1), (1, 17), (8, 1), (8, 17), (2, 3), (5, 13)])
+@pytest.mark.parametrize("kq", ["pre", "post"])
+def test_kernel_sizes(c_q, c_k, kq):
+    mix = "post" if kq == "pre" else "pre"
+    cfg = mta_inputs.MTAConfig("ks", 1, 133, 4, 128, c_q, c_k, 2, kq, mix, True, "bf16", 0.2, 0.2, 1.0, 0.0,
+                               0.8, seed=12)
+    inp = case(cfg)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"{kq} {c_q}x{c_k}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 31, 64, 65, 200])
+@pytest.mark.parametrize("placement", [("pre", "post", 2), ("post", "pre", 4)])
+def test_ragged_lengths(T, placement):
+    kq, mix, c_h = placement
+    cfg = mta_inputs.MTAConfig("ragged", 2, T, 4, 32, 4, 9, c_h, kq, mix, True, "bf16", 0.2, 0.2, 1.0, 0.0,
+                               0.8, seed=13)
+    inp = case(cfg)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"T={T}")
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "bf16"), (64, "bf16"), (96, "bf16"), (16, "fp32"), (32, "fp32"),
+                                     (64, "fp32")])
+@pytest.mark.parametrize("placement", [("pre", "post", 2), ("post", "pre", 4), ("pre", "post", 4)])
+def test_head_sizes(d, dtype, placement):
+    kq, mix, c_h = placement
+    cfg = mta_inputs.MTAConfig("hs", 1, 90, 4, d, 3, 5, c_h, kq, mix, True, dtype, 0.1, 0.1, 1.0, 0.0, 0.8,
+                               seed=14)
+    inp = case(cfg)
+    for path in ("fused", "materialized"):
+        compare(cfg, run(path, cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"{path} d={d}")
+
+
+def test_groupnorm_affine_values():
+    cfg = mta_inputs.MTAConfig("gn", 1, 70, 4, 64, 3, 5, 2, "pre", "post", True, "bf16", 0.1, 0.1, seed=15)
+    inp = dict(case(cfg))
+    rng = np.random.default_rng(16)
+    inp["gamma"] = rng.standard_normal(cfg.M * cfg.d).astype(np.float32)
+    inp["beta"] = rng.standard_normal(cfg.M * cfg.d).astype(np.float32)
+    inp["lam"] = 0.37
+    want = oracle.forward_cfg(cfg, inp)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), want, what="gn affine")
+
+
+# ---- properties on the GPU path --------------------------------------------------------
+def test_deterministic():
+    cfg = small(mta_inputs.config(4), T=300)
+    d = dev_inputs(cfg, case(cfg))
+    a = run("fused", cfg, d, 0.3)
+    b = run("fused", cfg, d, 0.3)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("idx", [1, 4])
+def test_causal_under_future_perturbation(idx):
+    cfg = small(mta_inputs.config(idx), T=256)
+    inp = case(cfg)
+    d = dev_inputs(cfg, inp)
+    base = run("fused", cfg, d, inp["lam"])
+    cut = 100
+    for n in ("q", "k", "v"):
+        d[n][:, cut + 1:] = torch.randn_like(d[n][:, cut + 1:]) * 3
+    pert = run("fused", cfg, d, inp["lam"])
+    assert np.array_equal(pert[:, :cut + 1], base[:, :cut + 1])
+    assert np.abs(pert[:, cut + 1:] - base[:, cut + 1:]).max() > 1e-3
+
+
+def test_stream_argument():
+    cfg = small(mta_inputs.config(1), T=64)
+    inp = case(cfg)
+    d = dev_inputs(cfg, inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], inp["lam"],
+                         c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn, stream=s)
+    s.synchronize()
+    compare(cfg, out.float().cpu().numpy().astype(np.float64), oracle_full(cfg), what="side stream")
+
+
+def test_workspace_too_small_is_reported():
+    cfg = small(mta_inputs.config(1), T=64)
+    d = dev_inputs(cfg, case(cfg))
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ta.MTAError) as e:
+        ta.forward_materialized(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], 0.8,
+                                c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn,
+                                workspace=ws)
+    assert e.value.status == 4

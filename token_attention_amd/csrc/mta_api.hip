@@ -1,0 +1,169 @@
+// C ABI of libmta: argument validation, dispatch to the kernel files, error reporting.
+// Declarations and the contract of every entry point are in include/mta.h.
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mta.h"
+#include "mta_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MTA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr unsigned kKnownFlags = MTA_KQ_PRE | MTA_KQ_POST | MTA_MIX_PRE | MTA_MIX_POST | MTA_GN | MTA_FP32;
+
+// Validates the arguments and fills *pr. Host-only: never touches the GPU.
+int validate(const void* q, const void* k, const void* v, const float* theta, const float* w,
+             const float* gamma, const float* beta, float lambda, const void* out, int B, int T, int M,
+             int d, int c_q, int c_k, int c_h, unsigned flags, mta::Problem* pr) {
+  if (flags & ~kKnownFlags) return fail(MTA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+  if (B <= 0 || T <= 0 || M <= 0 || d <= 0)
+    return fail(MTA_ERR_INVALID_ARG, "sizes must be positive (B=%d T=%d M=%d d=%d)", B, T, M, d);
+  if ((flags & MTA_KQ_PRE) && (flags & MTA_KQ_POST))
+    return fail(MTA_ERR_INVALID_ARG, "MTA_KQ_PRE and MTA_KQ_POST are mutually exclusive");
+  if ((flags & MTA_MIX_PRE) && (flags & MTA_MIX_POST))
+    return fail(MTA_ERR_INVALID_ARG, "MTA_MIX_PRE and MTA_MIX_POST are mutually exclusive");
+  if (!q || !k || !v || !out) return fail(MTA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(MTA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  const bool kq = flags & (MTA_KQ_PRE | MTA_KQ_POST);
+  const bool mix = flags & (MTA_MIX_PRE | MTA_MIX_POST);
+  if (kq) {
+    if (!theta) return fail(MTA_ERR_INVALID_ARG, "theta_kq is required with a KQ flag");
+    if (c_q <= 0 || c_k <= 0) return fail(MTA_ERR_INVALID_ARG, "c_q and c_k must be positive (c_q=%d c_k=%d)", c_q, c_k);
+    if (c_k % 2 == 0) return fail(MTA_ERR_UNSUPPORTED, "c_k must be odd (centred key taps), got %d", c_k);
+    if (c_q > 8 || c_k > 17) return fail(MTA_ERR_UNSUPPORTED, "kernel %dx%d exceeds the supported 8x17", c_q, c_k);
+  }
+  if (mix) {
+    if (!w) return fail(MTA_ERR_INVALID_ARG, "w_mix is required with a MIX flag");
+    if (c_h <= 0 || M % c_h != 0) return fail(MTA_ERR_INVALID_ARG, "M=%d must be a multiple of c_h=%d", M, c_h);
+    if (c_h != 1 && c_h != 2 && c_h != 4) return fail(MTA_ERR_UNSUPPORTED, "c_h=%d not in {1, 2, 4}", c_h);
+  }
+  if ((flags & MTA_GN) && (!gamma || !beta))
+    return fail(MTA_ERR_INVALID_ARG, "gn_gamma and gn_beta are required with MTA_GN");
+  const bool fp32 = flags & MTA_FP32;
+  if (fp32 ? !(d == 16 || d == 32 || d == 64) : !(d == 32 || d == 64 || d == 96 || d == 128))
+    return fail(MTA_ERR_UNSUPPORTED, "head size d=%d is not built for %s", d, fp32 ? "fp32" : "bf16");
+  if ((long long)B * T * M * d > (1LL << 40)) return fail(MTA_ERR_INVALID_ARG, "tensor too large");
+  if (out == q || out == k || out == v) return fail(MTA_ERR_INVALID_ARG, "out may not alias an input");
+  mta::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.theta = kq ? theta : nullptr;
+  p.w = mix ? w : nullptr;
+  p.gamma = (flags & MTA_GN) ? gamma : nullptr;
+  p.beta = (flags & MTA_GN) ? beta : nullptr;
+  p.lambda = lambda;
+  p.out = const_cast<void*>(out);
+  p.B = B;
+  p.T = T;
+  p.M = M;
+  p.d = d;
+  p.c_q = kq ? c_q : 1;
+  p.c_k = kq ? c_k : 1;
+  p.c_h = mix ? c_h : 1;
+  p.kq = (flags & MTA_KQ_PRE) ? mta::KQ_PRE : (flags & MTA_KQ_POST) ? mta::KQ_POST : mta::KQ_NONE;
+  p.mix = (flags & MTA_MIX_PRE) ? mta::MIX_PRE : (flags & MTA_MIX_POST) ? mta::MIX_POST : mta::MIX_NONE;
+  p.gn = (flags & MTA_GN) ? 1 : 0;
+  p.fp32 = fp32 ? 1 : 0;
+  *pr = p;
+  return MTA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MTA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mta_check_args(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                   const float* gn_gamma, const float* gn_beta, const void* out, int B, int T, int M, int d,
+                   int c_q, int c_k, int c_h, unsigned flags) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, 1.0f, out, B, T, M, d, c_q, c_k, c_h,
+                          flags, &p);
+  return st == MTA_OK ? ok() : st;
+}
+
+int mta_forward(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                const float* gn_gamma, const float* gn_beta, float lambda, void* out, int B, int T, int M,
+                int d, int c_q, int c_k, int c_h, unsigned flags, void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, out, B, T, M, d, c_q, c_k, c_h,
+                          flags, &p);
+  if (st != MTA_OK) return st;
+  bool unsupported = false;
+  const hipError_t e = mta::launch_fused(p, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no fused kernel for this shape");
+  return hip_status(e, "mta_forward launch");
+}
+
+size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags) {
+  (void)flags;
+  return mta::materialized_workspace_bytes(B, T, M);
+}
+
+int mta_forward_materialized(const void* q, const void* k, const void* v, const float* theta_kq,
+                             const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
+                             void* out, int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, out, B, T, M, d, c_q, c_k, c_h,
+                          flags, &p);
+  if (st != MTA_OK) return st;
+  const size_t need = mta::materialized_workspace_bytes(B, T, M);
+  if (!workspace || workspace_bytes < need)
+    return fail(MTA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(MTA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!mta::materialized_supported(p)) return fail(MTA_ERR_UNSUPPORTED, "materialized path needs T %% 4 == 0");
+  bool unsupported = false;
+  const hipError_t e = mta::launch_materialized(p, workspace, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no materialized kernel for this shape");
+  return hip_status(e, "mta_forward_materialized launch");
+}
+
+int mta_attention_plain(const void* q, const void* k, const void* v, void* out, int B, int T, int M, int d,
+                        unsigned flags, void* stream) {
+  if (flags & ~MTA_FP32) return fail(MTA_ERR_INVALID_ARG, "mta_attention_plain accepts only MTA_FP32");
+  return mta_forward(q, k, v, nullptr, nullptr, nullptr, nullptr, 1.0f, out, B, T, M, d, 1, 1, 1, flags, stream);
+}
+
+const char* mta_status_string(int status) {
+  switch (status) {
+    case MTA_OK: return "ok";
+    case MTA_ERR_INVALID_ARG: return "invalid argument";
+    case MTA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MTA_ERR_HIP: return "HIP runtime error";
+    case MTA_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+const char* mta_last_error(void) { return g_last_error.c_str(); }
+
+int mta_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Fused forward: shape dispatch. The kernel template is in mta_fused_impl.h; each
+// (dtype, head size) pair is instantiated in its own translation unit.
+#include "mta_internal.h"
+
+namespace mta {
+
+hipError_t launch_fused_f32_d16(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_f32_d32(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_f32_d64(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d32(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d64(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d96(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d128(const Problem& p, hipStream_t stream);
+
+bool fused_supported(const Problem& p) {
+  const int ch = p.mix ? p.c_h : 1;
+  if (ch != 1 && ch != 2 && ch != 4) return false;
+  if (p.kq && (p.c_q < 1 || p.c_q > 8 || p.c_k < 1 || p.c_k > 17 || p.c_k % 2 == 0)) return false;
+  if (p.fp32) return p.d == 16 || p.d == 32 || p.d == 64;
+  return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
+}
+
+hipError_t launch_fused(const Problem& p, hipStream_t stream, bool* unsupported) {
+  *unsupported = false;
+  if (!fused_supported(p)) {
+    *unsupported = true;
+    return hipSuccess;
+  }
+  if (p.fp32) {
+    switch (p.d) {
+      case 16: return launch_fused_f32_d16(p, stream);
+      case 32: return launch_fused_f32_d32(p, stream);
+      case 64: return launch_fused_f32_d64(p, stream);
+    }
+  } else {
+    switch (p.d) {
+      case 32: return launch_fused_bf16_d32(p, stream);
+      case 64: return launch_fused_bf16_d64(p, stream);
+      case 96: return launch_fused_bf16_d96(p, stream);
+      case 128: return launch_fused_bf16_d128(p, stream);
+    }
+  }
+  *unsupported = true;
+  return hipSuccess;
+}
+
+}  // namespace mta

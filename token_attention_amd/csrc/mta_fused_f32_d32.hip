@@ -1,0 +1,8 @@
+// Fused kernel instantiations for f32 tensors with head size 32.
+#include "mta_fused_impl.h"
+
+namespace mta {
+hipError_t launch_fused_f32_d32(const Problem& p, hipStream_t stream) {
+  return fused::launch_d<float, 32>(p, stream);
+}
+}  // namespace mta

@@ -1,0 +1,42 @@
+// Internal interface between the C-ABI layer (mta_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mta {
+
+enum KqMode { KQ_NONE = 0, KQ_PRE = 1, KQ_POST = 2 };
+enum MixMode { MIX_NONE = 0, MIX_PRE = 1, MIX_POST = 2 };
+
+// A fully validated problem description (sizes already checked by the API layer).
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* theta;  // [M, c_q, c_k] or null
+  const float* w;      // [M/c_h, c_h, c_h] or null
+  const float* gamma;  // [M*d] or null
+  const float* beta;   // [M*d] or null
+  float lambda;
+  void* out;
+  int B, T, M, d, c_q, c_k, c_h;
+  int kq;    // KqMode
+  int mix;   // MixMode
+  int gn;    // 0/1
+  int fp32;  // 0: bf16 tensors, 1: fp32 tensors
+};
+
+// Returns hipSuccess or the launch error; sets *unsupported when no kernel is
+// instantiated for the shape.
+hipError_t launch_fused(const Problem& p, hipStream_t stream, bool* unsupported);
+bool fused_supported(const Problem& p);
+
+size_t materialized_workspace_bytes(int B, int T, int M);
+hipError_t launch_materialized(const Problem& p, void* workspace, hipStream_t stream,
+                               bool* unsupported);
+bool materialized_supported(const Problem& p);
+
+}  // namespace mta

@@ -1,0 +1,396 @@
+// Unfused Multi-Token Attention forward: one kernel per step, fp32 [B, M, T, T] maps
+// in HBM. This is the implementation style whose memory and runtime cost the page
+// "Multi-Token Attention | Summary" reports for MTA (Appendix F, complexity table);
+// it is kept as a comparison path for the fused kernel.
+//
+// Chain (X and Y are the two workspace maps; every map kernel touches all T x T
+// entries, writing the masked value above the diagonal):
+//   logits      X = Q K^T / sqrt(d)                                   (§2)
+//   [mix pre]   X_u <- sum_u' w[u][u'] X_u'  (in place)               (§3.2)
+//   [kq pre]    Y = Mask_-inf(Conv2d_theta(Mask_0(X)))                (§3.1)
+//   softmax     causal row softmax, in place, zeros above the diagonal (§2)
+//   [kq post]   Y = Mask_0(Conv2d_theta(A))                           (§3.1)
+//   [mix post]  in place                                              (§3.2)
+//   AV + GroupNorm + gate -> out                                      (§2, §3.3)
+// Map indices are 64-bit (a [16, 16384, 16384] map has 2^32 entries).
+#include "mta_device.h"
+#include "mta_internal.h"
+
+namespace mta {
+namespace {
+
+constexpr int MT_THREADS = 256;
+
+__device__ __forceinline__ size_t map_index(int bm, int T, int i, int j) {
+  return ((size_t)bm * T + i) * T + j;
+}
+
+// ---- logits: X[b,m,i,j] = q_i . k_j / sqrt(d) for a 64 x 64 tile --------------------
+template <typename T, int D>
+__global__ __launch_bounds__(MT_THREADS) void logits_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           float* __restrict__ X, int Tn, int M, float scale) {
+  typedef Mfma<T> MT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int bm = blockIdx.z, b = bm / M, m = bm % M;
+  const int i0 = blockIdx.y * 64 + wave * 16, j0 = blockIdx.x * 64;
+  const T* qb = q + (size_t)b * Tn * M * D;
+  const T* kb = k + (size_t)b * Tn * M * D;
+  constexpr int KQ = D / MT::K;
+  typename MT::frag qf[KQ];
+  const int qi = i0 + lr;
+#pragma unroll
+  for (int ks = 0; ks < KQ; ++ks)
+    qf[ks] = qi < Tn ? MT::load(qb + ((size_t)qi * M + m) * D + ks * MT::K + lg * MT::KPL) : MT::zero();
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int kj = j0 + cb * 16 + lr;
+    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KQ; ++ks) {
+      const typename MT::frag bf =
+          kj < Tn ? MT::load(kb + ((size_t)kj * M + m) * D + ks * MT::K + lg * MT::KPL) : MT::zero();
+      c = MT::mma(qf[ks], bf, c);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 4 * lg + r;
+      if (i < Tn && kj < Tn) X[map_index(bm, Tn, i, kj)] = c[r] * scale;
+    }
+  }
+}
+
+// ---- head mixing, in place: X_u <- sum_u' w[g][u][u'] X_u' ---------------------------
+template <int CH>
+__global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* __restrict__ X, const float* __restrict__ w,
+                                                        int Tn, int M, size_t n4_per_map) {
+  const int bg = blockIdx.y;  // b * (M/CH) + g
+  const int G = M / CH;
+  const int b = bg / G, g = bg % G;
+  float wl[CH][CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+#pragma unroll
+    for (int x = 0; x < CH; ++x) wl[u][x] = w[((size_t)g * CH + u) * CH + x];
+  float4* base = reinterpret_cast<float4*>(X) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
+  for (size_t e = (size_t)blockIdx.x * MT_THREADS + threadIdx.x; e < n4_per_map;
+       e += (size_t)gridDim.x * MT_THREADS) {
+    float4 in[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) in[u] = base[(size_t)u * n4_per_map + e];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int x = 0; x < CH; ++x) {
+        o.x += wl[u][x] * in[x].x;
+        o.y += wl[u][x] * in[x].y;
+        o.z += wl[u][x] * in[x].z;
+        o.w += wl[u][x] * in[x].w;
+      }
+      base[(size_t)u * n4_per_map + e] = o;
+    }
+  }
+}
+
+// ---- key-query convolution on a 64 x 64 output tile ----------------------------------
+// PRE:  input Mask_0(X) (zero for s > r and outside the map); output -inf for j > i.
+// POST: input A (already zero above the diagonal); output 0 for j > i (Mask_0).
+template <int CK, bool PRE>
+__global__ __launch_bounds__(MT_THREADS) void conv_kernel(const float* __restrict__ X, float* __restrict__ Y,
+                                                         const float* __restrict__ theta, int Tn, int M,
+                                                         int c_q) {
+  constexpr int H0 = (CK - 1) / 2;
+  constexpr int TW = 64 + CK - 1;  // input tile width
+  constexpr int LD = TW + 1;
+  __shared__ float tile[(64 + 7) * LD];
+  __shared__ float th[8 * CK];
+  const int bm = blockIdx.z, m = bm % M;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int rows = 64 + c_q - 1;
+  for (int x = threadIdx.x; x < c_q * CK; x += MT_THREADS) th[x] = theta[(size_t)m * c_q * CK + x];
+  for (int x = threadIdx.x; x < rows * TW; x += MT_THREADS) {
+    const int rr = x / TW, cc = x % TW;
+    const int r = i0 - (c_q - 1) + rr, s = j0 - H0 + cc;
+    float val = 0.0f;
+    if (r >= 0 && r < Tn && s >= 0 && s < Tn && (!PRE || s <= r)) val = X[map_index(bm, Tn, r, s)];
+    tile[rr * LD + cc] = val;
+  }
+  __syncthreads();
+  const int orow = threadIdx.x >> 2;         // 0..63
+  const int oc0 = (threadIdx.x & 3) * 16;    // 16 output columns
+  float acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = 0.0f;
+  for (int a = 0; a < c_q; ++a) {
+    // output (orow, oc0 + c) reads tile row orow + c_q - 1 - a, tile column oc0 + c - e + 2*H0
+    const float* src = tile + (orow + c_q - 1 - a) * LD + oc0;
+    float seg[16 + CK - 1];
+#pragma unroll
+    for (int x = 0; x < 16 + CK - 1; ++x) seg[x] = src[x];
+#pragma unroll
+    for (int e = 0; e < CK; ++e) {
+      const float t = th[a * CK + e];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[c] += t * seg[c - e + 2 * H0];
+    }
+  }
+  const int i = i0 + orow;
+  if (i < Tn) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int j = j0 + oc0 + c;
+      if (j < Tn) Y[map_index(bm, Tn, i, j)] = (j > i) ? (PRE ? -__builtin_inff() : 0.0f) : acc[c];
+    }
+  }
+}
+
+// ---- causal row softmax, in place; one workgroup per (b, m, i) row --------------------
+__global__ __launch_bounds__(MT_THREADS) void softmax_kernel(float* __restrict__ X, int Tn) {
+  __shared__ float red[MT_THREADS / 64];
+  const size_t row = blockIdx.x;  // (b*M + m)*T + i
+  const int i = (int)(row % Tn);
+  float* x = X + row * Tn;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float mx = -__builtin_inff();
+  for (int j = threadIdx.x; j <= i; j += MT_THREADS) mx = fmaxf(mx, x[j]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.0f;
+  for (int j = threadIdx.x; j <= i; j += MT_THREADS) sum += expf(x[j] - mx);
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  sum = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sum;
+  for (int j = threadIdx.x; j < Tn; j += MT_THREADS) x[j] = (j <= i) ? expf(x[j] - mx) * inv : 0.0f;
+}
+
+// ---- AV + GroupNorm + gate: 128 query rows x d of one (b, m) per workgroup ------------
+template <typename T, int D>
+__global__ __launch_bounds__(MT_THREADS) void av_kernel(const float* __restrict__ A, const T* __restrict__ v,
+                                                       T* __restrict__ out, const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta, float lambda, int gn,
+                                                       int Tn, int M) {
+  typedef Mfma<T> MT;
+  constexpr int BKA = 32;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int LDA = BKA + PAD;
+  constexpr int LDV = BKA + PAD;
+  constexpr int NB = D / 16;
+  constexpr int KV = BKA / MT::K;
+  __shared__ __attribute__((aligned(16))) T As[128 * LDA];
+  __shared__ __attribute__((aligned(16))) T Vt[D * LDV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int bm = blockIdx.y, b = bm / M, m = bm % M;
+  const int i0 = blockIdx.x * 128;
+  const T* vb = v + (size_t)b * Tn * M * D;
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < Tn; j0 += BKA) {
+    __syncthreads();
+    // A tile: 128 rows x 32 keys, fp32 -> T
+    for (int x = threadIdx.x; x < 128 * (BKA / 4); x += MT_THREADS) {
+      const int r = x / (BKA / 4), c4 = (x % (BKA / 4)) * 4;
+      const int i = i0 + r;
+      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < Tn) {
+        const float* src = A + map_index(bm, Tn, i, j0 + c4);
+        if (j0 + c4 + 3 < Tn) {
+          val = *reinterpret_cast<const float4*>(src);
+        } else {
+          float tmp[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int e = 0; e < 4; ++e)
+            if (j0 + c4 + e < Tn) tmp[e] = src[e];
+          val = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        }
+      }
+      T* dst = As + r * LDA + c4;
+      dst[0] = T(val.x);
+      dst[1] = T(val.y);
+      dst[2] = T(val.z);
+      dst[3] = T(val.w);
+    }
+    // V^T tile: Vt[c][kk] = V[j0 + kk][c], read in 16-byte chunks of one key row
+    constexpr int EPC = 16 / (int)sizeof(T);
+    for (int x = threadIdx.x; x < BKA * (D / EPC); x += MT_THREADS) {
+      const int kk = x % BKA, c0 = (x / BKA) * EPC;
+      const int j = j0 + kk;
+      T vals[EPC];
+      if (j < Tn) {
+        *reinterpret_cast<uint4*>(vals) = *reinterpret_cast<const uint4*>(vb + ((size_t)j * M + m) * D + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vals[e] = T(0.0f);
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) Vt[(c0 + e) * LDV + kk] = vals[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kv = 0; kv < KV; ++kv)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const typename MT::frag af = MT::load(As + (wave * 32 + rb * 16 + lr) * LDA + kv * MT::K + lg * MT::KPL);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const typename MT::frag bf = MT::load(Vt + (nb * 16 + lr) * LDV + kv * MT::K + lg * MT::KPL);
+          acc[rb][nb] = MT::mma(af, bf, acc[rb][nb]);
+        }
+      }
+  }
+  T* ob = out + (size_t)b * Tn * M * D;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + wave * 32 + rb * 16 + 4 * lg + r;
+      float mean = 0.0f, inv = 1.0f;
+      if (gn) {
+        float s = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s += acc[rb][nb][r];
+        mean = row16_sum(s) * (1.0f / D);
+        float sq = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float dv = acc[rb][nb][r] - mean;
+          sq += dv * dv;
+        }
+        inv = 1.0f / sqrtf(row16_sum(sq) * (1.0f / D) + 1e-5f);
+      }
+      if (i < Tn) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int c = nb * 16 + lr;
+          float y = acc[rb][nb][r];
+          if (gn) y = lambda * (gamma[(size_t)m * D + c] * (y - mean) * inv + beta[(size_t)m * D + c]);
+          ob[((size_t)i * M + m) * D + c] = T(y);
+        }
+      }
+    }
+}
+
+template <int CK>
+hipError_t launch_conv_ck(bool pre, const float* X, float* Y, const Problem& p, hipStream_t st) {
+  const dim3 grid((p.T + 63) / 64, (p.T + 63) / 64, p.B * p.M);
+  if (pre)
+    hipLaunchKernelGGL((conv_kernel<CK, true>), grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q);
+  else
+    hipLaunchKernelGGL((conv_kernel<CK, false>), grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hipStream_t st) {
+  switch (p.c_k) {
+    case 1: return launch_conv_ck<1>(pre, X, Y, p, st);
+    case 3: return launch_conv_ck<3>(pre, X, Y, p, st);
+    case 5: return launch_conv_ck<5>(pre, X, Y, p, st);
+    case 7: return launch_conv_ck<7>(pre, X, Y, p, st);
+    case 9: return launch_conv_ck<9>(pre, X, Y, p, st);
+    case 11: return launch_conv_ck<11>(pre, X, Y, p, st);
+    case 13: return launch_conv_ck<13>(pre, X, Y, p, st);
+    case 15: return launch_conv_ck<15>(pre, X, Y, p, st);
+    case 17: return launch_conv_ck<17>(pre, X, Y, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mix(float* X, const Problem& p, hipStream_t st) {
+  const size_t n4 = (size_t)p.T * p.T / 4;
+  const int G = p.M / p.c_h;
+  size_t want = (n4 + MT_THREADS - 1) / MT_THREADS;
+  const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
+  const dim3 grid(gx, p.B * G);
+  switch (p.c_h) {
+    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, p.w, p.T, p.M, n4); break;
+    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, p.w, p.T, p.M, n4); break;
+    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, p.w, p.T, p.M, n4); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
+  const T* q = reinterpret_cast<const T*>(p.q);
+  const T* k = reinterpret_cast<const T*>(p.k);
+  const T* v = reinterpret_cast<const T*>(p.v);
+  T* out = reinterpret_cast<T*>(p.out);
+  hipError_t e;
+  const float scale = (float)(1.0 / __builtin_sqrt((double)p.d));
+  hipLaunchKernelGGL((logits_kernel<T, D>), dim3((p.T + 63) / 64, (p.T + 63) / 64, p.B * p.M), dim3(MT_THREADS),
+                     0, st, q, k, X, p.T, p.M, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  float* cur = X;
+  float* other = Y;
+  if (p.mix == MIX_PRE && (e = launch_mix(cur, p, st)) != hipSuccess) return e;
+  if (p.kq == KQ_PRE) {
+    if ((e = launch_conv(true, cur, other, p, st)) != hipSuccess) return e;
+    float* t = cur;
+    cur = other;
+    other = t;
+  }
+  hipLaunchKernelGGL(softmax_kernel, dim3((unsigned)((size_t)p.B * p.M * p.T)), dim3(MT_THREADS), 0, st, cur, p.T);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.kq == KQ_POST) {
+    if ((e = launch_conv(false, cur, other, p, st)) != hipSuccess) return e;
+    float* t = cur;
+    cur = other;
+    other = t;
+  }
+  if (p.mix == MIX_POST && (e = launch_mix(cur, p, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((av_kernel<T, D>), dim3((p.T + 127) / 128, p.B * p.M), dim3(MT_THREADS), 0, st, cur, v, out,
+                     p.gamma, p.beta, p.lambda, p.gn, p.T, p.M);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t materialized_workspace_bytes(int B, int T, int M) {
+  if (B <= 0 || T <= 0 || M <= 0) return 0;
+  return 2 * (size_t)B * M * T * T * sizeof(float);
+}
+
+bool materialized_supported(const Problem& p) {
+  if (p.mix && !(p.c_h == 1 || p.c_h == 2 || p.c_h == 4)) return false;
+  if (p.kq && (p.c_q < 1 || p.c_q > 8 || p.c_k < 1 || p.c_k > 17 || p.c_k % 2 == 0)) return false;
+  if (p.T % 4 != 0) return false;  // float4 streaming of map rows
+  if (p.fp32) return p.d == 16 || p.d == 32 || p.d == 64;
+  return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
+}
+
+hipError_t launch_materialized(const Problem& p, void* workspace, hipStream_t st, bool* unsupported) {
+  *unsupported = false;
+  if (!materialized_supported(p)) {
+    *unsupported = true;
+    return hipSuccess;
+  }
+  float* X = reinterpret_cast<float*>(workspace);
+  float* Y = X + (size_t)p.B * p.M * p.T * p.T;
+  if (p.fp32) {
+    switch (p.d) {
+      case 16: return run_chain<float, 16>(p, X, Y, st);
+      case 32: return run_chain<float, 32>(p, X, Y, st);
+      case 64: return run_chain<float, 64>(p, X, Y, st);
+    }
+  } else {
+    switch (p.d) {
+      case 32: return run_chain<__bf16, 32>(p, X, Y, st);
+      case 64: return run_chain<__bf16, 64>(p, X, Y, st);
+      case 96: return run_chain<__bf16, 96>(p, X, Y, st);
+      case 128: return run_chain<__bf16, 128>(p, X, Y, st);
+    }
+  }
+  *unsupported = true;
+  return hipSuccess;
+}
+
+}  // namespace mta

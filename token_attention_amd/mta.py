@@ -1,0 +1,177 @@
+"""ctypes binding of libmta (argument marshalling only).
+
+Every function forwards torch device tensors to the C ABI declared in
+``include/mta.h``; all arithmetic runs in the library's HIP kernels. There is no
+CPU fallback: a missing library or a CPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmta.so")
+
+# flag bits, identical to include/mta.h
+KQ_PRE = 0x1
+KQ_POST = 0x2
+MIX_PRE = 0x4
+MIX_POST = 0x8
+GN = 0x10
+FP32 = 0x20
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
+
+EXPORTED = [
+    "mta_forward", "mta_forward_materialized", "mta_materialized_workspace_bytes",
+    "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
+]
+
+_lib = None
+
+
+class MTAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libmta status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmta.so (built by ``token_attention_amd.build``); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing; run `python -m token_attention_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, fp, i, u = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
+        L.mta_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 7 + [u, vp]
+        L.mta_forward.restype = i
+        L.mta_forward_materialized.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 7 + \
+            [u, vp, ctypes.c_size_t, vp]
+        L.mta_forward_materialized.restype = i
+        L.mta_materialized_workspace_bytes.argtypes = [i, i, i, u]
+        L.mta_materialized_workspace_bytes.restype = ctypes.c_size_t
+        L.mta_attention_plain.argtypes = [vp, vp, vp, vp, i, i, i, i, u, vp]
+        L.mta_attention_plain.restype = i
+        L.mta_check_args.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [u]
+        L.mta_check_args.restype = i
+        L.mta_status_string.argtypes = [i]
+        L.mta_status_string.restype = ctypes.c_char_p
+        L.mta_last_error.argtypes = []
+        L.mta_last_error.restype = ctypes.c_char_p
+        L.mta_version.argtypes = []
+        L.mta_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        msg = lib().mta_last_error().decode() or lib().mta_status_string(status).decode()
+        raise MTAError(status, msg)
+
+
+def placement_flags(kq: Optional[str], mix: Optional[str], gn: bool, fp32: bool) -> int:
+    f = {None: 0, "pre": KQ_PRE, "post": KQ_POST}[kq]
+    f |= {None: 0, "pre": MIX_PRE, "post": MIX_POST}[mix]
+    if gn:
+        f |= GN
+    if fp32:
+        f |= FP32
+    return f
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _common(q, k, v, out):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, M, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("tensors must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    return out
+
+
+def forward(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, c_q: int = 1,
+            c_k: int = 1, c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None,
+            gn: bool = False, out=None, stream=None) -> torch.Tensor:
+    """Fused forward (``mta_forward``). q, k, v: [B, T, M, d] bf16 or fp32 on the GPU."""
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
+    _check(lib().mta_forward(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, fl, _stream(stream)))
+    return out
+
+
+def materialized_workspace_bytes(B: int, T: int, M: int) -> int:
+    return int(lib().mta_materialized_workspace_bytes(B, T, M, 0))
+
+
+def forward_materialized(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *,
+                         c_q: int = 1, c_k: int = 1, c_h: int = 1, kq: Optional[str] = None,
+                         mix: Optional[str] = None, gn: bool = False, out=None, workspace=None,
+                         stream=None) -> torch.Tensor:
+    """Unfused forward (``mta_forward_materialized``) with fp32 T x T maps in ``workspace``."""
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    need = materialized_workspace_bytes(B, T, M)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
+    _check(lib().mta_forward_materialized(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, fl, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attention_plain(q, k, v, *, out=None, stream=None) -> torch.Tensor:
+    """Plain causal attention (``mta_attention_plain``)."""
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    fl = FP32 if q.dtype == torch.float32 else 0
+    _check(lib().mta_attention_plain(_dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+                                     _dev(out, "out"), B, T, M, d, fl, _stream(stream)))
+    return out
+
+
+def check_args(q_ptr, k_ptr, v_ptr, theta_ptr, w_ptr, gamma_ptr, beta_ptr, out_ptr, B, T, M, d, c_q, c_k,
+               c_h, flags) -> int:
+    """Host-only validation (``mta_check_args``) on raw pointer values; returns the status."""
+    return int(lib().mta_check_args(q_ptr, k_ptr, v_ptr, theta_ptr, w_ptr, gamma_ptr, beta_ptr, out_ptr,
+                                    B, T, M, d, c_q, c_k, c_h, flags))
+
+
+def last_error() -> str:
+    return lib().mta_last_error().decode()
