@@ -99,8 +99,8 @@ int mta_forward_materialized(const void* q, const void* k, const void* v, const 
                              int c_h, unsigned flags, void* workspace, size_t workspace_bytes,
                              void* stream);
 
-/* Workspace needed by mta_forward_materialized: two fp32 [B, M, T, T] maps. Returns 0
- * for invalid sizes. */
+/* Workspace needed by mta_forward_materialized: two fp32 [B, M, T, LD] maps, LD = T
+ * rounded up to a multiple of 4. Returns 0 for invalid sizes. */
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags);
 
 /*

@@ -97,6 +97,7 @@ def test_status_strings_and_version():
 
 def test_workspace_size():
     assert ta.materialized_workspace_bytes(2, 64, 4) == 2 * 2 * 4 * 64 * 64 * 4
+    assert ta.materialized_workspace_bytes(1, 65, 2) == 2 * 1 * 2 * 65 * 68 * 4
     assert ta.materialized_workspace_bytes(0, 64, 4) == 0
 
 

@@ -23,8 +23,8 @@ TOL = {"fp32": (1e-5, None), "bf16": (2e-2, 2e-3)}
 
 
 def log(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+    sys.__stdout__.write(msg + "\n")
+    sys.__stdout__.flush()
 
 
 def dev_inputs(cfg, inp):

@@ -138,7 +138,6 @@ int mta_forward_materialized(const void* q, const void* k, const void* v, const 
   if (!workspace || workspace_bytes < need)
     return fail(MTA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   if (!aligned16(workspace)) return fail(MTA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (!mta::materialized_supported(p)) return fail(MTA_ERR_UNSUPPORTED, "materialized path needs T %% 4 == 0");
   bool unsupported = false;
   const hipError_t e = mta::launch_materialized(p, workspace, reinterpret_cast<hipStream_t>(stream), &unsupported);
   if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no materialized kernel for this shape");

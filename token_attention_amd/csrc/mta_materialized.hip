@@ -12,7 +12,8 @@
 //   [kq post]   Y = Mask_0(Conv2d_theta(A))                           (§3.1)
 //   [mix post]  in place                                              (§3.2)
 //   AV + GroupNorm + gate -> out                                      (§2, §3.3)
-// Map indices are 64-bit (a [16, 16384, 16384] map has 2^32 entries).
+// Map indices are 64-bit (a [16, 16384, 16384] map has 2^32 entries). Map rows are
+// padded to a multiple of 4 floats (LD = T rounded up) so that rows stream as float4.
 #include "mta_device.h"
 #include "mta_internal.h"
 
@@ -21,8 +22,10 @@ namespace {
 
 constexpr int MT_THREADS = 256;
 
+__host__ __device__ __forceinline__ int map_ld(int T) { return (T + 3) & ~3; }
+
 __device__ __forceinline__ size_t map_index(int bm, int T, int i, int j) {
-  return ((size_t)bm * T + i) * T + j;
+  return ((size_t)bm * T + i) * map_ld(T) + j;
 }
 
 // ---- logits: X[b,m,i,j] = q_i . k_j / sqrt(d) for a 64 x 64 tile --------------------
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(MT_THREADS) void softmax_kernel(float* __restrict__
   __shared__ float red[MT_THREADS / 64];
   const size_t row = blockIdx.x;  // (b*M + m)*T + i
   const int i = (int)(row % Tn);
-  float* x = X + row * Tn;
+  float* x = X + row * map_ld(Tn);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float mx = -__builtin_inff();
   for (int j = threadIdx.x; j <= i; j += MT_THREADS) mx = fmaxf(mx, x[j]);
@@ -304,7 +307,7 @@ hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hip
 }
 
 hipError_t launch_mix(float* X, const Problem& p, hipStream_t st) {
-  const size_t n4 = (size_t)p.T * p.T / 4;
+  const size_t n4 = (size_t)p.T * map_ld(p.T) / 4;  // whole padded map, padding included
   const int G = p.M / p.c_h;
   size_t want = (n4 + MT_THREADS - 1) / MT_THREADS;
   const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
@@ -356,13 +359,12 @@ hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
 
 size_t materialized_workspace_bytes(int B, int T, int M) {
   if (B <= 0 || T <= 0 || M <= 0) return 0;
-  return 2 * (size_t)B * M * T * T * sizeof(float);
+  return 2 * (size_t)B * M * T * map_ld(T) * sizeof(float);
 }
 
 bool materialized_supported(const Problem& p) {
   if (p.mix && !(p.c_h == 1 || p.c_h == 2 || p.c_h == 4)) return false;
   if (p.kq && (p.c_q < 1 || p.c_q > 8 || p.c_k < 1 || p.c_k > 17 || p.c_k % 2 == 0)) return false;
-  if (p.T % 4 != 0) return false;  // float4 streaming of map rows
   if (p.fp32) return p.d == 16 || p.d == 32 || p.d == 64;
   return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
 }
@@ -374,7 +376,7 @@ hipError_t launch_materialized(const Problem& p, void* workspace, hipStream_t st
     return hipSuccess;
   }
   float* X = reinterpret_cast<float*>(workspace);
-  float* Y = X + (size_t)p.B * p.M * p.T * p.T;
+  float* Y = X + (size_t)p.B * p.M * p.T * map_ld(p.T);
   if (p.fp32) {
     switch (p.d) {
       case 16: return run_chain<float, 16>(p, X, Y, st);
