@@ -1,8 +1,8 @@
-// Fused kernel instantiations for bf16 tensors with head size 128.
-#include "mta_fused_impl.h"
+// Fused kernel instantiations for bf16 tensors with head size 128 (key-major schedule).
+#include "mta_kmajor_impl.h"
 
 namespace mta {
 hipError_t launch_fused_bf16_d128(const Problem& p, hipStream_t stream) {
-  return fused::launch_d<__bf16, 128>(p, stream);
+  return kmajor::launch_d<128>(p, stream);
 }
 }  // namespace mta

@@ -1,8 +1,8 @@
-// Fused kernel instantiations for bf16 tensors with head size 32.
-#include "mta_fused_impl.h"
+// Fused kernel instantiations for bf16 tensors with head size 32 (key-major schedule).
+#include "mta_kmajor_impl.h"
 
 namespace mta {
 hipError_t launch_fused_bf16_d32(const Problem& p, hipStream_t stream) {
-  return fused::launch_d<__bf16, 32>(p, stream);
+  return kmajor::launch_d<32>(p, stream);
 }
 }  // namespace mta

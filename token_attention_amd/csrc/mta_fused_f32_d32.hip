@@ -1,4 +1,4 @@
-// Fused kernel instantiations for f32 tensors with head size 32.
+// Fused kernel instantiations for fp32 tensors with head size 32 (row-major schedule).
 #include "mta_fused_impl.h"
 
 namespace mta {
