@@ -62,7 +62,7 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_attention_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("mta_fused") or name in ("mta_device.h", "mta_internal.h"):
+        if name.startswith(("mta_fused", "mta_kmajor")) or name in ("mta_device.h", "mta_internal.h"):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
     ap.add_argument("--only-fused", action="store_true", help="time the fused kernel only (profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -145,6 +147,16 @@ def main():
 
     import torch
     import token_attention_amd as ta
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
 
     ta.lib()  # fail loudly if the HIP library is missing
     cfg = mta_inputs.config(HEADLINE)

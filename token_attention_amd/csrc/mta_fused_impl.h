@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int hu = wave / C::WPH;  // head (within the group) owned by this wave
   const int ws = wave % C::WPH;  // row slab of this wave
   const int lr = lane & 15;      // D layout: column

@@ -7,10 +7,11 @@
 // Orientation. Every logit tile is computed transposed, S^T = K Q^T (keys are the MFMA
 // rows, queries the columns), so that in the 16x16 accumulator layout a lane owns one
 // query and four consecutive keys. Consequences:
-//   * softmax statistics of a query are reduced in-lane plus two cross-lane steps;
+//   * softmax statistics of a query reduce in-lane plus two cross-row exchanges
+//     (v_permlane16_swap / v_permlane32_swap), no LDS traffic;
 //   * the weights P^T feed the AV product O^T = V^T P^T directly as the B operand from
-//     registers (no LDS round trip): the eight k-slots of lane group g are keys
-//     {4g..4g+3} of one 16-key block and {16+4g..16+4g+3} of the next;
+//     registers: the eight k-slots of lane group g are keys {4g..4g+3} of one 16-key
+//     block and {16+4g..16+4g+3} of the next;
 //   * V stays row-major in LDS; its transposed A operand (same k-slot permutation) is
 //     read with ds_read_b64_tr_b16, which transposes a 4 x 16 block of b16 values
 //     within each 16-lane group.
@@ -18,14 +19,15 @@
 // Work split. One workgroup (4 waves) owns batch b, head group g (c_h heads) and a tile
 // of R query rows; tile row t is global row i0 - (c_q - 1) + t (the first c_q - 1 rows
 // are the query halo of the convolution). Wave w owns head hu = w / (4/c_h) and a slab
-// of QW rows.
+// of QW rows. When a wave owns all rows of its head (c_h = 4) it stages that head's K
+// and V tiles itself and nothing but the mixing exchange needs a workgroup barrier.
 //
-// Key tiles of BK keys stream through LDS. While a tile is being computed the next
-// one is already loading into registers (global -> VGPR prefetch), written to LDS
-// after the tile. With a convolution the logits of a tile cover keys
-// [j0 - 8, j0 + BK + 8): 16-key blocks 0..BK/16, where block 0 equals the last block
-// of the previous tile, so each tile computes only BK new key columns (sliding key
-// halo); the convolution input lives in an LDS ring of BK/16 + 1 blocks per row.
+// Key tiles of BK keys stream through LDS; the next tile is loaded into registers
+// while the current one is computed (global -> VGPR prefetch) and written to LDS
+// afterwards. With a convolution the logits of a tile cover keys [j0 - 8, j0 + BK + 8):
+// 16-key blocks 0..BK/16, where block 0 equals the last block of the previous tile, so
+// each tile computes only BK new key columns (sliding key halo); the convolution
+// input lives in an LDS ring of BK/16 + 1 blocks per row.
 //
 // The c_q x c_k convolution runs on fp16 MFMA: output keys of one 16-key block read a
 // 32-key window (blocks ob, ob+1); for each query lag a the banded Toeplitz matrix of
@@ -33,13 +35,22 @@
 // query rows is the B operand.
 //
 // Schedules:
-//   one pass  (no convolution, or convolution before softmax): online softmax. With
-//             mixing after softmax each wave exchanges its weights through LDS and keeps
-//             c_h accumulators Acc[u'] = sum_j exp(s_u' - m_u') V_hu, rescaled with
-//             head u''s running max; epilogue O = sum_u' w[hu][u'] Acc[u'] / l_u'.
-//   two phase (convolution after softmax): phase 1 exact (max, sum) per row, phase 2
-//             exact weights -> convolution -> Mask_0 -> AV.
-// Mixing before softmax exchanges the scaled logits of the new key blocks through LDS.
+//   one pass  (no convolution, or convolution before softmax): every query row keeps one
+//             fixed reference, the maximum of its first key tile, and its weights
+//             exp2(x - ref) are never rescaled, so the accumulators see MFMA only. If a row's
+//             sum exceeds 2^64 (a later key far above the first tile's maximum) the
+//             workgroup repeats the loop: one pass for the exact row maxima, one weighted
+//             pass with them as references. With mixing after softmax the waves exchange
+//             their weights through LDS and keep c_h accumulators
+//             Acc[u'] = sum_j exp2(s_u' - ref_u') V_hu; epilogue O = sum_u' w[hu][u'] Acc[u'] / l_u'.
+//   two phase (convolution after softmax): phase 1 the row sums (fixed reference as above,
+//             an exact online pass if a sum exceeds 2^64), phase 2 exact weights ->
+//             convolution -> Mask_0 -> AV.
+// Mixing before softmax exchanges the logits of the new key blocks through LDS (fp16;
+// a wave's own head stays fp32).
+//
+// K and V tiles are loaded with buffer loads whose range ends at the last key row, so rows
+// past the sequence read as zero (they are masked) without per-row clamping.
 #pragma once
 
 #include "mta_device.h"
@@ -50,11 +61,12 @@ namespace kmajor {
 
 constexpr int NW = 4;
 constexpr int NT = 64 * NW;
-constexpr int CQ_MAX = 8;
-constexpr int ZPRE = 8;  // zero rows above the tile in the convolution input ring
+constexpr int ZPRE = 8;               // zero rows above the tile in the convolution input ring
+constexpr float SUM_LIMIT = 0x1p64f;  // largest row sum accepted with a fixed reference
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 struct Args {
   const __bf16* q;
@@ -68,7 +80,7 @@ struct Args {
   __bf16* out;
   int B, T, M;
   int c_q, c_k;
-  int kq, mix, gn;
+  int mix, gn;
   int r_out;
   int n_tiles;
   int n_groups;
@@ -76,47 +88,47 @@ struct Args {
   int xcd_remap;
 };
 
-template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool PAIRS_>
+template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool PAIRS_, int CQM_, bool MIXPRE_>
 struct Cfg {
-  static constexpr int D = D_, CH = CH_, QW = QW_, BK = BK_;
-  static constexpr bool KQ = KQ_, TWO = TWO_, PAIRS = PAIRS_;
-  static constexpr int WPH = NW / CH;        // waves per head
-  static constexpr int R = QW * WPH;         // tile rows
-  static constexpr int NQB = QW / 16;        // query blocks per wave
-  static constexpr int NKB = BK / 16;        // new key blocks per tile
+  static constexpr int D = D_, CH = CH_, QW = QW_, BK = BK_, CQM = CQM_;
+  static constexpr bool KQ = KQ_, TWO = TWO_, PAIRS = PAIRS_, MIXPRE = MIXPRE_;
+  static constexpr int WPH = NW / CH;          // waves per head
+  static constexpr bool PRIV = WPH == 1;       // a wave owns its head: private K/V staging
+  static constexpr int TEAM = PRIV ? 64 : NT;  // threads staging one head set
+  static constexpr int R = QW * WPH;           // tile rows
+  static constexpr int NQB = QW / 16;          // query blocks per wave
+  static constexpr int NKB = BK / 16;          // new key blocks per tile
   static constexpr int LB = KQ ? NKB + 1 : NKB;  // logit blocks per tile (with the carried halo)
-  static constexpr int KS = D / 32;          // k-steps of QK^T
-  static constexpr int NB = D / 16;          // channel blocks
-  static constexpr int NC = BK / 32;         // 32-key chunks of AV
+  static constexpr int KS = D / 32;            // k-steps of QK^T
+  static constexpr int NB = D / 16;            // channel blocks
+  static constexpr int NC = BK / 32;           // 32-key chunks of AV
   static constexpr int NP = PAIRS ? CH : 1;
   static constexpr int KROWS = KQ ? BK + 16 : BK;  // K rows in LDS
-  static constexpr int LDK = D + 8;          // K row stride (bf16): 16-byte reads conflict-free
-  static constexpr int LDV = D + 16;         // V row stride (bf16): transposed reads conflict-free
-  static constexpr int ZW = LB * 16;         // ring width (keys)
-  static constexpr int LDZ = ZW + 8;         // fp16 stride
+  static constexpr int LDK = D + 8;            // K row stride (bf16): 16-byte reads conflict-free
+  static constexpr int LDV = D + 16;           // V row stride (bf16): transposed reads conflict-free
+  static constexpr int ZW = LB * 16;           // ring width (keys)
+  static constexpr int LDZ = ZW + 8;           // fp16 stride
   static constexpr int ZROWS = ZPRE + R;
-  static constexpr int LDX = LB * 16 + 4;    // fp32 mixing exchange stride
+  static constexpr int LDX = LB * 16 + 8;      // fp16 mixing exchange stride
   static constexpr size_t KS_BYTES = (size_t)CH * KROWS * LDK * 2;
-  static constexpr size_t SX_BYTES = (size_t)CH * R * LDX * 4;
-  static constexpr size_t U_BYTES = KS_BYTES > SX_BYTES ? KS_BYTES : SX_BYTES;
+  static constexpr size_t SX_BYTES = MIXPRE ? (size_t)CH * R * LDX * 2 : 0;
   static constexpr size_t VS_BYTES = (size_t)CH * BK * LDV * 2;
   static constexpr size_t ZB_BYTES = KQ ? (size_t)CH * ZROWS * LDZ * 2 : 0;
-  static constexpr size_t PB_BYTES = PAIRS ? (size_t)CH * WPH * NQB * NC * 64 * 16 : 0;
-  static constexpr size_t ST_BYTES = (size_t)CH * R * 2 * 4;
-  static constexpr size_t OFF_U = 0;
-  static constexpr size_t OFF_VS = OFF_U + U_BYTES;
+  static constexpr size_t PB_BYTES = PAIRS ? 2 * (size_t)CH * WPH * NQB * NC * 64 * 16 : 0;
+  static constexpr size_t ST_BYTES = (size_t)CH * R * 4;
+  static constexpr size_t OFF_KS = 0;
+  static constexpr size_t OFF_SX = OFF_KS + KS_BYTES;
+  static constexpr size_t OFF_VS = OFF_SX + SX_BYTES;
   static constexpr size_t OFF_ZB = OFF_VS + VS_BYTES;
   static constexpr size_t OFF_PB = OFF_ZB + ZB_BYTES;
   static constexpr size_t OFF_ST = OFF_PB + PB_BYTES;
   static constexpr size_t LDS_BYTES = OFF_ST + ST_BYTES;
-  // register prefetch of one regular tile (16-byte chunks per thread)
-  static constexpr int KCH = CH * BK * (D / 8);
-  static constexpr int VCH = CH * BK * (D / 8);
-  static constexpr int KPT = (KCH + NT - 1) / NT;
-  static constexpr int VPT = (VCH + NT - 1) / NT;
+  // staging: 16-byte chunks per team member for one regular tile
+  static constexpr int HEADS = PRIV ? 1 : CH;
+  static constexpr int CPT = HEADS * BK * (D / 8) / TEAM;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget exceeded");
   static_assert(QW % 16 == 0 && BK % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(KCH % NT == 0 && VCH % NT == 0, "staging split");
+  static_assert((HEADS * BK * (D / 8)) % TEAM == 0, "staging split");
 };
 
 __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
@@ -132,16 +144,21 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
   return r;
 }
 
-__device__ __forceinline__ float xgroup_max(float x) {  // over the 4 lane groups (same query)
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Reductions over the four lane groups that hold the same query (lanes l, l^16, l^32,
+// l^48): v_permlane16_swap(x, x) returns (x[l & ~16], x[l | 16]) in every lane, and
+// v_permlane32_swap the same across halves of the wave.
+__device__ __forceinline__ float xgroup_max(float x) {
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 
 __device__ __forceinline__ float xgroup_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // Transposed read of V: lane i of each 16-lane group receives V[row0 + 0..3][col0 + i].
@@ -152,23 +169,36 @@ __device__ __forceinline__ s16x4 vtr(const __bf16* Vs, int row0, int col0, int l
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Synchronises the threads that share a staged K/V tile: the workgroup, or only the
+// wave itself when it owns its head (then a wavefront-scope fence keeps the LDS
+// accesses of the wave in program order).
+template <class C>
+__device__ __forceinline__ void team_sync() {
+  if constexpr (C::PRIV)
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  else
+    __syncthreads();
+}
+
 template <class C>
 __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  __bf16* Ks = reinterpret_cast<__bf16*>(smem + C::OFF_U);
-  float* Sx = reinterpret_cast<float*>(smem + C::OFF_U);  // aliases Ks (after QK^T)
+  __bf16* Ks = reinterpret_cast<__bf16*>(smem + C::OFF_KS);
+  _Float16* Sx = reinterpret_cast<_Float16*>(smem + C::OFF_SX);
   __bf16* Vs = reinterpret_cast<__bf16*>(smem + C::OFF_VS);
   _Float16* Zb = reinterpret_cast<_Float16*>(smem + C::OFF_ZB);
   u32x4* Pb = reinterpret_cast<u32x4*>(smem + C::OFF_PB);
-  float* St_a = reinterpret_cast<float*>(smem + C::OFF_ST);
-  float* St_l = St_a + C::CH * C::R;
+  float* St_l = reinterpret_cast<float*>(smem + C::OFF_ST);  // [CH][R] final row sums
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int hu = wave / C::WPH;
   const int slab = wave % C::WPH;
-  const int qs0 = slab * C::QW;  // first tile row of this wave
-  const int lq = lane & 15;      // query within a block (D layout column)
-  const int lg = lane >> 4;      // lane group: keys 4*lg..4*lg+3 of a block
+  const int qs0 = slab * C::QW;           // first tile row of this wave
+  const int lq = lane & 15;               // query within a block (D layout column)
+  const int lg = lane >> 4;               // lane group: keys 4*lg..4*lg+3 of a block
+  const int trank = C::PRIV ? lane : tid; // rank within the staging team
+  const int thead = C::PRIV ? hu : 0;     // first head staged by the team
 
   // ---- workgroup -> (b, group, tile), heaviest tiles first ----------------------------
   const int n_bg = A.B * A.n_groups;
@@ -191,40 +221,42 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
   const int last_row = min(i0 + A.r_out, T_) - 1;
   const int n_kt = last_row / C::BK + 1;
   const int m_head = g * C::CH + hu;
-  const bool mix_pre = A.mix == MIX_PRE;
-  const int wrow_min = row0 + qs0;           // smallest global row of this wave
+  constexpr bool mix_pre = C::MIXPRE;
+  const int wrow_min = row0 + qs0;  // smallest global row of this wave
   const size_t bstride = (size_t)T_ * M * C::D;
   const __bf16* qb_ = A.q + b * bstride;
   const __bf16* kb_ = A.k + b * bstride;
   const __bf16* vb_ = A.v + b * bstride;
+  // logits are kept unscaled; sc turns them into log2 units (mixing folds the scale in)
+  const float sc = mix_pre ? 1.0f : A.qk_scale;
 
   // ---- Q^T operands (B of QK^T) in registers ------------------------------------------
   bf16x8 qf[C::NQB][C::KS];
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
     const int gr = row0 + qs0 + qb * 16 + lq;
+    const int grc = min(max(gr, 0), T_ - 1);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      if (gr >= 0 && gr < T_)
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qb_ + ((size_t)gr * M + m_head) * C::D + ks * 32 + lg * 8);
-      else
-        qf[qb][ks] = bf16x8{};
+      qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qb_ + ((size_t)grc * M + m_head) * C::D + ks * 32 + lg * 8);
+      if (gr != grc) qf[qb][ks] = bf16x8{};
     }
   }
 
   // ---- Toeplitz A operands: out key n (row), window key k = 8*lg + s (slot) ------------
   // window key k is global key j0 - 8 + 16*ob + k; out key is j0 + 16*ob + n;
-  // tap e = n - k + 8 + h0.
-  f16x8 tz[C::KQ ? CQ_MAX : 1];
+  // tap e = n - k + 8 + h0. Before softmax the logit scale is folded in.
+  f16x8 tz[C::KQ ? C::CQM : 1];
   if constexpr (C::KQ) {
     const float* th = A.theta + (size_t)m_head * A.c_q * A.c_k;
+    const float tscale = (!C::TWO && !mix_pre) ? A.qk_scale : 1.0f;
 #pragma unroll
-    for (int a = 0; a < CQ_MAX; ++a) {
+    for (int a = 0; a < C::CQM; ++a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int e = lq - (8 * lg + s) + 8 + h0;
         float t = 0.0f;
-        if (a < A.c_q && e >= 0 && e < A.c_k) t = th[a * A.c_k + e];
+        if (a < A.c_q && e >= 0 && e < A.c_k) t = th[a * A.c_k + e] * tscale;
         tz[a][s] = (_Float16)t;
       }
     }
@@ -234,10 +266,12 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
     }
   }
 
-  float wmix[C::CH];
+  float wmix[C::CH];  // w[g][hu][:]; before softmax times the logit scale
 #pragma unroll
-  for (int u = 0; u < C::CH; ++u)
-    wmix[u] = A.mix ? A.w[((size_t)g * C::CH + hu) * C::CH + u] : 0.0f;
+  for (int u = 0; u < C::CH; ++u) {
+    const float wv = A.mix ? A.w[((size_t)g * C::CH + hu) * C::CH + u] : 0.0f;
+    wmix[u] = mix_pre ? wv * A.qk_scale : wv;
+  }
 
   f32x4 acc[C::NP][C::NB][C::NQB];
 #pragma unroll
@@ -247,143 +281,136 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) acc[p][nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float m_run[C::NQB], l_run[C::NQB];  // per query (replicated over lane groups)
+  float m_run[C::NQB], l_run[C::NQB];  // reference max (logit units), per-lane partial sums
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
     m_run[qb] = -1e30f;
-    l_run[qb] = 0.0f;  // per-lane partial sum in the one-pass schedule
+    l_run[qb] = 0.0f;
   }
   const float NEG_INF = -__builtin_inff();
 
-  // ---- staging helpers ------------------------------------------------------------------
-  // K rows [kfirst, kfirst + nrows) of the group's heads -> Ks rows [lrow, lrow + nrows)
+  // ---- staging (team = the wave itself when it owns its head, else the workgroup) ------
+  auto chunk_src = [&](const __bf16* base, int c, int rowfirst, int nrows_per_head) {
+    const int u = thead + c / (nrows_per_head * (C::D / 8));
+    const int rem = c % (nrows_per_head * (C::D / 8));
+    const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
+    const int j = min(max(rowfirst + r, 0), T_ - 1);  // rows outside the map are masked later
+    return base + ((size_t)j * M + g * C::CH + u) * C::D + cc * 8;
+  };
+  auto k_dst = [&](int c, int lrow, int nrows_per_head) {
+    const int u = thead + c / (nrows_per_head * (C::D / 8));
+    const int rem = c % (nrows_per_head * (C::D / 8));
+    const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
+    return Ks + ((size_t)u * C::KROWS + lrow + r) * C::LDK + cc * 8;
+  };
+  auto v_dst = [&](int c) {
+    const int u = thead + c / (C::BK * (C::D / 8));
+    const int rem = c % (C::BK * (C::D / 8));
+    const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
+    return Vs + ((size_t)u * C::BK + r) * C::LDV + cc * 8;
+  };
   auto stage_k_direct = [&](int kfirst, int nrows, int lrow) {
-    const int total = C::CH * nrows * (C::D / 8);
-    for (int c = tid; c < total; c += NT) {
-      const int u = c / (nrows * (C::D / 8));
-      const int rem = c - u * nrows * (C::D / 8);
-      const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
-      const int j = kfirst + r;
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (j >= 0 && j < T_) val = *reinterpret_cast<const u32x4*>(kb_ + ((size_t)j * M + g * C::CH + u) * C::D + cc * 8);
-      *reinterpret_cast<u32x4*>(Ks + ((size_t)u * C::KROWS + lrow + r) * C::LDK + cc * 8) = val;
-    }
+    const int total = C::HEADS * nrows * (C::D / 8);
+    for (int c = trank; c < total; c += C::TEAM)
+      *reinterpret_cast<u32x4*>(k_dst(c, lrow, nrows)) = *reinterpret_cast<const u32x4*>(chunk_src(kb_, c, kfirst, nrows));
   };
   auto stage_v_direct = [&](int j0) {
-    constexpr int total = C::CH * C::BK * (C::D / 8);
-    for (int c = tid; c < total; c += NT) {
-      const int u = c / (C::BK * (C::D / 8));
-      const int rem = c - u * C::BK * (C::D / 8);
-      const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
-      const int j = j0 + r;
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (j < T_) val = *reinterpret_cast<const u32x4*>(vb_ + ((size_t)j * M + g * C::CH + u) * C::D + cc * 8);
-      *reinterpret_cast<u32x4*>(Vs + ((size_t)u * C::BK + r) * C::LDV + cc * 8) = val;
-    }
+    constexpr int total = C::HEADS * C::BK * (C::D / 8);
+    for (int c = trank; c < total; c += C::TEAM)
+      *reinterpret_cast<u32x4*>(v_dst(c)) = *reinterpret_cast<const u32x4*>(chunk_src(vb_, c, j0, C::BK));
   };
-  u32x4 pk[C::KPT], pv[C::VPT];
+  // Regular tiles (BK rows per head, rows >= 0): chunk x of a team member is row r_x of
+  // head thead + u_x, 16-byte column cc_x; its byte offset from the tile's first row and
+  // its LDS element offsets do not change from tile to tile.
+  int goff[C::CPT], koff[C::CPT], voff[C::CPT];
+#pragma unroll
+  for (int x = 0; x < C::CPT; ++x) {
+    const int c = trank + x * C::TEAM;
+    const int u = thead + c / (C::BK * (C::D / 8));
+    const int rem = c % (C::BK * (C::D / 8));
+    const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
+    goff[x] = ((r * M + g * C::CH + u) * C::D + cc * 8) * 2;
+    koff[x] = (u * C::KROWS + r) * C::LDK + cc * 8;
+    voff[x] = (u * C::BK + r) * C::LDV + cc * 8;
+  }
+  // buffer resource over rows jfirst .. T-1 of a K or V tensor of batch b
+  auto tile_rsrc = [&](const __bf16* base, int jfirst) {
+    const int rows = max(T_ - jfirst, 0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jfirst * M * C::D), (short)0,
+                                             rows * M * C::D * 2, 0x00020000);
+  };
+  u32x4 pk[C::CPT], pv[C::CPT];
   auto prefetch = [&](int kfirst, int j0, bool with_v) {
+    const auto rk = tile_rsrc(kb_, kfirst);
 #pragma unroll
-    for (int x = 0; x < C::KPT; ++x) {
-      const int c = tid + x * NT;
-      const int u = c / (C::BK * (C::D / 8));
-      const int rem = c - u * C::BK * (C::D / 8);
-      const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
-      const int j = kfirst + r;
-      pk[x] = (j >= 0 && j < T_) ? *reinterpret_cast<const u32x4*>(kb_ + ((size_t)j * M + g * C::CH + u) * C::D + cc * 8)
-                                 : u32x4{0, 0, 0, 0};
-    }
+    for (int x = 0; x < C::CPT; ++x)
+      pk[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[x], 0, 0));
     if (with_v) {
+      const auto rv = tile_rsrc(vb_, j0);
 #pragma unroll
-      for (int x = 0; x < C::VPT; ++x) {
-        const int c = tid + x * NT;
-        const int u = c / (C::BK * (C::D / 8));
-        const int rem = c - u * C::BK * (C::D / 8);
-        const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
-        const int j = j0 + r;
-        pv[x] = (j < T_) ? *reinterpret_cast<const u32x4*>(vb_ + ((size_t)j * M + g * C::CH + u) * C::D + cc * 8)
-                         : u32x4{0, 0, 0, 0};
-      }
+      for (int x = 0; x < C::CPT; ++x)
+        pv[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[x], 0, 0));
     }
   };
   auto commit = [&](int lrow, bool with_v) {
 #pragma unroll
-    for (int x = 0; x < C::KPT; ++x) {
-      const int c = tid + x * NT;
-      const int u = c / (C::BK * (C::D / 8));
-      const int rem = c - u * C::BK * (C::D / 8);
-      const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
-      *reinterpret_cast<u32x4*>(Ks + ((size_t)u * C::KROWS + lrow + r) * C::LDK + cc * 8) = pk[x];
-    }
+    for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks + koff[x] + lrow * C::LDK) = pk[x];
     if (with_v) {
 #pragma unroll
-      for (int x = 0; x < C::VPT; ++x) {
-        const int c = tid + x * NT;
-        const int u = c / (C::BK * (C::D / 8));
-        const int rem = c - u * C::BK * (C::D / 8);
-        const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
-        *reinterpret_cast<u32x4*>(Vs + ((size_t)u * C::BK + r) * C::LDV + cc * 8) = pv[x];
-      }
+      for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Vs + voff[x]) = pv[x];
     }
   };
 
   // ---- compute helpers --------------------------------------------------------------------
   f32x4 s[C::LB][C::NQB];
-  // S^T of logit blocks [lb0, lb1) from K rows at Ks row 16*lb (times the scale), then
-  // the optional mixing across heads (through LDS) of the same blocks.
-  auto logits = [&](int lb0, int lb1) {
+  // raw S^T of logit block lb (Ks rows 16*lb .. 16*lb+15)
+  auto logit_block = [&](int lb) {
 #pragma unroll
-    for (int lb = 0; lb < C::LB; ++lb) {
-      if (lb < lb0 || lb >= lb1) continue;
+    for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+          Ks + ((size_t)hu * C::KROWS + lb * 16 + lq) * C::LDK + ks * 32 + lg * 8);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-            Ks + ((size_t)hu * C::KROWS + lb * 16 + lq) * C::LDK + ks * 32 + lg * 8);
+      for (int qb = 0; qb < C::NQB; ++qb)
+        s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
+    }
+  };
+  // mixing of logit blocks [LB0, LB1) across the heads of the group: fp16 exchange of the
+  // other heads through LDS; result in log2 units
+  auto mix_blocks = [&](auto lb0c, auto lb1c) {
+    constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value;
+    __syncthreads();  // the previous exchange has been read by every wave
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb)
-          s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
+    for (int lb = LB0; lb < LB1; ++lb) {
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const f16x4 h = {(_Float16)s[lb][qb][0], (_Float16)s[lb][qb][1], (_Float16)s[lb][qb][2],
+                         (_Float16)s[lb][qb][3]};
+        *reinterpret_cast<f16x4*>(Sx + ((size_t)hu * C::R + qs0 + qb * 16 + lq) * C::LDX + (lb - LB0) * 16 + lg * 4) = h;
       }
     }
-    if (mix_pre) {
-      __syncthreads();  // all waves finished reading Ks (Sx aliases it)
+    __syncthreads();
 #pragma unroll
-      for (int lb = 0; lb < C::LB; ++lb) {
-        if (lb < lb0 || lb >= lb1) continue;
+    for (int lb = LB0; lb < LB1; ++lb) {
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb)
-          *reinterpret_cast<f32x4*>(Sx + ((size_t)hu * C::R + qs0 + qb * 16 + lq) * C::LDX + (lb - lb0) * 16 + lg * 4) =
-              s[lb][qb] * A.qk_scale;
-      }
-      __syncthreads();
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        f32x4 x = s[lb][qb] * wmix[hu];
 #pragma unroll
-      for (int lb = 0; lb < C::LB; ++lb) {
-        if (lb < lb0 || lb >= lb1) continue;
+        for (int u = 0; u < C::CH; ++u) {
+          if (u == hu) continue;
+          const f16x4 o = *reinterpret_cast<const f16x4*>(
+              Sx + ((size_t)u * C::R + qs0 + qb * 16 + lq) * C::LDX + (lb - LB0) * 16 + lg * 4);
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int u = 0; u < C::CH; ++u) {
-            const f32x4 o = *reinterpret_cast<const f32x4*>(
-                Sx + ((size_t)u * C::R + qs0 + qb * 16 + lq) * C::LDX + (lb - lb0) * 16 + lg * 4);
-            x += wmix[u] * o;
-          }
-          s[lb][qb] = x;
+          for (int i = 0; i < 4; ++i) x[i] += wmix[u] * (float)o[i];
         }
-      }
-    } else {
-#pragma unroll
-      for (int lb = 0; lb < C::LB; ++lb) {
-        if (lb < lb0 || lb >= lb1) continue;
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] *= A.qk_scale;
+        s[lb][qb] = x;
       }
     }
   };
 
   // convolution of the ring (logical blocks of tile kt) -> cv[ob][qb]
-  f32x4 cv[C::NKB][C::NQB];
+  f32x4 cv[C::KQ ? C::NKB : 1][C::NQB];
   auto ring_col = [&](int kt, int lb) { return ((kt * C::NKB + lb) % C::LB) * 16; };
   auto convolve = [&](int kt) {
 #pragma unroll
@@ -395,7 +422,7 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
       // slots of lane group lg: window keys 8*lg .. 8*lg+7 = block ob (lg < 2) or ob+1
       const int col = ring_col(kt, ob + (lg >> 1)) + (lg & 1) * 8;
 #pragma unroll
-      for (int a = 0; a < CQ_MAX; ++a) {
+      for (int a = 0; a < C::CQM; ++a) {
         if (a < A.c_q) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
@@ -407,267 +434,362 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
       }
     }
   };
-  // write logit-derived values of block lb (D layout) into the ring
   auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) {
-    _Float16 h[4] = {(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
-    *reinterpret_cast<uint2*>(Zb + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq) * C::LDZ + ring_col(kt, lb) +
-                              lg * 4) = *reinterpret_cast<uint2*>(h);
+    const f16x4 h = {(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
+    *reinterpret_cast<f16x4*>(Zb + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq) * C::LDZ +
+                              ring_col(kt, lb) + lg * 4) = h;
   };
 
-  // AV of the weight blocks pw[NKB][NQB] (out keys of this tile) against V of head hu
-  auto av = [&](f32x4 (&pw)[C::NKB][C::NQB]) {
-    if constexpr (C::PAIRS) {
-      // publish this wave's weights in the fragment layout, then use every head's
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          const bf16x8 bp = pack_bf16(pw[2 * c][qb], pw[2 * c + 1][qb]);
-          Pb[(((size_t)hu * C::WPH + slab) * C::NQB + qb) * C::NC * 64 + c * 64 + lane] =
-              *reinterpret_cast<const u32x4*>(&bp);
-        }
-      __syncthreads();
-    }
+  // AV of weight fragments against V of head hu. Fragments come from w (own weights,
+  // blocks w[ob0 .. ob0 + NKB)) or, with mixing after softmax, from the exchange buffer.
+  auto av = [&](auto& wts, auto ob0c, const u32x4* pbuf) {
+    constexpr int OB0 = decltype(ob0c)::value;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
-      bf16x8 bp[C::NP][C::NQB];
 #pragma unroll
-      for (int p = 0; p < C::NP; ++p)
+      for (int p = 0; p < C::NP; ++p) {
+        bf16x8 bp[C::NQB];
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           if constexpr (C::PAIRS) {
-            const u32x4 raw = Pb[(((size_t)p * C::WPH + slab) * C::NQB + qb) * C::NC * 64 + c * 64 + lane];
-            bp[p][qb] = *reinterpret_cast<const bf16x8*>(&raw);
+            const u32x4 raw = pbuf[(((size_t)p * C::WPH + slab) * C::NQB + qb) * C::NC * 64 + c * 64 + lane];
+            bp[qb] = *reinterpret_cast<const bf16x8*>(&raw);
           } else {
-            bp[p][qb] = pack_bf16(pw[2 * c][qb], pw[2 * c + 1][qb]);
+            bp[qb] = pack_bf16(wts[OB0 + 2 * c][qb], wts[OB0 + 2 * c + 1][qb]);
           }
         }
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        // V^T operand: channels nb*16 + (lane & 15); k-slots = keys {4lg..4lg+3} of
-        // block 2c and {16+4lg..} of block 2c+1 of this tile
-        const s16x4 lo = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 4 * lg, nb * 16, C::LDV, lane);
-        const s16x4 hi = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 16 + 4 * lg, nb * 16, C::LDV, lane);
-        s16x4 v8[2] = {lo, hi};
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(v8);
-#pragma unroll
-        for (int p = 0; p < C::NP; ++p)
+        for (int nb = 0; nb < C::NB; ++nb) {
+          // V^T operand: channels nb*16 + (lane & 15); k-slots = keys {4lg..4lg+3} of
+          // block 2c and {16+4lg..} of block 2c+1 of this tile
+          const s16x4 lo = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 4 * lg, nb * 16, C::LDV, lane);
+          const s16x4 hi = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 16 + 4 * lg, nb * 16, C::LDV, lane);
+          s16x4 v8[2] = {lo, hi};
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(v8);
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb)
-            acc[p][nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[p][qb], acc[p][nb][qb], 0, 0, 0);
+            acc[p][nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[qb], acc[p][nb][qb], 0, 0, 0);
+        }
       }
     }
   };
-
-  f32x4 pw[C::NKB][C::NQB];
+  // publish this wave's weights in fragment layout (mixing after softmax)
+  auto publish = [&](auto& wts, auto ob0c, u32x4* pbuf) {
+    constexpr int OB0 = decltype(ob0c)::value;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const bf16x8 bp = pack_bf16(wts[OB0 + 2 * c][qb], wts[OB0 + 2 * c + 1][qb]);
+        pbuf[(((size_t)hu * C::WPH + slab) * C::NQB + qb) * C::NC * 64 + c * 64 + lane] =
+            *reinterpret_cast<const u32x4*>(&bp);
+      }
+  };
+  typedef std::integral_constant<int, 0> I0;
+  typedef std::integral_constant<int, 1> I1;
+  typedef std::integral_constant<int, C::NKB> INKB;
+  typedef std::integral_constant<int, C::LB> ILB;
+  constexpr size_t PB_HALF = (size_t)C::CH * C::WPH * C::NQB * C::NC * 64;
+  // first logit block of the tile that is new (block 0 is the carried key halo)
+  typedef std::integral_constant<int, C::KQ ? 1 : 0> INEW;
 
   if constexpr (!C::TWO) {
     // ============================= one pass ==============================================
-    if constexpr (C::KQ) stage_k_direct(-8, C::BK + 16, 0);
-    else stage_k_direct(0, C::BK, 0);
-    stage_v_direct(0);
-    __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int j0 = kt * C::BK;
-      const bool more = kt + 1 < n_kt;
-      if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, true);
-      const int lb0 = (C::KQ && kt > 0) ? 1 : 0;
-      logits(lb0, C::LB);
+    // the softmax sees log2 units: the convolution already folded the scale in
+    const float ssc = C::KQ ? 1.0f : sc;
+    // mode 0: reference = the row's maximum over its first key tile (the normal case);
+    // mode 1: exact row maxima only (no weights); mode 2: weighted pass with those maxima.
+    int mode = 0;
+    for (;;) {
+      // prologue: tile 0's K rows (with the left halo block) and V rows; halo block 0 of
+      // the convolution input computed here so that every tile computes blocks 1..NKB
+      if constexpr (C::KQ) stage_k_direct(-8, C::BK + 16, 0);
+      else stage_k_direct(0, C::BK, 0);
+      if (mode != 1) stage_v_direct(0);
+      team_sync<C>();
       if constexpr (C::KQ) {
-        // Mask_0 on the new blocks (keys kbase + 16 lb + 4 lg + i, kbase = j0 - 8)
-        const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0);
+        logit_block(0);
+        if constexpr (mix_pre) mix_blocks(I0{}, I1{});
 #pragma unroll
-        for (int lb = 0; lb < C::LB; ++lb) {
-          if (lb < lb0) continue;
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const int gr = row0 + qs0 + qb * 16 + lq;
+          f32x4 z = s[0][qb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = -8 + 4 * lg + i;
+            if (!(gr >= 0 && j >= 0 && j <= gr)) z[i] = 0.0f;
+          }
+          ring_store(0, 0, qb, z);
+        }
+      }
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int j0 = kt * C::BK;
+        const bool more = kt + 1 < n_kt;
+        if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, mode != 1);
+#pragma unroll
+        for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
+        if constexpr (mix_pre) mix_blocks(INEW{}, ILB{});
+        // weights of this tile: cv (after the convolution) or the logits themselves
+        auto& xw = [&]() -> auto& {
+          if constexpr (C::KQ) return cv;
+          else return s;
+        }();
+        if constexpr (C::KQ) {
+          // Mask_0 on the new blocks (keys j0 - 8 + 16 lb + 4 lg + i)
+          const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0);
+#pragma unroll
+          for (int lb = 1; lb < C::LB; ++lb) {
+#pragma unroll
+            for (int qb = 0; qb < C::NQB; ++qb) {
+              f32x4 z = s[lb][qb];
+              if (edge) {
+                const int gr = row0 + qs0 + qb * 16 + lq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int j = j0 - 8 + lb * 16 + 4 * lg + i;
+                  if (!(gr >= 0 && j >= 0 && j <= gr)) z[i] = 0.0f;
+                }
+              }
+              ring_store(kt, lb, qb, z);
+            }
+          }
+          team_sync<C>();  // rows of the neighbouring slab are read by the convolution
+          convolve(kt);
+        }
+        // Mask_-inf
+        const bool edge = (j0 + C::BK - 1 > wrow_min) || (qs0 < cq1) || (wrow_min + C::QW > T_);
+        if (edge) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
-            f32x4 z = s[lb][qb];
-            if (edge) {
-              const int gr = row0 + qs0 + qb * 16 + lq;
+            const int t = qs0 + qb * 16 + lq;
+            const int gr = row0 + t;
+            const bool row_ok = t >= cq1 && gr < T_;
+#pragma unroll
+            for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int j = j0 - 8 + lb * 16 + 4 * lg + i;
-                if (!(gr >= 0 && j >= 0 && j <= gr)) z[i] = 0.0f;
+                const int j = j0 + ob * 16 + 4 * lg + i;
+                if (!(row_ok && j <= gr)) xw[ob][qb][i] = NEG_INF;
               }
-            }
-            ring_store(kt, lb, qb, z);
           }
         }
-        __syncthreads();
-        convolve(kt);
-      } else {
+        if (mode == 1 || (mode == 0 && kt == 0)) {
+          // reference update: every tile in mode 1, the first tile in mode 0
 #pragma unroll
-        for (int ob = 0; ob < C::NKB; ++ob)
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            float mx = NEG_INF;
 #pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) cv[ob][qb] = s[ob][qb];
-      }
-      // Mask_-inf and online softmax per query
-      const bool edge = (j0 + C::BK - 1 > wrow_min) || (qs0 < cq1) || (wrow_min + C::QW > T_);
+            for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        const int t = qs0 + qb * 16 + lq;
-        const int gr = row0 + t;
-        const bool row_ok = t >= cq1 && gr < T_;
-        float mx = NEG_INF;
-#pragma unroll
-        for (int ob = 0; ob < C::NKB; ++ob)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = cv[ob][qb][i];
-            if (edge) {
-              const int j = j0 + ob * 16 + 4 * lg + i;
-              if (!(row_ok && j <= gr)) x = NEG_INF;
-            }
-            cv[ob][qb][i] = x;
-            mx = fmaxf(mx, x);
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, xw[ob][qb][i]);
+            m_run[qb] = fmaxf(m_run[qb], xgroup_max(mx));
           }
-        mx = xgroup_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = fast_exp2(m_run[qb] - m_new);
-        float sum = 0.0f;
-#pragma unroll
-        for (int ob = 0; ob < C::NKB; ++ob)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = fast_exp2(cv[ob][qb][i] - m_new);
-            pw[ob][qb][i] = pv;
-            sum += pv;
-          }
-        l_run[qb] = l_run[qb] * alpha + sum;
-        m_run[qb] = m_new;
-        if constexpr (C::PAIRS) {
-          if (lg == 0) St_a[hu * C::R + t] = alpha;
-        } else {
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) acc[0][nb][qb] *= alpha;
         }
+        if (mode != 1) {
+          // weights exp2(x - ref) in place; partial row sums per lane
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            const float mref = m_run[qb] * ssc;
+            float sum = 0.0f;
+#pragma unroll
+            for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float pv = fast_exp2(__builtin_fmaf(xw[ob][qb][i], ssc, -mref));
+                xw[ob][qb][i] = pv;
+                sum += pv;
+              }
+            l_run[qb] += sum;
+          }
+          if constexpr (C::PAIRS) {
+            u32x4* pbuf = Pb + (kt & 1) * PB_HALF;
+            publish(xw, I0{}, pbuf);
+            __syncthreads();
+            av(xw, I0{}, pbuf);
+          } else {
+            av(xw, I0{}, nullptr);
+          }
+        }
+        team_sync<C>();  // the team is done with Ks, Vs and the ring of this tile
+        if (more) commit(C::KQ ? 16 : 0, mode != 1);
+        team_sync<C>();
       }
-      if constexpr (C::PAIRS) {
-        __syncthreads();  // rescale factors of every head are visible (and Pb reuse is safe)
+      if (mode == 1) {
+        mode = 2;
 #pragma unroll
         for (int p = 0; p < C::NP; ++p)
 #pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) {
-            const float al = St_a[p * C::R + qs0 + qb * 16 + lq];
+          for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) acc[p][nb][qb] *= al;
-          }
+            for (int qb = 0; qb < C::NQB; ++qb) acc[p][nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        continue;
       }
-      av(pw);
-      __syncthreads();  // every wave is done with Ks, Vs, Zb, Pb of this tile
-      if (more) commit(C::KQ ? 16 : 0, true);
-      __syncthreads();
-    }
-    // final per-query sums (partial per lane group until here)
+      // final per-query sums (partial per lane group until here)
+      bool big = false;
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      l_run[qb] = xgroup_sum(l_run[qb]);
-      if (lg == 0) St_l[hu * C::R + qs0 + qb * 16 + lq] = l_run[qb];
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        l_run[qb] = xgroup_sum(l_run[qb]);
+        big |= !(l_run[qb] <= SUM_LIMIT);
+      }
+      if (mode == 0 && __syncthreads_or(big ? 1 : 0)) {
+        mode = 1;
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          m_run[qb] = -1e30f;
+          l_run[qb] = 0.0f;
+        }
+        continue;
+      }
+      break;
     }
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb)
+      if (lg == 0) St_l[hu * C::R + qs0 + qb * 16 + lq] = l_run[qb];
     __syncthreads();
   } else {
     // ============================= two phase ============================================
-    // phase 1: exact (max, sum) of every tile row of head hu (after mixing)
-    stage_k_direct(0, C::BK, 0);
-    __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int j0 = kt * C::BK;
-      const bool more = kt + 1 < n_kt;
-      if (more) prefetch(j0 + C::BK, 0, false);
-      logits(0, C::NKB);  // phase 1 needs no key halo
-      const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
+    // phase 1: the row sums of head hu (after mixing) against a fixed reference, the
+    // maximum of the row's first key tile; if a sum exceeds 2^64 the workgroup repeats the
+    // phase as an exact online pass (running maximum, rescaled sum). The K tile rows
+    // j0 .. j0+BK-1 sit at Ks rows 16 .. 16+BK-1 (logit blocks 1..NKB).
+    float lsum[C::NQB];
+    for (int exact = 0;; exact = 1) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
-        const int gr = row0 + qs0 + qb * 16 + lq;
-        const bool row_ok = gr >= 0 && gr < T_;
-        float mx = NEG_INF;
-#pragma unroll
-        for (int ob = 0; ob < C::NKB; ++ob)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = s[ob][qb][i];
-            if (edge) {
-              const int j = j0 + ob * 16 + 4 * lg + i;
-              if (!(row_ok && j <= gr)) x = NEG_INF;
-            }
-            s[ob][qb][i] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = xgroup_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx);
-        float sum = 0.0f;
-#pragma unroll
-        for (int ob = 0; ob < C::NKB; ++ob)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sum += fast_exp2(s[ob][qb][i] - m_new);
-        l_run[qb] = l_run[qb] * fast_exp2(m_run[qb] - m_new) + sum;
-        m_run[qb] = m_new;
+        m_run[qb] = -1e30f;
+        l_run[qb] = 0.0f;
       }
-      __syncthreads();
-      if (more) commit(0, false);
-      __syncthreads();
+      stage_k_direct(0, C::BK, 16);
+      team_sync<C>();
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int j0 = kt * C::BK;
+        const bool more = kt + 1 < n_kt;
+        if (more) prefetch(j0 + C::BK, 0, false);
+#pragma unroll
+        for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
+        if constexpr (mix_pre) mix_blocks(I1{}, ILB{});
+        const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
+        if (edge) {
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            const int gr = row0 + qs0 + qb * 16 + lq;
+            const bool row_ok = gr >= 0 && gr < T_;
+#pragma unroll
+            for (int lb = 1; lb < C::LB; ++lb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int j = j0 + (lb - 1) * 16 + 4 * lg + i;
+                if (!(row_ok && j <= gr)) s[lb][qb][i] = NEG_INF;
+              }
+          }
+        }
+        if (exact || kt == 0) {
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            float mx = NEG_INF;
+#pragma unroll
+            for (int lb = 1; lb < C::LB; ++lb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[lb][qb][i]);
+            const float m_new = fmaxf(m_run[qb], xgroup_max(mx));
+            l_run[qb] *= fast_exp2((m_run[qb] - m_new) * sc);
+            m_run[qb] = m_new;
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const float mref = m_run[qb] * sc;
+          float sum = 0.0f;
+#pragma unroll
+          for (int lb = 1; lb < C::LB; ++lb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -mref));
+          l_run[qb] += sum;
+        }
+        team_sync<C>();
+        if (more) commit(16, false);
+        team_sync<C>();
+      }
+      bool big = false;
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        lsum[qb] = xgroup_sum(l_run[qb]);
+        big |= !(lsum[qb] <= SUM_LIMIT);
+      }
+      if (exact || !__syncthreads_or(big ? 1 : 0)) break;
     }
-    // per-query normaliser folded into the exponent: p = exp2(x - (m + log2 l))
+    // per-query normaliser folded into the exponent: p = exp2(x*sc - (m*sc + log2 l))
     float shift[C::NQB];
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
-      const float l = xgroup_sum(l_run[qb]);
-      shift[qb] = l > 0.0f ? m_run[qb] + __builtin_log2f(l) : 1e30f;
+      const float l = lsum[qb];
+      shift[qb] = l > 0.0f ? m_run[qb] * sc + __builtin_log2f(l) : 1e30f;
     }
+    auto weights = [&](int kt, int lb, bool edge) {
+      const int j0 = kt * C::BK;
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const int gr = row0 + qs0 + qb * 16 + lq;
+        f32x4 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -shift[qb]));
+          if (edge) {
+            const int j = j0 - 8 + lb * 16 + 4 * lg + i;
+            if (!(gr >= 0 && gr < T_ && j >= 0 && j <= gr)) pv[i] = 0.0f;
+          }
+        }
+        ring_store(kt, lb, qb, pv);
+      }
+    };
 
     // phase 2: exact weights (sliding key halo) -> convolution -> Mask_0 -> AV
     stage_k_direct(-8, C::BK + 16, 0);
     stage_v_direct(0);
-    __syncthreads();
+    team_sync<C>();
+    logit_block(0);
+    if constexpr (mix_pre) mix_blocks(I0{}, I1{});
+    weights(0, 0, true);
     for (int kt = 0; kt < n_kt; ++kt) {
       const int j0 = kt * C::BK;
       const bool more = kt + 1 < n_kt;
       if (more) prefetch(j0 + C::BK + 8, j0 + C::BK, true);
-      const int lb0 = kt > 0 ? 1 : 0;
-      logits(lb0, C::LB);
+#pragma unroll
+      for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
+      if constexpr (mix_pre) mix_blocks(I1{}, ILB{});
       const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) ||
                         (wrow_min + C::QW > T_);
 #pragma unroll
-      for (int lb = 0; lb < C::LB; ++lb) {
-        if (lb < lb0) continue;
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          const int gr = row0 + qs0 + qb * 16 + lq;
-          f32x4 pv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = fast_exp2(s[lb][qb][i] - shift[qb]);
-            if (edge) {
-              const int j = j0 - 8 + lb * 16 + 4 * lg + i;
-              if (!(gr >= 0 && gr < T_ && j >= 0 && j <= gr)) pv[i] = 0.0f;
-            }
-          }
-          ring_store(kt, lb, qb, pv);
-        }
-      }
-      __syncthreads();
+      for (int lb = 1; lb < C::LB; ++lb) weights(kt, lb, edge);
+      team_sync<C>();
       convolve(kt);
       const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < cq1) || (wrow_min + C::QW > T_);
+      if (edge2) {
 #pragma unroll
-      for (int ob = 0; ob < C::NKB; ++ob)
+        for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          f32x4 c = cv[ob][qb];
-          if (edge2) {
+          for (int qb = 0; qb < C::NQB; ++qb) {
             const int t = qs0 + qb * 16 + lq;
             const int gr = row0 + t;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int j = j0 + ob * 16 + 4 * lg + i;
-              if (!(t >= cq1 && gr < T_ && j <= gr)) c[i] = 0.0f;
+              if (!(t >= cq1 && gr < T_ && j <= gr)) cv[ob][qb][i] = 0.0f;
             }
           }
-          pw[ob][qb] = c;
-        }
-      av(pw);
-      __syncthreads();
+      }
+      if constexpr (C::PAIRS) {
+        u32x4* pbuf = Pb + (kt & 1) * PB_HALF;
+        publish(cv, I0{}, pbuf);
+        __syncthreads();
+        av(cv, I0{}, pbuf);
+      } else {
+        av(cv, I0{}, nullptr);
+      }
+      team_sync<C>();
       if (more) commit(16, true);
-      __syncthreads();
+      team_sync<C>();
     }
   }
 
@@ -683,25 +805,25 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
       for (int nb = 0; nb < C::NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < C::NP; ++p) {
-        float sc = wmix[p];
+        float scl = wmix[p];
         if constexpr (!C::TWO) {
           const float l = St_l[p * C::R + t];
-          sc = l > 0.0f ? sc / l : 0.0f;
+          scl = l > 0.0f ? scl / l : 0.0f;
         }
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) o[nb] += acc[p][nb][qb] * sc;
+        for (int nb = 0; nb < C::NB; ++nb) o[nb] += acc[p][nb][qb] * scl;
       }
     } else {
-      float sc = 1.0f;
-      if constexpr (!C::TWO) sc = l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f;
+      float scl = 1.0f;
+      if constexpr (!C::TWO) scl = l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[0][nb][qb] * sc;
+      for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[0][nb][qb] * scl;
     }
     float mean = 0.0f, inv = 1.0f;
     if (A.gn) {
       float sum = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) sum += o[nb][0] + o[nb][1] + o[nb][2] + o[nb][3];
+      for (int nb = 0; nb < C::NB; ++nb) sum += (o[nb][0] + o[nb][1]) + (o[nb][2] + o[nb][3]);
       mean = xgroup_sum(sum) * (1.0f / C::D);
       float sq = 0.0f;
 #pragma unroll
@@ -718,16 +840,14 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
         const int c0 = nb * 16 + 4 * lg;
-        __bf16 y[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float val = o[nb][i];
-          if (A.gn)
-            val = A.lambda * (A.gamma[(size_t)m_head * C::D + c0 + i] * (val - mean) * inv +
-                              A.beta[(size_t)m_head * C::D + c0 + i]);
-          y[i] = (__bf16)val;
+        f32x4 y = o[nb];
+        if (A.gn) {
+          const f32x4 ga = *reinterpret_cast<const f32x4*>(A.gamma + (size_t)m_head * C::D + c0);
+          const f32x4 be = *reinterpret_cast<const f32x4*>(A.beta + (size_t)m_head * C::D + c0);
+          y = A.lambda * (ga * ((y - mean) * inv) + be);
         }
-        *reinterpret_cast<uint2*>(dst + c0) = *reinterpret_cast<const uint2*>(y);
+        __bf16 h[4] = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+        *reinterpret_cast<uint2*>(dst + c0) = *reinterpret_cast<const uint2*>(h);
       }
     }
   }
@@ -749,7 +869,6 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.B = p.B;
   a.T = p.T;
   a.M = p.M;
-  a.kq = p.kq;
   a.mix = p.mix;
   a.gn = p.gn;
   a.c_q = p.kq ? p.c_q : 1;
@@ -766,27 +885,41 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile shapes: per-pair accumulators take c_h * d * QW fp32 per wave, which limits QW.
-template <int D, int CH, bool KQ, bool TWO, bool PAIRS>
+// Tile shapes: per-pair accumulators take c_h * d * QW fp32 per wave, which limits QW;
+// LDS limits the key tile to 32 keys for groups of four heads.
+template <int D, int CH, bool KQ, bool TWO, bool PAIRS, int CQM>
 hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr int BK = (CH == 4) ? 32 : 64;
   constexpr int QW = (PAIRS || CH == 2) ? 32 : 64;
-  return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS>>(p, stream);
+  if constexpr (!PAIRS) {
+    if (p.mix == MIX_PRE) return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, true>>(p, stream);
+  }
+  return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, false>>(p, stream);
+}
+
+template <int D, int CH, bool KQ, bool TWO, bool PAIRS>
+hipError_t launch_cq(const Problem& p, hipStream_t stream) {
+  if constexpr (!KQ) {
+    return launch_shape<D, CH, KQ, TWO, PAIRS, 1>(p, stream);
+  } else {
+    if (p.c_q <= 4) return launch_shape<D, CH, KQ, TWO, PAIRS, 4>(p, stream);
+    return launch_shape<D, CH, KQ, TWO, PAIRS, 8>(p, stream);
+  }
 }
 
 template <int D, int CH>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
   const bool pairs = p.mix == MIX_POST && CH > 1;
   if (p.kq == KQ_POST) {
-    if (pairs) return launch_shape<D, CH, true, true, true>(p, stream);
-    return launch_shape<D, CH, true, true, false>(p, stream);
+    if (pairs) return launch_cq<D, CH, true, true, true>(p, stream);
+    return launch_cq<D, CH, true, true, false>(p, stream);
   }
   if (p.kq == KQ_PRE) {
-    if (pairs) return launch_shape<D, CH, true, false, true>(p, stream);
-    return launch_shape<D, CH, true, false, false>(p, stream);
+    if (pairs) return launch_cq<D, CH, true, false, true>(p, stream);
+    return launch_cq<D, CH, true, false, false>(p, stream);
   }
-  if (pairs) return launch_shape<D, CH, false, false, true>(p, stream);
-  return launch_shape<D, CH, false, false, false>(p, stream);
+  if (pairs) return launch_cq<D, CH, false, false, true>(p, stream);
+  return launch_cq<D, CH, false, false, false>(p, stream);
 }
 
 template <int D>
