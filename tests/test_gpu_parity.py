@@ -161,6 +161,30 @@ def test_every_placement(kq, mix, path):
     compare(cfg, run(path, cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"{path} {kq}/{mix}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kq,mix,c_h", [(None, None, 1), ("pre", None, 1), ("post", None, 1), (None, "post", 4),
+                                        (None, "pre", 2), ("pre", "post", 2), ("pre", "post", 4),
+                                        ("post", "pre", 4)])
+def test_late_dominant_key(kq, mix, c_h, d):
+    """One key far past the first key tile whose logit for one query exceeds everything
+    before it by ~130 (natural-log units, 2^187 as a weight against the first tile's
+    maximum, past the fp32 range): the fused kernel's first-tile reference is then too
+    small and the workgroup must take its exact fallback pass."""
+    cfg = mta_inputs.MTAConfig("late", 1, 300, 8, d, 4, 9, c_h, kq, mix, True, "bf16", 0.05, 0.05, 1.0, 0.0,
+                               0.8, seed=17)
+    inp = dict(case(cfg))
+    q, k = inp["q"].astype(np.float64), inp["k"].copy()
+    jkey, iq = 200, 260
+    for m in range(cfg.M):
+        qv = q[0, iq, m]
+        k[0, jkey, m] = 130.0 * np.sqrt(d) / float(qv @ qv) * qv
+    inp["k"] = mta_inputs.round_bf16(k.astype(np.float32))
+    logit = float(inp["q"][0, iq, 0].astype(np.float64) @ inp["k"][0, jkey, 0]) / np.sqrt(d)
+    assert logit > 120.0
+    want = oracle.forward_cfg(cfg, inp)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), want, what=f"late key {kq}/{mix}/{c_h} d={d}")
+
+
 @pytest.mark.parametrize("c_q,c_k", [(1, 1), (1, 17), (8, 1), (8, 17), (2, 3), (5, 13)])
 @pytest.mark.parametrize("kq", ["pre", "post"])
 def test_kernel_sizes(c_q, c_k, kq):
