@@ -133,10 +133,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
-    ap.add_argument("--only-fused", action="store_true", help="time the fused kernel only (profiling)")
+    ap.add_argument("--only", choices=["fused", "plain", "default", "materialized"], default=None,
+                    help="run one path only (for counter collection); prints its timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
@@ -163,13 +164,56 @@ def main():
     inp, d = gpu_inputs(cfg, torch)
     kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
     out = torch.empty_like(d["q"])
+    tokens = cfg.B * cfg.T
+    n_c = cfg.T * (cfg.T + 1) // 2
 
     def fused():
         ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out, **kw)
 
+    def plain():
+        ta.attention_plain(d["q"], d["k"], d["v"], out=out)
+
+    dflt = cfg.replace(kq="pre", mix="post")
+    kw2 = dict(kw, kq="pre", mix="post")
+
+    def fused_default():
+        ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out, **kw2)
+
+    def plain_record(ms_plain, ms):
+        return {"ms": ms_plain, "tflops": cfg.B * cfg.M * n_c * 4 * cfg.d / (ms_plain * 1e-3) / 1e12,
+                "mta_slowdown": ms / ms_plain if ms else None}
+
+    def default_record(ms_dflt, ms_plain):
+        tf = flops(dflt) / (ms_dflt * 1e-3) / 1e12
+        return {"ms": ms_dflt, "tokens_per_s": tokens / (ms_dflt * 1e-3), "tflops": tf,
+                "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+                "mta_slowdown_vs_plain": ms_dflt / ms_plain if ms_plain else None}
+
+    def materialized_record(ms):
+        ws = torch.empty(ta.materialized_workspace_bytes(cfg.B, cfg.T, cfg.M), dtype=torch.uint8, device="cuda")
+
+        def mat():
+            ta.forward_materialized(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"],
+                                    d["lam"], out=out, workspace=ws, **kw)
+        ms_mat = time_launches(mat, max(2, args.steps // 4), 1, torch)
+        mb = materialized_bytes(cfg)
+        rec = {"ms": ms_mat, "tokens_per_s": tokens / (ms_mat * 1e-3), "bytes": mb,
+               "gbs": mb / (ms_mat * 1e-3) / 1e9, "frac_hbm_peak": mb / (ms_mat * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "workspace_gib": ws.numel() / 2 ** 30, "fused_speedup": ms_mat / ms if ms else None}
+        del ws
+        return rec
+
+    if args.only:
+        fn = {"fused": fused, "plain": plain, "default": fused_default}.get(args.only)
+        if fn is not None:
+            ms_only = time_launches(fn, args.steps, args.warmup, torch)
+            print(json.dumps({"only": args.only, "ms": ms_only}))
+        else:
+            print(json.dumps({"only": args.only, **materialized_record(None)}))
+        return
+
     ms = time_launches(fused, args.steps, args.warmup, torch)
     F = flops(cfg)
-    tokens = cfg.B * cfg.T
     tflops = F / (ms * 1e-3) / 1e12
     result = {
         "metric": METRIC,
@@ -197,48 +241,16 @@ def main():
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
         },
     }
-    if not args.only_fused:
-        def plain():
-            ta.attention_plain(d["q"], d["k"], d["v"], out=out)
-        ms_plain = time_launches(plain, args.steps, args.warmup, torch)
-        dflt = cfg.replace(kq="pre", mix="post")
-        kw2 = dict(kw, kq="pre", mix="post")
-
-        def fused_default():
-            ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out,
-                       **kw2)
-        ms_dflt = time_launches(fused_default, args.steps, args.warmup, torch)
-        result["plain_attention"] = {
-            "ms": ms_plain, "tflops": cfg.B * cfg.M * (cfg.T * (cfg.T + 1) // 2) * 4 * cfg.d / (ms_plain * 1e-3) / 1e12,
-            "mta_slowdown": ms / ms_plain,
-        }
-        result["default_placement_same_shape"] = {
-            "ms": ms_dflt, "tokens_per_s": tokens / (ms_dflt * 1e-3),
-            "tflops": flops(dflt) / (ms_dflt * 1e-3) / 1e12,
-            "pct_bf16_peak": 100.0 * flops(dflt) / (ms_dflt * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "mta_slowdown_vs_plain": ms_dflt / ms_plain,
-        }
-        if not args.no_materialized:
-            ws = torch.empty(ta.materialized_workspace_bytes(cfg.B, cfg.T, cfg.M), dtype=torch.uint8, device="cuda")
-
-            def mat():
-                ta.forward_materialized(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"],
-                                        d["lam"], out=out, workspace=ws, **kw)
-            ms_mat = time_launches(mat, max(2, args.steps // 4), 1, torch)
-            mb = materialized_bytes(cfg)
-            result["materialized"] = {
-                "ms": ms_mat, "tokens_per_s": tokens / (ms_mat * 1e-3), "bytes": mb,
-                "gbs": mb / (ms_mat * 1e-3) / 1e9, "frac_hbm_peak": mb / (ms_mat * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                "workspace_gib": ws.numel() / 2 ** 30, "fused_speedup": ms_mat / ms,
-            }
-            del ws
+    ms_plain = time_launches(plain, args.steps, args.warmup, torch)
+    result["plain_attention"] = plain_record(ms_plain, ms)
+    result["default_placement_same_shape"] = default_record(
+        time_launches(fused_default, args.steps, args.warmup, torch), ms_plain)
+    if not args.no_materialized:
+        result["materialized"] = materialized_record(ms)
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "gcn_arch": getattr(props, "gcnArchName", "")}
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
-    else:
-        result["cpu_baseline"] = None
+    result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(cfg, inp, args.cpu_rows)
     print(json.dumps(result))
 
 
