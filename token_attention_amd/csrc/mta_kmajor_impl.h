@@ -109,9 +109,10 @@ struct Cfg {
   static constexpr int ZW = LB * 16;           // ring width (keys)
   static constexpr int LDZ = ZW + 8;           // fp16 stride
   static constexpr int ZROWS = ZPRE + R;
-  static constexpr int LDX = LB * 16 + 8;      // fp16 mixing exchange stride
+  static constexpr int XW = NKB * 4;           // exchange halves per lane and query block
+  static constexpr size_t SX_HALF = (size_t)CH * R * BK;  // one exchange buffer (halves)
   static constexpr size_t KS_BYTES = (size_t)CH * KROWS * LDK * 2;
-  static constexpr size_t SX_BYTES = MIXPRE ? (size_t)CH * R * LDX * 2 : 0;
+  static constexpr size_t SX_BYTES = MIXPRE ? 2 * SX_HALF * 2 : 0;  // double buffered
   static constexpr size_t VS_BYTES = (size_t)CH * BK * LDV * 2;
   static constexpr size_t ZB_BYTES = KQ ? (size_t)CH * ZROWS * LDZ * 2 : 0;
   static constexpr size_t PB_BYTES = PAIRS ? 2 * (size_t)CH * WPH * NQB * NC * 64 * 16 : 0;
@@ -266,11 +267,13 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
     }
   }
 
-  float wmix[C::CH];  // w[g][hu][:]; before softmax times the logit scale
+  float wmix[C::CH];  // w[g][hu][:] (mixing after softmax)
+  float wrot[C::CH];  // w[g][hu][(hu + k) % c_h] times the logit scale (mixing before softmax)
 #pragma unroll
   for (int u = 0; u < C::CH; ++u) {
-    const float wv = A.mix ? A.w[((size_t)g * C::CH + hu) * C::CH + u] : 0.0f;
-    wmix[u] = mix_pre ? wv * A.qk_scale : wv;
+    const float* wrow = A.w + ((size_t)g * C::CH + hu) * C::CH;
+    wmix[u] = A.mix ? wrow[u] : 0.0f;
+    wrot[u] = mix_pre ? wrow[(hu + u) & (C::CH - 1)] * A.qk_scale : 0.0f;
   }
 
   f32x4 acc[C::NP][C::NB][C::NQB];
@@ -376,37 +379,51 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
         s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
     }
   };
-  // mixing of logit blocks [LB0, LB1) across the heads of the group: fp16 exchange of the
-  // other heads through LDS; result in log2 units
+  // mixing of logit blocks [LB0, LB1) across the heads of the group: every wave writes its
+  // blocks (fp16) to the exchange buffer, lane-contiguous, and reads those of the other
+  // heads for the same rows; result in log2 units. The buffer alternates between two
+  // halves, so one barrier per exchange suffices: a half is rewritten only after every
+  // wave has passed the barrier of the exchange in between.
+  int xbuf = 0;
   auto mix_blocks = [&](auto lb0c, auto lb1c) {
-    constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value;
-    __syncthreads();  // the previous exchange has been read by every wave
+    constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value, XB = LB1 - LB0;
+    static_assert(XB >= 1 && XB <= C::NKB, "exchange width");
+    _Float16* X = Sx + xbuf * C::SX_HALF;
+    auto slot = [&](int u, int qb) {
+      return X + ((((size_t)u * C::WPH + slab) * C::NQB + qb) * 64 + lane) * C::XW;
+    };
 #pragma unroll
-    for (int lb = LB0; lb < LB1; ++lb) {
+    for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
+      for (int lb = LB0; lb < LB1; ++lb) {
         const f16x4 h = {(_Float16)s[lb][qb][0], (_Float16)s[lb][qb][1], (_Float16)s[lb][qb][2],
                          (_Float16)s[lb][qb][3]};
-        *reinterpret_cast<f16x4*>(Sx + ((size_t)hu * C::R + qs0 + qb * 16 + lq) * C::LDX + (lb - LB0) * 16 + lg * 4) = h;
+        *reinterpret_cast<f16x4*>(slot(hu, qb) + (lb - LB0) * 4) = h;
       }
     }
     __syncthreads();
+    f16x4 o[C::CH > 1 ? C::CH - 1 : 1][C::NQB][XB];
 #pragma unroll
-    for (int lb = LB0; lb < LB1; ++lb) {
+    for (int k = 1; k < C::CH; ++k) {
+      const int u = (hu + k) & (C::CH - 1);
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        f32x4 x = s[lb][qb] * wmix[hu];
+      for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-        for (int u = 0; u < C::CH; ++u) {
-          if (u == hu) continue;
-          const f16x4 o = *reinterpret_cast<const f16x4*>(
-              Sx + ((size_t)u * C::R + qs0 + qb * 16 + lq) * C::LDX + (lb - LB0) * 16 + lg * 4);
+        for (int x = 0; x < XB; ++x) o[k - 1][qb][x] = *reinterpret_cast<const f16x4*>(slot(u, qb) + x * 4);
+    }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] += wmix[u] * (float)o[i];
-        }
+    for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+      for (int lb = LB0; lb < LB1; ++lb) {
+        f32x4 x = s[lb][qb] * wrot[0];
+#pragma unroll
+        for (int k = 1; k < C::CH; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(wrot[k], (float)o[k - 1][qb][lb - LB0][i], x[i]);
         s[lb][qb] = x;
       }
     }
+    xbuf ^= 1;
   };
 
   // convolution of the ring (logical blocks of tile kt) -> cv[ob][qb]
