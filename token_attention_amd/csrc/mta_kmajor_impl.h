@@ -438,15 +438,14 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
     for (int ob = 0; ob < C::NKB; ++ob) {
       // slots of lane group lg: window keys 8*lg .. 8*lg+7 = block ob (lg < 2) or ob+1
       const int col = ring_col(kt, ob + (lg >> 1)) + (lg & 1) * 8;
+      // lags a >= c_q have an all-zero Toeplitz operand
 #pragma unroll
       for (int a = 0; a < C::CQM; ++a) {
-        if (a < A.c_q) {
 #pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) {
-            const f16x8 bz = *reinterpret_cast<const f16x8*>(
-                Zb + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq - a) * C::LDZ + col);
-            cv[ob][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tz[a], bz, cv[ob][qb], 0, 0, 0);
-          }
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const f16x8 bz = *reinterpret_cast<const f16x8*>(
+              Zb + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq - a) * C::LDZ + col);
+          cv[ob][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tz[a], bz, cv[ob][qb], 0, 0, 0);
         }
       }
     }
@@ -534,7 +533,7 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = -8 + 4 * lg + i;
-            if (!(gr >= 0 && j >= 0 && j <= gr)) z[i] = 0.0f;
+            z[i] = ((gr >= 0) & (j >= 0) & (j <= gr)) ? z[i] : 0.0f;
           }
           ring_store(0, 0, qb, z);
         }
@@ -564,7 +563,7 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                   const int j = j0 - 8 + lb * 16 + 4 * lg + i;
-                  if (!(gr >= 0 && j >= 0 && j <= gr)) z[i] = 0.0f;
+                  z[i] = ((gr >= 0) & (j >= 0) & (j <= gr)) ? z[i] : 0.0f;
                 }
               }
               ring_store(kt, lb, qb, z);
@@ -580,13 +579,13 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
           for (int qb = 0; qb < C::NQB; ++qb) {
             const int t = qs0 + qb * 16 + lq;
             const int gr = row0 + t;
-            const bool row_ok = t >= cq1 && gr < T_;
+            const bool row_ok = (t >= cq1) & (gr < T_);
 #pragma unroll
             for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int j = j0 + ob * 16 + 4 * lg + i;
-                if (!(row_ok && j <= gr)) xw[ob][qb][i] = NEG_INF;
+                xw[ob][qb][i] = (row_ok & (j <= gr)) ? xw[ob][qb][i] : NEG_INF;
               }
           }
         }
@@ -691,13 +690,13 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
             const int gr = row0 + qs0 + qb * 16 + lq;
-            const bool row_ok = gr >= 0 && gr < T_;
+            const bool row_ok = (gr >= 0) & (gr < T_);
 #pragma unroll
             for (int lb = 1; lb < C::LB; ++lb)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int j = j0 + (lb - 1) * 16 + 4 * lg + i;
-                if (!(row_ok && j <= gr)) s[lb][qb][i] = NEG_INF;
+                s[lb][qb][i] = (row_ok & (j <= gr)) ? s[lb][qb][i] : NEG_INF;
               }
           }
         }
@@ -745,20 +744,25 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
     }
     auto weights = [&](int kt, int lb, bool edge) {
       const int j0 = kt * C::BK;
+      f32x4 pv[C::NQB];
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        const int gr = row0 + qs0 + qb * 16 + lq;
-        f32x4 pv;
+      for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -shift[qb]));
-          if (edge) {
+        for (int i = 0; i < 4; ++i) pv[qb][i] = fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -shift[qb]));
+      if (edge) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const int gr = row0 + qs0 + qb * 16 + lq;
+          const bool row_ok = (gr >= 0) & (gr < T_);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             const int j = j0 - 8 + lb * 16 + 4 * lg + i;
-            if (!(gr >= 0 && gr < T_ && j >= 0 && j <= gr)) pv[i] = 0.0f;
+            pv[qb][i] = (row_ok & (j >= 0) & (j <= gr)) ? pv[qb][i] : 0.0f;
           }
         }
-        ring_store(kt, lb, qb, pv);
       }
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) ring_store(kt, lb, qb, pv[qb]);
     };
 
     // phase 2: exact weights (sliding key halo) -> convolution -> Mask_0 -> AV
@@ -792,7 +796,7 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int j = j0 + ob * 16 + 4 * lg + i;
-              if (!(t >= cq1 && gr < T_ && j <= gr)) cv[ob][qb][i] = 0.0f;
+              cv[ob][qb][i] = ((t >= cq1) & (gr < T_) & (j <= gr)) ? cv[ob][qb][i] : 0.0f;
             }
           }
       }
