@@ -59,8 +59,6 @@
 namespace mta {
 namespace kmajor {
 
-constexpr int NW = 4;
-constexpr int NT = 64 * NW;
 constexpr int ZPRE = 8;               // zero rows above the tile in the convolution input ring
 constexpr float SUM_LIMIT = 0x1p64f;  // largest row sum accepted with a fixed reference
 
@@ -88,9 +86,11 @@ struct Args {
   int xcd_remap;
 };
 
-template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool PAIRS_, int CQM_, bool MIXPRE_>
+template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool PAIRS_, int CQM_, bool MIXPRE_, int NW_ = 4>
 struct Cfg {
   static constexpr int D = D_, CH = CH_, QW = QW_, BK = BK_, CQM = CQM_;
+  static constexpr int NW = NW_;               // waves per workgroup
+  static constexpr int NT = 64 * NW;
   static constexpr bool KQ = KQ_, TWO = TWO_, PAIRS = PAIRS_, MIXPRE = MIXPRE_;
   static constexpr int WPH = NW / CH;          // waves per head
   static constexpr bool PRIV = WPH == 1;       // a wave owns its head: private K/V staging
@@ -182,7 +182,7 @@ __device__ __forceinline__ void team_sync() {
 }
 
 template <class C>
-__global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
+__global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   __bf16* Ks = reinterpret_cast<__bf16*>(smem + C::OFF_KS);
   _Float16* Sx = reinterpret_cast<_Float16*>(smem + C::OFF_SX);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NT, 1) void kmajor_kernel(Args A) {
         tz[a][s] = (_Float16)t;
       }
     }
-    for (int x = tid; x < C::CH * ZPRE * C::LDZ; x += NT) {
+    for (int x = tid; x < C::CH * ZPRE * C::LDZ; x += C::NT) {
       const int u = x / (ZPRE * C::LDZ);
       Zb[(size_t)u * C::ZROWS * C::LDZ + (x - u * ZPRE * C::LDZ)] = (_Float16)0.0f;
     }
@@ -902,7 +902,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.xcd_remap = (n_bg % 8 == 0) ? 1 : 0;
   const long long blocks = (long long)n_bg * a.n_tiles;
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kmajor_kernel<C>, dim3((unsigned)blocks), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(kmajor_kernel<C>, dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -913,7 +913,10 @@ hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr int BK = (CH == 4) ? 32 : 64;
   constexpr int QW = (PAIRS || CH == 2) ? 32 : 64;
   if constexpr (!PAIRS) {
-    if (p.mix == MIX_PRE) return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, true>>(p, stream);
+    if (p.mix == MIX_PRE) {
+      if constexpr (CH == 4 && TWO) return launch<Cfg<D, CH, 32, BK, KQ, TWO, PAIRS, CQM, true, 8>>(p, stream);
+      else return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, true>>(p, stream);
+    }
   }
   return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, false>>(p, stream);
 }
