@@ -126,10 +126,10 @@ struct Cfg {
   static constexpr size_t LDS_BYTES = OFF_ST + ST_BYTES;
   // staging: 16-byte chunks per team member for one regular tile
   static constexpr int HEADS = PRIV ? 1 : CH;
-  static constexpr int CPT = HEADS * BK * (D / 8) / TEAM;
+  static constexpr int CHUNKS = HEADS * BK * (D / 8);  // 16-byte chunks of one regular tile
+  static constexpr int CPT = (CHUNKS + TEAM - 1) / TEAM;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget exceeded");
   static_assert(QW % 16 == 0 && BK % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert((HEADS * BK * (D / 8)) % TEAM == 0, "staging split");
 };
 
 __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
@@ -328,7 +328,8 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   int goff[C::CPT], koff[C::CPT], voff[C::CPT];
 #pragma unroll
   for (int x = 0; x < C::CPT; ++x) {
-    const int c = trank + x * C::TEAM;
+    // surplus team members of the last round repeat the last chunk (identical writes)
+    const int c = min(trank + x * C::TEAM, C::CHUNKS - 1);
     const int u = thead + c / (C::BK * (C::D / 8));
     const int rem = c % (C::BK * (C::D / 8));
     const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
@@ -906,19 +907,22 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile shapes: per-pair accumulators take c_h * d * QW fp32 per wave, which limits QW;
-// LDS limits the key tile to 32 keys for groups of four heads.
+// Tile shapes. Without per-pair accumulators a workgroup has 8 waves of 32 query rows
+// (two waves per SIMD, so one wave's MFMA work overlaps the other's LDS and VALU work);
+// per-pair accumulators take c_h * d * QW fp32 per wave and keep 4 waves. LDS limits
+// the key tile to 32 keys for groups of four heads and for mixing before softmax.
 template <int D, int CH, bool KQ, bool TWO, bool PAIRS, int CQM>
 hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr int BK = (CH == 4) ? 32 : 64;
-  constexpr int QW = (PAIRS || CH == 2) ? 32 : 64;
-  if constexpr (!PAIRS) {
-    if (p.mix == MIX_PRE) {
-      if constexpr (CH == 4 && TWO) return launch<Cfg<D, CH, 32, BK, KQ, TWO, PAIRS, CQM, true, 8>>(p, stream);
-      else return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, true>>(p, stream);
-    }
+  // 8-wave tiles: 32-key tiles when the convolution runs before softmax (the ring, the
+  // convolution output and the logits are live together) or with mixing before softmax
+  constexpr int BK8 = (KQ && !TWO) ? 32 : BK;
+  if constexpr (PAIRS) {
+    return launch<Cfg<D, CH, 32, BK, KQ, TWO, true, CQM, false, 4>>(p, stream);
+  } else {
+    if (p.mix == MIX_PRE) return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK8), KQ, TWO, false, CQM, true, 8>>(p, stream);
+    return launch<Cfg<D, CH, 32, BK8, KQ, TWO, false, CQM, false, 8>>(p, stream);
   }
-  return launch<Cfg<D, CH, QW, BK, KQ, TWO, PAIRS, CQM, false>>(p, stream);
 }
 
 template <int D, int CH, bool KQ, bool TWO, bool PAIRS>
