@@ -185,6 +185,19 @@ def test_late_dominant_key(kq, mix, c_h, d):
     compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), want, what=f"late key {kq}/{mix}/{c_h} d={d}")
 
 
+@pytest.mark.parametrize("kq,mix", [(None, "pre"), (None, "post"), ("pre", "post"), ("post", "pre"), ("post", "post")])
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+def test_single_head_groups_scale(kq, mix, path):
+    """c_h = 1: each head is its own group and the mixing weight is a scalar per head;
+    without GroupNorm a negative weight must show up as a scaled (pre: sharpened or
+    flattened and reversed) output."""
+    cfg = mta_inputs.MTAConfig("ch1", 1, 90, 4, 64, 3, 5, 1, kq, mix, False, "bf16", 0.1, 0.0, seed=19)
+    inp = dict(case(cfg))
+    inp["w"] = np.array([-0.7, 1.3, 0.4, -1.1], dtype=np.float32).reshape(4, 1, 1)
+    want = oracle.forward_cfg(cfg, inp)
+    compare(cfg, run(path, cfg, dev_inputs(cfg, inp), inp["lam"]), want, what=f"{path} c_h=1 {kq}/{mix}")
+
+
 @pytest.mark.parametrize("c_q,c_k", [(1, 1), (1, 17), (8, 1), (8, 17), (2, 3), (5, 13)])
 @pytest.mark.parametrize("kq", ["pre", "post"])
 def test_kernel_sizes(c_q, c_k, kq):

@@ -86,12 +86,15 @@ struct Args {
   int xcd_remap;
 };
 
-template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool PAIRS_, int CQM_, bool MIXPRE_, int NW_ = 4>
+// KQ: a key-query convolution (TWO: after softmax); MIXPRE / MIXPOST: head mixing before /
+// after softmax.
+template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool MIXPOST_, int CQM_, bool MIXPRE_, int NW_ = 8>
 struct Cfg {
   static constexpr int D = D_, CH = CH_, QW = QW_, BK = BK_, CQM = CQM_;
   static constexpr int NW = NW_;               // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr bool KQ = KQ_, TWO = TWO_, PAIRS = PAIRS_, MIXPRE = MIXPRE_;
+  static constexpr bool KQ = KQ_, TWO = TWO_, MIXPOST = MIXPOST_, MIXPRE = MIXPRE_;
+  static constexpr bool MIX = MIXPRE || MIXPOST;
   static constexpr int WPH = NW / CH;          // waves per head
   static constexpr bool PRIV = WPH == 1;       // a wave owns its head: private K/V staging
   static constexpr int TEAM = PRIV ? 64 : NT;  // threads staging one head set
@@ -102,7 +105,6 @@ struct Cfg {
   static constexpr int KS = D / 32;            // k-steps of QK^T
   static constexpr int NB = D / 16;            // channel blocks
   static constexpr int NC = BK / 32;           // 32-key chunks of AV
-  static constexpr int NP = PAIRS ? CH : 1;
   static constexpr int KROWS = KQ ? BK + 16 : BK;  // K rows in LDS
   static constexpr int LDK = D + 8;            // K row stride (bf16): 16-byte reads conflict-free
   static constexpr int LDV = D + 16;           // V row stride (bf16): transposed reads conflict-free
@@ -112,18 +114,14 @@ struct Cfg {
   static constexpr int XW = NKB * 4;           // exchange halves per lane and query block
   static constexpr size_t SX_HALF = (size_t)CH * R * BK;  // one exchange buffer (halves)
   static constexpr size_t KS_BYTES = (size_t)CH * KROWS * LDK * 2;
-  static constexpr size_t SX_BYTES = MIXPRE ? 2 * SX_HALF * 2 : 0;  // double buffered
+  static constexpr size_t SX_BYTES = MIX ? 2 * SX_HALF * 2 : 0;  // double buffered
   static constexpr size_t VS_BYTES = (size_t)CH * BK * LDV * 2;
   static constexpr size_t ZB_BYTES = KQ ? (size_t)CH * ZROWS * LDZ * 2 : 0;
-  static constexpr size_t PB_BYTES = PAIRS ? 2 * (size_t)CH * WPH * NQB * NC * 64 * 16 : 0;
-  static constexpr size_t ST_BYTES = (size_t)CH * R * 4;
   static constexpr size_t OFF_KS = 0;
   static constexpr size_t OFF_SX = OFF_KS + KS_BYTES;
   static constexpr size_t OFF_VS = OFF_SX + SX_BYTES;
   static constexpr size_t OFF_ZB = OFF_VS + VS_BYTES;
-  static constexpr size_t OFF_PB = OFF_ZB + ZB_BYTES;
-  static constexpr size_t OFF_ST = OFF_PB + PB_BYTES;
-  static constexpr size_t LDS_BYTES = OFF_ST + ST_BYTES;
+  static constexpr size_t LDS_BYTES = OFF_ZB + ZB_BYTES;
   // staging: 16-byte chunks per team member for one regular tile
   static constexpr int HEADS = PRIV ? 1 : CH;
   static constexpr int CHUNKS = HEADS * BK * (D / 8);  // 16-byte chunks of one regular tile
@@ -188,8 +186,6 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   _Float16* Sx = reinterpret_cast<_Float16*>(smem + C::OFF_SX);
   __bf16* Vs = reinterpret_cast<__bf16*>(smem + C::OFF_VS);
   _Float16* Zb = reinterpret_cast<_Float16*>(smem + C::OFF_ZB);
-  u32x4* Pb = reinterpret_cast<u32x4*>(smem + C::OFF_PB);
-  float* St_l = reinterpret_cast<float*>(smem + C::OFF_ST);  // [CH][R] final row sums
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -267,22 +263,22 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     }
   }
 
-  float wmix[C::CH];  // w[g][hu][:] (mixing after softmax)
-  float wrot[C::CH];  // w[g][hu][(hu + k) % c_h] times the logit scale (mixing before softmax)
+  // w[g][hu][(hu + k) % c_h]; before softmax times the logit scale
+  float wrot[C::CH];
 #pragma unroll
   for (int u = 0; u < C::CH; ++u) {
     const float* wrow = A.w + ((size_t)g * C::CH + hu) * C::CH;
-    wmix[u] = A.mix ? wrow[u] : 0.0f;
-    wrot[u] = mix_pre ? wrow[(hu + u) & (C::CH - 1)] * A.qk_scale : 0.0f;
+    wrot[u] = C::MIX ? wrow[(hu + u) & (C::CH - 1)] * (mix_pre ? A.qk_scale : 1.0f) : 0.0f;
   }
 
-  f32x4 acc[C::NP][C::NB][C::NQB];
-#pragma unroll
-  for (int p = 0; p < C::NP; ++p)
+  f32x4 acc[C::NB][C::NQB];
+  auto clear_acc = [&]() {
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) acc[p][nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < C::NQB; ++qb) acc[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  clear_acc();
 
   float m_run[C::NQB], l_run[C::NQB];  // reference max (logit units), per-lane partial sums
 #pragma unroll
@@ -380,15 +376,22 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
     }
   };
-  // mixing of logit blocks [LB0, LB1) across the heads of the group: every wave writes its
-  // blocks (fp16) to the exchange buffer, lane-contiguous, and reads those of the other
-  // heads for the same rows; result in log2 units. The buffer alternates between two
-  // halves, so one barrier per exchange suffices: a half is rewritten only after every
-  // wave has passed the barrier of the exchange in between.
+  // Head mixing of blocks [LB0, LB1) of arr (logits before softmax, weights after) across
+  // the heads of the group: every wave writes its blocks (fp16) to the exchange buffer,
+  // lane-contiguous, and reads those of the other heads for the same rows. The buffer
+  // alternates between two halves, so one barrier per exchange suffices: a half is
+  // rewritten only after every wave has passed the barrier of the exchange in between.
   int xbuf = 0;
-  auto mix_blocks = [&](auto lb0c, auto lb1c) {
+  auto mix_blocks = [&](auto& arr, auto lb0c, auto lb1c) {
     constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value, XB = LB1 - LB0;
     static_assert(XB >= 1 && XB <= C::NKB, "exchange width");
+    if constexpr (C::CH == 1) {  // a group of one head: a scalar weight
+#pragma unroll
+      for (int lb = LB0; lb < LB1; ++lb)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) arr[lb][qb] = arr[lb][qb] * wrot[0];
+      return;
+    }
     _Float16* X = Sx + xbuf * C::SX_HALF;
     auto slot = [&](int u, int qb) {
       return X + ((((size_t)u * C::WPH + slab) * C::NQB + qb) * 64 + lane) * C::XW;
@@ -397,8 +400,8 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
       for (int lb = LB0; lb < LB1; ++lb) {
-        const f16x4 h = {(_Float16)s[lb][qb][0], (_Float16)s[lb][qb][1], (_Float16)s[lb][qb][2],
-                         (_Float16)s[lb][qb][3]};
+        const f16x4 h = {(_Float16)arr[lb][qb][0], (_Float16)arr[lb][qb][1], (_Float16)arr[lb][qb][2],
+                         (_Float16)arr[lb][qb][3]};
         *reinterpret_cast<f16x4*>(slot(hu, qb) + (lb - LB0) * 4) = h;
       }
     }
@@ -416,12 +419,12 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
       for (int lb = LB0; lb < LB1; ++lb) {
-        f32x4 x = s[lb][qb] * wrot[0];
+        f32x4 x = arr[lb][qb] * wrot[0];
 #pragma unroll
         for (int k = 1; k < C::CH; ++k)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(wrot[k], (float)o[k - 1][qb][lb - LB0][i], x[i]);
-        s[lb][qb] = x;
+        arr[lb][qb] = x;
       }
     }
     xbuf ^= 1;
@@ -457,76 +460,63 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
                               ring_col(kt, lb) + lg * 4) = h;
   };
 
-  // AV of weight fragments against V of head hu. Fragments come from w (own weights,
-  // blocks w[ob0 .. ob0 + NKB)) or, with mixing after softmax, from the exchange buffer.
-  auto av = [&](auto& wts, auto ob0c, const u32x4* pbuf) {
+  // AV of the weights of key blocks ob0 .. ob0 + NKB - 1 against V of head hu
+  auto av = [&](auto& wts, auto ob0c) {
     constexpr int OB0 = decltype(ob0c)::value;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
+      bf16x8 bp[C::NQB];
 #pragma unroll
-      for (int p = 0; p < C::NP; ++p) {
-        bf16x8 bp[C::NQB];
+      for (int qb = 0; qb < C::NQB; ++qb) bp[qb] = pack_bf16(wts[OB0 + 2 * c][qb], wts[OB0 + 2 * c + 1][qb]);
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          if constexpr (C::PAIRS) {
-            const u32x4 raw = pbuf[(((size_t)p * C::WPH + slab) * C::NQB + qb) * C::NC * 64 + c * 64 + lane];
-            bp[qb] = *reinterpret_cast<const bf16x8*>(&raw);
-          } else {
-            bp[qb] = pack_bf16(wts[OB0 + 2 * c][qb], wts[OB0 + 2 * c + 1][qb]);
-          }
-        }
+      for (int nb = 0; nb < C::NB; ++nb) {
+        // V^T operand: channels nb*16 + (lane & 15); k-slots = keys {4lg..4lg+3} of
+        // block 2c and {16+4lg..} of block 2c+1 of this tile
+        const s16x4 lo = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 4 * lg, nb * 16, C::LDV, lane);
+        const s16x4 hi = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 16 + 4 * lg, nb * 16, C::LDV, lane);
+        s16x4 v8[2] = {lo, hi};
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(v8);
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          // V^T operand: channels nb*16 + (lane & 15); k-slots = keys {4lg..4lg+3} of
-          // block 2c and {16+4lg..} of block 2c+1 of this tile
-          const s16x4 lo = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 4 * lg, nb * 16, C::LDV, lane);
-          const s16x4 hi = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 16 + 4 * lg, nb * 16, C::LDV, lane);
-          s16x4 v8[2] = {lo, hi};
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(v8);
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb)
-            acc[p][nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[qb], acc[p][nb][qb], 0, 0, 0);
-        }
+        for (int qb = 0; qb < C::NQB; ++qb)
+          acc[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[qb], acc[nb][qb], 0, 0, 0);
       }
     }
-  };
-  // publish this wave's weights in fragment layout (mixing after softmax)
-  auto publish = [&](auto& wts, auto ob0c, u32x4* pbuf) {
-    constexpr int OB0 = decltype(ob0c)::value;
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        const bf16x8 bp = pack_bf16(wts[OB0 + 2 * c][qb], wts[OB0 + 2 * c + 1][qb]);
-        pbuf[(((size_t)hu * C::WPH + slab) * C::NQB + qb) * C::NC * 64 + c * 64 + lane] =
-            *reinterpret_cast<const u32x4*>(&bp);
-      }
   };
   typedef std::integral_constant<int, 0> I0;
   typedef std::integral_constant<int, 1> I1;
   typedef std::integral_constant<int, C::NKB> INKB;
   typedef std::integral_constant<int, C::LB> ILB;
-  constexpr size_t PB_HALF = (size_t)C::CH * C::WPH * C::NQB * C::NC * 64;
   // first logit block of the tile that is new (block 0 is the carried key halo)
   typedef std::integral_constant<int, C::KQ ? 1 : 0> INEW;
 
+  // exact weights of the last pass (mixing after softmax): no division in the epilogue
+  bool normalized = false;
   if constexpr (!C::TWO) {
-    // ============================= one pass ==============================================
+    // ====================== key loop without a convolution after softmax ====================
     // the softmax sees log2 units: the convolution already folded the scale in
     const float ssc = C::KQ ? 1.0f : sc;
-    // mode 0: reference = the row's maximum over its first key tile (the normal case);
-    // mode 1: exact row maxima only (no weights); mode 2: weighted pass with those maxima.
-    int mode = 0;
+    // Passes over the keys. Without mixing after softmax: REF (reference = the row's
+    // maximum over its first key tile, weights exp2(x - ref), AV), and only if a row sum
+    // exceeds 2^64: MAX (exact row maxima) then FIXED (weights against them, AV).
+    // With mixing after softmax the weights of all heads must be exact before they are
+    // mixed: SUM (row sums against the first-tile reference; if too large MAX then
+    // SUMFIX), then NORM (exact weights, mixing, AV).
+    enum { REF, MAX, FIXED, SUM, SUMFIX, NORM };
+    int pass = C::MIXPOST ? SUM : REF;
+    float shift[C::NQB];  // NORM: m * ssc + log2(l) per row
     for (;;) {
+      const bool upd_first = pass == REF || pass == SUM;
+      const bool weigh = pass != MAX;
+      const bool with_av = pass == REF || pass == FIXED || pass == NORM;
       // prologue: tile 0's K rows (with the left halo block) and V rows; halo block 0 of
       // the convolution input computed here so that every tile computes blocks 1..NKB
       if constexpr (C::KQ) stage_k_direct(-8, C::BK + 16, 0);
       else stage_k_direct(0, C::BK, 0);
-      if (mode != 1) stage_v_direct(0);
+      if (with_av) stage_v_direct(0);
       team_sync<C>();
       if constexpr (C::KQ) {
         logit_block(0);
-        if constexpr (mix_pre) mix_blocks(I0{}, I1{});
+        if constexpr (mix_pre) mix_blocks(s, I0{}, I1{});
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           const int gr = row0 + qs0 + qb * 16 + lq;
@@ -542,11 +532,11 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int kt = 0; kt < n_kt; ++kt) {
         const int j0 = kt * C::BK;
         const bool more = kt + 1 < n_kt;
-        if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, mode != 1);
+        if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, with_av);
 #pragma unroll
         for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
-        if constexpr (mix_pre) mix_blocks(INEW{}, ILB{});
-        // weights of this tile: cv (after the convolution) or the logits themselves
+        if constexpr (mix_pre) mix_blocks(s, INEW{}, ILB{});
+        // softmax input of this tile: cv (after the convolution) or the logits themselves
         auto& xw = [&]() -> auto& {
           if constexpr (C::KQ) return cv;
           else return s;
@@ -590,8 +580,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
               }
           }
         }
-        if (mode == 1 || (mode == 0 && kt == 0)) {
-          // reference update: every tile in mode 1, the first tile in mode 0
+        if (pass == MAX || (upd_first && kt == 0)) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
             float mx = NEG_INF;
@@ -602,11 +591,11 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             m_run[qb] = fmaxf(m_run[qb], xgroup_max(mx));
           }
         }
-        if (mode != 1) {
-          // weights exp2(x - ref) in place; partial row sums per lane
+        if (weigh) {
+          // weights exp2(x - ref) (NORM: exact, exp2(x - shift)) in place; row sums per lane
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
-            const float mref = m_run[qb] * ssc;
+            const float mref = pass == NORM ? shift[qb] : m_run[qb] * ssc;
             float sum = 0.0f;
 #pragma unroll
             for (int ob = 0; ob < C::NKB; ++ob)
@@ -618,30 +607,24 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
               }
             l_run[qb] += sum;
           }
-          if constexpr (C::PAIRS) {
-            u32x4* pbuf = Pb + (kt & 1) * PB_HALF;
-            publish(xw, I0{}, pbuf);
-            __syncthreads();
-            av(xw, I0{}, pbuf);
-          } else {
-            av(xw, I0{}, nullptr);
-          }
+        }
+        if (with_av) {
+          if constexpr (C::MIXPOST) mix_blocks(xw, I0{}, INKB{});
+          av(xw, I0{});
         }
         team_sync<C>();  // the team is done with Ks, Vs and the ring of this tile
-        if (more) commit(C::KQ ? 16 : 0, mode != 1);
+        if (more) commit(C::KQ ? 16 : 0, with_av);
         team_sync<C>();
       }
-      if (mode == 1) {
-        mode = 2;
+      if (pass == MAX) {
+        pass = C::MIXPOST ? SUMFIX : FIXED;
+        clear_acc();
 #pragma unroll
-        for (int p = 0; p < C::NP; ++p)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int qb = 0; qb < C::NQB; ++qb) acc[p][nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < C::NQB; ++qb) l_run[qb] = 0.0f;
         __syncthreads();
         continue;
       }
+      if (pass == NORM) break;
       // final per-query sums (partial per lane group until here)
       bool big = false;
 #pragma unroll
@@ -649,8 +632,8 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         l_run[qb] = xgroup_sum(l_run[qb]);
         big |= !(l_run[qb] <= SUM_LIMIT);
       }
-      if (mode == 0 && __syncthreads_or(big ? 1 : 0)) {
-        mode = 1;
+      if (upd_first && __syncthreads_or(big ? 1 : 0)) {
+        pass = MAX;
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           m_run[qb] = -1e30f;
@@ -658,12 +641,17 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         }
         continue;
       }
+      if (pass == SUM || pass == SUMFIX) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb)
+          shift[qb] = l_run[qb] > 0.0f ? m_run[qb] * ssc + __builtin_log2f(l_run[qb]) : 1e30f;
+        pass = NORM;
+        normalized = true;
+        __syncthreads();
+        continue;
+      }
       break;
     }
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb)
-      if (lg == 0) St_l[hu * C::R + qs0 + qb * 16 + lq] = l_run[qb];
-    __syncthreads();
   } else {
     // ============================= two phase ============================================
     // phase 1: the row sums of head hu (after mixing) against a fixed reference, the
@@ -685,7 +673,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if (more) prefetch(j0 + C::BK, 0, false);
 #pragma unroll
         for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-        if constexpr (mix_pre) mix_blocks(I1{}, ILB{});
+        if constexpr (mix_pre) mix_blocks(s, I1{}, ILB{});
         const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
         if (edge) {
 #pragma unroll
@@ -771,7 +759,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     stage_v_direct(0);
     team_sync<C>();
     logit_block(0);
-    if constexpr (mix_pre) mix_blocks(I0{}, I1{});
+    if constexpr (mix_pre) mix_blocks(s, I0{}, I1{});
     weights(0, 0, true);
     for (int kt = 0; kt < n_kt; ++kt) {
       const int j0 = kt * C::BK;
@@ -779,7 +767,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       if (more) prefetch(j0 + C::BK + 8, j0 + C::BK, true);
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-      if constexpr (mix_pre) mix_blocks(I1{}, ILB{});
+      if constexpr (mix_pre) mix_blocks(s, I1{}, ILB{});
       const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) ||
                         (wrow_min + C::QW > T_);
 #pragma unroll
@@ -801,14 +789,8 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             }
           }
       }
-      if constexpr (C::PAIRS) {
-        u32x4* pbuf = Pb + (kt & 1) * PB_HALF;
-        publish(cv, I0{}, pbuf);
-        __syncthreads();
-        av(cv, I0{}, pbuf);
-      } else {
-        av(cv, I0{}, nullptr);
-      }
+      if constexpr (C::MIXPOST) mix_blocks(cv, I0{}, INKB{});
+      av(cv, I0{});
       team_sync<C>();
       if (more) commit(16, true);
       team_sync<C>();
@@ -822,25 +804,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     const int t = qs0 + qb * 16 + lq;
     const int gr = row0 + t;
     f32x4 o[C::NB];
-    if constexpr (C::PAIRS) {
+    const float scl = (C::TWO || normalized) ? 1.0f : (l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f);
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < C::NP; ++p) {
-        float scl = wmix[p];
-        if constexpr (!C::TWO) {
-          const float l = St_l[p * C::R + t];
-          scl = l > 0.0f ? scl / l : 0.0f;
-        }
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) o[nb] += acc[p][nb][qb] * scl;
-      }
-    } else {
-      float scl = 1.0f;
-      if constexpr (!C::TWO) scl = l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[0][nb][qb] * scl;
-    }
+    for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[nb][qb] * scl;
     float mean = 0.0f, inv = 1.0f;
     if (A.gn) {
       float sum = 0.0f;
@@ -907,46 +873,42 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile shapes. Without per-pair accumulators a workgroup has 8 waves of 32 query rows
-// (two waves per SIMD, so one wave's MFMA work overlaps the other's LDS and VALU work);
-// per-pair accumulators take c_h * d * QW fp32 per wave and keep 4 waves. LDS limits
-// the key tile to 32 keys for groups of four heads and for mixing before softmax.
-template <int D, int CH, bool KQ, bool TWO, bool PAIRS, int CQM>
+// Tile shapes: 8 waves of 32 query rows (two waves per SIMD, so one wave's MFMA work
+// overlaps the other's LDS and VALU work). Key tiles of 64 keys, 32 when the LDS holds
+// four heads, the fp16 exchange of a mixing group, or (convolution before softmax) when
+// the ring, the convolution output and the logits are live in registers together.
+template <int D, int CH, bool KQ, bool TWO, bool MIXPOST, int CQM>
 hipError_t launch_shape(const Problem& p, hipStream_t stream) {
-  constexpr int BK = (CH == 4) ? 32 : 64;
-  // 8-wave tiles: 32-key tiles when the convolution runs before softmax (the ring, the
-  // convolution output and the logits are live together) or with mixing before softmax
-  constexpr int BK8 = (KQ && !TWO) ? 32 : BK;
-  if constexpr (PAIRS) {
-    return launch<Cfg<D, CH, 32, BK, KQ, TWO, true, CQM, false, 4>>(p, stream);
-  } else {
-    if (p.mix == MIX_PRE) return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK8), KQ, TWO, false, CQM, true, 8>>(p, stream);
-    return launch<Cfg<D, CH, 32, BK8, KQ, TWO, false, CQM, false, 8>>(p, stream);
+  constexpr bool small = CH == 4 || (CH > 1 && MIXPOST) || (KQ && !TWO);
+  constexpr int BK = small ? 32 : 64;
+  if constexpr (!MIXPOST) {
+    if (p.mix == MIX_PRE) return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true>>(p, stream);
   }
+  return launch<Cfg<D, CH, 32, BK, KQ, TWO, MIXPOST, CQM, false>>(p, stream);
 }
 
-template <int D, int CH, bool KQ, bool TWO, bool PAIRS>
+template <int D, int CH, bool KQ, bool TWO, bool MIXPOST>
 hipError_t launch_cq(const Problem& p, hipStream_t stream) {
   if constexpr (!KQ) {
-    return launch_shape<D, CH, KQ, TWO, PAIRS, 1>(p, stream);
+    return launch_shape<D, CH, KQ, TWO, MIXPOST, 1>(p, stream);
   } else {
-    if (p.c_q <= 4) return launch_shape<D, CH, KQ, TWO, PAIRS, 4>(p, stream);
-    return launch_shape<D, CH, KQ, TWO, PAIRS, 8>(p, stream);
+    if (p.c_q <= 4) return launch_shape<D, CH, KQ, TWO, MIXPOST, 4>(p, stream);
+    return launch_shape<D, CH, KQ, TWO, MIXPOST, 8>(p, stream);
   }
 }
 
 template <int D, int CH>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
-  const bool pairs = p.mix == MIX_POST && CH > 1;
+  const bool post = p.mix == MIX_POST;
   if (p.kq == KQ_POST) {
-    if (pairs) return launch_cq<D, CH, true, true, true>(p, stream);
+    if (post) return launch_cq<D, CH, true, true, true>(p, stream);
     return launch_cq<D, CH, true, true, false>(p, stream);
   }
   if (p.kq == KQ_PRE) {
-    if (pairs) return launch_cq<D, CH, true, false, true>(p, stream);
+    if (post) return launch_cq<D, CH, true, false, true>(p, stream);
     return launch_cq<D, CH, true, false, false>(p, stream);
   }
-  if (pairs) return launch_cq<D, CH, false, false, true>(p, stream);
+  if (post) return launch_cq<D, CH, false, false, true>(p, stream);
   return launch_cq<D, CH, false, false, false>(p, stream);
 }
 
