@@ -28,37 +28,58 @@ __device__ __forceinline__ size_t map_index(int bm, int T, int i, int j) {
   return ((size_t)bm * T + i) * map_ld(T) + j;
 }
 
-// ---- logits: X[b,m,i,j] = q_i . k_j / sqrt(d) for a 64 x 64 tile --------------------
+// ---- logits: X[b,m,i,j] = q_i . k_j / sqrt(d) on a 128-query x 128-key tile ----------
+// The K tile is staged in LDS; each wave computes S^T blocks (keys are the MFMA rows), so a
+// lane holds four consecutive keys of one query and writes them as one float4.
 template <typename T, int D>
 __global__ __launch_bounds__(MT_THREADS) void logits_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            float* __restrict__ X, int Tn, int M, float scale) {
   typedef Mfma<T> MT;
+  constexpr int KT = 128, QPW = 32;             // keys per tile, queries per wave
+  constexpr int EPC = 16 / (int)sizeof(T);      // elements per 16-byte chunk
+  constexpr int LDKE = D + EPC;                 // padded K row (elements)
+  __shared__ __attribute__((aligned(16))) T Ks[KT * LDKE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int bm = blockIdx.z, b = bm / M, m = bm % M;
-  const int i0 = blockIdx.y * 64 + wave * 16, j0 = blockIdx.x * 64;
+  const int i0 = blockIdx.y * (4 * QPW) + wave * QPW, j0 = blockIdx.x * KT;
   const T* qb = q + (size_t)b * Tn * M * D;
   const T* kb = k + (size_t)b * Tn * M * D;
+  for (int x = threadIdx.x; x < KT * (D / EPC); x += MT_THREADS) {
+    const int r = x / (D / EPC), c = x % (D / EPC);
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (j0 + r < Tn) val = *reinterpret_cast<const uint4*>(kb + ((size_t)(j0 + r) * M + m) * D + c * EPC);
+    *reinterpret_cast<uint4*>(Ks + r * LDKE + c * EPC) = val;
+  }
   constexpr int KQ = D / MT::K;
-  typename MT::frag qf[KQ];
-  const int qi = i0 + lr;
+  typename MT::frag qf[QPW / 16][KQ];
 #pragma unroll
-  for (int ks = 0; ks < KQ; ++ks)
-    qf[ks] = qi < Tn ? MT::load(qb + ((size_t)qi * M + m) * D + ks * MT::K + lg * MT::KPL) : MT::zero();
+  for (int qb2 = 0; qb2 < QPW / 16; ++qb2) {
+    const int qi = i0 + qb2 * 16 + lr;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int kj = j0 + cb * 16 + lr;
-    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KQ; ++ks)
+      qf[qb2][ks] = qi < Tn ? MT::load(qb + ((size_t)qi * M + m) * D + ks * MT::K + lg * MT::KPL) : MT::zero();
+  }
+  __syncthreads();
+  const int ld = map_ld(Tn);
+#pragma unroll 2
+  for (int kb2 = 0; kb2 < KT / 16; ++kb2) {
+    f32x4 c[QPW / 16];
+#pragma unroll
+    for (int qb2 = 0; qb2 < QPW / 16; ++qb2) c[qb2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KQ; ++ks) {
-      const typename MT::frag bf =
-          kj < Tn ? MT::load(kb + ((size_t)kj * M + m) * D + ks * MT::K + lg * MT::KPL) : MT::zero();
-      c = MT::mma(qf[ks], bf, c);
-    }
+      const typename MT::frag kf = MT::load(Ks + (kb2 * 16 + lr) * LDKE + ks * MT::K + lg * MT::KPL);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + 4 * lg + r;
-      if (i < Tn && kj < Tn) X[map_index(bm, Tn, i, kj)] = c[r] * scale;
+      for (int qb2 = 0; qb2 < QPW / 16; ++qb2) c[qb2] = MT::mma(kf, qf[qb2][ks], c[qb2]);
+    }
+    const int j = j0 + kb2 * 16 + 4 * lg;
+#pragma unroll
+    for (int qb2 = 0; qb2 < QPW / 16; ++qb2) {
+      const int qi = i0 + qb2 * 16 + lr;
+      if (qi < Tn && j < ld)  // columns T .. ld-1 are row padding, never read
+        *reinterpret_cast<float4*>(X + map_index(bm, Tn, qi, j)) =
+            make_float4(c[qb2][0] * scale, c[qb2][1] * scale, c[qb2][2] * scale, c[qb2][3] * scale);
     }
   }
 }
@@ -99,25 +120,35 @@ __global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* __restrict__ X, 
 // ---- key-query convolution on a 64 x 64 output tile ----------------------------------
 // PRE:  input Mask_0(X) (zero for s > r and outside the map); output -inf for j > i.
 // POST: input A (already zero above the diagonal); output 0 for j > i (Mask_0).
+// The input tile (c_q - 1 halo rows, 16 halo columns each side) is staged with float4 loads;
+// each thread computes 16 consecutive outputs of one row and stores them as four float4.
 template <int CK, bool PRE>
 __global__ __launch_bounds__(MT_THREADS) void conv_kernel(const float* __restrict__ X, float* __restrict__ Y,
                                                          const float* __restrict__ theta, int Tn, int M,
                                                          int c_q) {
   constexpr int H0 = (CK - 1) / 2;
-  constexpr int TW = 64 + CK - 1;  // input tile width
-  constexpr int LD = TW + 1;
-  __shared__ float tile[(64 + 7) * LD];
+  constexpr int TW = 64 + 32;     // input columns j0 - 16 .. j0 + 79
+  constexpr int LD = TW + 4;
+  __shared__ __attribute__((aligned(16))) float tile[(64 + 7) * LD];
   __shared__ float th[8 * CK];
   const int bm = blockIdx.z, m = bm % M;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const int rows = 64 + c_q - 1;
+  const int ld = map_ld(Tn);
   for (int x = threadIdx.x; x < c_q * CK; x += MT_THREADS) th[x] = theta[(size_t)m * c_q * CK + x];
-  for (int x = threadIdx.x; x < rows * TW; x += MT_THREADS) {
-    const int rr = x / TW, cc = x % TW;
-    const int r = i0 - (c_q - 1) + rr, s = j0 - H0 + cc;
-    float val = 0.0f;
-    if (r >= 0 && r < Tn && s >= 0 && s < Tn && (!PRE || s <= r)) val = X[map_index(bm, Tn, r, s)];
-    tile[rr * LD + cc] = val;
+  for (int x = threadIdx.x; x < rows * (TW / 4); x += MT_THREADS) {
+    const int rr = x / (TW / 4), c4 = (x % (TW / 4)) * 4;
+    const int r = i0 - (c_q - 1) + rr, s = j0 - 16 + c4;
+    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r >= 0 && r < Tn && s >= 0 && s < ld) {  // a 4-aligned chunk is wholly inside or outside
+      val = *reinterpret_cast<const float4*>(X + map_index(bm, Tn, r, s));
+      const int lim = PRE ? min(r, Tn - 1) : Tn - 1;  // zero padding columns (and s > r before softmax)
+      if (s + 0 > lim) val.x = 0.0f;
+      if (s + 1 > lim) val.y = 0.0f;
+      if (s + 2 > lim) val.z = 0.0f;
+      if (s + 3 > lim) val.w = 0.0f;
+    }
+    *reinterpret_cast<float4*>(tile + rr * LD + c4) = val;
   }
   __syncthreads();
   const int orow = threadIdx.x >> 2;         // 0..63
@@ -126,8 +157,8 @@ __global__ __launch_bounds__(MT_THREADS) void conv_kernel(const float* __restric
 #pragma unroll
   for (int c = 0; c < 16; ++c) acc[c] = 0.0f;
   for (int a = 0; a < c_q; ++a) {
-    // output (orow, oc0 + c) reads tile row orow + c_q - 1 - a, tile column oc0 + c - e + 2*H0
-    const float* src = tile + (orow + c_q - 1 - a) * LD + oc0;
+    // output (orow, oc0 + c) reads tile row orow + c_q - 1 - a, tile column oc0 + 16 + c - e + H0
+    const float* src = tile + (orow + c_q - 1 - a) * LD + oc0 + 16 - H0;
     float seg[16 + CK - 1];
 #pragma unroll
     for (int x = 0; x < 16 + CK - 1; ++x) seg[x] = src[x];
@@ -140,36 +171,99 @@ __global__ __launch_bounds__(MT_THREADS) void conv_kernel(const float* __restric
   }
   const int i = i0 + orow;
   if (i < Tn) {
+    const float masked = PRE ? -__builtin_inff() : 0.0f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int j = j0 + oc0 + c;
-      if (j < Tn) Y[map_index(bm, Tn, i, j)] = (j > i) ? (PRE ? -__builtin_inff() : 0.0f) : acc[c];
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int j = j0 + oc0 + 4 * v4;
+      if (j < ld) {
+        float4 o;
+        o.x = (j + 0 > i) ? masked : acc[4 * v4 + 0];
+        o.y = (j + 1 > i) ? masked : acc[4 * v4 + 1];
+        o.z = (j + 2 > i) ? masked : acc[4 * v4 + 2];
+        o.w = (j + 3 > i) ? masked : acc[4 * v4 + 3];
+        *reinterpret_cast<float4*>(Y + map_index(bm, Tn, i, j)) = o;
+      }
     }
   }
 }
 
 // ---- causal row softmax, in place; one workgroup per (b, m, i) row --------------------
+// The row is read once into registers (NV float4 per thread), then written once.
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float t = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, t) : v + t;
+  }
+  __syncthreads();  // red is reused between the two reductions
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+#pragma unroll
+  for (int w = 1; w < MT_THREADS / 64; ++w) v = is_max ? fmaxf(v, red[w]) : v + red[w];
+  return v;
+}
+
+template <int NV>
 __global__ __launch_bounds__(MT_THREADS) void softmax_kernel(float* __restrict__ X, int Tn) {
   __shared__ float red[MT_THREADS / 64];
   const size_t row = blockIdx.x;  // (b*M + m)*T + i
   const int i = (int)(row % Tn);
+  const int ld = map_ld(Tn);
+  float4* x = reinterpret_cast<float4*>(X + row * ld);
+  const float NEG = -__builtin_inff();
+  float4 v[NV];
+  float mx = NEG;
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    const int j = (c * MT_THREADS + threadIdx.x) * 4;
+    v[c] = j < ld ? x[j / 4] : make_float4(NEG, NEG, NEG, NEG);
+    if (j + 0 > i) v[c].x = NEG;
+    if (j + 1 > i) v[c].y = NEG;
+    if (j + 2 > i) v[c].z = NEG;
+    if (j + 3 > i) v[c].w = NEG;
+    mx = fmaxf(mx, fmaxf(fmaxf(v[c].x, v[c].y), fmaxf(v[c].z, v[c].w)));
+  }
+  mx = block_reduce(mx, red, true);
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    v[c] = make_float4(expf(v[c].x - mx), expf(v[c].y - mx), expf(v[c].z - mx), expf(v[c].w - mx));
+    sum += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+  }
+  const float inv = 1.0f / block_reduce(sum, red, false);
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    const int j = (c * MT_THREADS + threadIdx.x) * 4;
+    if (j < ld) x[j / 4] = make_float4(v[c].x * inv, v[c].y * inv, v[c].z * inv, v[c].w * inv);
+  }
+}
+
+// rows longer than 16 * 4 * MT_THREADS: three passes over the row
+__global__ __launch_bounds__(MT_THREADS) void softmax_long_kernel(float* __restrict__ X, int Tn) {
+  __shared__ float red[MT_THREADS / 64];
+  const size_t row = blockIdx.x;
+  const int i = (int)(row % Tn);
   float* x = X + row * map_ld(Tn);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float mx = -__builtin_inff();
   for (int j = threadIdx.x; j <= i; j += MT_THREADS) mx = fmaxf(mx, x[j]);
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
+  mx = block_reduce(mx, red, true);
   float sum = 0.0f;
   for (int j = threadIdx.x; j <= i; j += MT_THREADS) sum += expf(x[j] - mx);
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-  if (lane == 0) red[wave] = sum;
-  __syncthreads();
-  sum = red[0] + red[1] + red[2] + red[3];
-  const float inv = 1.0f / sum;
+  const float inv = 1.0f / block_reduce(sum, red, false);
   for (int j = threadIdx.x; j < Tn; j += MT_THREADS) x[j] = (j <= i) ? expf(x[j] - mx) * inv : 0.0f;
+}
+
+hipError_t launch_softmax(float* X, const Problem& p, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)p.B * p.M * p.T));
+  const int nv = (map_ld(p.T) / 4 + MT_THREADS - 1) / MT_THREADS;
+  if (nv <= 1) hipLaunchKernelGGL(softmax_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  else if (nv <= 2) hipLaunchKernelGGL(softmax_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  else if (nv <= 4) hipLaunchKernelGGL(softmax_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  else if (nv <= 8) hipLaunchKernelGGL(softmax_kernel<8>, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  else if (nv <= 16) hipLaunchKernelGGL(softmax_kernel<16>, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  else hipLaunchKernelGGL(softmax_long_kernel, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  return hipGetLastError();
 }
 
 // ---- AV + GroupNorm + gate: 128 query rows x d of one (b, m) per workgroup ------------
@@ -329,8 +423,8 @@ hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
   T* out = reinterpret_cast<T*>(p.out);
   hipError_t e;
   const float scale = (float)(1.0 / __builtin_sqrt((double)p.d));
-  hipLaunchKernelGGL((logits_kernel<T, D>), dim3((p.T + 63) / 64, (p.T + 63) / 64, p.B * p.M), dim3(MT_THREADS),
-                     0, st, q, k, X, p.T, p.M, scale);
+  hipLaunchKernelGGL((logits_kernel<T, D>), dim3((p.T + 127) / 128, (p.T + 127) / 128, p.B * p.M),
+                     dim3(MT_THREADS), 0, st, q, k, X, p.T, p.M, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   float* cur = X;
   float* other = Y;
@@ -341,8 +435,7 @@ hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
     cur = other;
     other = t;
   }
-  hipLaunchKernelGGL(softmax_kernel, dim3((unsigned)((size_t)p.B * p.M * p.T)), dim3(MT_THREADS), 0, st, cur, p.T);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_softmax(cur, p, st)) != hipSuccess) return e;
   if (p.kq == KQ_POST) {
     if ((e = launch_conv(false, cur, other, p, st)) != hipSuccess) return e;
     float* t = cur;
