@@ -375,6 +375,139 @@ __global__ __launch_bounds__(MT_THREADS) void av_kernel(const float* __restrict_
     }
 }
 
+// ---- AV + GroupNorm + gate for bf16 tensors: O^T = V^T A^T on MFMA ------------------
+// 128 query rows of one (b, m) per workgroup, 32 per wave. The weights stream from the fp32
+// map straight into B operands: per 32 keys a lane reads two 16-byte pieces of its query row
+// (keys 4g..4g+3 and 16+4g..16+4g+3 for lane group g). V tiles are staged row-major in LDS and
+// read transposed (ds_read_b64_tr_b16) in the same key order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 v_transposed(const __bf16* Vs, int row0, int col0, int ld, int lane) {
+  const int j = lane & 15;  // lane 4k + m of a 16-lane group supplies row row0 + k, columns col0 + 4m ..
+  const __bf16* p = Vs + (size_t)(row0 + (j >> 2)) * ld + col0 + 4 * (j & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+template <int D>
+__global__ __launch_bounds__(MT_THREADS) void av_bf16_kernel(const float* __restrict__ A, const __bf16* __restrict__ v,
+                                                            __bf16* __restrict__ out, const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta, float lambda, int gn,
+                                                            int Tn, int M) {
+  constexpr int BKA = 32, NB = D / 16, NQ = 2;
+  constexpr int LDV = D + 16;
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[BKA * LDV];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lq = lane & 15, lg = lane >> 4;
+  const int bm = blockIdx.y, b = bm / M, m = bm % M;
+  const int i0 = blockIdx.x * 128 + wave * 32;
+  const __bf16* vb = v + (size_t)b * Tn * M * D;
+  const int ld = map_ld(Tn);
+  f32x4 acc[NB][NQ];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) acc[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_w = [&](int j0, float4 (&w)[NQ][2]) {
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      const int i = i0 + qb * 16 + lq;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = j0 + 16 * h + 4 * lg;
+        w[qb][h] = (i < Tn && j < ld) ? *reinterpret_cast<const float4*>(A + map_index(bm, Tn, i, j))
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  float4 wcur[NQ][2];
+  load_w(0, wcur);
+  for (int j0 = 0; j0 < Tn; j0 += BKA) {
+    __syncthreads();  // every wave is done with the previous V tile
+    for (int x = threadIdx.x; x < BKA * (D / 8); x += MT_THREADS) {
+      const int r = x / (D / 8), c = x % (D / 8);
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (j0 + r < Tn) val = *reinterpret_cast<const uint4*>(vb + ((size_t)(j0 + r) * M + m) * D + c * 8);
+      *reinterpret_cast<uint4*>(Vs + r * LDV + c * 8) = val;
+    }
+    float4 wnext[NQ][2];
+    load_w(j0 + BKA, wnext);  // next chunk in flight while this one is multiplied
+    __syncthreads();
+    bf16x8 bp[NQ];
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      const float4 lo = wcur[qb][0], hi = wcur[qb][1];
+      bp[qb] = bf16x8{(__bf16)lo.x, (__bf16)lo.y, (__bf16)lo.z, (__bf16)lo.w,
+                      (__bf16)hi.x, (__bf16)hi.y, (__bf16)hi.z, (__bf16)hi.w};
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      s16x4 v8[2] = {v_transposed(Vs, 4 * lg, nb * 16, LDV, lane), v_transposed(Vs, 16 + 4 * lg, nb * 16, LDV, lane)};
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(v8);
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) acc[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[qb], acc[nb][qb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      wcur[qb][0] = wnext[qb][0];
+      wcur[qb][1] = wnext[qb][1];
+    }
+  }
+  // lane (lq, lg) holds O[query i0 + 16 qb + lq][channels 16 nb + 4 lg .. +3]
+  __bf16* ob = out + (size_t)b * Tn * M * D;
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const int i = i0 + qb * 16 + lq;
+    float mean = 0.0f, inv = 1.0f;
+    if (gn) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sum += (acc[nb][qb][0] + acc[nb][qb][1]) + (acc[nb][qb][2] + acc[nb][qb][3]);
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      mean = sum * (1.0f / D);
+      float sq = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dv = acc[nb][qb][r] - mean;
+          sq += dv * dv;
+        }
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      inv = 1.0f / sqrtf(sq * (1.0f / D) + 1e-5f);
+    }
+    if (i < Tn) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int c0 = nb * 16 + 4 * lg;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          y[r] = acc[nb][qb][r];
+          if (gn) y[r] = lambda * (gamma[(size_t)m * D + c0 + r] * (y[r] - mean) * inv + beta[(size_t)m * D + c0 + r]);
+        }
+        __bf16 h[4] = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+        *reinterpret_cast<uint2*>(ob + ((size_t)i * M + m) * D + c0) = *reinterpret_cast<const uint2*>(h);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_av(const float* A, const Problem& p, hipStream_t st) {
+  const T* v = reinterpret_cast<const T*>(p.v);
+  T* out = reinterpret_cast<T*>(p.out);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((av_bf16_kernel<D>), dim3((p.T + 127) / 128, p.B * p.M), dim3(MT_THREADS), 0, st, A, v, out,
+                       p.gamma, p.beta, p.lambda, p.gn, p.T, p.M);
+  } else {
+    hipLaunchKernelGGL((av_kernel<T, D>), dim3((p.T + 127) / 128, p.B * p.M), dim3(MT_THREADS), 0, st, A, v, out,
+                       p.gamma, p.beta, p.lambda, p.gn, p.T, p.M);
+  }
+  return hipGetLastError();
+}
+
 template <int CK>
 hipError_t launch_conv_ck(bool pre, const float* X, float* Y, const Problem& p, hipStream_t st) {
   const dim3 grid((p.T + 63) / 64, (p.T + 63) / 64, p.B * p.M);
@@ -443,9 +576,7 @@ hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
     other = t;
   }
   if (p.mix == MIX_POST && (e = launch_mix(cur, p, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((av_kernel<T, D>), dim3((p.T + 127) / 128, p.B * p.M), dim3(MT_THREADS), 0, st, cur, v, out,
-                     p.gamma, p.beta, p.lambda, p.gn, p.T, p.M);
-  return hipGetLastError();
+  return launch_av<T, D>(cur, p, st);
 }
 
 }  // namespace
