@@ -85,6 +85,8 @@ __global__ __launch_bounds__(MT_THREADS) void logits_kernel(const T* __restrict_
 }
 
 // ---- head mixing, in place: X_u <- sum_u' w[g][u][u'] X_u' ---------------------------
+// Each thread mixes two consecutive float4 of every map of the group per step (2 x c_h
+// 16-byte loads in flight).
 template <int CH>
 __global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* __restrict__ X, const float* __restrict__ w,
                                                         int Tn, int M, size_t n4_per_map) {
@@ -96,23 +98,25 @@ __global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* __restrict__ X, 
   for (int u = 0; u < CH; ++u)
 #pragma unroll
     for (int x = 0; x < CH; ++x) wl[u][x] = w[((size_t)g * CH + u) * CH + x];
-  float4* base = reinterpret_cast<float4*>(X) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
-  for (size_t e = (size_t)blockIdx.x * MT_THREADS + threadIdx.x; e < n4_per_map;
-       e += (size_t)gridDim.x * MT_THREADS) {
-    float4 in[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) in[u] = base[(size_t)u * n4_per_map + e];
+  f32x4* base = reinterpret_cast<f32x4*>(X) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
+  for (size_t e = ((size_t)blockIdx.x * MT_THREADS + threadIdx.x) * 2; e < n4_per_map;
+       e += (size_t)gridDim.x * MT_THREADS * 2) {
+    const bool two = e + 1 < n4_per_map;
+    f32x4 in[CH][2];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      in[u][0] = base[(size_t)u * n4_per_map + e];
+      in[u][1] = two ? base[(size_t)u * n4_per_map + e + 1] : in[u][0];
+    }
 #pragma unroll
-      for (int x = 0; x < CH; ++x) {
-        o.x += wl[u][x] * in[x].x;
-        o.y += wl[u][x] * in[x].y;
-        o.z += wl[u][x] * in[x].z;
-        o.w += wl[u][x] * in[x].w;
+    for (int u = 0; u < CH; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 o = in[0][h] * wl[u][0];
+#pragma unroll
+        for (int x = 1; x < CH; ++x) o += in[x][h] * wl[u][x];
+        if (h == 0 || two) base[(size_t)u * n4_per_map + e + h] = o;
       }
-      base[(size_t)u * n4_per_map + e] = o;
     }
   }
 }
@@ -536,7 +540,7 @@ hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hip
 hipError_t launch_mix(float* X, const Problem& p, hipStream_t st) {
   const size_t n4 = (size_t)p.T * map_ld(p.T) / 4;  // whole padded map, padding included
   const int G = p.M / p.c_h;
-  size_t want = (n4 + MT_THREADS - 1) / MT_THREADS;
+  size_t want = (n4 + 2 * MT_THREADS - 1) / (2 * MT_THREADS);
   const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
   const dim3 grid(gx, p.B * G);
   switch (p.c_h) {
