@@ -892,7 +892,9 @@ hipError_t launch_cq(const Problem& p, hipStream_t stream) {
   if constexpr (!KQ) {
     return launch_shape<D, CH, KQ, TWO, MIXPOST, 1>(p, stream);
   } else {
+    // Toeplitz operands held in registers: one per query lag, rounded up
     if (p.c_q <= 4) return launch_shape<D, CH, KQ, TWO, MIXPOST, 4>(p, stream);
+    if (p.c_q <= 6) return launch_shape<D, CH, KQ, TWO, MIXPOST, 6>(p, stream);
     return launch_shape<D, CH, KQ, TWO, MIXPOST, 8>(p, stream);
   }
 }
