@@ -107,6 +107,29 @@ def time_launches(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps
 
 
+def launch_spread(fn, reps, torch):
+    """Min and median ms of reps individually timed calls (an event pair around each)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[0], t[len(t) // 2]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, n_rows: int):
     """The fp64 oracle on the host cores: every row of the workload (n_rows <= 0), or a seeded
     sample of n_rows query rows of batch 0."""
@@ -131,6 +154,7 @@ def cpu_baseline(cfg, inp, n_rows: int):
         "value": n_tok / dt,
         "unit": "tokens/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{what} (fp64 C++ oracle, OpenMP); {dt:.1f} s",
     }
@@ -146,6 +170,8 @@ def main():
     ap.add_argument("--no-materialized", action="store_true")
     ap.add_argument("--only", choices=["fused", "plain", "default", "materialized"], default=None,
                     help="run one path only (for counter collection); prints its timing")
+    ap.add_argument("--workload", type=int, default=HEADLINE,
+                    help="index of the workload in mta_inputs.CONFIGS for --only runs (profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
@@ -168,7 +194,10 @@ def main():
         return
 
     ta.lib()  # fail loudly if the HIP library is missing
-    cfg = mta_inputs.config(HEADLINE)
+    if args.workload != HEADLINE and not args.only:
+        print(json.dumps({"error": "--workload selects a profiling workload and needs --only"}))
+        sys.exit(2)
+    cfg = mta_inputs.config(args.workload)
     inp, d = gpu_inputs(cfg, torch)
     kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
     out = torch.empty_like(d["q"])
@@ -215,12 +244,13 @@ def main():
         fn = {"fused": fused, "plain": plain, "default": fused_default}.get(args.only)
         if fn is not None:
             ms_only = time_launches(fn, args.steps, args.warmup, torch)
-            print(json.dumps({"only": args.only, "ms": ms_only}))
+            print(json.dumps({"only": args.only, "workload": cfg.name, "ms": ms_only}))
         else:
-            print(json.dumps({"only": args.only, **materialized_record(None)}))
+            print(json.dumps({"only": args.only, "workload": cfg.name, **materialized_record(None)}))
         return
 
     ms = time_launches(fused, args.steps, args.warmup, torch)
+    ms_min, ms_med = launch_spread(fused, args.steps, torch)
     F = flops(cfg)
     tflops = F / (ms * 1e-3) / 1e12
     result = {
@@ -231,6 +261,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_launch_min": ms_min,
+        "ms_launch_median": ms_med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
