@@ -28,6 +28,17 @@ __device__ __forceinline__ size_t map_index(int bm, int T, int i, int j) {
   return ((size_t)bm * T + i) * map_ld(T) + j;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (separate L2 caches). Renumber a
+// 3D grid so that every XCD receives one contiguous run of tiles: neighbouring tiles, which
+// share halo cache lines, then run on the same XCD at about the same time.
+__device__ __forceinline__ uint3 xcd_tile() {
+  const unsigned gx = gridDim.x, gy = gridDim.y, n = gx * gy * gridDim.z;
+  const unsigned l = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const unsigned xcd = l % 8, k = l / 8, per = n / 8, rem = n % 8;
+  const unsigned t = xcd * per + (xcd < rem ? xcd : rem) + k;
+  return make_uint3(t % gx, (t / gx) % gy, t / (gx * gy));
+}
+
 // ---- logits: X[b,m,i,j] = q_i . k_j / sqrt(d) on a 128-query x 128-key tile ----------
 // The K tile is staged in LDS; each wave computes S^T blocks (keys are the MFMA rows), so a
 // lane holds four consecutive keys of one query and writes them as one float4.
@@ -45,11 +56,24 @@ __global__ __launch_bounds__(MT_THREADS) void logits_kernel(const T* __restrict_
   const int i0 = blockIdx.y * (4 * QPW) + wave * QPW, j0 = blockIdx.x * KT;
   const T* qb = q + (size_t)b * Tn * M * D;
   const T* kb = k + (size_t)b * Tn * M * D;
-  for (int x = threadIdx.x; x < KT * (D / EPC); x += MT_THREADS) {
-    const int r = x / (D / EPC), c = x % (D / EPC);
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (j0 + r < Tn) val = *reinterpret_cast<const uint4*>(kb + ((size_t)(j0 + r) * M + m) * D + c * EPC);
-    *reinterpret_cast<uint4*>(Ks + r * LDKE + c * EPC) = val;
+  {
+    // all loads first (their latencies overlap), then the LDS stores; rows past T are zero
+    constexpr int NL = KT * (D / EPC) / MT_THREADS;
+    static_assert(KT * (D / EPC) % MT_THREADS == 0, "K staging split");
+    uint4 buf[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int r = x / (D / EPC), c = x % (D / EPC);
+      const bool in = j0 + r < Tn;
+      buf[u] = *reinterpret_cast<const uint4*>(kb + ((size_t)(in ? j0 + r : 0) * M + m) * D + c * EPC);
+      if (!in) buf[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      *reinterpret_cast<uint4*>(Ks + (x / (D / EPC)) * LDKE + (x % (D / EPC)) * EPC) = buf[u];
+    }
   }
   constexpr int KQ = D / MT::K;
   typename MT::frag qf[QPW / 16][KQ];
@@ -135,24 +159,33 @@ __global__ __launch_bounds__(MT_THREADS) void conv_kernel(const float* __restric
   constexpr int LD = TW + 4;
   __shared__ __attribute__((aligned(16))) float tile[(64 + 7) * LD];
   __shared__ float th[8 * CK];
-  const int bm = blockIdx.z, m = bm % M;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const uint3 tl = xcd_tile();
+  const int bm = tl.z, m = bm % M;
+  const int i0 = tl.y * 64, j0 = tl.x * 64;
   const int rows = 64 + c_q - 1;
   const int ld = map_ld(Tn);
   for (int x = threadIdx.x; x < c_q * CK; x += MT_THREADS) th[x] = theta[(size_t)m * c_q * CK + x];
-  for (int x = threadIdx.x; x < rows * (TW / 4); x += MT_THREADS) {
+  // all loads of a thread are issued before any is stored, so their latencies overlap;
+  // chunks outside the map load a valid address and are zeroed afterwards
+  constexpr int NL = ((64 + 7) * (TW / 4) + MT_THREADS - 1) / MT_THREADS;
+  float4 buf[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int x = threadIdx.x + u * MT_THREADS;
     const int rr = x / (TW / 4), c4 = (x % (TW / 4)) * 4;
     const int r = i0 - (c_q - 1) + rr, s = j0 - 16 + c4;
-    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r >= 0 && r < Tn && s >= 0 && s < ld) {  // a 4-aligned chunk is wholly inside or outside
-      val = *reinterpret_cast<const float4*>(X + map_index(bm, Tn, r, s));
-      const int lim = PRE ? min(r, Tn - 1) : Tn - 1;  // zero padding columns (and s > r before softmax)
-      if (s + 0 > lim) val.x = 0.0f;
-      if (s + 1 > lim) val.y = 0.0f;
-      if (s + 2 > lim) val.z = 0.0f;
-      if (s + 3 > lim) val.w = 0.0f;
-    }
-    *reinterpret_cast<float4*>(tile + rr * LD + c4) = val;
+    const bool in = (x < rows * (TW / 4)) & (r >= 0) & (r < Tn) & (s >= 0) & (s < ld);
+    buf[u] = *reinterpret_cast<const float4*>(X + map_index(bm, Tn, in ? r : 0, in ? s : 0));
+    const int lim = PRE ? min(r, Tn - 1) : Tn - 1;  // padding columns, s > r before softmax
+    buf[u].x = (in & (s + 0 <= lim)) ? buf[u].x : 0.0f;
+    buf[u].y = (in & (s + 1 <= lim)) ? buf[u].y : 0.0f;
+    buf[u].z = (in & (s + 2 <= lim)) ? buf[u].z : 0.0f;
+    buf[u].w = (in & (s + 3 <= lim)) ? buf[u].w : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const int x = threadIdx.x + u * MT_THREADS;
+    if (x < rows * (TW / 4)) *reinterpret_cast<float4*>(tile + (x / (TW / 4)) * LD + (x % (TW / 4)) * 4) = buf[u];
   }
   __syncthreads();
   const int orow = threadIdx.x >> 2;         // 0..63
