@@ -456,18 +456,33 @@ __global__ __launch_bounds__(MT_THREADS) void av_bf16_kernel(const float* __rest
       }
     }
   };
+  // V rows of a chunk: NVL 16-byte pieces per thread (the last round may be partial)
+  constexpr int NVL = (BKA * (D / 8) + MT_THREADS - 1) / MT_THREADS;
+  auto load_v = [&](int j0, uint4 (&vv)[NVL]) {
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int r = x / (D / 8), c = x % (D / 8);
+      const bool in = (x < BKA * (D / 8)) & (j0 + r < Tn);
+      vv[u] = *reinterpret_cast<const uint4*>(vb + ((size_t)(in ? j0 + r : 0) * M + m) * D + (in ? c * 8 : 0));
+      if (!in) vv[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
   float4 wcur[NQ][2];
+  uint4 vcur[NVL];
   load_w(0, wcur);
+  load_v(0, vcur);
   for (int j0 = 0; j0 < Tn; j0 += BKA) {
     __syncthreads();  // every wave is done with the previous V tile
-    for (int x = threadIdx.x; x < BKA * (D / 8); x += MT_THREADS) {
-      const int r = x / (D / 8), c = x % (D / 8);
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (j0 + r < Tn) val = *reinterpret_cast<const uint4*>(vb + ((size_t)(j0 + r) * M + m) * D + c * 8);
-      *reinterpret_cast<uint4*>(Vs + r * LDV + c * 8) = val;
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      if (x < BKA * (D / 8)) *reinterpret_cast<uint4*>(Vs + (x / (D / 8)) * LDV + (x % (D / 8)) * 8) = vcur[u];
     }
     float4 wnext[NQ][2];
+    uint4 vnext[NVL];
     load_w(j0 + BKA, wnext);  // next chunk in flight while this one is multiplied
+    load_v(j0 + BKA, vnext);
     __syncthreads();
     bf16x8 bp[NQ];
 #pragma unroll
@@ -488,6 +503,8 @@ __global__ __launch_bounds__(MT_THREADS) void av_bf16_kernel(const float* __rest
       wcur[qb][0] = wnext[qb][0];
       wcur[qb][1] = wnext[qb][1];
     }
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) vcur[u] = vnext[u];
   }
   // lane (lq, lg) holds O[query i0 + 16 qb + lq][channels 16 nb + 4 lg .. +3]
   __bf16* ob = out + (size_t)b * Tn * M * D;
