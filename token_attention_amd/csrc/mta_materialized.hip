@@ -21,6 +21,7 @@ namespace mta {
 namespace {
 
 constexpr int MT_THREADS = 256;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 __host__ __device__ __forceinline__ int map_ld(int T) { return (T + 3) & ~3; }
 
@@ -218,6 +219,98 @@ __global__ __launch_bounds__(MT_THREADS) void conv_kernel(const float* __restric
         o.y = (j + 1 > i) ? masked : acc[4 * v4 + 1];
         o.z = (j + 2 > i) ? masked : acc[4 * v4 + 2];
         o.w = (j + 3 > i) ? masked : acc[4 * v4 + 3];
+        *reinterpret_cast<float4*>(Y + map_index(bm, Tn, i, j)) = o;
+      }
+    }
+  }
+}
+
+// ---- key-query convolution on fp16 MFMA (bf16 problems), 64 x 64 output tiles ----------
+// Same masks and staging as conv_kernel, the tile held as fp16. For every query lag a the
+// banded Toeplitz matrix of theta[m][a][.] (out key n x 32 window keys) is the A operand and
+// 8 consecutive window keys of input row i - a the B operand, so a lane ends with four
+// consecutive output keys of one query row, stored as one float4. A workgroup walks CT
+// consecutive tiles of one (b, m) map: the Toeplitz operands are built once, and the next
+// tile's loads are in flight while the current tile is multiplied.
+constexpr int CT = 8;
+
+template <bool PRE>
+__global__ __launch_bounds__(MT_THREADS) void conv_mfma_kernel(const float* __restrict__ X, float* __restrict__ Y,
+                                                              const float* __restrict__ theta, int Tn, int M,
+                                                              int c_q, int c_k, int ntx, int ntiles) {
+  constexpr int TW = 64 + 32;   // input columns j0 - 16 .. j0 + 79
+  constexpr int LDT = TW + 8;   // fp16 row stride
+  constexpr int NL = ((64 + 7) * (TW / 4) + MT_THREADS - 1) / MT_THREADS;
+  __shared__ __attribute__((aligned(16))) _Float16 tile[(64 + 7) * LDT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lq = lane & 15, lg = lane >> 4;
+  const int bm = blockIdx.y, m = bm % M;
+  const int h0 = (c_k - 1) / 2;
+  const int rows = 64 + c_q - 1;
+  const int ld = map_ld(Tn);
+  const int tfirst = blockIdx.x * CT, tend = min(tfirst + CT, ntiles);
+  float4 buf[NL];
+  auto load_tile = [&](int t) {
+    const int i0 = (t / ntx) * 64, j0 = (t % ntx) * 64;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int rr = x / (TW / 4), c4 = (x % (TW / 4)) * 4;
+      const int r = i0 - (c_q - 1) + rr, s = j0 - 16 + c4;
+      const bool in = (x < rows * (TW / 4)) & (r >= 0) & (r < Tn) & (s >= 0) & (s < ld);
+      buf[u] = *reinterpret_cast<const float4*>(X + map_index(bm, Tn, in ? r : 0, in ? s : 0));
+      const int lim = PRE ? min(r, Tn - 1) : Tn - 1;
+      buf[u].x = (in & (s + 0 <= lim)) ? buf[u].x : 0.0f;
+      buf[u].y = (in & (s + 1 <= lim)) ? buf[u].y : 0.0f;
+      buf[u].z = (in & (s + 2 <= lim)) ? buf[u].z : 0.0f;
+      buf[u].w = (in & (s + 3 <= lim)) ? buf[u].w : 0.0f;
+    }
+  };
+  load_tile(tfirst);
+  // Toeplitz operands: out key n = lq, window key k = 8 lg + t, tap e = n - k + 8 + h0
+  f16x8 tz[8];
+  const float* th = theta + (size_t)m * c_q * c_k;
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = lq - (8 * lg + t) + 8 + h0;
+      tz[a][t] = (_Float16)((a < c_q && e >= 0 && e < c_k) ? th[a * c_k + e] : 0.0f);
+    }
+  const float masked = PRE ? -__builtin_inff() : 0.0f;
+  for (int t = tfirst; t < tend; ++t) {
+    const int i0 = (t / ntx) * 64, j0 = (t % ntx) * 64;
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      if (x < rows * (TW / 4)) {
+        const f16x4 h = {(_Float16)buf[u].x, (_Float16)buf[u].y, (_Float16)buf[u].z, (_Float16)buf[u].w};
+        *reinterpret_cast<f16x4*>(tile + (x / (TW / 4)) * LDT + (x % (TW / 4)) * 4) = h;
+      }
+    }
+    __syncthreads();
+    if (t + 1 < tend) load_tile(t + 1);
+    const int rl = wave * 16 + lq;  // output row within the tile
+    const int i = i0 + rl;
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        if (a < c_q) {
+          // window keys j0 + 16 ob - 8 + k: tile column 16 ob + 8 + k
+          const f16x8 bz = *reinterpret_cast<const f16x8*>(tile + (rl + c_q - 1 - a) * LDT + 16 * ob + 8 + 8 * lg);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(tz[a], bz, c, 0, 0, 0);
+        }
+      }
+      const int j = j0 + 16 * ob + 4 * lg;
+      if (i < Tn && j < ld) {
+        float4 o;
+        o.x = (j + 0 > i) ? masked : c[0];
+        o.y = (j + 1 > i) ? masked : c[1];
+        o.z = (j + 2 > i) ? masked : c[2];
+        o.w = (j + 3 > i) ? masked : c[3];
         *reinterpret_cast<float4*>(Y + map_index(bm, Tn, i, j)) = o;
       }
     }
@@ -573,6 +666,17 @@ hipError_t launch_conv_ck(bool pre, const float* X, float* Y, const Problem& p, 
 }
 
 hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hipStream_t st) {
+  if (!p.fp32) {  // bf16 problems: fp16 MFMA Toeplitz convolution (fp32 problems stay exact)
+    const int ntx = (p.T + 63) / 64, ntiles = ntx * ntx;
+    const dim3 grid((ntiles + CT - 1) / CT, p.B * p.M);
+    if (pre)
+      hipLaunchKernelGGL(conv_mfma_kernel<true>, grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q,
+                         p.c_k, ntx, ntiles);
+    else
+      hipLaunchKernelGGL(conv_mfma_kernel<false>, grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q,
+                         p.c_k, ntx, ntiles);
+    return hipGetLastError();
+  }
   switch (p.c_k) {
     case 1: return launch_conv_ck<1>(pre, X, Y, p, st);
     case 3: return launch_conv_ck<3>(pre, X, Y, p, st);
