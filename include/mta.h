@@ -53,7 +53,8 @@ typedef enum mta_status {
   MTA_ERR_INVALID_ARG = 1, /* sizes <= 0, M % c_h != 0, NULL/misaligned pointers,
                               conflicting placement flags                        */
   MTA_ERR_UNSUPPORTED = 2, /* valid but not built: d, dtype, c_q > 8, even c_k,
-                              c_k > 17, c_h not in {1, 2, 4}                      */
+                              c_k > 17, c_h not in {1, 2, 4}, one batch of a
+                              tensor (T*M*d elements) of 2 GiB or more            */
   MTA_ERR_HIP = 3,         /* the HIP runtime reported an error                   */
   MTA_ERR_WORKSPACE = 4    /* workspace missing or smaller than required          */
 } mta_status;

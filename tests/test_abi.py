@@ -76,6 +76,7 @@ def test_valid_arguments_pass():
     (dict(d=80), mta.ERR_UNSUPPORTED),
     (dict(d=128, flags=mta.FP32), mta.ERR_UNSUPPORTED),
     (dict(c_q=0), mta.ERR_INVALID_ARG),
+    (dict(T=1 << 17, M=64, d=128), mta.ERR_UNSUPPORTED),  # one batch of q is 2 GiB
 ])
 def test_invalid_arguments_are_rejected(kw, status):
     assert _check(**kw) == status

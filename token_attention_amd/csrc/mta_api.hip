@@ -64,6 +64,9 @@ int validate(const void* q, const void* k, const void* v, const float* theta, co
   if (fp32 ? !(d == 16 || d == 32 || d == 64) : !(d == 32 || d == 64 || d == 96 || d == 128))
     return fail(MTA_ERR_UNSUPPORTED, "head size d=%d is not built for %s", d, fp32 ? "fp32" : "bf16");
   if ((long long)B * T * M * d > (1LL << 40)) return fail(MTA_ERR_INVALID_ARG, "tensor too large");
+  // the kernels address one batch of q, k, v or out with 32-bit byte offsets
+  if ((long long)T * M * d * (fp32 ? 4 : 2) >= (1LL << 31))
+    return fail(MTA_ERR_UNSUPPORTED, "one batch of a tensor (T*M*d elements) must be below 2 GiB");
   if (out == q || out == k || out == v) return fail(MTA_ERR_INVALID_ARG, "out may not alias an input");
   mta::Problem p;
   p.q = q;
