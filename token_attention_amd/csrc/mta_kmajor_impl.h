@@ -16,11 +16,13 @@
 //     read with ds_read_b64_tr_b16, which transposes a 4 x 16 block of b16 values
 //     within each 16-lane group.
 //
-// Work split. One workgroup (4 waves) owns batch b, head group g (c_h heads) and a tile
-// of R query rows; tile row t is global row i0 - (c_q - 1) + t (the first c_q - 1 rows
-// are the query halo of the convolution). Wave w owns head hu = w / (4/c_h) and a slab
-// of QW rows. When a wave owns all rows of its head (c_h = 4) it stages that head's K
-// and V tiles itself and nothing but the mixing exchange needs a workgroup barrier.
+// Work split. One workgroup of NW waves (8 in every launched shape: two per SIMD, so one
+// wave's MFMA work overlaps the other's LDS and VALU work) owns batch b, head group g (c_h
+// heads) and a tile of R query rows; tile row t is global row i0 - (c_q - 1) + t (the first
+// c_q - 1 rows are the query halo of the convolution). Wave w owns head hu = w / (NW/c_h)
+// and a slab of QW = 32 rows. The workgroup stages the K and V tiles of all its heads
+// together (a wave that owned all rows of its head would stage them alone and synchronise
+// with a wavefront fence only; no launched shape uses that).
 //
 // Key tiles of BK keys stream through LDS; the next tile is loaded into registers
 // while the current one is computed (global -> VGPR prefetch) and written to LDS
@@ -34,20 +36,17 @@
 // theta[a][.] is the A operand (constant per workgroup) and the input tile shifted by a
 // query rows is the B operand.
 //
-// Schedules:
-//   one pass  (no convolution, or convolution before softmax): every query row keeps one
-//             fixed reference, the maximum of its first key tile, and its weights
-//             exp2(x - ref) are never rescaled, so the accumulators see MFMA only. If a row's
-//             sum exceeds 2^64 (a later key far above the first tile's maximum) the
-//             workgroup repeats the loop: one pass for the exact row maxima, one weighted
-//             pass with them as references. With mixing after softmax the waves exchange
-//             their weights through LDS and keep c_h accumulators
-//             Acc[u'] = sum_j exp2(s_u' - ref_u') V_hu; epilogue O = sum_u' w[hu][u'] Acc[u'] / l_u'.
-//   two phase (convolution after softmax): phase 1 the row sums (fixed reference as above,
-//             an exact online pass if a sum exceeds 2^64), phase 2 exact weights ->
-//             convolution -> Mask_0 -> AV.
-// Mixing before softmax exchanges the logits of the new key blocks through LDS (fp16;
-// a wave's own head stays fp32).
+// Passes over the keys (every query row keeps one fixed softmax reference, the maximum of
+// its first key tile, so weights exp2(x - ref) are never rescaled and the accumulators are
+// touched by MFMA only; if a row sum exceeds 2^64 - a later key far above the first tile's
+// maximum - the workgroup repeats with exact row maxima):
+//   one pass   (no convolution after softmax, no mixing after softmax): weights against
+//              the reference, AV, division by the row sum in the epilogue;
+//   two passes (convolution or mixing after softmax): a statistics pass (row sums), then
+//              exact normalised weights -> [convolution -> Mask_0] -> [mixing] -> AV.
+// Mixing exchanges fp16 blocks of the other heads of the group through a double-buffered
+// LDS buffer: logits before softmax (a wave's own head stays fp32), normalised weights
+// after softmax.
 //
 // K and V tiles are loaded with buffer loads whose range ends at the last key row, so rows
 // past the sequence read as zero (they are masked) without per-row clamping.
