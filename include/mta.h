@@ -100,6 +100,27 @@ int mta_forward_materialized(const void* q, const void* k, const void* v, const 
                              int c_h, unsigned flags, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * mta_forward_rows: mta_forward for the output rows row_begin .. T-1 only, against
+ * all keys 0 .. T-1. Every output row depends only on keys up to itself and on the
+ * c_q-1 query rows before it (§2 causal mask; §3.1: the convolution reaches only
+ * current and past queries), so a suffix of rows can be computed on its own: with a
+ * cache holding k and v (and q) of the earlier positions this is the decode step
+ * (row_begin = T-1) or a prefill chunk. The rows written are identical to the same
+ * rows of mta_forward.
+ *   q            [B,T,M,d]; rows max(0, row_begin-(c_q-1)) .. T-1 are read (with a
+ *                KQ flag; rows row_begin .. T-1 without); earlier rows are not read
+ *   k, v         [B,T,M,d]; all rows are read
+ *   out          [B,T,M,d]; rows row_begin .. T-1 are written, earlier rows are left
+ *                as they were
+ *   row_begin    0 <= row_begin < T, else MTA_ERR_INVALID_ARG
+ * Other arguments and errors as for mta_forward. Allocates nothing.
+ */
+int mta_forward_rows(const void* q, const void* k, const void* v, const float* theta_kq,
+                     const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
+                     void* out, int B, int T, int M, int d, int c_q, int c_k, int c_h, int row_begin,
+                     unsigned flags, void* stream);
+
 /* Workspace needed by mta_forward_materialized: two fp32 [B, M, T, LD] maps, LD = T
  * rounded up to a multiple of 4. Returns 0 for invalid sizes. */
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags);

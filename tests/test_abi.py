@@ -107,3 +107,12 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ta.attention_plain(q, q.clone(), q.clone())
+
+
+@pytest.mark.parametrize("row_begin", [-1, 64, 1000])
+def test_row_range_outside_the_sequence_is_rejected(row_begin):
+    # validation happens before anything is launched, so this runs without a GPU
+    st = mta.lib().mta_forward_rows(P, P, P, P, P, P, P, 1.0, P + 0x100, 1, 64, 4, 128, 3, 5, 2, row_begin,
+                                    mta.KQ_PRE | mta.MIX_POST | mta.GN, None)
+    assert st == mta.ERR_INVALID_ARG
+    assert "row_begin" in mta.last_error()

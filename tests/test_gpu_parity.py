@@ -288,3 +288,48 @@ def test_workspace_too_small_is_reported():
                                 c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn,
                                 workspace=ws)
     assert e.value.status == 4
+
+
+# ---- row ranges: decode step and prefill chunks ------------------------------------------
+@pytest.mark.parametrize("row_begin", [0, 1, 97, 150, 299])
+@pytest.mark.parametrize("kq,mix,c_h,dtype,d", [(None, None, 1, "bf16", 128), ("pre", "post", 2, "bf16", 96),
+                                                ("post", "pre", 4, "bf16", 128), ("pre", "pre", 4, "bf16", 64),
+                                                ("post", "post", 2, "bf16", 128), ("pre", "post", 2, "fp32", 32)])
+def test_row_range_equals_full_forward(row_begin, kq, mix, c_h, dtype, d):
+    """mta_forward_rows writes exactly rows row_begin.. of mta_forward (same values, bit for
+    bit: every row is computed from the same keys in the same order) and leaves the rows
+    before it untouched."""
+    cfg = mta_inputs.MTAConfig("rows", 2, 300, 8, d, 4, 9, c_h, kq, mix, True, dtype, 0.1, 0.1, 1.0, 0.0, 0.8,
+                               seed=21)
+    inp = case(cfg)
+    dv = dev_inputs(cfg, inp)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    args = (dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"])
+    full = ta.forward(*args, **kw)
+    part = torch.full_like(full, 7.0)
+    ta.forward_rows(*args, row_begin=row_begin, out=part, **kw)
+    torch.cuda.synchronize()
+    f, p = full.float().cpu(), part.float().cpu()
+    log(f"  rows {row_begin}.. {kq}/{mix}/{c_h} {dtype}: max diff {float((f[:, row_begin:] - p[:, row_begin:]).abs().max()):.3e}")
+    assert torch.equal(p[:, row_begin:], f[:, row_begin:])
+    assert bool((p[:, :row_begin] == 7.0).all())
+
+
+@pytest.mark.parametrize("row_begin", [4095, 3584])
+def test_decode_step_and_chunk_at_full_size(row_begin):
+    """Decode step (the last row) and a 512-row prefill chunk of the T=4096 workload
+    against the oracle."""
+    cfg = mta_inputs.config(4)
+    inp = case(cfg)
+    rows = np.arange(row_begin, cfg.T, dtype=np.int32)
+    if len(rows) > 8:
+        rows = np.unique(np.concatenate([rows[:4], rows[-4:], mta_inputs.sample_rows(cfg.T, row_tile=61, n_random=8)]))
+        rows = rows[rows >= row_begin].astype(np.int32)
+    want = oracle.forward_cfg(cfg, inp, rows=rows)
+    dv = dev_inputs(cfg, inp)
+    out = ta.forward_rows(dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"],
+                          row_begin=row_begin, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix,
+                          gn=cfg.gn)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    compare(cfg, got, want, rows=rows, what=f"rows {row_begin}.. ({len(rows)} checked)")

@@ -5,5 +5,5 @@ this package only marshals torch device tensors into it.
 """
 from .mta import (  # noqa: F401
     FP32, GN, KQ_POST, KQ_PRE, MIX_POST, MIX_PRE, MTAError, attention_plain, check_args, forward,
-    forward_materialized, last_error, lib, library_path, materialized_workspace_bytes, placement_flags,
+    forward_materialized, forward_rows, last_error, lib, library_path, materialized_workspace_bytes, placement_flags,
 )

@@ -124,6 +124,22 @@ int mta_forward(const void* q, const void* k, const void* v, const float* theta_
   return hip_status(e, "mta_forward launch");
 }
 
+int mta_forward_rows(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                     const float* gn_gamma, const float* gn_beta, float lambda, void* out, int B, int T, int M,
+                     int d, int c_q, int c_k, int c_h, int row_begin, unsigned flags, void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, out, B, T, M, d, c_q, c_k, c_h,
+                          flags, &p);
+  if (st != MTA_OK) return st;
+  if (row_begin < 0 || row_begin >= T)
+    return fail(MTA_ERR_INVALID_ARG, "row_begin=%d must lie in [0, T=%d)", row_begin, T);
+  p.row_begin = row_begin;
+  bool unsupported = false;
+  const hipError_t e = mta::launch_fused(p, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no fused kernel for this shape");
+  return hip_status(e, "mta_forward_rows launch");
+}
+
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags) {
   (void)flags;
   return mta::materialized_workspace_bytes(B, T, M);

@@ -53,6 +53,7 @@ struct FusedArgs {
   int B, T, M;
   int c_q, c_k;
   int kq, mix, gn;
+  int row_begin;  // first output row
   int r_out;     // output rows per query tile
   int n_tiles;   // query tiles per (b, group)
   int n_groups;  // M / CH
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
   const int kq = A.kq;
   const int cq1 = kq ? A.c_q - 1 : 0;
   const int h0 = kq ? (A.c_k - 1) / 2 : 0;
-  const int i0 = qt * A.r_out;
+  const int i0 = A.row_begin + qt * A.r_out;
   const int row0 = i0 - cq1;  // global row of tile row 0
   const int last_row = min(i0 + A.r_out, T_) - 1;
   const int n_kt = last_row / C::BK + 1;
@@ -628,7 +629,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.c_q = p.kq ? p.c_q : 1;
   a.c_k = p.kq ? p.c_k : 1;
   a.r_out = C::R - (a.c_q - 1);
-  a.n_tiles = (p.T + a.r_out - 1) / a.r_out;
+  a.row_begin = p.row_begin;
+  a.n_tiles = (p.T - p.row_begin + a.r_out - 1) / a.r_out;
   a.n_groups = p.M / C::CH;
   a.qk_scale = (float)(1.4426950408889634 / __builtin_sqrt((double)p.d));
   const int n_bg = p.B * a.n_groups;

@@ -27,6 +27,7 @@ struct Problem {
   int mix;   // MixMode
   int gn;    // 0/1
   int fp32;  // 0: bf16 tensors, 1: fp32 tensors
+  int row_begin = 0;  // fused path: output rows row_begin .. T-1 only
 };
 
 // Returns hipSuccess or the launch error; sets *unsupported when no kernel is

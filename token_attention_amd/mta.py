@@ -25,7 +25,7 @@ FP32 = 0x20
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 EXPORTED = [
-    "mta_forward", "mta_forward_materialized", "mta_materialized_workspace_bytes",
+    "mta_forward", "mta_forward_rows", "mta_forward_materialized", "mta_materialized_workspace_bytes",
     "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
 ]
 
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         vp, fp, i, u = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
         L.mta_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 7 + [u, vp]
         L.mta_forward.restype = i
+        L.mta_forward_rows.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 8 + [u, vp]
+        L.mta_forward_rows.restype = i
         L.mta_forward_materialized.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 7 + \
             [u, vp, ctypes.c_size_t, vp]
         L.mta_forward_materialized.restype = i
@@ -130,6 +132,21 @@ def forward(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
         _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
         float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, fl, _stream(stream)))
+    return out
+
+
+def forward_rows(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, row_begin: int,
+                 c_q: int = 1, c_k: int = 1, c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None,
+                 gn: bool = False, out=None, stream=None) -> torch.Tensor:
+    """``mta_forward_rows``: output rows row_begin .. T-1 only (decode step, prefill chunk);
+    rows of ``out`` before row_begin are left as they are."""
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
+    _check(lib().mta_forward_rows(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, int(row_begin), fl, _stream(stream)))
     return out
 
 
