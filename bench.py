@@ -285,6 +285,16 @@ def main():
     result["plain_attention"] = plain_record(ms_plain, ms)
     result["default_placement_same_shape"] = default_record(
         time_launches(fused_default, args.steps, args.warmup, torch), ms_plain)
+    # a suffix of rows against all keys: one decode step (the last row of every sequence) and
+    # a 512-row prefill chunk, both at the headline placement
+    rows_rec = {}
+    for name, rb in (("decode_step", cfg.T - 1), ("prefill_chunk_512", cfg.T - 512)):
+        def part(rb=rb):
+            ta.forward_rows(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"],
+                            row_begin=rb, out=out, **kw)
+        ms_rows = time_launches(part, args.steps, args.warmup, torch)
+        rows_rec[name] = {"row_begin": rb, "ms": ms_rows, "tokens_per_s": cfg.B * (cfg.T - rb) / (ms_rows * 1e-3)}
+    result["rows_forward"] = rows_rec
     if not args.no_materialized:
         result["materialized"] = materialized_record(ms)
     props = torch.cuda.get_device_properties(0)
