@@ -28,9 +28,15 @@ CFLAGS = [
 ]
 
 
+# The two-phase kernels (convolution after softmax) schedule better with the backend's
+# instruction-level-parallelism strategy; the other kernels keep the default.
+EXTRA_FLAGS = {"_postconv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    extra = [f for suffix, fl in EXTRA_FLAGS.items() if src.endswith(suffix) for f in fl]
+    cmd = [HIPCC] + CFLAGS + extra + ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
     if r.returncode != 0:

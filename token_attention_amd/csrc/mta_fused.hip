@@ -11,6 +11,10 @@ hipError_t launch_fused_bf16_d32(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d64(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d96(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d128(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d32_postconv(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d64_postconv(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d96_postconv(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d128_postconv(const Problem& p, hipStream_t stream);
 
 bool fused_supported(const Problem& p) {
   const int ch = p.mix ? p.c_h : 1;
@@ -31,6 +35,13 @@ hipError_t launch_fused(const Problem& p, hipStream_t stream, bool* unsupported)
       case 16: return launch_fused_f32_d16(p, stream);
       case 32: return launch_fused_f32_d32(p, stream);
       case 64: return launch_fused_f32_d64(p, stream);
+    }
+  } else if (p.kq == KQ_POST) {
+    switch (p.d) {
+      case 32: return launch_fused_bf16_d32_postconv(p, stream);
+      case 64: return launch_fused_bf16_d64_postconv(p, stream);
+      case 96: return launch_fused_bf16_d96_postconv(p, stream);
+      case 128: return launch_fused_bf16_d128_postconv(p, stream);
     }
   } else {
     switch (p.d) {

@@ -1,8 +1,9 @@
-// Fused kernel instantiations for bf16 tensors with head size 32 (key-major schedule).
+// Fused kernel instantiations for bf16 tensors with head size 32 (key-major schedule):
+// placements without a convolution after softmax.
 #include "mta_kmajor_impl.h"
 
 namespace mta {
 hipError_t launch_fused_bf16_d32(const Problem& p, hipStream_t stream) {
-  return kmajor::launch_d<32>(p, stream);
+  return kmajor::launch_d<32, false>(p, stream);
 }
 }  // namespace mta

@@ -1,8 +1,9 @@
-// Fused kernel instantiations for bf16 tensors with head size 64 (key-major schedule).
+// Fused kernel instantiations for bf16 tensors with head size 64 (key-major schedule):
+// placements without a convolution after softmax.
 #include "mta_kmajor_impl.h"
 
 namespace mta {
 hipError_t launch_fused_bf16_d64(const Problem& p, hipStream_t stream) {
-  return kmajor::launch_d<64>(p, stream);
+  return kmajor::launch_d<64, false>(p, stream);
 }
 }  // namespace mta

@@ -900,28 +900,31 @@ hipError_t launch_cq(const Problem& p, hipStream_t stream) {
   }
 }
 
-template <int D, int CH>
+// The schedules with a convolution after softmax (POSTCONV) and the others are instantiated in
+// separate translation units, which are compiled with different instruction-scheduling options.
+template <int D, int CH, bool POSTCONV>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
   const bool post = p.mix == MIX_POST;
-  if (p.kq == KQ_POST) {
+  if constexpr (POSTCONV) {
     if (post) return launch_cq<D, CH, true, true, true>(p, stream);
     return launch_cq<D, CH, true, true, false>(p, stream);
+  } else {
+    if (p.kq == KQ_PRE) {
+      if (post) return launch_cq<D, CH, true, false, true>(p, stream);
+      return launch_cq<D, CH, true, false, false>(p, stream);
+    }
+    if (post) return launch_cq<D, CH, false, false, true>(p, stream);
+    return launch_cq<D, CH, false, false, false>(p, stream);
   }
-  if (p.kq == KQ_PRE) {
-    if (post) return launch_cq<D, CH, true, false, true>(p, stream);
-    return launch_cq<D, CH, true, false, false>(p, stream);
-  }
-  if (post) return launch_cq<D, CH, false, false, true>(p, stream);
-  return launch_cq<D, CH, false, false, false>(p, stream);
 }
 
-template <int D>
+template <int D, bool POSTCONV>
 hipError_t launch_d(const Problem& p, hipStream_t stream) {
   const int ch = p.mix ? p.c_h : 1;
   switch (ch) {
-    case 1: return launch_ch<D, 1>(p, stream);
-    case 2: return launch_ch<D, 2>(p, stream);
-    case 4: return launch_ch<D, 4>(p, stream);
+    case 1: return launch_ch<D, 1, POSTCONV>(p, stream);
+    case 2: return launch_ch<D, 2, POSTCONV>(p, stream);
+    case 4: return launch_ch<D, 4, POSTCONV>(p, stream);
   }
   return hipErrorInvalidValue;
 }
