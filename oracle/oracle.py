@@ -13,8 +13,8 @@ _SRC = os.path.join(_HERE, "mta_oracle.cpp")
 _LIB = os.path.join(_HERE, "libmta_oracle.so")
 _lib = None
 
-_KQ = {None: 0, "pre": 1, "post": 2}
-_MIX = {None: 0, "pre": 1, "post": 2}
+# placement bits: 1 before softmax, 2 after softmax, 3 both sides
+_SIDES = {None: 0, "pre": 1, "post": 2, "both": 3}
 
 
 def library_path() -> str:
@@ -67,7 +67,10 @@ def forward(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0
             n_threads: int = 0):
     """Evaluate the layer in fp64.
 
-    q, k, v: ``[B, T, M, d]``. theta ``[M, c_q, c_k]``; w ``[M/c_h, c_h, c_h]``;
+    q, k, v: ``[B, T, M, d]``. ``kq`` and ``mix`` are ``None``, ``"pre"``, ``"post"`` or
+    ``"both"`` (before and after softmax, each side with its own parameters). theta
+    ``[M, c_q, c_k]`` (``[2, M, c_q, c_k]`` for ``"both"``: the kernels before softmax,
+    then those after); w ``[M/c_h, c_h, c_h]`` (``[2, M/c_h, c_h, c_h]`` for ``"both"``);
     gamma, beta ``[M*d]``. ``rows``: optional list of query rows to compute (all
     otherwise). Returns ``out`` (``[B, T, M, d]`` float64; rows not requested are
     NaN) and, with ``return_maps``, the attention rows applied to V
@@ -78,12 +81,14 @@ def forward(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0
     assert k.shape == q.shape and v.shape == q.shape
     if kq is None:
         c_q = c_k = 1
+    n_kq = 2 if kq == "both" else 1
+    n_mix = 2 if mix == "both" else 1
     th = _f64(theta) if kq is not None else np.zeros((M, c_q, c_k))
     ww = _f64(w) if mix is not None else np.zeros((M // c_h, c_h, c_h))
     ga = _f64(gamma) if gn else np.ones(M * d)
     be = _f64(beta) if gn else np.zeros(M * d)
-    assert th.shape == (M, c_q, c_k), th.shape
-    assert ww.shape == (M // c_h, c_h, c_h), ww.shape
+    assert th.shape == ((n_kq,) if n_kq > 1 else ()) + (M, c_q, c_k), th.shape
+    assert ww.shape == ((n_mix,) if n_mix > 1 else ()) + (M // c_h, c_h, c_h), ww.shape
     out = np.full((B, T, M, d), np.nan)
     if rows is None:
         rows_arr, n_rows, rows_ptr = None, T, None
@@ -94,7 +99,7 @@ def forward(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0
     maps = np.zeros((B, M, n_rows, T)) if return_maps else None
     rc = _load().mta_oracle_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(th), _ptr(ww), _ptr(ga), _ptr(be), float(lam), _ptr(out),
-        B, T, M, d, c_q, c_k, c_h, _KQ[kq], _MIX[mix], int(bool(gn)), rows_ptr,
+        B, T, M, d, c_q, c_k, c_h, _SIDES[kq], _SIDES[mix], int(bool(gn)), rows_ptr,
         n_rows if rows_arr is not None else 0, _ptr(maps), int(n_threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")

@@ -32,32 +32,43 @@ def _conv_full(Z: np.ndarray, th: np.ndarray) -> np.ndarray:
     return Y
 
 
+def _sides(placement, params):
+    """(before-softmax, after-softmax) parameters of a placement; None where absent."""
+    if placement == "both":
+        return params[0], params[1]
+    return (params if placement == "pre" else None), (params if placement == "post" else None)
+
+
 def forward(q, k, v, theta, w, gamma, beta, lam, *, c_q, c_k, c_h, kq, mix, gn):
+    """kq / mix: None, "pre", "post" or "both"; with "both" theta / w hold the
+    before-softmax parameters at index 0 and the after-softmax ones at index 1."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, T, M, d = q.shape
+    th_pre, th_post = _sides(kq, theta)
+    w_pre, w_post = _sides(mix, w)
     out = np.zeros((B, T, M, d))
     future = np.triu(np.ones((T, T), dtype=bool), 1)  # j > i
     for b in range(B):
         for g in range(M // c_h):
             heads = [g * c_h + u for u in range(c_h)]
             logit = [q[b, :, m, :] @ k[b, :, m, :].T / math.sqrt(d) for m in heads]
-            if mix == "pre":
-                logit = [sum(w[g, u, x] * logit[x] for x in range(c_h)) for u in range(c_h)]
+            if w_pre is not None:
+                logit = [sum(w_pre[g, u, x] * logit[x] for x in range(c_h)) for u in range(c_h)]
             A = []
             for u, m in enumerate(heads):
                 L = logit[u]
-                if kq == "pre":
-                    L = _conv_full(np.where(future, 0.0, L), np.asarray(theta[m], np.float64))
+                if th_pre is not None:
+                    L = _conv_full(np.where(future, 0.0, L), np.asarray(th_pre[m], np.float64))
                 L = np.where(future, -np.inf, L)
                 P = np.exp(L - L.max(axis=1, keepdims=True))
                 P = P / P.sum(axis=1, keepdims=True)
-                if kq == "post":
-                    P = np.where(future, 0.0, _conv_full(P, np.asarray(theta[m], np.float64)))
+                if th_post is not None:
+                    P = np.where(future, 0.0, _conv_full(P, np.asarray(th_post[m], np.float64)))
                 A.append(P)
-            if mix == "post":
-                A = [sum(w[g, u, x] * A[x] for x in range(c_h)) for u in range(c_h)]
+            if w_post is not None:
+                A = [sum(w_post[g, u, x] * A[x] for x in range(c_h)) for u in range(c_h)]
             for u, m in enumerate(heads):
                 O = A[u] @ v[b, :, m, :]
                 if gn:

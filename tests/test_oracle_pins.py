@@ -57,12 +57,17 @@ def _softmax_rows(L):
 # (§4.6 ablation on initialisation; Appendix I inserts identity-initialised MTA into
 # pretrained models).
 @pytest.mark.parametrize("kq,mix,c_q,c_k,c_h", [("pre", "post", 3, 5, 2), ("post", "pre", 4, 9, 4),
-                                                ("pre", "post", 6, 11, 4), (None, None, 1, 1, 1)])
+                                                ("pre", "post", 6, 11, 4), (None, None, 1, 1, 1),
+                                                ("both", "both", 3, 5, 2)])
 def test_identity_kernels_equal_sdpa(kq, mix, c_q, c_k, c_h):
     B, T, M, d = 2, 37, 4, 8
     q, k, v = _rand(B, T, M, d, 1)
-    out = oracle.forward(q, k, v, _delta(M, c_q, c_k), _eye(M, c_h), c_q=c_q, c_k=c_k, c_h=c_h,
-                         kq=kq, mix=mix, gn=False)
+    th, w = _delta(M, c_q, c_k), _eye(M, c_h)
+    if kq == "both":
+        th = np.stack([th, th])
+    if mix == "both":
+        w = np.stack([w, w])
+    out = oracle.forward(q, k, v, th, w, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=False)
     np.testing.assert_allclose(out, _sdpa(q, k, v), rtol=0, atol=1e-12)
 
 
@@ -220,13 +225,14 @@ def test_rows_sum_to_one_after_pre_conv():
             np.testing.assert_allclose(maps[0, g * c_h + u].sum(-1), w[g, u].sum(), atol=1e-12)
 
 
-@pytest.mark.parametrize("kq,mix", [("pre", "post"), ("post", "pre"), ("pre", "pre"), ("post", "post")])
+@pytest.mark.parametrize("kq,mix", [("pre", "post"), ("post", "pre"), ("pre", "pre"), ("post", "post"),
+                                    ("both", "both")])
 def test_causality_under_future_perturbation(kq, mix):
     B, T, M, d, c_q, c_k, c_h = 1, 24, 4, 8, 3, 5, 2
     q, k, v = _rand(B, T, M, d, 17)
     rng = np.random.default_rng(18)
-    th = rng.standard_normal((M, c_q, c_k))
-    w = rng.standard_normal((M // c_h, c_h, c_h))
+    th = rng.standard_normal(((2,) if kq == "both" else ()) + (M, c_q, c_k))
+    w = rng.standard_normal(((2,) if mix == "both" else ()) + (M // c_h, c_h, c_h))
     gamma, beta = rng.standard_normal(M * d), rng.standard_normal(M * d)
     kw = dict(c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=True)
     base = oracle.forward(q, k, v, th, w, gamma, beta, 0.7, **kw)
@@ -237,6 +243,74 @@ def test_causality_under_future_perturbation(kq, mix):
         pert = oracle.forward(q2, k2, v2, th, w, gamma, beta, 0.7, **kw)
         np.testing.assert_allclose(pert[:, :i + 1], base[:, :i + 1], atol=1e-13)
         assert np.abs(pert[:, i + 1:] - base[:, i + 1:]).max() > 1e-6
+
+
+# --- both sides of softmax (§4: the default placement of the experiments) ----------
+def test_both_sides_kernel_order():
+    # Before softmax alpha*delta(0, centre) sharpens the logits (temperature alpha);
+    # after softmax delta(1, centre) hands row i the weights of row i-1. So
+    # O_i = SDPA_alpha(i-1) and O_0 = 0. With the two kernels swapped the result is a
+    # different function (row i would see the lagged logits [S[i-1][0..i-1], 0]).
+    B, T, M, d, c_q, c_k = 2, 23, 2, 8, 3, 5
+    q, k, v = _rand(B, T, M, d, 31)
+    alpha = 1.6
+    th = np.stack([_delta(M, c_q, c_k, scale=alpha), _delta(M, c_q, c_k, a=1)])
+    out = oracle.forward(q, k, v, th, None, c_q=c_q, c_k=c_k, c_h=1, kq="both")
+    exp = _sdpa(q, k, v, scale=alpha / math.sqrt(d))
+    np.testing.assert_allclose(out[:, 1:], exp[:, :-1], atol=1e-12)
+    np.testing.assert_allclose(out[:, 0], 0.0, atol=0)
+
+
+def test_both_sides_lag_kernels_compose():
+    # delta(1, centre) on both sides: before softmax row r gets [S[r-1][0..r-1], 0]
+    # (row 0: [1]); after softmax row i takes row i-1 of that. So O_i is the lagged
+    # softmax of row i-1 applied to V, and O_0 = 0.
+    B, T, M, d, c_q, c_k = 1, 19, 2, 8, 2, 3
+    q, k, v = _rand(B, T, M, d, 32)
+    lag = _delta(M, c_q, c_k, a=1)
+    out = oracle.forward(q, k, v, np.stack([lag, lag]), None, c_q=c_q, c_k=c_k, c_h=1, kq="both")
+    S = _plain_logits(q, k)
+    exp = np.zeros_like(out)
+    for m in range(M):
+        for i in range(1, T):
+            r = i - 1
+            row = np.array([S[0, m, r - 1, j] if j < r else 0.0 for j in range(r + 1)])
+            exp[0, i, m] = _softmax_rows(row) @ v[0, :r + 1, m]
+    np.testing.assert_allclose(out, exp, atol=1e-12)
+
+
+def test_both_sides_reduce_to_one_side():
+    # An identity kernel on one side leaves the other side's placement.
+    B, T, M, d, c_q, c_k, c_h = 1, 21, 4, 8, 3, 5, 2
+    q, k, v = _rand(B, T, M, d, 33)
+    rng = np.random.default_rng(34)
+    th = rng.standard_normal((M, c_q, c_k)) * 0.5
+    w = rng.standard_normal((M // c_h, c_h, c_h))
+    dl, ey = _delta(M, c_q, c_k), _eye(M, c_h)
+    kw = dict(c_q=c_q, c_k=c_k, c_h=c_h)
+    f = lambda th_, w_, kq, mix: oracle.forward(q, k, v, th_, w_, kq=kq, mix=mix, **kw)
+    np.testing.assert_allclose(f(np.stack([dl, th]), None, "both", None), f(th, None, "post", None), atol=1e-12)
+    np.testing.assert_allclose(f(np.stack([th, dl]), None, "both", None), f(th, None, "pre", None), atol=1e-12)
+    np.testing.assert_allclose(f(None, np.stack([ey, w]), None, "both"), f(None, w, None, "post"), atol=1e-12)
+    np.testing.assert_allclose(f(None, np.stack([w, ey]), None, "both"), f(None, w, None, "pre"), atol=1e-12)
+
+
+def test_both_sides_mix_permutations_compose():
+    # Permutation mixing: before softmax head u takes the logits of head pi(u), after
+    # softmax the weights of head sigma(u); so head u attends with the plain map of
+    # head pi(sigma(u)) over its own values. pi and sigma do not commute, so swapping
+    # the two sides' parameters gives another result.
+    B, T, M, d, c_h = 1, 17, 4, 8, 4
+    q, k, v = _rand(B, T, M, d, 35)
+    pi, sigma = [1, 2, 3, 0], [1, 0, 2, 3]
+    w = np.stack([np.eye(c_h)[pi][None], np.eye(c_h)[sigma][None]])
+    out = oracle.forward(q, k, v, None, w, c_h=c_h, mix="both")
+    exp = np.zeros_like(out)
+    for u in range(c_h):
+        src = pi[sigma[u]]
+        exp[:, :, u] = _sdpa(q[:, :, src:src + 1], k[:, :, src:src + 1], v[:, :, u:u + 1])[:, :, 0]
+    np.testing.assert_allclose(out, exp, atol=1e-12)
+    assert pi[sigma[0]] != sigma[pi[0]]
 
 
 # --- GroupNorm and gate (§3.3) ------------------------------------------------------
@@ -278,7 +352,8 @@ def test_hand_examples():
         T = ex["T"]
         shape = (1, T, 1, 1)
         q, k, v = (np.array(ex[n], dtype=np.float64).reshape(shape) for n in ("q", "k", "v"))
-        th = np.array(ex["theta"], dtype=np.float64)[None]
+        th = np.array(ex["theta"], dtype=np.float64)
+        th = th[:, None] if ex["placement"]["kq"] == "both" else th[None]
         out = oracle.forward(q, k, v, th, None, c_q=ex["c_q"], c_k=ex["c_k"], c_h=1,
                              kq=ex["placement"]["kq"])
         np.testing.assert_allclose(out.reshape(-1), ex["expected_out"], atol=1e-14, err_msg=ex["name"])
@@ -287,13 +362,15 @@ def test_hand_examples():
 # --- agreement with the independent transcription, and row sampling ---------------
 @pytest.mark.parametrize("kq,mix,gn", [("pre", "post", True), ("post", "pre", True), ("pre", None, False),
                                        (None, "post", False), ("post", "post", True), ("pre", "pre", True),
-                                       (None, None, False)])
+                                       (None, None, False), ("both", None, False), ("both", "both", True),
+                                       ("both", "post", True), ("both", "pre", False), ("pre", "both", True),
+                                       ("post", "both", False), (None, "both", True)])
 def test_cpp_oracle_matches_python_transcription(kq, mix, gn):
     B, T, M, d, c_q, c_k, c_h = 2, 14, 4, 4, 3, 5, 2
     q, k, v = _rand(B, T, M, d, 23)
     rng = np.random.default_rng(24)
-    th = rng.standard_normal((M, c_q, c_k))
-    w = rng.standard_normal((M // c_h, c_h, c_h))
+    th = rng.standard_normal(((2,) if kq == "both" else ()) + (M, c_q, c_k))
+    w = rng.standard_normal(((2,) if mix == "both" else ()) + (M // c_h, c_h, c_h))
     gamma, beta = rng.standard_normal(M * d), rng.standard_normal(M * d)
     kw = dict(c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn)
     a = oracle.forward(q, k, v, th, w, gamma, beta, 0.6, **kw)
