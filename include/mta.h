@@ -16,18 +16,22 @@
  *   theta_kq    [M, c_q, c_k] fp32. theta[m][a][e] weighs the map entry at
  *               (query i-a, key j-e+h0), h0 = (c_k-1)/2: the query axis reaches only
  *               current and past rows (§3.1), the key axis is centred. Entries
- *               outside the T x T map count as 0.
+ *               outside the T x T map count as 0. With MTA_KQ_PRE | MTA_KQ_POST it is
+ *               [2, M, c_q, c_k]: the kernels before softmax, then those after.
  *   w_mix       [M/c_h, c_h, c_h] fp32, w[g][out][in] (§3.2 mixing equations);
- *               group g holds heads g*c_h .. g*c_h+c_h-1.
+ *               group g holds heads g*c_h .. g*c_h+c_h-1. With MTA_MIX_PRE |
+ *               MTA_MIX_POST it is [2, M/c_h, c_h, c_h], the side before softmax first.
  *   GroupNorm   per (token, head) over the d channels, biased variance, eps 1e-5:
  *               out = lambda * (gamma[m*d+t] * (O_t - mean) / sqrt(var + eps) +
  *               beta[m*d+t]); gn_gamma, gn_beta are [M*d] fp32. lambda is the gate
  *               value itself (already passed through its sigmoid or depth rule).
- *   Placement   the key-query convolution is MTA_KQ_PRE or MTA_KQ_POST (or
- *               absent); head mixing is MTA_MIX_PRE or MTA_MIX_POST (or absent).
- *               When both act on the same side of softmax they are applied in
- *               sequence: mixing before the convolution on the pre side, the
- *               convolution before mixing on the post side.
+ *   Placement   the key-query convolution acts before softmax (MTA_KQ_PRE), after
+ *               it (MTA_KQ_POST), on both sides (both flags, each side with its own
+ *               kernels: the default of the page's experiments, §4) or not at all;
+ *               head mixing likewise (MTA_MIX_PRE, MTA_MIX_POST). On one side of
+ *               softmax the two act in sequence: mixing before the convolution on
+ *               the pre side, the convolution before mixing on the post side (§3.3:
+ *               together they form one convolution over queries, keys and heads).
  *   Memory      every pointer is device memory owned by the caller. Nothing is
  *               retained after a call returns; buffers must stay alive until the
  *               queued work completes. q, k, v, out and workspace must be 16-byte
@@ -51,10 +55,11 @@ extern "C" {
 typedef enum mta_status {
   MTA_OK = 0,
   MTA_ERR_INVALID_ARG = 1, /* sizes <= 0, M % c_h != 0, NULL/misaligned pointers,
-                              conflicting placement flags                        */
+                              unknown flag bits                                  */
   MTA_ERR_UNSUPPORTED = 2, /* valid but not built: d, dtype, c_q > 8, even c_k,
                               c_k > 17, c_h not in {1, 2, 4}, one batch of a
-                              tensor (T*M*d elements) of 2 GiB or more            */
+                              tensor (T*M*d elements) of 2 GiB or more, fused
+                              fp32 with a convolution or mixing on both sides    */
   MTA_ERR_HIP = 3,         /* the HIP runtime reported an error                   */
   MTA_ERR_WORKSPACE = 4    /* workspace missing or smaller than required          */
 } mta_status;
@@ -63,6 +68,7 @@ typedef enum mta_status {
 #define MTA_KQ_POST 0x2u  /* key-query convolution after softmax, then Mask_0     */
 #define MTA_MIX_PRE 0x4u  /* head mixing of the logits, before softmax (§3.2)     */
 #define MTA_MIX_POST 0x8u /* head mixing of the softmax weights (§3.2)            */
+/* Both bits of a pair: that operation on both sides of softmax. */
 #define MTA_GN 0x10u      /* per-head GroupNorm and scalar gate (§3.3)            */
 #define MTA_FP32 0x20u    /* q, k, v, out are fp32 instead of bf16                */
 
@@ -72,14 +78,18 @@ typedef enum mta_status {
  * head group and one tile of query rows and recomputes the logits of the c_q-1
  * preceding rows and of the key halo it needs. Allocates nothing.
  *   q, k, v      inputs [B,T,M,d]
- *   theta_kq     required iff a KQ flag is set (ignored otherwise)
- *   w_mix        required iff a MIX flag is set (ignored otherwise)
+ *   theta_kq     required iff a KQ flag is set (ignored otherwise); [2, M, c_q, c_k]
+ *                with both KQ flags
+ *   w_mix        required iff a MIX flag is set (ignored otherwise); [2, M/c_h, c_h,
+ *                c_h] with both MIX flags
  *   gn_gamma/beta, lambda   required iff MTA_GN (ignored otherwise)
  *   out          [B,T,M,d] output; may not alias the inputs
  *   c_q, c_k     kernel size; ignored without a KQ flag. 1 <= c_q <= 8, c_k odd <= 17
  *   c_h          head-group size; M % c_h == 0; c_h in {1,2,4}; ignored without MIX
  *   flags        MTA_* bits above
  * Supported head sizes: d in {32, 64, 96, 128} for bf16, d in {16, 32, 64} for fp32.
+ * fp32 tensors: one side per operation (both-side placements return UNSUPPORTED;
+ * mta_forward_materialized takes them).
  */
 int mta_forward(const void* q, const void* k, const void* v, const float* theta_kq,
                 const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
@@ -103,13 +113,14 @@ int mta_forward_materialized(const void* q, const void* k, const void* v, const 
 /*
  * mta_forward_rows: mta_forward for the output rows row_begin .. T-1 only, against
  * all keys 0 .. T-1. Every output row depends only on keys up to itself and on the
- * c_q-1 query rows before it (§2 causal mask; §3.1: the convolution reaches only
- * current and past queries), so a suffix of rows can be computed on its own: with a
- * cache holding k and v (and q) of the earlier positions this is the decode step
- * (row_begin = T-1) or a prefill chunk. The rows written are identical to the same
- * rows of mta_forward.
- *   q            [B,T,M,d]; rows max(0, row_begin-(c_q-1)) .. T-1 are read (with a
- *                KQ flag; rows row_begin .. T-1 without); earlier rows are not read
+ * c_q-1 query rows before it, 2(c_q-1) with both KQ flags (§2 causal mask; §3.1: the
+ * convolution reaches only current and past queries), so a suffix of rows can be
+ * computed on its own: with a cache holding k and v (and q) of the earlier positions
+ * this is the decode step (row_begin = T-1) or a prefill chunk. The rows written are
+ * identical to the same rows of mta_forward.
+ *   q            [B,T,M,d]; rows max(0, row_begin-(c_q-1)) .. T-1 are read with one
+ *                KQ flag, max(0, row_begin-2(c_q-1)) .. T-1 with both, rows
+ *                row_begin .. T-1 without; earlier rows are not read
  *   k, v         [B,T,M,d]; all rows are read
  *   out          [B,T,M,d]; rows row_begin .. T-1 are written, earlier rows are left
  *                as they were

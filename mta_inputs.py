@@ -9,8 +9,9 @@ Workload recipe (every array is produced by ``numpy.random.default_rng(seed)``):
 * draw order: q, k, v (each ``[B, T, M, d]``, standard normal, float32), then the
   key-query kernel noise ``[M, c_q, c_k]``, then the head-mixing noise
   ``[M/c_h, c_h, c_h]``, then (long-context workload only) the planted key pairs;
+  a placement on both sides of softmax draws a leading axis of 2 (before, after);
 * ``theta = delta(0, centre) + sigma_theta * noise``; ``w = I + sigma_w * noise``
-  (sigma is a standard deviation);
+  (sigma is a standard deviation), on each side;
 * bf16 workloads round q, k, v to bfloat16 (round-to-nearest-even) once, after
   planting; both the GPU and the oracle then see the identical rounded values.
 
@@ -40,7 +41,7 @@ __all__ = [
 
 @dataclasses.dataclass(frozen=True)
 class MTAConfig:
-    """One synthetic workload. ``kq``/``mix`` are ``"pre"``, ``"post"`` or ``None``."""
+    """One synthetic workload. ``kq``/``mix`` are ``"pre"``, ``"post"``, ``"both"`` or ``None``."""
 
     name: str
     B: int
@@ -86,6 +87,10 @@ CONFIGS = [
               0.05, 0.05, 1.0, 0.0, 0.8, seed=3, plant_block=512),
     MTAConfig("variant_bf16", 2, 4096, 32, 128, 4, 9, 4, "post", "pre", True, "bf16",
               0.05, 0.05, 1.0, 0.0, 1.0 / math.sqrt(12.0), seed=4),
+    # Both convolutions on both sides of softmax (the experiments' default placement, §4
+    # of the page) at the T=4096 shape above.
+    MTAConfig("both_sides_bf16", 2, 4096, 32, 128, 4, 9, 4, "both", "both", True, "bf16",
+              0.05, 0.05, 1.0, 0.0, 1.0 / math.sqrt(12.0), seed=5),
 ]
 
 
@@ -125,8 +130,10 @@ def make_inputs(cfg: MTAConfig) -> dict:
     q = rng.standard_normal(shape, dtype=np.float32)
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
-    theta_noise = rng.standard_normal((cfg.M, cfg.c_q, cfg.c_k), dtype=np.float32)
-    w_noise = rng.standard_normal((cfg.M // cfg.c_h, cfg.c_h, cfg.c_h), dtype=np.float32)
+    sides_kq = (2,) if cfg.kq == "both" else ()
+    sides_mix = (2,) if cfg.mix == "both" else ()
+    theta_noise = rng.standard_normal(sides_kq + (cfg.M, cfg.c_q, cfg.c_k), dtype=np.float32)
+    w_noise = rng.standard_normal(sides_mix + (cfg.M // cfg.c_h, cfg.c_h, cfg.c_h), dtype=np.float32)
 
     if cfg.plant_block > 0:
         blk, gap, rho = cfg.plant_block, cfg.plant_gap, cfg.plant_rho
@@ -138,10 +145,10 @@ def make_inputs(cfg: MTAConfig) -> dict:
                 k[b, p + gap] = np.float32(rho) * k[b, p] + np.float32(math.sqrt(1.0 - rho * rho)) * z
 
     theta = (cfg.theta_sigma * theta_noise).astype(np.float32)
-    theta[:, 0, (cfg.c_k - 1) // 2] += np.float32(1.0)
+    theta[..., 0, (cfg.c_k - 1) // 2] += np.float32(1.0)
     w = (cfg.w_sigma * w_noise).astype(np.float32)
     for u in range(cfg.c_h):
-        w[:, u, u] += np.float32(1.0)
+        w[..., u, u] += np.float32(1.0)
 
     if cfg.dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)

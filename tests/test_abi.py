@@ -53,6 +53,9 @@ def test_valid_arguments_pass():
     assert _check(flags=mta.KQ_POST | mta.MIX_PRE | mta.GN, c_q=4, c_k=9, c_h=4) == mta.OK
     assert _check(flags=0, theta=0, w=0, gamma=0, beta=0) == mta.OK  # plain attention
     assert _check(flags=mta.FP32 | mta.KQ_PRE, d=16, w=0) == mta.OK
+    # both sides of softmax (parameters of the side before softmax first)
+    assert _check(flags=mta.KQ_PRE | mta.KQ_POST | mta.MIX_PRE | mta.MIX_POST | mta.GN) == mta.OK
+    assert _check(flags=mta.KQ_PRE | mta.KQ_POST, w=0) == mta.OK
     assert mta.last_error() == ""
 
 
@@ -66,8 +69,6 @@ def test_valid_arguments_pass():
     (dict(theta=0), mta.ERR_INVALID_ARG),                 # KQ flag without theta
     (dict(w=0), mta.ERR_INVALID_ARG),                     # MIX flag without w
     (dict(gamma=0), mta.ERR_INVALID_ARG),                 # GN without gamma
-    (dict(flags=mta.KQ_PRE | mta.KQ_POST), mta.ERR_INVALID_ARG),
-    (dict(flags=mta.MIX_PRE | mta.MIX_POST), mta.ERR_INVALID_ARG),
     (dict(flags=0x400), mta.ERR_INVALID_ARG),
     (dict(c_k=4), mta.ERR_UNSUPPORTED),                   # even key size
     (dict(c_q=9), mta.ERR_UNSUPPORTED),

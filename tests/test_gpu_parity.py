@@ -149,7 +149,8 @@ def test_plain_attention(shape, dtype):
 
 # ---- placements, kernel sizes, head sizes, ragged lengths -------------------------------
 COMBOS = [("pre", "post"), ("post", "pre"), ("pre", None), ("post", None), (None, "post"), (None, "pre"),
-          ("pre", "pre"), ("post", "post"), (None, None)]
+          ("pre", "pre"), ("post", "post"), (None, None), ("both", None), ("both", "both"), ("both", "post"),
+          ("both", "pre"), ("pre", "both"), ("post", "both"), (None, "both")]
 
 
 @pytest.mark.parametrize("kq,mix", COMBOS)
@@ -333,3 +334,84 @@ def test_decode_step_and_chunk_at_full_size(row_begin):
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     compare(cfg, got, want, rows=rows, what=f"rows {row_begin}.. ({len(rows)} checked)")
+
+
+# ---- both sides of softmax ------------------------------------------------------------------
+@pytest.mark.parametrize("c_q,c_k", [(1, 1), (2, 3), (4, 9), (6, 11), (8, 17), (5, 1)])
+@pytest.mark.parametrize("mix,c_h", [(None, 1), ("both", 4), ("post", 2), ("pre", 4), ("both", 1)])
+def test_both_convolutions_kernel_sizes(c_q, c_k, mix, c_h):
+    cfg = mta_inputs.MTAConfig("dual", 1, 133, 4, 128, c_q, c_k, c_h, "both", mix, True, "bf16", 0.2, 0.2, 1.0,
+                               0.0, 0.8, seed=23)
+    inp = case(cfg)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg),
+            what=f"both {c_q}x{c_k} mix={mix}/{c_h}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 33, 64, 65, 200])
+@pytest.mark.parametrize("d", [32, 96])
+def test_both_sides_ragged_lengths_and_head_sizes(T, d):
+    cfg = mta_inputs.MTAConfig("dual_ragged", 2, T, 4, d, 4, 9, 2, "both", "both", True, "bf16", 0.2, 0.2, 1.0,
+                               0.0, 0.8, seed=24)
+    inp = case(cfg)
+    for path in ("fused", "materialized"):
+        compare(cfg, run(path, cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"{path} T={T} d={d}")
+
+
+@pytest.mark.parametrize("mix,c_h", [(None, 1), ("both", 4), ("pre", 2)])
+def test_both_sides_late_dominant_key(mix, c_h):
+    """The exact fallback of the statistics phase with both convolutions: one key far past
+    the lead-in tile dominates one query's softmax input by ~130 natural-log units."""
+    d = 128
+    cfg = mta_inputs.MTAConfig("dual_late", 1, 300, 8, d, 4, 9, c_h, "both", mix, True, "bf16", 0.05, 0.05, 1.0,
+                               0.0, 0.8, seed=25)
+    inp = dict(case(cfg))
+    q, k = inp["q"].astype(np.float64), inp["k"].copy()
+    jkey, iq = 200, 260
+    for m in range(cfg.M):
+        qv = q[0, iq, m]
+        k[0, jkey, m] = 130.0 * np.sqrt(d) / float(qv @ qv) * qv
+    inp["k"] = mta_inputs.round_bf16(k.astype(np.float32))
+    want = oracle.forward_cfg(cfg, inp)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), want, what=f"late key both/{mix}/{c_h}")
+
+
+def test_both_sides_fp32_materialized_and_fused_refusal():
+    """fp32 tensors: the materialized chain takes every placement; the fp32 fused kernel
+    implements one side per convolution and reports both-side placements unsupported."""
+    cfg = mta_inputs.MTAConfig("dual_fp32", 1, 64, 4, 16, 3, 5, 2, "both", "both", True, "fp32", 0.1, 0.1, 1.0,
+                               0.0, 0.8, seed=26)
+    inp = case(cfg)
+    d = dev_inputs(cfg, inp)
+    compare(cfg, run("materialized", cfg, d, inp["lam"]), oracle_full(cfg), what="materialized fp32 both")
+    with pytest.raises(ta.MTAError) as e:
+        run("fused", cfg, d, inp["lam"])
+    assert e.value.status == ta.mta.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("row_begin", [0, 1, 97, 299])
+@pytest.mark.parametrize("mix,c_h", [("both", 4), (None, 1)])
+def test_both_sides_row_range_equals_full_forward(row_begin, mix, c_h):
+    cfg = mta_inputs.MTAConfig("dual_rows", 2, 300, 8, 128, 4, 9, c_h, "both", mix, True, "bf16", 0.1, 0.1, 1.0,
+                               0.0, 0.8, seed=27)
+    inp = case(cfg)
+    dv = dev_inputs(cfg, inp)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    args = (dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"])
+    full = ta.forward(*args, **kw)
+    part = torch.full_like(full, 7.0)
+    ta.forward_rows(*args, row_begin=row_begin, out=part, **kw)
+    torch.cuda.synchronize()
+    f, p = full.float().cpu(), part.float().cpu()
+    assert torch.equal(p[:, row_begin:], f[:, row_begin:])
+    assert bool((p[:, :row_begin] == 7.0).all())
+
+
+@pytest.mark.parametrize("path", ["fused", "materialized"])
+def test_both_sides_full_size_sampled_rows(path):
+    cfg = mta_inputs.config("both_sides_bf16")
+    log(f"[{path}] full size {cfg}")
+    rows, want = oracle_rows(cfg)
+    inp = case(cfg)
+    got = run(path, cfg, dev_inputs(cfg, inp), inp["lam"])
+    compare(cfg, got, want, rows=rows, what=f"{path} rows={len(rows)}")
+    assert np.isfinite(got).all()

@@ -38,10 +38,6 @@ int validate(const void* q, const void* k, const void* v, const float* theta, co
   if (flags & ~kKnownFlags) return fail(MTA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~kKnownFlags);
   if (B <= 0 || T <= 0 || M <= 0 || d <= 0)
     return fail(MTA_ERR_INVALID_ARG, "sizes must be positive (B=%d T=%d M=%d d=%d)", B, T, M, d);
-  if ((flags & MTA_KQ_PRE) && (flags & MTA_KQ_POST))
-    return fail(MTA_ERR_INVALID_ARG, "MTA_KQ_PRE and MTA_KQ_POST are mutually exclusive");
-  if ((flags & MTA_MIX_PRE) && (flags & MTA_MIX_POST))
-    return fail(MTA_ERR_INVALID_ARG, "MTA_MIX_PRE and MTA_MIX_POST are mutually exclusive");
   if (!q || !k || !v || !out) return fail(MTA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(MTA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
@@ -72,8 +68,13 @@ int validate(const void* q, const void* k, const void* v, const float* theta, co
   p.q = q;
   p.k = k;
   p.v = v;
-  p.theta = kq ? theta : nullptr;
-  p.w = mix ? w : nullptr;
+  // with both sides the parameters before softmax come first, then those after
+  const bool kq_both = (flags & MTA_KQ_PRE) && (flags & MTA_KQ_POST);
+  const bool mix_both = (flags & MTA_MIX_PRE) && (flags & MTA_MIX_POST);
+  p.theta_pre = (flags & MTA_KQ_PRE) ? theta : nullptr;
+  p.theta_post = (flags & MTA_KQ_POST) ? theta + (kq_both ? (size_t)M * c_q * c_k : 0) : nullptr;
+  p.w_pre = (flags & MTA_MIX_PRE) ? w : nullptr;
+  p.w_post = (flags & MTA_MIX_POST) ? w + (mix_both ? (size_t)M * c_h : 0) : nullptr;
   p.gamma = (flags & MTA_GN) ? gamma : nullptr;
   p.beta = (flags & MTA_GN) ? beta : nullptr;
   p.lambda = lambda;
@@ -85,8 +86,8 @@ int validate(const void* q, const void* k, const void* v, const float* theta, co
   p.c_q = kq ? c_q : 1;
   p.c_k = kq ? c_k : 1;
   p.c_h = mix ? c_h : 1;
-  p.kq = (flags & MTA_KQ_PRE) ? mta::KQ_PRE : (flags & MTA_KQ_POST) ? mta::KQ_POST : mta::KQ_NONE;
-  p.mix = (flags & MTA_MIX_PRE) ? mta::MIX_PRE : (flags & MTA_MIX_POST) ? mta::MIX_POST : mta::MIX_NONE;
+  p.kq = ((flags & MTA_KQ_PRE) ? mta::KQ_PRE : 0) | ((flags & MTA_KQ_POST) ? mta::KQ_POST : 0);
+  p.mix = ((flags & MTA_MIX_PRE) ? mta::MIX_PRE : 0) | ((flags & MTA_MIX_POST) ? mta::MIX_POST : 0);
   p.gn = (flags & MTA_GN) ? 1 : 0;
   p.fp32 = fp32 ? 1 : 0;
   *pr = p;

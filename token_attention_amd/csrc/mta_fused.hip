@@ -20,6 +20,7 @@ bool fused_supported(const Problem& p) {
   const int ch = p.mix ? p.c_h : 1;
   if (ch != 1 && ch != 2 && ch != 4) return false;
   if (p.kq && (p.c_q < 1 || p.c_q > 8 || p.c_k < 1 || p.c_k > 17 || p.c_k % 2 == 0)) return false;
+  if (p.fp32 && (p.kq == KQ_BOTH || p.mix == MIX_BOTH)) return false;
   if (p.fp32) return p.d == 16 || p.d == 32 || p.d == 64;
   return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
 }
@@ -36,7 +37,7 @@ hipError_t launch_fused(const Problem& p, hipStream_t stream, bool* unsupported)
       case 32: return launch_fused_f32_d32(p, stream);
       case 64: return launch_fused_f32_d64(p, stream);
     }
-  } else if (p.kq == KQ_POST) {
+  } else if (p.kq & KQ_POST) {
     switch (p.d) {
       case 32: return launch_fused_bf16_d32_postconv(p, stream);
       case 64: return launch_fused_bf16_d64_postconv(p, stream);

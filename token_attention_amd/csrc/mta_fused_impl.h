@@ -614,8 +614,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.q = p.q;
   a.k = p.k;
   a.v = p.v;
-  a.theta = p.theta;
-  a.w = p.w;
+  a.theta = p.kq == KQ_PRE ? p.theta_pre : p.theta_post;
+  a.w = p.mix == MIX_PRE ? p.w_pre : p.w_post;
   a.gamma = p.gamma;
   a.beta = p.beta;
   a.lambda = p.lambda;

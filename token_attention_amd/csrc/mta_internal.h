@@ -8,23 +8,26 @@
 
 namespace mta {
 
-enum KqMode { KQ_NONE = 0, KQ_PRE = 1, KQ_POST = 2 };
-enum MixMode { MIX_NONE = 0, MIX_PRE = 1, MIX_POST = 2 };
+// Placements are bit sets: before softmax, after softmax, or both sides.
+enum KqMode { KQ_NONE = 0, KQ_PRE = 1, KQ_POST = 2, KQ_BOTH = 3 };
+enum MixMode { MIX_NONE = 0, MIX_PRE = 1, MIX_POST = 2, MIX_BOTH = 3 };
 
 // A fully validated problem description (sizes already checked by the API layer).
 struct Problem {
   const void* q;
   const void* k;
   const void* v;
-  const float* theta;  // [M, c_q, c_k] or null
-  const float* w;      // [M/c_h, c_h, c_h] or null
+  const float* theta_pre;   // [M, c_q, c_k] kernels before softmax, or null
+  const float* theta_post;  // [M, c_q, c_k] kernels after softmax, or null
+  const float* w_pre;       // [M/c_h, c_h, c_h] mixing before softmax, or null
+  const float* w_post;      // [M/c_h, c_h, c_h] mixing after softmax, or null
   const float* gamma;  // [M*d] or null
   const float* beta;   // [M*d] or null
   float lambda;
   void* out;
   int B, T, M, d, c_q, c_k, c_h;
-  int kq;    // KqMode
-  int mix;   // MixMode
+  int kq;    // KqMode bits
+  int mix;   // MixMode bits
   int gn;    // 0/1
   int fp32;  // 0: bf16 tensors, 1: fp32 tensors
   int row_begin = 0;  // fused path: output rows row_begin .. T-1 only

@@ -69,8 +69,10 @@ struct Args {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
-  const float* theta;
-  const float* w;
+  const float* theta;   // convolution kernels [M, c_q, c_k] (the one before softmax if DUAL)
+  const float* theta2;  // DUAL: the kernels after softmax
+  const float* w_pre;   // mixing before softmax [M/c_h, c_h, c_h]
+  const float* w_post;  // mixing after softmax
   const float* gamma;
   const float* beta;
   float lambda;
@@ -88,12 +90,15 @@ struct Args {
 
 // KQ: a key-query convolution (TWO: after softmax); MIXPRE / MIXPOST: head mixing before /
 // after softmax.
-template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool MIXPOST_, int CQM_, bool MIXPRE_, int NW_ = 8>
+// DUAL: key-query convolutions on both sides of softmax (implies KQ and TWO).
+template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool MIXPOST_, int CQM_, bool MIXPRE_, int NW_ = 8,
+          bool DUAL_ = false>
 struct Cfg {
   static constexpr int D = D_, CH = CH_, QW = QW_, BK = BK_, CQM = CQM_;
   static constexpr int NW = NW_;               // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr bool KQ = KQ_, TWO = TWO_, MIXPOST = MIXPOST_, MIXPRE = MIXPRE_;
+  static constexpr bool KQ = KQ_, TWO = TWO_, MIXPOST = MIXPOST_, MIXPRE = MIXPRE_, DUAL = DUAL_;
+  static_assert(!DUAL || (KQ && TWO), "both convolutions use the two-phase schedule");
   static constexpr bool MIX = MIXPRE || MIXPOST;
   static constexpr int WPH = NW / CH;          // waves per head
   static constexpr bool PRIV = WPH == 1;       // a wave owns its head: private K/V staging
@@ -105,7 +110,8 @@ struct Cfg {
   static constexpr int KS = D / 32;            // k-steps of QK^T
   static constexpr int NB = D / 16;            // channel blocks
   static constexpr int NC = BK / 32;           // 32-key chunks of AV
-  static constexpr int KROWS = KQ ? BK + 16 : BK;  // K rows in LDS
+  // K rows in LDS: the one-convolution schedules stage a 16-key halo block in front
+  static constexpr int KROWS = (KQ && !DUAL) ? BK + 16 : BK;
   static constexpr int LDK = D + 8;            // K row stride (bf16): 16-byte reads conflict-free
   static constexpr int LDV = D + 16;           // V row stride (bf16): transposed reads conflict-free
   static constexpr int ZW = LB * 16;           // ring width (keys)
@@ -114,9 +120,14 @@ struct Cfg {
   static constexpr int XW = NKB * 4;           // exchange halves per lane and query block
   static constexpr size_t SX_HALF = (size_t)CH * R * BK;  // one exchange buffer (halves)
   static constexpr size_t KS_BYTES = (size_t)CH * KROWS * LDK * 2;
-  static constexpr size_t SX_BYTES = MIX ? 2 * SX_HALF * 2 : 0;  // double buffered
+  // double buffered; with both convolutions every two exchanges are already separated by
+  // a workgroup barrier (ring writes -> convolution reads), so one buffer suffices
+  static constexpr int XBUFS = DUAL ? 1 : 2;
+  static constexpr size_t SX_BYTES = MIX ? XBUFS * SX_HALF * 2 : 0;
   static constexpr size_t VS_BYTES = (size_t)CH * BK * LDV * 2;
-  static constexpr size_t ZB_BYTES = KQ ? (size_t)CH * ZROWS * LDZ * 2 : 0;
+  static constexpr size_t ZRING = (size_t)CH * ZROWS * LDZ;  // halves of one ring
+  // rings: the convolution input; with both convolutions the logits and the weights
+  static constexpr size_t ZB_BYTES = KQ ? (DUAL ? 2 : 1) * ZRING * 2 : 0;
   static constexpr size_t OFF_KS = 0;
   static constexpr size_t OFF_SX = OFF_KS + KS_BYTES;
   static constexpr size_t OFF_VS = OFF_SX + SX_BYTES;
@@ -212,9 +223,11 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   const int b = bg / A.n_groups, g = bg % A.n_groups;
   const int T_ = A.T, M = A.M;
   const int cq1 = C::KQ ? A.c_q - 1 : 0;
+  // query halo: c_q - 1 rows per convolution (both: logits -> weights -> output rows)
+  const int halo = C::DUAL ? 2 * cq1 : cq1;
   const int h0 = C::KQ ? (A.c_k - 1) / 2 : 0;
   const int i0 = A.row_begin + qt * A.r_out;
-  const int row0 = i0 - cq1;
+  const int row0 = i0 - halo;
   const int last_row = min(i0 + A.r_out, T_) - 1;
   const int n_kt = last_row / C::BK + 1;
   const int m_head = g * C::CH + hu;
@@ -243,10 +256,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // ---- Toeplitz A operands: out key n (row), window key k = 8*lg + s (slot) ------------
   // window key k is global key j0 - 8 + 16*ob + k; out key is j0 + 16*ob + n;
   // tap e = n - k + 8 + h0. Before softmax the logit scale is folded in.
-  f16x8 tz[C::KQ ? C::CQM : 1];
-  if constexpr (C::KQ) {
-    const float* th = A.theta + (size_t)m_head * A.c_q * A.c_k;
-    const float tscale = (!C::TWO && !mix_pre) ? A.qk_scale : 1.0f;
+  f16x8 tz[C::KQ ? C::CQM : 1], tz2[C::DUAL ? C::CQM : 1];
+  auto toeplitz = [&](f16x8 (&dst)[C::KQ ? C::CQM : 1], const float* theta, float tscale) {
+    const float* th = theta + (size_t)m_head * A.c_q * A.c_k;
 #pragma unroll
     for (int a = 0; a < C::CQM; ++a) {
 #pragma unroll
@@ -254,21 +266,29 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         const int e = lq - (8 * lg + s) + 8 + h0;
         float t = 0.0f;
         if (a < A.c_q && e >= 0 && e < A.c_k) t = th[a * A.c_k + e] * tscale;
-        tz[a][s] = (_Float16)t;
+        dst[a][s] = (_Float16)t;
       }
     }
-    for (int x = tid; x < C::CH * ZPRE * C::LDZ; x += C::NT) {
+  };
+  if constexpr (C::KQ) {
+    // before softmax the logit scale is folded in (unless the mixing weights carry it)
+    toeplitz(tz, A.theta, ((!C::TWO || C::DUAL) && !mix_pre) ? A.qk_scale : 1.0f);
+    if constexpr (C::DUAL) toeplitz(tz2, A.theta2, 1.0f);
+    // zero rows above every ring
+    constexpr int NRING = C::DUAL ? 2 : 1;
+    for (int x = tid; x < NRING * C::CH * ZPRE * C::LDZ; x += C::NT) {
       const int u = x / (ZPRE * C::LDZ);
       Zb[(size_t)u * C::ZROWS * C::LDZ + (x - u * ZPRE * C::LDZ)] = (_Float16)0.0f;
     }
   }
 
-  // w[g][hu][(hu + k) % c_h]; before softmax times the logit scale
-  float wrot[C::CH];
+  // w[g][hu][(hu + k) % c_h] of each side; before softmax times the logit scale
+  float wpre[C::CH], wpost[C::CH];
 #pragma unroll
   for (int u = 0; u < C::CH; ++u) {
-    const float* wrow = A.w + ((size_t)g * C::CH + hu) * C::CH;
-    wrot[u] = C::MIX ? wrow[(hu + u) & (C::CH - 1)] * (mix_pre ? A.qk_scale : 1.0f) : 0.0f;
+    const int src = (hu + u) & (C::CH - 1);
+    wpre[u] = C::MIXPRE ? A.w_pre[((size_t)g * C::CH + hu) * C::CH + src] * A.qk_scale : 0.0f;
+    wpost[u] = C::MIXPOST ? A.w_post[((size_t)g * C::CH + hu) * C::CH + src] : 0.0f;
   }
 
   f32x4 acc[C::NB][C::NQB];
@@ -363,14 +383,14 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 
   // ---- compute helpers --------------------------------------------------------------------
   f32x4 s[C::LB][C::NQB];
-  // raw S^T of logit block lb (Ks rows 16*lb .. 16*lb+15)
-  auto logit_block = [&](int lb) {
+  // raw S^T of logit block lb (Ks rows 16*lb - kofs .. 16*lb - kofs + 15)
+  auto logit_block = [&](int lb, int kofs = 0) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-          Ks + ((size_t)hu * C::KROWS + lb * 16 + lq) * C::LDK + ks * 32 + lg * 8);
+          Ks + ((size_t)hu * C::KROWS + lb * 16 - kofs + lq) * C::LDK + ks * 32 + lg * 8);
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb)
         s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
@@ -382,7 +402,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // alternates between two halves, so one barrier per exchange suffices: a half is
   // rewritten only after every wave has passed the barrier of the exchange in between.
   int xbuf = 0;
-  auto mix_blocks = [&](auto& arr, auto lb0c, auto lb1c) {
+  auto mix_blocks = [&](auto& arr, const float (&wrot)[C::CH], auto lb0c, auto lb1c) {
     constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value, XB = LB1 - LB0;
     static_assert(XB >= 1 && XB <= C::NKB, "exchange width");
     if constexpr (C::CH == 1) {  // a group of one head: a scalar weight
@@ -427,17 +447,20 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         arr[lb][qb] = x;
       }
     }
-    xbuf ^= 1;
+    if constexpr (C::XBUFS == 2) xbuf ^= 1;
   };
 
-  // convolution of the ring (logical blocks of tile kt) -> cv[ob][qb]
+  // Convolution of a ring (logical blocks of tile kt): output block ob covers the 16 keys
+  // that start 8 keys after ring block ob, so it reads ring blocks ob and ob + 1.
   f32x4 cv[C::KQ ? C::NKB : 1][C::NQB];
+  _Float16* const Zw = Zb + (C::DUAL ? C::ZRING : 0);  // ring of the weights (both convolutions)
   auto ring_col = [&](int kt, int lb) { return ((kt * C::NKB + lb) % C::LB) * 16; };
-  auto convolve = [&](int kt) {
+  auto convolve_ring = [&](const _Float16* ring, const f16x8 (&tzs)[C::KQ ? C::CQM : 1],
+                           f32x4 (&res)[C::KQ ? C::NKB : 1][C::NQB], int kt) {
 #pragma unroll
     for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) cv[ob][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < C::NQB; ++qb) res[ob][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ob = 0; ob < C::NKB; ++ob) {
       // slots of lane group lg: window keys 8*lg .. 8*lg+7 = block ob (lg < 2) or ob+1
@@ -448,17 +471,19 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           const f16x8 bz = *reinterpret_cast<const f16x8*>(
-              Zb + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq - a) * C::LDZ + col);
-          cv[ob][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tz[a], bz, cv[ob][qb], 0, 0, 0);
+              ring + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq - a) * C::LDZ + col);
+          res[ob][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tzs[a], bz, res[ob][qb], 0, 0, 0);
         }
       }
     }
   };
-  auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) {
+  auto convolve = [&](int kt) { convolve_ring(Zb, tz, cv, kt); };
+  auto ring_store_to = [&](_Float16* ring, int kt, int lb, int qb, const f32x4& val) {
     const f16x4 h = {(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
-    *reinterpret_cast<f16x4*>(Zb + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq) * C::LDZ +
+    *reinterpret_cast<f16x4*>(ring + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq) * C::LDZ +
                               ring_col(kt, lb) + lg * 4) = h;
   };
+  auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) { ring_store_to(Zb, kt, lb, qb, val); };
 
   // AV of the weights of key blocks ob0 .. ob0 + NKB - 1 against V of head hu
   auto av = [&](auto& wts, auto ob0c) {
@@ -516,7 +541,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       team_sync<C>();
       if constexpr (C::KQ) {
         logit_block(0);
-        if constexpr (mix_pre) mix_blocks(s, I0{}, I1{});
+        if constexpr (mix_pre) mix_blocks(s, wpre, I0{}, I1{});
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           const int gr = row0 + qs0 + qb * 16 + lq;
@@ -535,7 +560,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, with_av);
 #pragma unroll
         for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
-        if constexpr (mix_pre) mix_blocks(s, INEW{}, ILB{});
+        if constexpr (mix_pre) mix_blocks(s, wpre, INEW{}, ILB{});
         // softmax input of this tile: cv (after the convolution) or the logits themselves
         auto& xw = [&]() -> auto& {
           if constexpr (C::KQ) return cv;
@@ -609,7 +634,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           }
         }
         if (with_av) {
-          if constexpr (C::MIXPOST) mix_blocks(xw, I0{}, INKB{});
+          if constexpr (C::MIXPOST) mix_blocks(xw, wpost, I0{}, INKB{});
           av(xw, I0{});
         }
         team_sync<C>();  // the team is done with Ks, Vs and the ring of this tile
@@ -652,6 +677,157 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
       break;
     }
+  } else if constexpr (C::DUAL) {
+    // ===================== convolutions before and after softmax ========================
+    // Tile kt (j0 = kt * BK; kt = -1 is a lead-in tile that only fills the rings) computes
+    // the logits of keys [j0 + 16, j0 + BK + 16) into logit-ring blocks 1..NKB (block b
+    // holds keys j0 + 16 b ..), the convolution before softmax of keys [j0 + 8, j0 + BK + 8)
+    // (it reads logit blocks ob, ob + 1), and in phase 2 the normalised weights of those
+    // keys into weight-ring blocks 1..NKB (block b holds keys j0 - 8 + 16 b ..), then the
+    // convolution after softmax of keys [j0, j0 + BK). The ring tile index is kt + 1. The K
+    // tile of tile kt (rows j0 + 16 .. j0 + BK + 15) sits at Ks rows 0 .. BK - 1.
+    f32x4 cp[C::NKB][C::NQB];  // convolution before softmax, log2 units
+    auto front = [&](int kt) {
+      const int j0 = kt * C::BK, kr = kt + 1;
+#pragma unroll
+      for (int lb = 1; lb < C::LB; ++lb) logit_block(lb, 16);
+      if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
+      // Mask_0 on keys j0 + 16 lb + 4 lg + i
+      const bool edge0 = (j0 < 0) || (j0 + C::BK + 16 - 1 > wrow_min) || (wrow_min < 0);
+#pragma unroll
+      for (int lb = 1; lb < C::LB; ++lb) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          f32x4 z = s[lb][qb];
+          if (edge0) {
+            const int gr = row0 + qs0 + qb * 16 + lq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = j0 + 16 * lb + 4 * lg + i;
+              z[i] = ((gr >= 0) & (j >= 0) & (j <= gr)) ? z[i] : 0.0f;
+            }
+          }
+          ring_store(kr, lb, qb, z);
+        }
+      }
+      team_sync<C>();  // rows of the neighbouring slab are read by the convolution
+      convolve_ring(Zb, tz, cp, kr);
+      // Mask_-inf: a softmax row needs all c_q logit rows of its convolution inside the
+      // tile (t >= c_q - 1) and lies in the map; keys 0 .. gr
+      const bool edge1 = (j0 + 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (qs0 < cq1) || (wrow_min < 0) ||
+                         (wrow_min + C::QW > T_);
+      if (edge1) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const int t = qs0 + qb * 16 + lq;
+          const int gr = row0 + t;
+          const bool row_ok = (t >= cq1) & (gr >= 0) & (gr < T_);
+#pragma unroll
+          for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = j0 + 8 + ob * 16 + 4 * lg + i;
+              cp[ob][qb][i] = (row_ok & (j >= 0) & (j <= gr)) ? cp[ob][qb][i] : NEG_INF;
+            }
+        }
+      }
+    };
+
+    // phase 1: row sums of the softmax input against a fixed reference (the maximum of the
+    // lead-in tile); if a sum exceeds 2^64 the workgroup repeats the phase exactly
+    float lsum[C::NQB];
+    for (int exact = 0;; exact = 1) {
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        m_run[qb] = -1e30f;
+        l_run[qb] = 0.0f;
+      }
+      stage_k_direct(16 - C::BK, C::BK, 0);
+      team_sync<C>();
+      for (int kt = -1; kt < n_kt; ++kt) {
+        const bool more = kt + 1 < n_kt;
+        if (more) prefetch((kt + 1) * C::BK + 16, 0, false);
+        front(kt);
+        if (exact || kt < 0) {
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            float mx = NEG_INF;
+#pragma unroll
+            for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, cp[ob][qb][i]);
+            const float m_new = fmaxf(m_run[qb], xgroup_max(mx));
+            l_run[qb] *= fast_exp2(m_run[qb] - m_new);
+            m_run[qb] = m_new;
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += fast_exp2(cp[ob][qb][i] - m_run[qb]);
+          l_run[qb] += sum;
+        }
+        team_sync<C>();
+        if (more) commit(0, false);
+        team_sync<C>();
+      }
+      bool big = false;
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        lsum[qb] = xgroup_sum(l_run[qb]);
+        big |= !(lsum[qb] <= SUM_LIMIT);
+      }
+      if (exact || !__syncthreads_or(big ? 1 : 0)) break;
+    }
+    float shift[C::NQB];  // p = exp2(x - (m + log2 l))
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) shift[qb] = lsum[qb] > 0.0f ? m_run[qb] + __builtin_log2f(lsum[qb]) : 1e30f;
+
+    // phase 2: weights -> weight ring -> convolution after softmax -> Mask_0 -> [mixing] -> AV
+    stage_k_direct(16 - C::BK, C::BK, 0);
+    team_sync<C>();
+    for (int kt = -1; kt < n_kt; ++kt) {
+      const int j0 = kt * C::BK, kr = kt + 1;
+      const bool more = kt + 1 < n_kt;
+      if (more) prefetch((kt + 1) * C::BK + 16, (kt + 1) * C::BK, true);
+      front(kt);
+#pragma unroll
+      for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          f32x4 pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(cp[ob][qb][i] - shift[qb]);
+          ring_store_to(Zw, kr, ob + 1, qb, pv);
+        }
+      team_sync<C>();
+      if (kt >= 0) {
+        convolve_ring(Zw, tz2, cv, kr);
+        const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < halo) || (wrow_min + C::QW > T_);
+        if (edge2) {
+#pragma unroll
+          for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+            for (int qb = 0; qb < C::NQB; ++qb) {
+              const int t = qs0 + qb * 16 + lq;
+              const int gr = row0 + t;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int j = j0 + ob * 16 + 4 * lg + i;
+                cv[ob][qb][i] = ((t >= halo) & (gr < T_) & (j <= gr)) ? cv[ob][qb][i] : 0.0f;
+              }
+            }
+        }
+        if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
+        av(cv, I0{});
+      }
+      team_sync<C>();
+      if (more) commit(0, true);
+      team_sync<C>();
+    }
   } else {
     // ============================= two phase ============================================
     // phase 1: the row sums of head hu (after mixing) against a fixed reference, the
@@ -673,7 +849,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if (more) prefetch(j0 + C::BK, 0, false);
 #pragma unroll
         for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-        if constexpr (mix_pre) mix_blocks(s, I1{}, ILB{});
+        if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
         const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
         if (edge) {
 #pragma unroll
@@ -759,7 +935,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     stage_v_direct(0);
     team_sync<C>();
     logit_block(0);
-    if constexpr (mix_pre) mix_blocks(s, I0{}, I1{});
+    if constexpr (mix_pre) mix_blocks(s, wpre, I0{}, I1{});
     weights(0, 0, true);
     for (int kt = 0; kt < n_kt; ++kt) {
       const int j0 = kt * C::BK;
@@ -767,7 +943,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       if (more) prefetch(j0 + C::BK + 8, j0 + C::BK, true);
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-      if constexpr (mix_pre) mix_blocks(s, I1{}, ILB{});
+      if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
       const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) ||
                         (wrow_min + C::QW > T_);
 #pragma unroll
@@ -789,7 +965,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             }
           }
       }
-      if constexpr (C::MIXPOST) mix_blocks(cv, I0{}, INKB{});
+      if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
       av(cv, I0{});
       team_sync<C>();
       if (more) commit(16, true);
@@ -823,7 +999,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         }
       inv = 1.0f / sqrtf(xgroup_sum(sq) * (1.0f / C::D) + 1e-5f);
     }
-    if (t >= cq1 && gr < T_) {
+    if (t >= halo && gr < T_) {
       __bf16* dst = ob_ + ((size_t)gr * M + m_head) * C::D;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
@@ -848,8 +1024,10 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.q = reinterpret_cast<const __bf16*>(p.q);
   a.k = reinterpret_cast<const __bf16*>(p.k);
   a.v = reinterpret_cast<const __bf16*>(p.v);
-  a.theta = p.theta;
-  a.w = p.w;
+  a.theta = (p.kq & KQ_PRE) ? p.theta_pre : p.theta_post;
+  a.theta2 = p.theta_post;
+  a.w_pre = p.w_pre;
+  a.w_post = p.w_post;
   a.gamma = p.gamma;
   a.beta = p.beta;
   a.lambda = p.lambda;
@@ -861,7 +1039,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.gn = p.gn;
   a.c_q = p.kq ? p.c_q : 1;
   a.c_k = p.kq ? p.c_k : 1;
-  a.r_out = C::R - (a.c_q - 1);
+  a.r_out = C::R - (C::DUAL ? 2 : 1) * (a.c_q - 1);
   a.row_begin = p.row_begin;
   a.n_tiles = (p.T - p.row_begin + a.r_out - 1) / a.r_out;
   a.n_groups = p.M / C::CH;
@@ -884,6 +1062,8 @@ hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr int BK = small ? 32 : 64;
   if constexpr (!MIXPOST) {
     if (p.mix == MIX_PRE) return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true>>(p, stream);
+  } else {
+    if (p.mix == MIX_BOTH) return launch<Cfg<D, CH, 32, BK, KQ, TWO, true, CQM, true>>(p, stream);
   }
   return launch<Cfg<D, CH, 32, BK, KQ, TWO, MIXPOST, CQM, false>>(p, stream);
 }
@@ -900,12 +1080,30 @@ hipError_t launch_cq(const Problem& p, hipStream_t stream) {
   }
 }
 
+// Convolutions on both sides: 32-key tiles (two rings, two sets of Toeplitz operands).
+template <int D, int CH, bool MIXPOST, int CQM>
+hipError_t launch_dual_shape(const Problem& p, hipStream_t stream) {
+  if (p.mix & MIX_PRE) return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, true, 8, true>>(p, stream);
+  return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, false, 8, true>>(p, stream);
+}
+
+template <int D, int CH, bool MIXPOST>
+hipError_t launch_dual(const Problem& p, hipStream_t stream) {
+  if (p.c_q <= 4) return launch_dual_shape<D, CH, MIXPOST, 4>(p, stream);
+  if (p.c_q <= 6) return launch_dual_shape<D, CH, MIXPOST, 6>(p, stream);
+  return launch_dual_shape<D, CH, MIXPOST, 8>(p, stream);
+}
+
 // The schedules with a convolution after softmax (POSTCONV) and the others are instantiated in
 // separate translation units, which are compiled with different instruction-scheduling options.
 template <int D, int CH, bool POSTCONV>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
-  const bool post = p.mix == MIX_POST;
+  const bool post = (p.mix & MIX_POST) != 0;
   if constexpr (POSTCONV) {
+    if (p.kq == KQ_BOTH) {
+      if (post) return launch_dual<D, CH, true>(p, stream);
+      return launch_dual<D, CH, false>(p, stream);
+    }
     if (post) return launch_cq<D, CH, true, true, true>(p, stream);
     return launch_cq<D, CH, true, true, false>(p, stream);
   } else {

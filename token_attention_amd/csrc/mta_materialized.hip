@@ -659,22 +659,24 @@ template <int CK>
 hipError_t launch_conv_ck(bool pre, const float* X, float* Y, const Problem& p, hipStream_t st) {
   const dim3 grid((p.T + 63) / 64, (p.T + 63) / 64, p.B * p.M);
   if (pre)
-    hipLaunchKernelGGL((conv_kernel<CK, true>), grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q);
+    hipLaunchKernelGGL((conv_kernel<CK, true>), grid, dim3(MT_THREADS), 0, st, X, Y, p.theta_pre, p.T, p.M, p.c_q);
   else
-    hipLaunchKernelGGL((conv_kernel<CK, false>), grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q);
+    hipLaunchKernelGGL((conv_kernel<CK, false>), grid, dim3(MT_THREADS), 0, st, X, Y, p.theta_post, p.T, p.M,
+                       p.c_q);
   return hipGetLastError();
 }
 
+// pre: the convolution before softmax (kernels theta_pre), else after it (theta_post)
 hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hipStream_t st) {
   if (!p.fp32) {  // bf16 problems: fp16 MFMA Toeplitz convolution (fp32 problems stay exact)
     const int ntx = (p.T + 63) / 64, ntiles = ntx * ntx;
     const dim3 grid((ntiles + CT - 1) / CT, p.B * p.M);
     if (pre)
-      hipLaunchKernelGGL(conv_mfma_kernel<true>, grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q,
+      hipLaunchKernelGGL(conv_mfma_kernel<true>, grid, dim3(MT_THREADS), 0, st, X, Y, p.theta_pre, p.T, p.M, p.c_q,
                          p.c_k, ntx, ntiles);
     else
-      hipLaunchKernelGGL(conv_mfma_kernel<false>, grid, dim3(MT_THREADS), 0, st, X, Y, p.theta, p.T, p.M, p.c_q,
-                         p.c_k, ntx, ntiles);
+      hipLaunchKernelGGL(conv_mfma_kernel<false>, grid, dim3(MT_THREADS), 0, st, X, Y, p.theta_post, p.T, p.M,
+                         p.c_q, p.c_k, ntx, ntiles);
     return hipGetLastError();
   }
   switch (p.c_k) {
@@ -691,16 +693,17 @@ hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hip
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_mix(float* X, const Problem& p, hipStream_t st) {
+// w: the mixing weights of the side being applied (w_pre or w_post)
+hipError_t launch_mix(float* X, const float* w, const Problem& p, hipStream_t st) {
   const size_t n4 = (size_t)p.T * map_ld(p.T) / 4;  // whole padded map, padding included
   const int G = p.M / p.c_h;
   size_t want = (n4 + 2 * MT_THREADS - 1) / (2 * MT_THREADS);
   const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
   const dim3 grid(gx, p.B * G);
   switch (p.c_h) {
-    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, p.w, p.T, p.M, n4); break;
-    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, p.w, p.T, p.M, n4); break;
-    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, p.w, p.T, p.M, n4); break;
+    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, w, p.T, p.M, n4); break;
+    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, w, p.T, p.M, n4); break;
+    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, w, p.T, p.M, n4); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -719,21 +722,21 @@ hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   float* cur = X;
   float* other = Y;
-  if (p.mix == MIX_PRE && (e = launch_mix(cur, p, st)) != hipSuccess) return e;
-  if (p.kq == KQ_PRE) {
+  if ((p.mix & MIX_PRE) && (e = launch_mix(cur, p.w_pre, p, st)) != hipSuccess) return e;
+  if (p.kq & KQ_PRE) {
     if ((e = launch_conv(true, cur, other, p, st)) != hipSuccess) return e;
     float* t = cur;
     cur = other;
     other = t;
   }
   if ((e = launch_softmax(cur, p, st)) != hipSuccess) return e;
-  if (p.kq == KQ_POST) {
+  if (p.kq & KQ_POST) {
     if ((e = launch_conv(false, cur, other, p, st)) != hipSuccess) return e;
     float* t = cur;
     cur = other;
     other = t;
   }
-  if (p.mix == MIX_POST && (e = launch_mix(cur, p, st)) != hipSuccess) return e;
+  if ((p.mix & MIX_POST) && (e = launch_mix(cur, p.w_post, p, st)) != hipSuccess) return e;
   return launch_av<T, D>(cur, p, st);
 }
 

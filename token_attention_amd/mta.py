@@ -80,8 +80,10 @@ def _check(status: int):
 
 
 def placement_flags(kq: Optional[str], mix: Optional[str], gn: bool, fp32: bool) -> int:
-    f = {None: 0, "pre": KQ_PRE, "post": KQ_POST}[kq]
-    f |= {None: 0, "pre": MIX_PRE, "post": MIX_POST}[mix]
+    """Flag bits of a placement: kq / mix are None, "pre", "post" or "both" (with "both"
+    theta holds [2, M, c_q, c_k] and w [2, M/c_h, c_h, c_h], the side before softmax first)."""
+    f = {None: 0, "pre": KQ_PRE, "post": KQ_POST, "both": KQ_PRE | KQ_POST}[kq]
+    f |= {None: 0, "pre": MIX_PRE, "post": MIX_POST, "both": MIX_PRE | MIX_POST}[mix]
     if gn:
         f |= GN
     if fp32:
