@@ -9,7 +9,8 @@ fp32 accumulation). Inputs are seeded synthetic tensors already resident in HBM.
 Printed: one JSON line with tokens/s (``value``), effective TFLOP/s and the fraction
 of the bf16 MFMA peak, the roofline of the fused kernel (HIP events on its launch
 stream), the library's plain causal attention and the default placement at the same
-shape, the unfused T^2 path, and the fp64 CPU oracle timed on a bounded row sample.
+shape, both convolutions on both sides of softmax at the same shape, the unfused T^2
+path, and the fp64 CPU oracle.
 """
 from __future__ import annotations
 
@@ -34,24 +35,23 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = 4  # index of the T=4096 workload in mta_inputs.CONFIGS
 
 
+def sides(placement) -> int:
+    """Number of sides of softmax an operation acts on."""
+    return {None: 0, "pre": 1, "post": 1, "both": 2}[placement]
+
+
 def flops(cfg) -> int:
-    """Algorithmic flops: causal pairs x (QK^T 2d + AV 2d + conv 2*c_q*c_k + mix 2*c_h)."""
+    """Algorithmic flops: causal pairs x (QK^T 2d + AV 2d + conv 2*c_q*c_k + mix 2*c_h),
+    the convolution and mixing terms once per side they act on."""
     n_c = cfg.T * (cfg.T + 1) // 2
-    per = 4 * cfg.d
-    if cfg.kq:
-        per += 2 * cfg.c_q * cfg.c_k
-    if cfg.mix:
-        per += 2 * cfg.c_h
+    per = 4 * cfg.d + sides(cfg.kq) * 2 * cfg.c_q * cfg.c_k + sides(cfg.mix) * 2 * cfg.c_h
     return cfg.B * cfg.M * n_c * per
 
 
 def materialized_bytes(cfg) -> int:
     """Map traffic of the unfused chain (fp32 T x T maps) plus q, k, v, out."""
     maps = 1  # logits write
-    if cfg.mix:
-        maps += 2
-    if cfg.kq:
-        maps += 2
+    maps += 2 * sides(cfg.mix) + 2 * sides(cfg.kq)  # read + write per step
     maps += 2  # softmax read + write
     maps += 1  # AV read
     elt = 2 if cfg.dtype == "bf16" else 4
@@ -168,7 +168,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for cpu_baseline (0: the whole workload)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
-    ap.add_argument("--only", choices=["fused", "plain", "default", "materialized"], default=None,
+    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized"], default=None,
                     help="run one path only (for counter collection); prints its timing")
     ap.add_argument("--workload", type=int, default=HEADLINE,
                     help="index of the workload in mta_inputs.CONFIGS for --only runs (profiling)")
@@ -216,6 +216,25 @@ def main():
     def fused_default():
         ta.forward(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out, **kw2)
 
+    # both convolutions on both sides of softmax, same shape (own seeded inputs)
+    both_cfg = mta_inputs.config("both_sides_bf16")
+    both_d = {}
+
+    def fused_both():
+        if not both_d:
+            both_d.update(gpu_inputs(both_cfg, torch)[1])
+        b = both_d
+        ta.forward(b["q"], b["k"], b["v"], b["theta"], b["w"], b["gamma"], b["beta"], b["lam"], out=out,
+                   c_q=both_cfg.c_q, c_k=both_cfg.c_k, c_h=both_cfg.c_h, kq=both_cfg.kq, mix=both_cfg.mix,
+                   gn=both_cfg.gn)
+
+    def both_record(ms_both, ms_plain):
+        tf = flops(both_cfg) / (ms_both * 1e-3) / 1e12
+        return {"placement": "convolution and mixing before and after softmax, c_q=4 c_k=9 c_h=4, GroupNorm",
+                "ms": ms_both, "tokens_per_s": tokens / (ms_both * 1e-3), "tflops": tf,
+                "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+                "mta_slowdown_vs_plain": ms_both / ms_plain if ms_plain else None}
+
     def plain_record(ms_plain, ms):
         return {"ms": ms_plain, "tflops": cfg.B * cfg.M * n_c * 4 * cfg.d / (ms_plain * 1e-3) / 1e12,
                 "mta_slowdown": ms / ms_plain if ms else None}
@@ -241,7 +260,7 @@ def main():
         return rec
 
     if args.only:
-        fn = {"fused": fused, "plain": plain, "default": fused_default}.get(args.only)
+        fn = {"fused": fused, "plain": plain, "default": fused_default, "both": fused_both}.get(args.only)
         if fn is not None:
             ms_only = time_launches(fn, args.steps, args.warmup, torch)
             print(json.dumps({"only": args.only, "workload": cfg.name, "ms": ms_only}))
@@ -285,6 +304,10 @@ def main():
     result["plain_attention"] = plain_record(ms_plain, ms)
     result["default_placement_same_shape"] = default_record(
         time_launches(fused_default, args.steps, args.warmup, torch), ms_plain)
+    if cfg.T == both_cfg.T and cfg.B == both_cfg.B and cfg.M == both_cfg.M and cfg.d == both_cfg.d:
+        result["both_sides_same_shape"] = both_record(time_launches(fused_both, args.steps, args.warmup, torch),
+                                                      ms_plain)
+        both_d.clear()
     # a suffix of rows against all keys: one decode step (the last row of every sequence) and
     # a 512-row prefill chunk, both at the headline placement
     rows_rec = {}
