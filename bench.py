@@ -59,12 +59,18 @@ def materialized_bytes(cfg) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of what the headline fused kernel is compiled from: its sources and the compiler
+    flags of its translation unit."""
+    from token_attention_amd import build as tab
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "token_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.startswith(("mta_fused", "mta_kmajor")) or name in ("mta_device.h", "mta_internal.h"):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    tu = "mta_fused_bf16_d128_postconv.hip"
+    for name in ("mta_kmajor_impl.h", "mta_device.h", "mta_internal.h", tu):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    flags = list(tab.CFLAGS) + [f for suffix, fl in tab.EXTRA_FLAGS.items() if tu.endswith(suffix) for f in fl]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
