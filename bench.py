@@ -174,7 +174,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for cpu_baseline (0: the whole workload)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
-    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized"], default=None,
+    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward"], default=None,
                     help="run one path only (for counter collection); prints its timing")
     ap.add_argument("--workload", type=int, default=HEADLINE,
                     help="index of the workload in mta_inputs.CONFIGS for --only runs (profiling)")
@@ -265,6 +265,27 @@ def main():
         del ws
         return rec
 
+    def backward_record(ms_fwd_mat):
+        """The gradients of the layer at this workload (mta_backward_materialized), one call per step."""
+        kwb = dict(kw)
+        need = ta.backward_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h,
+                                           kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        dout = torch.randn(d["q"].shape, generator=gen, device="cuda").to(d["q"].dtype)
+
+        def bwd():
+            ta.backward_materialized(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"],
+                                     dout=dout, workspace=ws, **kwb)
+        ms_b = time_launches(bwd, max(2, args.steps // 4), 1, torch)
+        rec = {"ms": ms_b, "tokens_per_s": tokens / (ms_b * 1e-3), "workspace_gib": need / 2 ** 30,
+               "vs_materialized_forward": ms_b / ms_fwd_mat if ms_fwd_mat else None}
+        del ws
+        return rec
+
+    if args.only == "backward":
+        print(json.dumps({"only": "backward", "workload": cfg.name, **backward_record(None)}))
+        return
     if args.only:
         fn = {"fused": fused, "plain": plain, "default": fused_default, "both": fused_both}.get(args.only)
         if fn is not None:
@@ -326,6 +347,7 @@ def main():
     result["rows_forward"] = rows_rec
     if not args.no_materialized:
         result["materialized"] = materialized_record(ms)
+        result["backward_materialized"] = backward_record(result["materialized"]["ms"])
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "gcn_arch": getattr(props, "gcnArchName", "")}

@@ -137,6 +137,37 @@ int mta_forward_rows(const void* q, const void* k, const void* v, const float* t
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags);
 
 /*
+ * mta_backward_materialized: gradients of the layer (the same function as mta_forward)
+ * with respect to every input, for training. The loss gradient dout = dL/d(out) comes
+ * in; the forward maps are recomputed into the workspace and each step's adjoint runs
+ * as its own kernel over fp32 [B, M, T, T] maps (unfused, like
+ * mta_forward_materialized), in the reverse order of §2-§3.3.
+ *   q .. lambda      the forward arguments (same meaning and layout as mta_forward)
+ *   dout             [B,T,M,d], input dtype: gradient of the output
+ *   dq, dk, dv       [B,T,M,d], input dtype: written (not accumulated); distinct, and
+ *                    none may alias q, k, v or dout
+ *   dtheta_kq        shape of theta_kq (fp32), required iff a KQ flag is set
+ *   dw_mix           shape of w_mix (fp32), required iff a MIX flag is set
+ *   dgn_gamma, dgn_beta  [M*d] fp32, and dlambda (one fp32 value, the gradient of the
+ *                    gate value lambda), required iff MTA_GN; all written
+ *   workspace        device buffer of at least mta_backward_workspace_bytes()
+ * Parameter gradients are reduced in a fixed order: repeated calls give identical
+ * results. Errors as for mta_forward_materialized. Allocates nothing.
+ */
+int mta_backward_materialized(const void* q, const void* k, const void* v, const float* theta_kq,
+                              const float* w_mix, const float* gn_gamma, const float* gn_beta,
+                              float lambda, const void* dout, void* dq, void* dk, void* dv,
+                              float* dtheta_kq, float* dw_mix, float* dgn_gamma, float* dgn_beta,
+                              float* dlambda, int B, int T, int M, int d, int c_q, int c_k, int c_h,
+                              unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by mta_backward_materialized: between four and seven fp32 [B, M, T, LD]
+ * maps (LD = T rounded up to a multiple of 4; one more per step that the placement
+ * adds), the recomputed output before GroupNorm, and partial sums. 0 for invalid sizes. */
+size_t mta_backward_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k, int c_h,
+                                    unsigned flags);
+
+/*
  * mta_attention_plain: standard causal softmax attention softmax(QK^T/sqrt(d))V
  * (§2), computed by the same fused kernel with the convolution, mixing and
  * GroupNorm switched off. flags: 0 or MTA_FP32. Allocates nothing.

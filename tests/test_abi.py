@@ -117,3 +117,29 @@ def test_row_range_outside_the_sequence_is_rejected(row_begin):
                                     mta.KQ_PRE | mta.MIX_POST | mta.GN, None)
     assert st == mta.ERR_INVALID_ARG
     assert "row_begin" in mta.last_error()
+
+
+def test_backward_workspace_size():
+    # maps: S, P, G, G2 always; L with mixing before softmax, E with a convolution after it,
+    # A with mixing after it; plus O and dO with GroupNorm, the transposed weights and partials
+    B, T, M, d = 1, 64, 4, 32
+    one_map = B * M * T * T * 4
+    plain = ta.backward_workspace_bytes(B, T, M, d)
+    assert 4 * one_map <= plain < 5 * one_map
+    full = ta.backward_workspace_bytes(B, T, M, d, c_q=3, c_k=5, c_h=2, kq="both", mix="both", gn=True)
+    assert 7 * one_map <= full < 8 * one_map
+    assert ta.backward_workspace_bytes(0, T, M, d) == 0
+
+
+@pytest.mark.parametrize("which", ["dout", "dtheta", "dw", "dgamma", "dlambda", "workspace"])
+def test_backward_missing_buffers_are_rejected(which):
+    # validation happens before anything is launched, so this runs without a GPU
+    bufs = {n: P + 0x1000 * (i + 1) for i, n in enumerate(
+        ["dout", "dq", "dk", "dv", "dtheta", "dw", "dgamma", "dbeta", "dlambda", "workspace"])}
+    bufs[which] = 0
+    st = mta.lib().mta_backward_materialized(
+        P, P + 0x100, P + 0x200, P, P, P, P, 1.0, bufs["dout"], bufs["dq"], bufs["dk"], bufs["dv"], bufs["dtheta"],
+        bufs["dw"], bufs["dgamma"], bufs["dbeta"], bufs["dlambda"], 1, 64, 4, 128, 3, 5, 2,
+        mta.KQ_PRE | mta.MIX_POST | mta.GN, bufs["workspace"], 1 << 30, None)
+    assert st == (mta.ERR_WORKSPACE if which == "workspace" else mta.ERR_INVALID_ARG)
+    assert mta.last_error() != ""

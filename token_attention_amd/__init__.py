@@ -1,9 +1,10 @@
-"""token_attention_amd: Multi-Token Attention forward layer on AMD MI355X (gfx950).
+"""token_attention_amd: Multi-Token Attention layer (forward and gradients) on AMD MI355X (gfx950).
 
 The compute lives in ``libmta.so`` (hand-written HIP, C ABI in ``include/mta.h``);
 this package only marshals torch device tensors into it.
 """
 from .mta import (  # noqa: F401
-    FP32, GN, KQ_POST, KQ_PRE, MIX_POST, MIX_PRE, MTAError, attention_plain, check_args, forward,
-    forward_materialized, forward_rows, last_error, lib, library_path, materialized_workspace_bytes, placement_flags,
+    FP32, GN, KQ_POST, KQ_PRE, MIX_POST, MIX_PRE, MTAError, attention_plain, backward_materialized,
+    backward_workspace_bytes, check_args, forward, forward_materialized, forward_rows, last_error, lib, library_path,
+    materialized_workspace_bytes, placement_flags,
 )

@@ -6,6 +6,7 @@
 #include <string>
 
 #include "../../include/mta.h"
+#include "mta_backward.h"
 #include "mta_internal.h"
 
 namespace {
@@ -162,6 +163,59 @@ int mta_forward_materialized(const void* q, const void* k, const void* v, const 
   const hipError_t e = mta::launch_materialized(p, workspace, reinterpret_cast<hipStream_t>(stream), &unsupported);
   if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no materialized kernel for this shape");
   return hip_status(e, "mta_forward_materialized launch");
+}
+
+size_t mta_backward_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags) {
+  if (B <= 0 || T <= 0 || M <= 0 || d <= 0 || (flags & ~kKnownFlags)) return 0;
+  const bool kq = flags & (MTA_KQ_PRE | MTA_KQ_POST);
+  const bool mix = flags & (MTA_MIX_PRE | MTA_MIX_POST);
+  if ((kq && (c_q <= 0 || c_k <= 0)) || (mix && (c_h <= 0 || M % c_h != 0))) return 0;
+  mta::Problem p{};
+  p.B = B;
+  p.T = T;
+  p.M = M;
+  p.d = d;
+  p.c_q = kq ? c_q : 1;
+  p.c_k = kq ? c_k : 1;
+  p.c_h = mix ? c_h : 1;
+  p.kq = ((flags & MTA_KQ_PRE) ? mta::KQ_PRE : 0) | ((flags & MTA_KQ_POST) ? mta::KQ_POST : 0);
+  p.mix = ((flags & MTA_MIX_PRE) ? mta::MIX_PRE : 0) | ((flags & MTA_MIX_POST) ? mta::MIX_POST : 0);
+  p.gn = (flags & MTA_GN) ? 1 : 0;
+  p.fp32 = (flags & MTA_FP32) ? 1 : 0;
+  return mta::backward_workspace_bytes(p);
+}
+
+int mta_backward_materialized(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                              const float* gn_gamma, const float* gn_beta, float lambda, const void* dout, void* dq,
+                              void* dk, void* dv, float* dtheta_kq, float* dw_mix, float* dgn_gamma, float* dgn_beta,
+                              float* dlambda, int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, dq, B, T, M, d, c_q, c_k, c_h, flags,
+                          &p);
+  if (st != MTA_OK) return st;
+  if (!dout || !dk || !dv) return fail(MTA_ERR_INVALID_ARG, "dout, dq, dk and dv must not be NULL");
+  if (!aligned16(dout) || !aligned16(dk) || !aligned16(dv))
+    return fail(MTA_ERR_INVALID_ARG, "dout, dq, dk and dv must be 16-byte aligned");
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (void* o : outs)
+    for (const void* in : ins)
+      if (o == in) return fail(MTA_ERR_INVALID_ARG, "dq, dk and dv may not alias q, k, v or dout");
+  if (dq == dk || dq == dv || dk == dv) return fail(MTA_ERR_INVALID_ARG, "dq, dk and dv must be distinct");
+  if (p.kq && !dtheta_kq) return fail(MTA_ERR_INVALID_ARG, "dtheta_kq is required with a KQ flag");
+  if (p.mix && !dw_mix) return fail(MTA_ERR_INVALID_ARG, "dw_mix is required with a MIX flag");
+  if (p.gn && (!dgn_gamma || !dgn_beta || !dlambda))
+    return fail(MTA_ERR_INVALID_ARG, "dgn_gamma, dgn_beta and dlambda are required with MTA_GN");
+  const size_t need = mta::backward_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(MTA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(MTA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  mta::BwdGrads g{dout, dq, dk, dv, dtheta_kq, dw_mix, dgn_gamma, dgn_beta, dlambda};
+  bool unsupported = false;
+  const hipError_t e = mta::launch_backward(p, g, workspace, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no backward kernels for this shape");
+  return hip_status(e, "mta_backward_materialized launch");
 }
 
 int mta_attention_plain(const void* q, const void* k, const void* v, void* out, int B, int T, int M, int d,

@@ -1,0 +1,26 @@
+// Internal interface of the backward pass (mta_backward.hip).
+#pragma once
+
+#include "mta_internal.h"
+
+namespace mta {
+
+// Gradient buffers of one backward call (device memory; unused ones may be null).
+struct BwdGrads {
+  const void* dout;  // [B,T,M,d] input dtype: gradient of the layer output
+  void* dq;          // [B,T,M,d] input dtype
+  void* dk;
+  void* dv;
+  float* dtheta;  // shape of theta_kq
+  float* dw;      // shape of w_mix
+  float* dgamma;  // [M*d]
+  float* dbeta;   // [M*d]
+  float* dlambda;  // [1]
+};
+
+size_t backward_workspace_bytes(const Problem& p);
+bool backward_supported(const Problem& p);
+hipError_t launch_backward(const Problem& p, const BwdGrads& g, void* workspace, hipStream_t stream,
+                           bool* unsupported);
+
+}  // namespace mta

@@ -27,6 +27,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 EXPORTED = [
     "mta_forward", "mta_forward_rows", "mta_forward_materialized", "mta_materialized_workspace_bytes",
     "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
+    "mta_backward_materialized", "mta_backward_workspace_bytes",
 ]
 
 _lib = None
@@ -59,6 +60,11 @@ def lib() -> ctypes.CDLL:
         L.mta_forward_materialized.restype = i
         L.mta_materialized_workspace_bytes.argtypes = [i, i, i, u]
         L.mta_materialized_workspace_bytes.restype = ctypes.c_size_t
+        L.mta_backward_materialized.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp, vp, vp, vp, fp, fp,
+                                                fp, fp, fp] + [i] * 7 + [u, vp, ctypes.c_size_t, vp]
+        L.mta_backward_materialized.restype = i
+        L.mta_backward_workspace_bytes.argtypes = [i] * 7 + [u]
+        L.mta_backward_workspace_bytes.restype = ctypes.c_size_t
         L.mta_attention_plain.argtypes = [vp, vp, vp, vp, i, i, i, i, u, vp]
         L.mta_attention_plain.restype = i
         L.mta_check_args.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [u]
@@ -173,6 +179,43 @@ def forward_materialized(q, k, v, theta=None, w=None, gamma=None, beta=None, lam
         float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, fl, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def backward_workspace_bytes(B: int, T: int, M: int, d: int, *, c_q: int = 1, c_k: int = 1, c_h: int = 1,
+                             kq: Optional[str] = None, mix: Optional[str] = None, gn: bool = False,
+                             fp32: bool = False) -> int:
+    return int(lib().mta_backward_workspace_bytes(B, T, M, d, c_q, c_k, c_h, placement_flags(kq, mix, gn, fp32)))
+
+
+def backward_materialized(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, dout,
+                          c_q: int = 1, c_k: int = 1, c_h: int = 1, kq: Optional[str] = None,
+                          mix: Optional[str] = None, gn: bool = False, workspace=None, stream=None) -> dict:
+    """Gradients (``mta_backward_materialized``) of sum(out * dout). Returns a dict with
+    dq, dk, dv (input dtype) and, where the placement has them, dtheta, dw, dgamma, dbeta
+    (fp32, parameter shapes) and dlambda (fp32 tensor of one element)."""
+    _common(q, k, v, None)
+    if dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must match q in shape and dtype")
+    B, T, M, d = q.shape
+    fp32 = q.dtype == torch.float32
+    fl = placement_flags(kq, mix, gn, fp32)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q)}
+    g["dtheta"] = torch.empty_like(theta) if kq else None
+    g["dw"] = torch.empty_like(w) if mix else None
+    g["dgamma"] = torch.empty_like(gamma) if gn else None
+    g["dbeta"] = torch.empty_like(beta) if gn else None
+    g["dlambda"] = torch.empty(1, dtype=torch.float32, device=q.device) if gn else None
+    need = backward_workspace_bytes(B, T, M, d, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn, fp32=fp32)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().mta_backward_materialized(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(dout, "dout"), _dev(g["dq"], "dq"), _dev(g["dk"], "dk"), _dev(g["dv"], "dv"),
+        _dev(g["dtheta"], "dtheta"), _dev(g["dw"], "dw"), _dev(g["dgamma"], "dgamma"), _dev(g["dbeta"], "dbeta"),
+        _dev(g["dlambda"], "dlambda"), B, T, M, d, c_q, c_k, c_h, fl, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return g
 
 
 def attention_plain(q, k, v, *, out=None, stream=None) -> torch.Tensor:
