@@ -125,7 +125,7 @@ __global__ __launch_bounds__(MT_THREADS) void gn_backward_kernel(const float* __
 }
 
 // ---- out[j][c] = scale * sum_i Map[i][j] X[i][c] (Map^T X; Map is zero for i < j) --------------
-// 64 output rows j of one (b, m) per workgroup; thread (j, channel quarter). Chunks of 32 map rows
+// fp32 tensors (VALU): 64 output rows j of one (b, m) per workgroup; thread (j, channel quarter). Chunks of 32 map rows
 // and the matching rows of X are staged in LDS.
 template <typename T, int D>
 __global__ __launch_bounds__(MT_THREADS) void mapT_mat_kernel(const float* __restrict__ Map, const T* __restrict__ X,
@@ -175,6 +175,111 @@ __global__ __launch_bounds__(MT_THREADS) void mapT_mat_kernel(const float* __res
 #pragma unroll
     for (int c = 0; c < CPT; ++c) dst[c] = T(acc[c] * scale);
   }
+}
+
+// ---- the same product for bf16 tensors on MFMA: out^T = X^T Map ------------------------------
+// 128 output rows j per workgroup (32 per wave). Per chunk of 32 map rows i, the map chunk
+// (fp32 -> bf16) and the X chunk are staged row-major in LDS, and both MFMA operands are read
+// transposed (ds_read_b64_tr_b16) with the same k-slot order: chunk rows 4g..4g+3 and
+// 16+4g..16+4g+3 for lane group g.
+template <int D>
+__global__ __launch_bounds__(MT_THREADS) void mapT_mat_bf16_kernel(const float* __restrict__ Map,
+                                                                  const __bf16* __restrict__ X,
+                                                                  __bf16* __restrict__ out, float scale, int Tn,
+                                                                  int M) {
+  constexpr int JT = 128, IC = 32, NB = D / 16;
+  constexpr int LDX = D + 16, LDM = JT + 16;
+  constexpr int NML = IC * JT / 4 / MT_THREADS;                        // float4 of the map chunk per thread
+  constexpr int NXC = IC * D / 8;                                      // 16-byte pieces of the X chunk
+  constexpr int NXL = (NXC + MT_THREADS - 1) / MT_THREADS;
+  static_assert(IC * JT / 4 % MT_THREADS == 0, "map chunk split");
+  __shared__ __attribute__((aligned(16))) __bf16 Xs[IC * LDX];
+  __shared__ __attribute__((aligned(16))) __bf16 Ms[IC * LDM];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lq = lane & 15, lg = lane >> 4;
+  const int bm = blockIdx.y, b = bm / M, m = bm % M;
+  const int j0 = blockIdx.x * JT, jw = wave * 32;
+  const int ld = map_ld(Tn);
+  const __bf16* xb = X + (size_t)b * Tn * M * D;
+  f32x4 acc[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = j0; i0 < Tn; i0 += IC) {
+    float4 mv[NML];
+    uint4 xv[NXL];
+#pragma unroll
+    for (int u = 0; u < NML; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int r = x / (JT / 4), c4 = (x % (JT / 4)) * 4;
+      const int i = i0 + r, j = j0 + c4;
+      mv[u] = (i < Tn && j < ld) ? *reinterpret_cast<const float4*>(Map + map_index(bm, Tn, i, j))
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < NXL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int r = x / (D / 8), c = x % (D / 8);
+      const bool in = (x < NXC) & (i0 + r < Tn);
+      xv[u] = *reinterpret_cast<const uint4*>(xb + ((size_t)(in ? i0 + r : 0) * M + m) * D + (in ? c * 8 : 0));
+      if (!in) xv[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+    for (int u = 0; u < NML; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int r = x / (JT / 4), c4 = (x % (JT / 4)) * 4;
+      __bf16 h[4] = {(__bf16)mv[u].x, (__bf16)mv[u].y, (__bf16)mv[u].z, (__bf16)mv[u].w};
+      *reinterpret_cast<uint2*>(Ms + r * LDM + c4) = *reinterpret_cast<const uint2*>(h);
+    }
+#pragma unroll
+    for (int u = 0; u < NXL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      if (x < NXC) *reinterpret_cast<uint4*>(Xs + (x / (D / 8)) * LDX + (x % (D / 8)) * 8) = xv[u];
+    }
+    __syncthreads();
+    s16x4 bm8[2][2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      bm8[jb][0] = v_transposed(Ms, 4 * lg, jw + 16 * jb, LDM, lane);
+      bm8[jb][1] = v_transposed(Ms, 16 + 4 * lg, jw + 16 * jb, LDM, lane);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      s16x4 a8[2] = {v_transposed(Xs, 4 * lg, nb * 16, LDX, lane), v_transposed(Xs, 16 + 4 * lg, nb * 16, LDX, lane)};
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(a8);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 bf = *reinterpret_cast<const bf16x8*>(bm8[jb]);
+        acc[nb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[nb][jb], 0, 0, 0);
+      }
+    }
+  }
+  // lane (lq, lg) holds out[j0 + jw + 16 jb + lq][channels 16 nb + 4 lg .. +3]
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int j = j0 + jw + 16 * jb + lq;
+    if (j < Tn) {
+      __bf16* dst = out + ((size_t)b * Tn + j) * M * D + (size_t)m * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        __bf16 h[4] = {(__bf16)(acc[nb][jb][0] * scale), (__bf16)(acc[nb][jb][1] * scale),
+                       (__bf16)(acc[nb][jb][2] * scale), (__bf16)(acc[nb][jb][3] * scale)};
+        *reinterpret_cast<uint2*>(dst + nb * 16 + 4 * lg) = *reinterpret_cast<const uint2*>(h);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_mapT(const float* Map, const T* X, T* out, float scale, const Problem& p, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL(mapT_mat_bf16_kernel<D>, dim3((p.T + 127) / 128, p.B * p.M), dim3(MT_THREADS), 0, st, Map, X,
+                       out, scale, p.T, p.M);
+  } else {
+    hipLaunchKernelGGL((mapT_mat_kernel<T, D>), dim3((p.T + 63) / 64, p.B * p.M), dim3(MT_THREADS), 0, st, Map, X,
+                       out, scale, p.T, p.M);
+  }
+  return hipGetLastError();
 }
 
 // ---- head-mixing weights transposed: wT[g][u][u'] = w[g][u'][u] ---------------------------------
@@ -360,10 +465,12 @@ __global__ __launch_bounds__(MT_THREADS) void conv_adjoint_kernel(const float* _
   }
 }
 
-// ---- kernel-weight gradient partials on a 64 x 64 tile of the output gradient -------------------
-// part[a][e] = sum_{(i,j) in tile} G0[i][j] In0[i-a][j-e+h0], G0 as in conv_adjoint_kernel; In0
+// ---- kernel-weight gradient partials over one 64-row strip of the output gradient ------------
+// part[a][e] = sum_{(i,j) in strip} G0[i][j] In0[i-a][j-e+h0], G0 as in conv_adjoint_kernel; In0
 // is the forward convolution's input: Mask_0 of the logits before softmax (PRE), the softmax
-// weights after it, zero outside the map. Staging of In follows conv_kernel.
+// weights after it, zero outside the map. The workgroup walks the strip's 64 x 64 tiles on and
+// below the diagonal (the gradient is zero above it), staging In like conv_kernel, and keeps
+// the c_q x c_k sums in registers; heavy strips (near the end of the sequence) start first.
 template <int CK, bool PRE>
 __global__ __launch_bounds__(MT_THREADS) void conv_dtheta_kernel(const float* __restrict__ G,
                                                                 const float* __restrict__ In,
@@ -374,70 +481,68 @@ __global__ __launch_bounds__(MT_THREADS) void conv_dtheta_kernel(const float* __
   __shared__ __attribute__((aligned(16))) float tile[(64 + 7) * LD];
   __shared__ float red[4][8 * CK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tx = blockIdx.x, ty = blockIdx.y, bm = blockIdx.z, b = bm / M, m = bm % M;
-  const int ntiles = gridDim.x * gridDim.y, tile_id = ty * gridDim.x + tx;
-  const int i0 = ty * 64, j0 = tx * 64;
+  const int nty = gridDim.x, ty = nty - 1 - blockIdx.x, bm = blockIdx.y, b = bm / M, m = bm % M;
+  const int i0 = ty * 64;
   const int ld = map_ld(Tn);
-  float* dst = part + (((size_t)b * ntiles + tile_id) * M + m) * c_q * CK;
-  if (j0 > i0 + 63) {  // the output gradient is zero above the diagonal
-    for (int x = threadIdx.x; x < c_q * CK; x += MT_THREADS) dst[x] = 0.0f;
-    return;
-  }
   const int rows = 64 + c_q - 1;
-  constexpr int NL = ((64 + 7) * (TW / 4) + MT_THREADS - 1) / MT_THREADS;
-  float4 buf[NL];
-#pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const int x = threadIdx.x + u * MT_THREADS;
-    const int rr = x / (TW / 4), c4 = (x % (TW / 4)) * 4;
-    const int r = i0 - (c_q - 1) + rr, s = j0 - 16 + c4;
-    const bool in = (x < rows * (TW / 4)) & (r >= 0) & (r < Tn) & (s >= 0) & (s < ld);
-    buf[u] = *reinterpret_cast<const float4*>(In + map_index(bm, Tn, in ? r : 0, in ? s : 0));
-    const int lim = PRE ? min(r, Tn - 1) : Tn - 1;
-    buf[u].x = (in & (s + 0 <= lim)) ? buf[u].x : 0.0f;
-    buf[u].y = (in & (s + 1 <= lim)) ? buf[u].y : 0.0f;
-    buf[u].z = (in & (s + 2 <= lim)) ? buf[u].z : 0.0f;
-    buf[u].w = (in & (s + 3 <= lim)) ? buf[u].w : 0.0f;
-  }
-#pragma unroll
-  for (int u = 0; u < NL; ++u) {
-    const int x = threadIdx.x + u * MT_THREADS;
-    if (x < rows * (TW / 4)) *reinterpret_cast<float4*>(tile + (x / (TW / 4)) * LD + (x % (TW / 4)) * 4) = buf[u];
-  }
-  // this thread's 16 gradient values (row i0 + orow, columns j0 + oc0 ..), masked
   const int orow = threadIdx.x >> 2, oc0 = (threadIdx.x & 3) * 16;
   const int i = i0 + orow;
-  float g[16];
-#pragma unroll
-  for (int v4 = 0; v4 < 4; ++v4) {
-    const int j = j0 + oc0 + 4 * v4;
-    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i < Tn && j < ld) gv = *reinterpret_cast<const float4*>(G + map_index(bm, Tn, i, j));
-    g[4 * v4 + 0] = (i < Tn && j + 0 <= i) ? gv.x : 0.0f;
-    g[4 * v4 + 1] = (i < Tn && j + 1 <= i) ? gv.y : 0.0f;
-    g[4 * v4 + 2] = (i < Tn && j + 2 <= i) ? gv.z : 0.0f;
-    g[4 * v4 + 3] = (i < Tn && j + 3 <= i) ? gv.w : 0.0f;
-  }
-  __syncthreads();
+  constexpr int NL = ((64 + 7) * (TW / 4) + MT_THREADS - 1) / MT_THREADS;
   float acc[8][CK];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int e = 0; e < CK; ++e) acc[a][e] = 0.0f;
+  for (int tx = 0; tx <= ty; ++tx) {
+    const int j0 = tx * 64;
+    float4 buf[NL];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    if (a < c_q) {
-      // In0[i-a][j-e+h0] sits at tile row orow + c_q - 1 - a, column oc0 + c + 16 - e + H0
-      const float* src = tile + (orow + c_q - 1 - a) * LD + oc0 + 16 - H0;
-      float seg[16 + CK - 1];
+    for (int u = 0; u < NL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      const int rr = x / (TW / 4), c4 = (x % (TW / 4)) * 4;
+      const int r = i0 - (c_q - 1) + rr, s = j0 - 16 + c4;
+      const bool in = (x < rows * (TW / 4)) & (r >= 0) & (r < Tn) & (s >= 0) & (s < ld);
+      buf[u] = *reinterpret_cast<const float4*>(In + map_index(bm, Tn, in ? r : 0, in ? s : 0));
+      const int lim = PRE ? min(r, Tn - 1) : Tn - 1;
+      buf[u].x = (in & (s + 0 <= lim)) ? buf[u].x : 0.0f;
+      buf[u].y = (in & (s + 1 <= lim)) ? buf[u].y : 0.0f;
+      buf[u].z = (in & (s + 2 <= lim)) ? buf[u].z : 0.0f;
+      buf[u].w = (in & (s + 3 <= lim)) ? buf[u].w : 0.0f;
+    }
+    // this thread's 16 gradient values (row i, columns j0 + oc0 ..), masked
+    float g[16];
 #pragma unroll
-      for (int x = 0; x < 16 + CK - 1; ++x) seg[x] = src[x];
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int j = j0 + oc0 + 4 * v4;
+      float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < Tn && j < ld) gv = *reinterpret_cast<const float4*>(G + map_index(bm, Tn, i, j));
+      g[4 * v4 + 0] = (i < Tn && j + 0 <= i) ? gv.x : 0.0f;
+      g[4 * v4 + 1] = (i < Tn && j + 1 <= i) ? gv.y : 0.0f;
+      g[4 * v4 + 2] = (i < Tn && j + 2 <= i) ? gv.z : 0.0f;
+      g[4 * v4 + 3] = (i < Tn && j + 3 <= i) ? gv.w : 0.0f;
+    }
+    __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
-      for (int e = 0; e < CK; ++e) {
-        float s = 0.0f;
+    for (int u = 0; u < NL; ++u) {
+      const int x = threadIdx.x + u * MT_THREADS;
+      if (x < rows * (TW / 4)) *reinterpret_cast<float4*>(tile + (x / (TW / 4)) * LD + (x % (TW / 4)) * 4) = buf[u];
+    }
+    __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 16; ++c) s += g[c] * seg[c - e + 2 * H0];
-        acc[a][e] += s;
+    for (int a = 0; a < 8; ++a) {
+      if (a < c_q) {
+        // In0[i-a][j-e+h0] sits at tile row orow + c_q - 1 - a, column oc0 + c + 16 - e + H0
+        const float* src = tile + (orow + c_q - 1 - a) * LD + oc0 + 16 - H0;
+        float seg[16 + CK - 1];
+#pragma unroll
+        for (int x = 0; x < 16 + CK - 1; ++x) seg[x] = src[x];
+#pragma unroll
+        for (int e = 0; e < CK; ++e) {
+          float s = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) s += g[c] * seg[c - e + 2 * H0];
+          acc[a][e] += s;
+        }
       }
     }
   }
@@ -452,6 +557,7 @@ __global__ __launch_bounds__(MT_THREADS) void conv_dtheta_kernel(const float* __
     }
   }
   __syncthreads();
+  float* dst = part + (((size_t)b * nty + ty) * M + m) * c_q * CK;
   for (int x = threadIdx.x; x < c_q * CK; x += MT_THREADS) dst[x] = (red[0][x] + red[1][x]) + (red[2][x] + red[3][x]);
 }
 
@@ -471,7 +577,7 @@ hipError_t sum_rows(const float* part, size_t R, size_t K, float* out, hipStream
 
 template <int CK>
 hipError_t launch_dtheta_ck(bool pre, const float* G, const float* In, float* part, const Problem& p, hipStream_t st) {
-  const dim3 grid((p.T + 63) / 64, (p.T + 63) / 64, p.B * p.M);
+  const dim3 grid((p.T + 63) / 64, p.B * p.M);
   if (pre)
     hipLaunchKernelGGL((conv_dtheta_kernel<CK, true>), grid, dim3(MT_THREADS), 0, st, G, In, part, p.T, p.M, p.c_q);
   else
@@ -501,8 +607,8 @@ hipError_t conv_backward(bool pre, const float* G, const float* In, float* Y, co
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const size_t ntiles = (size_t)((p.T + 63) / 64) * ((p.T + 63) / 64);
-  return sum_rows(part, (size_t)p.B * ntiles, (size_t)p.M * p.c_q * p.c_k, dtheta_out, st);
+  const size_t nstrips = (size_t)(p.T + 63) / 64;
+  return sum_rows(part, (size_t)p.B * nstrips, (size_t)p.M * p.c_q * p.c_k, dtheta_out, st);
 }
 
 hipError_t launch_softmax_bwd(const float* P, float* G, const Problem& p, hipStream_t st) {
@@ -565,10 +671,10 @@ BwdLayout bwd_layout(const Problem& p) {
   l.O = take(p.gn ? tens * sizeof(float) : 0);
   l.dO = take(p.gn ? tens * (p.fp32 ? 4 : 2) : 0);
   l.wT = take((size_t)p.M * p.c_h * sizeof(float));
-  const size_t ntiles = (size_t)((p.T + 63) / 64) * ((p.T + 63) / 64);
+  const size_t nstrips = (size_t)(p.T + 63) / 64;
   const size_t nch = (size_t)(p.T + GN_RB - 1) / GN_RB;
   size_t part = 0;
-  if (p.kq) part = std::max(part, (size_t)p.B * ntiles * p.M * p.c_q * p.c_k);
+  if (p.kq) part = std::max(part, (size_t)p.B * nstrips * p.M * p.c_q * p.c_k);
   if (p.mix) part = std::max(part, (size_t)p.B * PD_CHUNKS * p.M * p.c_h);
   if (p.gn) part = std::max(part, 2 * (size_t)p.B * nch * p.M * p.d + (size_t)p.B * nch * p.M);
   l.part = take(part * sizeof(float));
@@ -587,7 +693,6 @@ hipError_t run_backward(const Problem& p, const BwdGrads& g, char* ws, hipStream
   const T* q = reinterpret_cast<const T*>(p.q);
   const T* k = reinterpret_cast<const T*>(p.k);
   const T* v = reinterpret_cast<const T*>(p.v);
-  const size_t map_bytes = (size_t)p.B * p.M * p.T * map_ld(p.T) * sizeof(float);
   const float scale = (float)(1.0 / __builtin_sqrt((double)p.d));
   hipError_t e;
   const dim3 lgrid((p.T + 127) / 128, (p.T + 127) / 128, p.B * p.M);
@@ -595,21 +700,15 @@ hipError_t run_backward(const Problem& p, const BwdGrads& g, char* ws, hipStream
   // ---- forward maps
   hipLaunchKernelGGL((logits_kernel<T, D>), lgrid, dim3(MT_THREADS), 0, st, q, k, mS, p.T, p.M, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.mix & MIX_PRE) {
-    if ((e = hipMemcpyAsync(mL, mS, map_bytes, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
-    if ((e = launch_mix(mL, p.w_pre, p, st)) != hipSuccess) return e;
-  }
+  if ((p.mix & MIX_PRE) && (e = launch_mix(mL, p.w_pre, p, st, mS)) != hipSuccess) return e;
   if (p.kq & KQ_PRE) {
     if ((e = launch_conv(true, mL, mP, p, st)) != hipSuccess) return e;
+    if ((e = launch_softmax(mP, p, st)) != hipSuccess) return e;
   } else {
-    if ((e = hipMemcpyAsync(mP, mL, map_bytes, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
+    if ((e = launch_softmax(mP, p, st, mL)) != hipSuccess) return e;
   }
-  if ((e = launch_softmax(mP, p, st)) != hipSuccess) return e;
   if ((p.kq & KQ_POST) && (e = launch_conv(false, mP, mE, p, st)) != hipSuccess) return e;
-  if (p.mix & MIX_POST) {
-    if ((e = hipMemcpyAsync(mA, mE, map_bytes, hipMemcpyDeviceToDevice, st)) != hipSuccess) return e;
-    if ((e = launch_mix(mA, p.w_post, p, st)) != hipSuccess) return e;
-  }
+  if ((p.mix & MIX_POST) && (e = launch_mix(mA, p.w_post, p, st, mE)) != hipSuccess) return e;
 
   // ---- GroupNorm / gate backward -> dO
   const T* dO = reinterpret_cast<const T*>(g.dout);
@@ -632,10 +731,7 @@ hipError_t run_backward(const Problem& p, const BwdGrads& g, char* ws, hipStream
   }
 
   // ---- dV = A^T dO, dA = dO V^T
-  const dim3 tgrid((p.T + 63) / 64, p.B * p.M);
-  hipLaunchKernelGGL((mapT_mat_kernel<T, D>), tgrid, dim3(MT_THREADS), 0, st, mA, dO, reinterpret_cast<T*>(g.dv),
-                     1.0f, p.T, p.M);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_mapT<T, D>(mA, dO, reinterpret_cast<T*>(g.dv), 1.0f, p, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((logits_kernel<T, D>), lgrid, dim3(MT_THREADS), 0, st, dO, v, G, p.T, p.M, 1.0f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -661,9 +757,7 @@ hipError_t run_backward(const Problem& p, const BwdGrads& g, char* ws, hipStream
   if ((e = launch_av_to<T, D, T>(G, k, reinterpret_cast<T*>(g.dq), nullptr, nullptr, 0.0f, 0, scale, p.B, p.T, p.M,
                                  st)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL((mapT_mat_kernel<T, D>), tgrid, dim3(MT_THREADS), 0, st, G, q, reinterpret_cast<T*>(g.dk), scale,
-                     p.T, p.M);
-  return hipGetLastError();
+  return launch_mapT<T, D>(G, q, reinterpret_cast<T*>(g.dk), scale, p, st);
 }
 
 }  // namespace

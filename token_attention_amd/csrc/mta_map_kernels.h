@@ -101,11 +101,11 @@ __global__ __launch_bounds__(MT_THREADS) void logits_kernel(const T* __restrict_
   }
 }
 
-// ---- head mixing, in place: X_u <- sum_u' w[g][u][u'] X_u' ---------------------------
+// ---- head mixing: X_u <- sum_u' w[g][u][u'] Src_u' (Src = X: in place) -----------------
 // Each thread mixes two consecutive float4 of every map of the group per step (2 x c_h
 // 16-byte loads in flight).
 template <int CH>
-__global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* __restrict__ X, const float* __restrict__ w,
+__global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* X, const float* Src, const float* __restrict__ w,
                                                         int Tn, int M, size_t n4_per_map) {
   const int bg = blockIdx.y;  // b * (M/CH) + g
   const int G = M / CH;
@@ -116,14 +116,15 @@ __global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* __restrict__ X, 
 #pragma unroll
     for (int x = 0; x < CH; ++x) wl[u][x] = w[((size_t)g * CH + u) * CH + x];
   f32x4* base = reinterpret_cast<f32x4*>(X) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
+  const f32x4* src = reinterpret_cast<const f32x4*>(Src) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
   for (size_t e = ((size_t)blockIdx.x * MT_THREADS + threadIdx.x) * 2; e < n4_per_map;
        e += (size_t)gridDim.x * MT_THREADS * 2) {
     const bool two = e + 1 < n4_per_map;
     f32x4 in[CH][2];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      in[u][0] = base[(size_t)u * n4_per_map + e];
-      in[u][1] = two ? base[(size_t)u * n4_per_map + e + 1] : in[u][0];
+      in[u][0] = src[(size_t)u * n4_per_map + e];
+      in[u][1] = two ? src[(size_t)u * n4_per_map + e + 1] : in[u][0];
     }
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
@@ -326,20 +327,22 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return v;
 }
 
+// reads the row from Src (= X: in place), writes it to X
 template <int NV>
-__global__ __launch_bounds__(MT_THREADS) void softmax_kernel(float* __restrict__ X, int Tn) {
+__global__ __launch_bounds__(MT_THREADS) void softmax_kernel(float* X, const float* Src, int Tn) {
   __shared__ float red[MT_THREADS / 64];
   const size_t row = blockIdx.x;  // (b*M + m)*T + i
   const int i = (int)(row % Tn);
   const int ld = map_ld(Tn);
   float4* x = reinterpret_cast<float4*>(X + row * ld);
+  const float4* xs = reinterpret_cast<const float4*>(Src + row * ld);
   const float NEG = -__builtin_inff();
   float4 v[NV];
   float mx = NEG;
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
     const int j = (c * MT_THREADS + threadIdx.x) * 4;
-    v[c] = j < ld ? x[j / 4] : make_float4(NEG, NEG, NEG, NEG);
+    v[c] = j < ld ? xs[j / 4] : make_float4(NEG, NEG, NEG, NEG);
     if (j + 0 > i) v[c].x = NEG;
     if (j + 1 > i) v[c].y = NEG;
     if (j + 2 > i) v[c].z = NEG;
@@ -362,29 +365,33 @@ __global__ __launch_bounds__(MT_THREADS) void softmax_kernel(float* __restrict__
 }
 
 // rows longer than 16 * 4 * MT_THREADS: three passes over the row
-__global__ __launch_bounds__(MT_THREADS) void softmax_long_kernel(float* __restrict__ X, int Tn) {
+__global__ __launch_bounds__(MT_THREADS) void softmax_long_kernel(float* X, const float* Src, int Tn) {
   __shared__ float red[MT_THREADS / 64];
   const size_t row = blockIdx.x;
   const int i = (int)(row % Tn);
   float* x = X + row * map_ld(Tn);
+  const float* xs = Src + row * map_ld(Tn);
   float mx = -__builtin_inff();
-  for (int j = threadIdx.x; j <= i; j += MT_THREADS) mx = fmaxf(mx, x[j]);
+  for (int j = threadIdx.x; j <= i; j += MT_THREADS) mx = fmaxf(mx, xs[j]);
   mx = block_reduce(mx, red, true);
   float sum = 0.0f;
-  for (int j = threadIdx.x; j <= i; j += MT_THREADS) sum += expf(x[j] - mx);
+  for (int j = threadIdx.x; j <= i; j += MT_THREADS) sum += expf(xs[j] - mx);
   const float inv = 1.0f / block_reduce(sum, red, false);
-  for (int j = threadIdx.x; j < Tn; j += MT_THREADS) x[j] = (j <= i) ? expf(x[j] - mx) * inv : 0.0f;
+  // every thread reads its own entries before writing them (in place is safe)
+  for (int j = threadIdx.x; j < Tn; j += MT_THREADS) x[j] = (j <= i) ? expf(xs[j] - mx) * inv : 0.0f;
 }
 
-hipError_t launch_softmax(float* X, const Problem& p, hipStream_t st) {
+// causal row softmax of Src (default: X itself) into X
+hipError_t launch_softmax(float* X, const Problem& p, hipStream_t st, const float* Src = nullptr) {
   const dim3 grid((unsigned)((size_t)p.B * p.M * p.T));
   const int nv = (map_ld(p.T) / 4 + MT_THREADS - 1) / MT_THREADS;
-  if (nv <= 1) hipLaunchKernelGGL(softmax_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, p.T);
-  else if (nv <= 2) hipLaunchKernelGGL(softmax_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, p.T);
-  else if (nv <= 4) hipLaunchKernelGGL(softmax_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, p.T);
-  else if (nv <= 8) hipLaunchKernelGGL(softmax_kernel<8>, grid, dim3(MT_THREADS), 0, st, X, p.T);
-  else if (nv <= 16) hipLaunchKernelGGL(softmax_kernel<16>, grid, dim3(MT_THREADS), 0, st, X, p.T);
-  else hipLaunchKernelGGL(softmax_long_kernel, grid, dim3(MT_THREADS), 0, st, X, p.T);
+  const float* S = Src ? Src : X;
+  if (nv <= 1) hipLaunchKernelGGL(softmax_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, S, p.T);
+  else if (nv <= 2) hipLaunchKernelGGL(softmax_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, S, p.T);
+  else if (nv <= 4) hipLaunchKernelGGL(softmax_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, S, p.T);
+  else if (nv <= 8) hipLaunchKernelGGL(softmax_kernel<8>, grid, dim3(MT_THREADS), 0, st, X, S, p.T);
+  else if (nv <= 16) hipLaunchKernelGGL(softmax_kernel<16>, grid, dim3(MT_THREADS), 0, st, X, S, p.T);
+  else hipLaunchKernelGGL(softmax_long_kernel, grid, dim3(MT_THREADS), 0, st, X, S, p.T);
   return hipGetLastError();
 }
 
@@ -697,17 +704,19 @@ hipError_t launch_conv(bool pre, const float* X, float* Y, const Problem& p, hip
   return hipErrorInvalidValue;
 }
 
-// w: the mixing weights of the side being applied (w_pre or w_post)
-hipError_t launch_mix(float* X, const float* w, const Problem& p, hipStream_t st) {
+// w: the mixing weights of the side being applied (w_pre or w_post); mixes Src (default: X
+// itself) into X
+hipError_t launch_mix(float* X, const float* w, const Problem& p, hipStream_t st, const float* Src = nullptr) {
+  const float* S = Src ? Src : X;
   const size_t n4 = (size_t)p.T * map_ld(p.T) / 4;  // whole padded map, padding included
   const int G = p.M / p.c_h;
   size_t want = (n4 + 2 * MT_THREADS - 1) / (2 * MT_THREADS);
   const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
   const dim3 grid(gx, p.B * G);
   switch (p.c_h) {
-    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, w, p.T, p.M, n4); break;
-    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, w, p.T, p.M, n4); break;
-    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, w, p.T, p.M, n4); break;
+    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.T, p.M, n4); break;
+    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.T, p.M, n4); break;
+    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.T, p.M, n4); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
