@@ -337,6 +337,7 @@ def main():
         both_d.clear()
     # a suffix of rows against all keys: one decode step (the last row of every sequence) and
     # a 512-row prefill chunk, both at the headline placement
+    # (mta_forward_rows: row tiles only; mta_forward_rows_split: key range split over workgroups)
     rows_rec = {}
     for name, rb in (("decode_step", cfg.T - 1), ("prefill_chunk_512", cfg.T - 512)):
         def part(rb=rb):
@@ -344,6 +345,15 @@ def main():
                             row_begin=rb, out=out, **kw)
         ms_rows = time_launches(part, args.steps, args.warmup, torch)
         rows_rec[name] = {"row_begin": rb, "ms": ms_rows, "tokens_per_s": cfg.B * (cfg.T - rb) / (ms_rows * 1e-3)}
+        need = ta.rows_split_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, row_begin=rb, **kw)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+        def part_split(rb=rb, ws=ws):
+            ta.forward_rows_split(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"],
+                                  row_begin=rb, out=out, workspace=ws, **kw)
+        ms_split = time_launches(part_split, args.steps, args.warmup, torch)
+        rows_rec[name + "_split"] = {"row_begin": rb, "ms": ms_split,
+                                     "tokens_per_s": cfg.B * (cfg.T - rb) / (ms_split * 1e-3)}
     result["rows_forward"] = rows_rec
     if not args.no_materialized:
         result["materialized"] = materialized_record(ms)

@@ -132,6 +132,31 @@ int mta_forward_rows(const void* q, const void* k, const void* v, const float* t
                      void* out, int B, int T, int M, int d, int c_q, int c_k, int c_h, int row_begin,
                      unsigned flags, void* stream);
 
+/*
+ * mta_forward_rows_split: mta_forward_rows with the key range of every row tile split over
+ * several workgroups, for short row ranges (a decode step, a small prefill chunk) where the
+ * row tiles alone would leave most of the GPU idle. Each workgroup covers one chunk of keys;
+ * the partial softmax statistics and AV sums of the chunks are combined exactly (statistics
+ * and sums over keys add up, §2), then GroupNorm and the gate are applied. With convolution
+ * or mixing after softmax a statistics pass and a weighted pass run per chunk. Results equal
+ * mta_forward_rows up to summation order (not bit for bit). When splitting does not pay (many
+ * row tiles, or fp32 tensors) it runs mta_forward_rows and needs no workspace.
+ *   workspace        device buffer of at least mta_forward_rows_split_workspace_bytes()
+ *                    (may be NULL when that is 0); 16-byte aligned
+ * Other arguments, reads and writes as for mta_forward_rows; errors as for
+ * mta_forward_materialized. Allocates nothing.
+ */
+int mta_forward_rows_split(const void* q, const void* k, const void* v, const float* theta_kq,
+                           const float* w_mix, const float* gn_gamma, const float* gn_beta,
+                           float lambda, void* out, int B, int T, int M, int d, int c_q, int c_k,
+                           int c_h, int row_begin, unsigned flags, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace needed by mta_forward_rows_split (0: no splitting for this shape, or invalid
+ * sizes): partial statistics and AV sums of up to 64 key chunks for rows row_begin-16 .. T-1. */
+size_t mta_forward_rows_split_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k,
+                                              int c_h, int row_begin, unsigned flags);
+
 /* Workspace needed by mta_forward_materialized: two fp32 [B, M, T, LD] maps, LD = T
  * rounded up to a multiple of 4. Returns 0 for invalid sizes. */
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags);

@@ -143,3 +143,22 @@ def test_backward_missing_buffers_are_rejected(which):
         mta.KQ_PRE | mta.MIX_POST | mta.GN, bufs["workspace"], 1 << 30, None)
     assert st == (mta.ERR_WORKSPACE if which == "workspace" else mta.ERR_INVALID_ARG)
     assert mta.last_error() != ""
+
+
+def test_rows_split_workspace_size():
+    kw = dict(c_q=4, c_k=9, c_h=4, kq="post", mix="pre", gn=True)
+    decode = ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4095, **kw)
+    assert decode > 0
+    # enough row tiles already (the whole sequence): no splitting, no workspace
+    assert ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=0, **kw) == 0
+    # fp32 tensors run the unsplit kernel
+    assert ta.rows_split_workspace_bytes(1, 90, 4, 32, row_begin=89, c_q=3, c_k=5, c_h=2, kq="pre", mix="post",
+                                         gn=True, fp32=True) == 0
+    assert ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4096, **kw) == 0
+
+
+@pytest.mark.parametrize("row_begin", [-1, 64])
+def test_rows_split_outside_the_sequence_is_rejected(row_begin):
+    st = mta.lib().mta_forward_rows_split(P, P + 0x100, P + 0x200, P, P, P, P, 1.0, P + 0x300, 1, 64, 4, 128, 3, 5,
+                                          2, row_begin, mta.KQ_PRE | mta.MIX_POST | mta.GN, None, 0, None)
+    assert st == mta.ERR_INVALID_ARG

@@ -415,3 +415,102 @@ def test_both_sides_full_size_sampled_rows(path):
     got = run(path, cfg, dev_inputs(cfg, inp), inp["lam"])
     compare(cfg, got, want, rows=rows, what=f"{path} rows={len(rows)}")
     assert np.isfinite(got).all()
+
+
+# ---- row ranges with the key range split over workgroups -----------------------------------
+SPLIT_PLACEMENTS = [(None, None, 1), ("pre", "post", 2), ("post", "pre", 4), ("pre", "pre", 4), ("post", "post", 2),
+                    ("both", "both", 4), ("both", None, 1), (None, "post", 4), ("pre", None, 1)]
+
+
+@pytest.mark.parametrize("row_begin", [299, 250, 0])
+@pytest.mark.parametrize("kq,mix,c_h", SPLIT_PLACEMENTS)
+def test_rows_split_against_oracle(row_begin, kq, mix, c_h):
+    """mta_forward_rows_split (key chunks combined afterwards) against the oracle and the
+    unsplit row range, for decode-like, chunk-like and whole ranges of every schedule."""
+    cfg = mta_inputs.MTAConfig("rows_split", 2, 300, 8, 128, 4, 9, c_h, kq, mix, True, "bf16", 0.1, 0.1, 1.0, 0.0,
+                               0.8, seed=41)
+    inp = case(cfg)
+    assert ta.rows_split_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, row_begin=row_begin, c_q=cfg.c_q, c_k=cfg.c_k,
+                                         c_h=cfg.c_h, kq=kq, mix=mix, gn=True) > 0
+    dv = dev_inputs(cfg, inp)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    args = (dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"])
+    part = torch.full_like(dv["q"], 7.0)
+    ta.forward_rows_split(*args, row_begin=row_begin, out=part, **kw)
+    ref = ta.forward_rows(*args, row_begin=row_begin, **kw)
+    torch.cuda.synchronize()
+    p = part.float().cpu()
+    assert bool((p[:, :row_begin] == 7.0).all())
+    got = p.numpy().astype(np.float64)
+    rows = np.arange(row_begin, cfg.T)
+    compare(cfg, got, oracle_full(cfg), rows=rows, what=f"split rows {row_begin}.. {kq}/{mix}/{c_h}")
+    diff = float((p[:, row_begin:] - ref.float().cpu()[:, row_begin:]).abs().max())
+    log(f"  vs unsplit: max diff {diff:.3e}")
+    assert diff <= 2e-2
+
+
+def test_rows_split_many_row_tiles():
+    """Several row tiles per sequence, each split into key chunks (the statistics of the rows a
+    tile shares with its neighbour are written once)."""
+    cfg = mta_inputs.MTAConfig("rows_split_tiles", 1, 600, 4, 128, 4, 9, 4, "both", "both", True, "bf16", 0.1, 0.1,
+                               1.0, 0.0, 0.8, seed=42)
+    inp = case(cfg)
+    dv = dev_inputs(cfg, inp)
+    out = ta.forward_rows_split(dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"],
+                                row_begin=0, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=True)
+    torch.cuda.synchronize()
+    compare(cfg, out.float().cpu().numpy().astype(np.float64), oracle_full(cfg), what="split, 11 row tiles")
+
+
+@pytest.mark.parametrize("kq,mix,c_h", [(None, None, 1), ("post", "pre", 4), ("both", "both", 4)])
+def test_rows_split_late_dominant_key(kq, mix, c_h):
+    """The exact fallback inside one key chunk: one key dominates one query's row by ~130."""
+    d = 128
+    cfg = mta_inputs.MTAConfig("split_late", 1, 300, 8, d, 4, 9, c_h, kq, mix, True, "bf16", 0.05, 0.05, 1.0, 0.0,
+                               0.8, seed=43)
+    inp = dict(case(cfg))
+    q, k = inp["q"].astype(np.float64), inp["k"].copy()
+    jkey, iq = 200, 299
+    for m in range(cfg.M):
+        qv = q[0, iq, m]
+        k[0, jkey, m] = 130.0 * np.sqrt(d) / float(qv @ qv) * qv
+    inp["k"] = mta_inputs.round_bf16(k.astype(np.float32))
+    want = oracle.forward_cfg(cfg, inp, rows=[299])
+    dv = dev_inputs(cfg, inp)
+    out = ta.forward_rows_split(dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"],
+                                row_begin=299, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=kq, mix=mix, gn=True)
+    torch.cuda.synchronize()
+    compare(cfg, out.float().cpu().numpy().astype(np.float64), want, rows=[299], what=f"split late {kq}/{mix}")
+
+
+@pytest.mark.parametrize("row_begin", [4095, 3584])
+def test_rows_split_at_full_size(row_begin):
+    """Decode step and a 512-row chunk of the T=4096 workload, split over key chunks."""
+    cfg = mta_inputs.config(4)
+    inp = case(cfg)
+    rows = np.arange(row_begin, cfg.T, dtype=np.int32)
+    if len(rows) > 8:
+        rows = np.unique(np.concatenate([rows[:4], rows[-4:], mta_inputs.sample_rows(cfg.T, row_tile=61, n_random=8)]))
+        rows = rows[rows >= row_begin].astype(np.int32)
+    want = oracle.forward_cfg(cfg, inp, rows=rows)
+    dv = dev_inputs(cfg, inp)
+    out = ta.forward_rows_split(dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"],
+                                row_begin=row_begin, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix,
+                                gn=cfg.gn)
+    torch.cuda.synchronize()
+    compare(cfg, out.float().cpu().numpy().astype(np.float64), want, rows=rows,
+            what=f"split rows {row_begin}.. ({len(rows)} checked)")
+
+
+def test_rows_split_fp32_runs_unsplit():
+    cfg = mta_inputs.MTAConfig("split_fp32", 1, 90, 4, 32, 3, 5, 2, "pre", "post", True, "fp32", 0.1, 0.1, 1.0, 0.0,
+                               0.8, seed=44)
+    assert ta.rows_split_workspace_bytes(1, 90, 4, 32, row_begin=89, c_q=3, c_k=5, c_h=2, kq="pre", mix="post",
+                                         gn=True, fp32=True) == 0
+    inp = case(cfg)
+    dv = dev_inputs(cfg, inp)
+    out = ta.forward_rows_split(dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"],
+                                row_begin=60, c_q=3, c_k=5, c_h=2, kq="pre", mix="post", gn=True)
+    torch.cuda.synchronize()
+    compare(cfg, out.float().cpu().numpy().astype(np.float64), oracle_full(cfg), rows=np.arange(60, 90),
+            what="fp32 rows 60..")

@@ -5,6 +5,6 @@ this package only marshals torch device tensors into it.
 """
 from .mta import (  # noqa: F401
     FP32, GN, KQ_POST, KQ_PRE, MIX_POST, MIX_PRE, MTAError, attention_plain, backward_materialized,
-    backward_workspace_bytes, check_args, forward, forward_materialized, forward_rows, last_error, lib, library_path,
-    materialized_workspace_bytes, placement_flags,
+    backward_workspace_bytes, check_args, forward, forward_materialized, forward_rows, forward_rows_split, last_error,
+    lib, library_path, materialized_workspace_bytes, placement_flags, rows_split_workspace_bytes,
 )

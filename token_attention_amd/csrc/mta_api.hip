@@ -95,6 +95,27 @@ int validate(const void* q, const void* k, const void* v, const float* theta, co
   return MTA_OK;
 }
 
+// The size and placement fields of a problem (no pointers), for workspace-size queries;
+// false for sizes that no call would accept.
+bool sizes_problem(int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags, mta::Problem* p) {
+  if (B <= 0 || T <= 0 || M <= 0 || d <= 0 || (flags & ~kKnownFlags)) return false;
+  const bool kq = flags & (MTA_KQ_PRE | MTA_KQ_POST);
+  const bool mix = flags & (MTA_MIX_PRE | MTA_MIX_POST);
+  if ((kq && (c_q <= 0 || c_k <= 0)) || (mix && (c_h <= 0 || M % c_h != 0))) return false;
+  p->B = B;
+  p->T = T;
+  p->M = M;
+  p->d = d;
+  p->c_q = kq ? c_q : 1;
+  p->c_k = kq ? c_k : 1;
+  p->c_h = mix ? c_h : 1;
+  p->kq = ((flags & MTA_KQ_PRE) ? mta::KQ_PRE : 0) | ((flags & MTA_KQ_POST) ? mta::KQ_POST : 0);
+  p->mix = ((flags & MTA_MIX_PRE) ? mta::MIX_PRE : 0) | ((flags & MTA_MIX_POST) ? mta::MIX_POST : 0);
+  p->gn = (flags & MTA_GN) ? 1 : 0;
+  p->fp32 = (flags & MTA_FP32) ? 1 : 0;
+  return true;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(MTA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -142,6 +163,35 @@ int mta_forward_rows(const void* q, const void* k, const void* v, const float* t
   return hip_status(e, "mta_forward_rows launch");
 }
 
+size_t mta_forward_rows_split_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k, int c_h, int row_begin,
+                                              unsigned flags) {
+  mta::Problem p{};
+  if (!sizes_problem(B, T, M, d, c_q, c_k, c_h, flags, &p) || row_begin < 0 || row_begin >= T) return 0;
+  p.row_begin = row_begin;
+  return mta::rows_split_workspace_bytes(p);
+}
+
+int mta_forward_rows_split(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                           const float* gn_gamma, const float* gn_beta, float lambda, void* out, int B, int T, int M,
+                           int d, int c_q, int c_k, int c_h, int row_begin, unsigned flags, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, out, B, T, M, d, c_q, c_k, c_h,
+                          flags, &p);
+  if (st != MTA_OK) return st;
+  if (row_begin < 0 || row_begin >= T)
+    return fail(MTA_ERR_INVALID_ARG, "row_begin=%d must lie in [0, T=%d)", row_begin, T);
+  p.row_begin = row_begin;
+  const size_t need = mta::rows_split_workspace_bytes(p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MTA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need > 0 && !aligned16(workspace)) return fail(MTA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  bool unsupported = false;
+  const hipError_t e = mta::launch_rows_split(p, workspace, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no fused kernel for this shape");
+  return hip_status(e, "mta_forward_rows_split launch");
+}
+
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags) {
   (void)flags;
   return mta::materialized_workspace_bytes(B, T, M);
@@ -166,22 +216,8 @@ int mta_forward_materialized(const void* q, const void* k, const void* v, const 
 }
 
 size_t mta_backward_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags) {
-  if (B <= 0 || T <= 0 || M <= 0 || d <= 0 || (flags & ~kKnownFlags)) return 0;
-  const bool kq = flags & (MTA_KQ_PRE | MTA_KQ_POST);
-  const bool mix = flags & (MTA_MIX_PRE | MTA_MIX_POST);
-  if ((kq && (c_q <= 0 || c_k <= 0)) || (mix && (c_h <= 0 || M % c_h != 0))) return 0;
   mta::Problem p{};
-  p.B = B;
-  p.T = T;
-  p.M = M;
-  p.d = d;
-  p.c_q = kq ? c_q : 1;
-  p.c_k = kq ? c_k : 1;
-  p.c_h = mix ? c_h : 1;
-  p.kq = ((flags & MTA_KQ_PRE) ? mta::KQ_PRE : 0) | ((flags & MTA_KQ_POST) ? mta::KQ_POST : 0);
-  p.mix = ((flags & MTA_MIX_PRE) ? mta::MIX_PRE : 0) | ((flags & MTA_MIX_POST) ? mta::MIX_POST : 0);
-  p.gn = (flags & MTA_GN) ? 1 : 0;
-  p.fp32 = (flags & MTA_FP32) ? 1 : 0;
+  if (!sizes_problem(B, T, M, d, c_q, c_k, c_h, flags, &p)) return 0;
   return mta::backward_workspace_bytes(p);
 }
 

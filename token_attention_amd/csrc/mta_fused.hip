@@ -11,6 +11,14 @@ hipError_t launch_fused_bf16_d32(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d64(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d96(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d128(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d32_split(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d64_split(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d96_split(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d128_split(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d32_split_postconv(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d64_split_postconv(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d96_split_postconv(const Problem& p, hipStream_t stream);
+hipError_t launch_fused_bf16_d128_split_postconv(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d32_postconv(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d64_postconv(const Problem& p, hipStream_t stream);
 hipError_t launch_fused_bf16_d96_postconv(const Problem& p, hipStream_t stream);
@@ -20,7 +28,7 @@ bool fused_supported(const Problem& p) {
   const int ch = p.mix ? p.c_h : 1;
   if (ch != 1 && ch != 2 && ch != 4) return false;
   if (p.kq && (p.c_q < 1 || p.c_q > 8 || p.c_k < 1 || p.c_k > 17 || p.c_k % 2 == 0)) return false;
-  if (p.fp32 && (p.kq == KQ_BOTH || p.mix == MIX_BOTH)) return false;
+  if (p.fp32 && (p.kq == KQ_BOTH || p.mix == MIX_BOTH || p.split_mode)) return false;
   if (p.fp32) return p.d == 16 || p.d == 32 || p.d == 64;
   return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
 }
@@ -36,6 +44,15 @@ hipError_t launch_fused(const Problem& p, hipStream_t stream, bool* unsupported)
       case 16: return launch_fused_f32_d16(p, stream);
       case 32: return launch_fused_f32_d32(p, stream);
       case 64: return launch_fused_f32_d64(p, stream);
+    }
+  } else if (p.split_mode) {  // one chunk of a split key range
+    const bool post = (p.kq & KQ_POST) != 0;
+    switch (p.d) {
+      case 32: return post ? launch_fused_bf16_d32_split_postconv(p, stream) : launch_fused_bf16_d32_split(p, stream);
+      case 64: return post ? launch_fused_bf16_d64_split_postconv(p, stream) : launch_fused_bf16_d64_split(p, stream);
+      case 96: return post ? launch_fused_bf16_d96_split_postconv(p, stream) : launch_fused_bf16_d96_split(p, stream);
+      case 128:
+        return post ? launch_fused_bf16_d128_split_postconv(p, stream) : launch_fused_bf16_d128_split(p, stream);
     }
   } else if (p.kq & KQ_POST) {
     switch (p.d) {

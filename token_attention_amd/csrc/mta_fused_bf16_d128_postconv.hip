@@ -4,6 +4,6 @@
 
 namespace mta {
 hipError_t launch_fused_bf16_d128_postconv(const Problem& p, hipStream_t stream) {
-  return kmajor::launch_d<128, true>(p, stream);
+  return kmajor::launch_d<128, true, false>(p, stream);
 }
 }  // namespace mta

@@ -4,6 +4,6 @@
 
 namespace mta {
 hipError_t launch_fused_bf16_d32_postconv(const Problem& p, hipStream_t stream) {
-  return kmajor::launch_d<32, true>(p, stream);
+  return kmajor::launch_d<32, true, false>(p, stream);
 }
 }  // namespace mta

@@ -4,6 +4,6 @@
 
 namespace mta {
 hipError_t launch_fused_bf16_d64(const Problem& p, hipStream_t stream) {
-  return kmajor::launch_d<64, false>(p, stream);
+  return kmajor::launch_d<64, false, false>(p, stream);
 }
 }  // namespace mta

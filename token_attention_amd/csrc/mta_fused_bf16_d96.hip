@@ -4,6 +4,6 @@
 
 namespace mta {
 hipError_t launch_fused_bf16_d96(const Problem& p, hipStream_t stream) {
-  return kmajor::launch_d<96, false>(p, stream);
+  return kmajor::launch_d<96, false, false>(p, stream);
 }
 }  // namespace mta

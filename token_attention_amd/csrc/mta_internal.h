@@ -31,12 +31,24 @@ struct Problem {
   int gn;    // 0/1
   int fp32;  // 0: bf16 tensors, 1: fp32 tensors
   int row_begin = 0;  // fused path: output rows row_begin .. T-1 only
+  // fused bf16 path: the key range split over split_n workgroups per row tile (0: no split)
+  int split_mode = 0;            // 1: write partial softmax statistics, 2: write partial AV
+  int split_keys = 0;            // keys per split, a multiple of 64
+  int split_n = 1;
+  float* part_stats = nullptr;   // partial buffers in the caller's workspace
+  float* part_o = nullptr;
+  const float* split_shift = nullptr;
 };
 
 // Returns hipSuccess or the launch error; sets *unsupported when no kernel is
 // instantiated for the shape.
 hipError_t launch_fused(const Problem& p, hipStream_t stream, bool* unsupported);
 bool fused_supported(const Problem& p);
+
+// Output rows row_begin .. T-1 with the key range split over workgroups (few row tiles: a
+// decode step or a short chunk); falls back to launch_fused when splitting does not pay.
+size_t rows_split_workspace_bytes(const Problem& p);
+hipError_t launch_rows_split(const Problem& p, void* workspace, hipStream_t stream, bool* unsupported);
 
 size_t materialized_workspace_bytes(int B, int T, int M);
 hipError_t launch_materialized(const Problem& p, void* workspace, hipStream_t stream,

@@ -59,6 +59,11 @@ namespace mta {
 namespace kmajor {
 
 constexpr int ZPRE = 8;               // zero rows above the tile in the convolution input ring
+// Split key ranges: partial results of row gr live at row index gr - row_begin + SPLIT_HPAD of
+// the partial buffers (the rows before row_begin that a tile also computes, at most 2 (c_q - 1),
+// need their softmax statistics too).
+constexpr int SPLIT_HPAD = 16;
+enum { SPLIT_NONE = 0, SPLIT_STATS = 1, SPLIT_PARTIAL = 2 };
 constexpr float SUM_LIMIT = 0x1p64f;  // largest row sum accepted with a fixed reference
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -86,14 +91,25 @@ struct Args {
   int n_groups;
   float qk_scale;  // log2(e)/sqrt(d)
   int xcd_remap;
+  // Split key range (SPLIT_STATS / SPLIT_PARTIAL): workgroup blockIdx.x / n_main covers key
+  // tiles [split * kt_chunk, (split + 1) * kt_chunk) and writes partial results instead of out.
+  int split_mode;
+  int kt_chunk;
+  int n_main;          // workgroups of one split (B * groups * row tiles)
+  int nr;              // rows of the partial buffers: T - row_begin + SPLIT_HPAD
+  float* part_stats;   // [split][B][nr][M][2]: row maximum (log2 units) and row sum against it
+  float* part_o;       // [split][B][nr][M][D]: AV partial
+  const float* shift;  // [B][nr][M]: global log2 normaliser (normalised schedules, SPLIT_PARTIAL)
 };
 
 // KQ: a key-query convolution (TWO: after softmax); MIXPRE / MIXPOST: head mixing before /
 // after softmax.
-// DUAL: key-query convolutions on both sides of softmax (implies KQ and TWO).
+// DUAL: key-query convolutions on both sides of softmax (implies KQ and TWO). SPLIT: the
+// instantiation that covers one chunk of the key range and writes partial results.
 template <int D_, int CH_, int QW_, int BK_, bool KQ_, bool TWO_, bool MIXPOST_, int CQM_, bool MIXPRE_, int NW_ = 8,
-          bool DUAL_ = false>
+          bool DUAL_ = false, bool SPLIT_ = false>
 struct Cfg {
+  static constexpr bool SPLIT = SPLIT_;
   static constexpr int D = D_, CH = CH_, QW = QW_, BK = BK_, CQM = CQM_;
   static constexpr int NW = NW_;               // waves per workgroup
   static constexpr int NT = 64 * NW;
@@ -208,16 +224,19 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   const int trank = C::PRIV ? lane : tid; // rank within the staging team
   const int thead = C::PRIV ? hu : 0;     // first head staged by the team
 
-  // ---- workgroup -> (b, group, tile), heaviest tiles first ----------------------------
+  // ---- workgroup -> (key split, b, group, tile), heaviest tiles first --------------------
+  constexpr bool split = C::SPLIT;
+  const int split_id = split ? (int)blockIdx.x / A.n_main : 0;
+  const int bid = split ? (int)blockIdx.x % A.n_main : (int)blockIdx.x;
   const int n_bg = A.B * A.n_groups;
   int bg, rank;
   if (A.xcd_remap) {
-    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3, per = n_bg >> 3;
+    const int xcd = bid & 7, kx = bid >> 3, per = n_bg >> 3;
     rank = kx / per;
     bg = (kx % per) * 8 + xcd;
   } else {
-    rank = blockIdx.x / n_bg;
-    bg = blockIdx.x % n_bg;
+    rank = bid / n_bg;
+    bg = bid % n_bg;
   }
   const int qt = A.n_tiles - 1 - rank;
   const int b = bg / A.n_groups, g = bg % A.n_groups;
@@ -230,6 +249,10 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   const int row0 = i0 - halo;
   const int last_row = min(i0 + A.r_out, T_) - 1;
   const int n_kt = last_row / C::BK + 1;
+  // key tiles of this workgroup: all of them, or one chunk when the key range is split
+  const int kt_lo = split ? min(split_id * A.kt_chunk, n_kt) : 0;
+  const int kt_hi = split ? min(kt_lo + A.kt_chunk, n_kt) : n_kt;
+  const int j0lo = kt_lo * C::BK;
   const int m_head = g * C::CH + hu;
   constexpr bool mix_pre = C::MIXPRE;
   const int wrow_min = row0 + qs0;  // smallest global row of this wave
@@ -307,6 +330,19 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     l_run[qb] = 0.0f;
   }
   const float NEG_INF = -__builtin_inff();
+  // statistics written by SPLIT_STATS: row maximum in log2 units and the row sum against it
+  float stat_m[C::NQB], stat_l[C::NQB];
+  auto split_row = [&](int gr) { return ((size_t)split_id * A.B + b) * A.nr + (gr - A.row_begin + SPLIT_HPAD); };
+  // normalised schedules in SPLIT_PARTIAL: the global normaliser of every tile row
+  auto load_shift = [&](float (&sh)[C::NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      const int gr = row0 + qs0 + qb * 16 + lq;
+      sh[qb] = (gr >= 0 && gr < T_)
+                   ? A.shift[((size_t)b * A.nr + (gr - A.row_begin + SPLIT_HPAD)) * M + m_head]
+                   : 1e30f;
+    }
+  };
 
   // ---- staging (team = the wave itself when it owns its head, else the workgroup) ------
   auto chunk_src = [&](const __bf16* base, int c, int rowfirst, int nrows_per_head) {
@@ -529,15 +565,20 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     enum { REF, MAX, FIXED, SUM, SUMFIX, NORM };
     int pass = C::MIXPOST ? SUM : REF;
     float shift[C::NQB];  // NORM: m * ssc + log2(l) per row
+    if (C::SPLIT && C::MIXPOST && A.split_mode == SPLIT_PARTIAL) {  // statistics of the whole key range given
+      load_shift(shift);
+      pass = NORM;
+      normalized = true;
+    }
     for (;;) {
       const bool upd_first = pass == REF || pass == SUM;
       const bool weigh = pass != MAX;
       const bool with_av = pass == REF || pass == FIXED || pass == NORM;
       // prologue: tile 0's K rows (with the left halo block) and V rows; halo block 0 of
       // the convolution input computed here so that every tile computes blocks 1..NKB
-      if constexpr (C::KQ) stage_k_direct(-8, C::BK + 16, 0);
-      else stage_k_direct(0, C::BK, 0);
-      if (with_av) stage_v_direct(0);
+      if constexpr (C::KQ) stage_k_direct(j0lo - 8, C::BK + 16, 0);
+      else stage_k_direct(j0lo, C::BK, 0);
+      if (with_av) stage_v_direct(j0lo);
       team_sync<C>();
       if constexpr (C::KQ) {
         logit_block(0);
@@ -548,15 +589,15 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           f32x4 z = s[0][qb];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int j = -8 + 4 * lg + i;
+            const int j = j0lo - 8 + 4 * lg + i;
             z[i] = ((gr >= 0) & (j >= 0) & (j <= gr)) ? z[i] : 0.0f;
           }
-          ring_store(0, 0, qb, z);
+          ring_store(kt_lo, 0, qb, z);
         }
       }
-      for (int kt = 0; kt < n_kt; ++kt) {
+      for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int j0 = kt * C::BK;
-        const bool more = kt + 1 < n_kt;
+        const bool more = kt + 1 < kt_hi;
         if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, with_av);
 #pragma unroll
         for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
@@ -605,7 +646,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
               }
           }
         }
-        if (pass == MAX || (upd_first && kt == 0)) {
+        if (pass == MAX || (upd_first && kt == kt_lo)) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
             float mx = NEG_INF;
@@ -667,6 +708,14 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         continue;
       }
       if (pass == SUM || pass == SUMFIX) {
+        if (C::SPLIT && A.split_mode == SPLIT_STATS) {  // the chunk's statistics are the result
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            stat_m[qb] = m_run[qb] * ssc;
+            stat_l[qb] = l_run[qb];
+          }
+          break;
+        }
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb)
           shift[qb] = l_run[qb] > 0.0f ? m_run[qb] * ssc + __builtin_log2f(l_run[qb]) : 1e30f;
@@ -676,6 +725,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         continue;
       }
       break;
+    }
+    if (C::SPLIT && !C::MIXPOST) {  // unnormalised partial: its reference and row sum go with it
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        stat_m[qb] = m_run[qb] * ssc;
+        stat_l[qb] = l_run[qb];
+      }
     }
   } else if constexpr (C::DUAL) {
     // ===================== convolutions before and after softmax ========================
@@ -734,21 +790,29 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     };
 
     // phase 1: row sums of the softmax input against a fixed reference (the maximum of the
-    // lead-in tile); if a sum exceeds 2^64 the workgroup repeats the phase exactly
+    // first counted tile); if a sum exceeds 2^64 the workgroup repeats the phase exactly.
+    // A key chunk starting at tile kt_lo > 0 counts tiles kt_lo.. (the lead-in tile's keys
+    // belong to the previous chunk); the first chunk also counts its lead-in (keys 0 .. 7).
     float lsum[C::NQB];
+    float shift[C::NQB];  // p = exp2(x - (m + log2 l))
+    const int kfirst = kt_lo == 0 ? -1 : kt_lo;
+    if (C::SPLIT && A.split_mode == SPLIT_PARTIAL) {
+      load_shift(shift);
+    } else {
     for (int exact = 0;; exact = 1) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
         m_run[qb] = -1e30f;
         l_run[qb] = 0.0f;
       }
-      stage_k_direct(16 - C::BK, C::BK, 0);
+      stage_k_direct(j0lo + 16 - C::BK, C::BK, 0);
       team_sync<C>();
-      for (int kt = -1; kt < n_kt; ++kt) {
-        const bool more = kt + 1 < n_kt;
+      for (int kt = kt_lo - 1; kt < kt_hi; ++kt) {
+        const bool more = kt + 1 < kt_hi;
         if (more) prefetch((kt + 1) * C::BK + 16, 0, false);
         front(kt);
-        if (exact || kt < 0) {
+        const bool counted = kt >= kfirst;
+        if (counted && (exact || kt == kfirst)) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
             float mx = NEG_INF;
@@ -761,14 +825,16 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             m_run[qb] = m_new;
           }
         }
+        if (counted) {
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          float sum = 0.0f;
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            float sum = 0.0f;
 #pragma unroll
-          for (int ob = 0; ob < C::NKB; ++ob)
+            for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += fast_exp2(cp[ob][qb][i] - m_run[qb]);
-          l_run[qb] += sum;
+              for (int i = 0; i < 4; ++i) sum += fast_exp2(cp[ob][qb][i] - m_run[qb]);
+            l_run[qb] += sum;
+          }
         }
         team_sync<C>();
         if (more) commit(0, false);
@@ -782,16 +848,21 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
       if (exact || !__syncthreads_or(big ? 1 : 0)) break;
     }
-    float shift[C::NQB];  // p = exp2(x - (m + log2 l))
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) shift[qb] = lsum[qb] > 0.0f ? m_run[qb] + __builtin_log2f(lsum[qb]) : 1e30f;
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      shift[qb] = lsum[qb] > 0.0f ? m_run[qb] + __builtin_log2f(lsum[qb]) : 1e30f;
+      stat_m[qb] = m_run[qb];
+      stat_l[qb] = lsum[qb];
+    }
+    }
 
     // phase 2: weights -> weight ring -> convolution after softmax -> Mask_0 -> [mixing] -> AV
-    stage_k_direct(16 - C::BK, C::BK, 0);
+    if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
+    stage_k_direct(j0lo + 16 - C::BK, C::BK, 0);
     team_sync<C>();
-    for (int kt = -1; kt < n_kt; ++kt) {
+    for (int kt = kt_lo - 1; kt < kt_hi; ++kt) {
       const int j0 = kt * C::BK, kr = kt + 1;
-      const bool more = kt + 1 < n_kt;
+      const bool more = kt + 1 < kt_hi;
       if (more) prefetch((kt + 1) * C::BK + 16, (kt + 1) * C::BK, true);
       front(kt);
 #pragma unroll
@@ -804,7 +875,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           ring_store_to(Zw, kr, ob + 1, qb, pv);
         }
       team_sync<C>();
-      if (kt >= 0) {
+      if (kt >= kt_lo) {
         convolve_ring(Zw, tz2, cv, kr);
         const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < halo) || (wrow_min + C::QW > T_);
         if (edge2) {
@@ -828,6 +899,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       if (more) commit(0, true);
       team_sync<C>();
     }
+    }
   } else {
     // ============================= two phase ============================================
     // phase 1: the row sums of head hu (after mixing) against a fixed reference, the
@@ -835,17 +907,22 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // phase as an exact online pass (running maximum, rescaled sum). The K tile rows
     // j0 .. j0+BK-1 sit at Ks rows 16 .. 16+BK-1 (logit blocks 1..NKB).
     float lsum[C::NQB];
+    // per-query normaliser folded into the exponent: p = exp2(x*sc - (m*sc + log2 l))
+    float shift[C::NQB];
+    if (C::SPLIT && A.split_mode == SPLIT_PARTIAL) {
+      load_shift(shift);
+    } else {
     for (int exact = 0;; exact = 1) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
         m_run[qb] = -1e30f;
         l_run[qb] = 0.0f;
       }
-      stage_k_direct(0, C::BK, 16);
+      stage_k_direct(j0lo, C::BK, 16);
       team_sync<C>();
-      for (int kt = 0; kt < n_kt; ++kt) {
+      for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int j0 = kt * C::BK;
-        const bool more = kt + 1 < n_kt;
+        const bool more = kt + 1 < kt_hi;
         if (more) prefetch(j0 + C::BK, 0, false);
 #pragma unroll
         for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
@@ -865,7 +942,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
               }
           }
         }
-        if (exact || kt == 0) {
+        if (exact || kt == kt_lo) {
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
             float mx = NEG_INF;
@@ -900,12 +977,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
       if (exact || !__syncthreads_or(big ? 1 : 0)) break;
     }
-    // per-query normaliser folded into the exponent: p = exp2(x*sc - (m*sc + log2 l))
-    float shift[C::NQB];
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       const float l = lsum[qb];
       shift[qb] = l > 0.0f ? m_run[qb] * sc + __builtin_log2f(l) : 1e30f;
+      stat_m[qb] = m_run[qb] * sc;
+      stat_l[qb] = l;
+    }
     }
     auto weights = [&](int kt, int lb, bool edge) {
       const int j0 = kt * C::BK;
@@ -931,15 +1009,16 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     };
 
     // phase 2: exact weights (sliding key halo) -> convolution -> Mask_0 -> AV
-    stage_k_direct(-8, C::BK + 16, 0);
-    stage_v_direct(0);
+    if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
+    stage_k_direct(j0lo - 8, C::BK + 16, 0);
+    stage_v_direct(j0lo);
     team_sync<C>();
     logit_block(0);
     if constexpr (mix_pre) mix_blocks(s, wpre, I0{}, I1{});
-    weights(0, 0, true);
-    for (int kt = 0; kt < n_kt; ++kt) {
+    weights(kt_lo, 0, true);
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
       const int j0 = kt * C::BK;
-      const bool more = kt + 1 < n_kt;
+      const bool more = kt + 1 < kt_hi;
       if (more) prefetch(j0 + C::BK + 8, j0 + C::BK, true);
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
@@ -971,6 +1050,40 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       if (more) commit(16, true);
       team_sync<C>();
     }
+    }
+  }
+
+  // ============================= split key range: partial results ==========================
+  if constexpr (C::SPLIT) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      const int t = qs0 + qb * 16 + lq;
+      const int gr = row0 + t;
+      if (A.split_mode == SPLIT_STATS) {
+        // Each row is written by one workgroup: the tile whose output row it is, or the first
+        // tile for the rows before row_begin that feed its convolutions. A tile's first c_q - 1
+        // rows have no softmax of their own when a convolution precedes it (one pass, both
+        // sides); after softmax alone (two phases) every tile row has its own.
+        const bool own = (t >= halo) || (qt == 0 && ((C::TWO && !C::DUAL) || t >= cq1));
+        if (own && lg == 0 && gr >= 0 && gr < T_) {
+          float* dst = A.part_stats + (split_row(gr) * M + m_head) * 2;
+          dst[0] = stat_m[qb];
+          dst[1] = stat_l[qb];
+        }
+      } else if (t >= halo && gr < T_) {
+        // output rows: the AV partial, and for unnormalised weights their reference and sum
+        float* dst = A.part_o + (split_row(gr) * M + m_head) * C::D;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+          *reinterpret_cast<f32x4*>(dst + nb * 16 + 4 * lg) = acc[nb][qb];
+        if (!C::TWO && !C::MIXPOST && lg == 0) {
+          float* st = A.part_stats + (split_row(gr) * M + m_head) * 2;
+          st[0] = stat_m[qb];
+          st[1] = stat_l[qb];
+        }
+      }
+    }
+    return;
   }
 
   // ============================= epilogue =================================================
@@ -1020,6 +1133,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 // ---------------------------------------------------------------------------------------------
 template <class C>
 hipError_t launch(const Problem& p, hipStream_t stream) {
+  if ((p.split_mode != 0) != C::SPLIT) return hipErrorInvalidValue;
   Args a;
   a.q = reinterpret_cast<const __bf16*>(p.q);
   a.k = reinterpret_cast<const __bf16*>(p.k);
@@ -1046,7 +1160,15 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.qk_scale = (float)(1.4426950408889634 / __builtin_sqrt((double)p.d));
   const int n_bg = p.B * a.n_groups;
   a.xcd_remap = (n_bg % 8 == 0) ? 1 : 0;
-  const long long blocks = (long long)n_bg * a.n_tiles;
+  a.split_mode = p.split_mode;
+  a.kt_chunk = p.split_mode ? p.split_keys / C::BK : 0;
+  a.n_main = n_bg * a.n_tiles;
+  a.nr = p.T - p.row_begin + SPLIT_HPAD;
+  a.part_stats = p.part_stats;
+  a.part_o = p.part_o;
+  a.shift = p.split_shift;
+  if (p.split_mode && (p.split_keys <= 0 || p.split_keys % C::BK != 0)) return hipErrorInvalidValue;
+  const long long blocks = (long long)n_bg * a.n_tiles * (p.split_mode ? p.split_n : 1);
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kmajor_kernel<C>, dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
@@ -1056,73 +1178,75 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 // overlaps the other's LDS and VALU work). Key tiles of 64 keys, 32 when the LDS holds
 // four heads, the fp16 exchange of a mixing group, or (convolution before softmax) when
 // the ring, the convolution output and the logits are live in registers together.
-template <int D, int CH, bool KQ, bool TWO, bool MIXPOST, int CQM>
+// SPLIT selects the instantiations that cover one chunk of a split key range.
+template <int D, int CH, bool KQ, bool TWO, bool MIXPOST, int CQM, bool SPLIT>
 hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr bool small = CH == 4 || (CH > 1 && MIXPOST) || (KQ && !TWO);
   constexpr int BK = small ? 32 : 64;
   if constexpr (!MIXPOST) {
-    if (p.mix == MIX_PRE) return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true>>(p, stream);
+    if (p.mix == MIX_PRE)
+      return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true, 8, false, SPLIT>>(p, stream);
   } else {
-    if (p.mix == MIX_BOTH) return launch<Cfg<D, CH, 32, BK, KQ, TWO, true, CQM, true>>(p, stream);
+    if (p.mix == MIX_BOTH) return launch<Cfg<D, CH, 32, BK, KQ, TWO, true, CQM, true, 8, false, SPLIT>>(p, stream);
   }
-  return launch<Cfg<D, CH, 32, BK, KQ, TWO, MIXPOST, CQM, false>>(p, stream);
+  return launch<Cfg<D, CH, 32, BK, KQ, TWO, MIXPOST, CQM, false, 8, false, SPLIT>>(p, stream);
 }
 
-template <int D, int CH, bool KQ, bool TWO, bool MIXPOST>
+template <int D, int CH, bool KQ, bool TWO, bool MIXPOST, bool SPLIT>
 hipError_t launch_cq(const Problem& p, hipStream_t stream) {
   if constexpr (!KQ) {
-    return launch_shape<D, CH, KQ, TWO, MIXPOST, 1>(p, stream);
+    return launch_shape<D, CH, KQ, TWO, MIXPOST, 1, SPLIT>(p, stream);
   } else {
     // Toeplitz operands held in registers: one per query lag, rounded up
-    if (p.c_q <= 4) return launch_shape<D, CH, KQ, TWO, MIXPOST, 4>(p, stream);
-    if (p.c_q <= 6) return launch_shape<D, CH, KQ, TWO, MIXPOST, 6>(p, stream);
-    return launch_shape<D, CH, KQ, TWO, MIXPOST, 8>(p, stream);
+    if (p.c_q <= 4) return launch_shape<D, CH, KQ, TWO, MIXPOST, 4, SPLIT>(p, stream);
+    if (p.c_q <= 6) return launch_shape<D, CH, KQ, TWO, MIXPOST, 6, SPLIT>(p, stream);
+    return launch_shape<D, CH, KQ, TWO, MIXPOST, 8, SPLIT>(p, stream);
   }
 }
 
 // Convolutions on both sides: 32-key tiles (two rings, two sets of Toeplitz operands).
-template <int D, int CH, bool MIXPOST, int CQM>
+template <int D, int CH, bool MIXPOST, int CQM, bool SPLIT>
 hipError_t launch_dual_shape(const Problem& p, hipStream_t stream) {
-  if (p.mix & MIX_PRE) return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, true, 8, true>>(p, stream);
-  return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, false, 8, true>>(p, stream);
+  if (p.mix & MIX_PRE) return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, true, 8, true, SPLIT>>(p, stream);
+  return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, false, 8, true, SPLIT>>(p, stream);
 }
 
-template <int D, int CH, bool MIXPOST>
+template <int D, int CH, bool MIXPOST, bool SPLIT>
 hipError_t launch_dual(const Problem& p, hipStream_t stream) {
-  if (p.c_q <= 4) return launch_dual_shape<D, CH, MIXPOST, 4>(p, stream);
-  if (p.c_q <= 6) return launch_dual_shape<D, CH, MIXPOST, 6>(p, stream);
-  return launch_dual_shape<D, CH, MIXPOST, 8>(p, stream);
+  if (p.c_q <= 4) return launch_dual_shape<D, CH, MIXPOST, 4, SPLIT>(p, stream);
+  if (p.c_q <= 6) return launch_dual_shape<D, CH, MIXPOST, 6, SPLIT>(p, stream);
+  return launch_dual_shape<D, CH, MIXPOST, 8, SPLIT>(p, stream);
 }
 
 // The schedules with a convolution after softmax (POSTCONV) and the others are instantiated in
 // separate translation units, which are compiled with different instruction-scheduling options.
-template <int D, int CH, bool POSTCONV>
+template <int D, int CH, bool POSTCONV, bool SPLIT>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
   const bool post = (p.mix & MIX_POST) != 0;
   if constexpr (POSTCONV) {
     if (p.kq == KQ_BOTH) {
-      if (post) return launch_dual<D, CH, true>(p, stream);
-      return launch_dual<D, CH, false>(p, stream);
+      if (post) return launch_dual<D, CH, true, SPLIT>(p, stream);
+      return launch_dual<D, CH, false, SPLIT>(p, stream);
     }
-    if (post) return launch_cq<D, CH, true, true, true>(p, stream);
-    return launch_cq<D, CH, true, true, false>(p, stream);
+    if (post) return launch_cq<D, CH, true, true, true, SPLIT>(p, stream);
+    return launch_cq<D, CH, true, true, false, SPLIT>(p, stream);
   } else {
     if (p.kq == KQ_PRE) {
-      if (post) return launch_cq<D, CH, true, false, true>(p, stream);
-      return launch_cq<D, CH, true, false, false>(p, stream);
+      if (post) return launch_cq<D, CH, true, false, true, SPLIT>(p, stream);
+      return launch_cq<D, CH, true, false, false, SPLIT>(p, stream);
     }
-    if (post) return launch_cq<D, CH, false, false, true>(p, stream);
-    return launch_cq<D, CH, false, false, false>(p, stream);
+    if (post) return launch_cq<D, CH, false, false, true, SPLIT>(p, stream);
+    return launch_cq<D, CH, false, false, false, SPLIT>(p, stream);
   }
 }
 
-template <int D, bool POSTCONV>
+template <int D, bool POSTCONV, bool SPLIT>
 hipError_t launch_d(const Problem& p, hipStream_t stream) {
   const int ch = p.mix ? p.c_h : 1;
   switch (ch) {
-    case 1: return launch_ch<D, 1, POSTCONV>(p, stream);
-    case 2: return launch_ch<D, 2, POSTCONV>(p, stream);
-    case 4: return launch_ch<D, 4, POSTCONV>(p, stream);
+    case 1: return launch_ch<D, 1, POSTCONV, SPLIT>(p, stream);
+    case 2: return launch_ch<D, 2, POSTCONV, SPLIT>(p, stream);
+    case 4: return launch_ch<D, 4, POSTCONV, SPLIT>(p, stream);
   }
   return hipErrorInvalidValue;
 }

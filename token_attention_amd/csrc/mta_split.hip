@@ -1,0 +1,207 @@
+// Output rows row_begin .. T-1 of the fused layer with the key range split over workgroups.
+//
+// A decode step (one new row per sequence) or a short chunk has few row tiles, so the fused
+// kernel would run a handful of workgroups that each walk every key. Here each row tile's keys
+// are cut into chunks of split_keys keys, one workgroup per (chunk, row tile), and the partial
+// results are combined afterwards, which is exact because softmax statistics and AV sums add
+// up over key chunks (page "Multi-Token Attention | Summary", §2: the output is a weighted sum
+// over keys; §3.1-§3.2: the convolutions and mixing act per key neighbourhood and head group):
+//   * weights against a per-chunk reference (no normalisation needed before AV): one pass
+//     writing (reference, row sum, AV partial) per chunk; the output is
+//     sum_c 2^(m_c - m) AV_c / sum_c 2^(m_c - m) l_c;
+//   * weights that must be exact first (a convolution or mixing after softmax): a statistics
+//     pass per chunk, their combination into one log2 normaliser per (row, head), then a
+//     weighted pass per chunk whose AV partials simply add up.
+// GroupNorm and the gate follow in the combining kernel.
+#include <algorithm>
+
+#include "mta_kmajor_impl.h"
+
+namespace mta {
+namespace {
+
+constexpr int HPAD = kmajor::SPLIT_HPAD;
+constexpr int NSPLIT_MAX = 64;
+constexpr int TARGET_WORKGROUPS = 512;  // two per compute unit
+
+struct SplitPlan {
+  int n, keys;
+};
+
+SplitPlan split_plan(const Problem& p) {
+  if (p.fp32) return {1, 0};
+  const int ch = p.mix ? p.c_h : 1;
+  const int R = 32 * (8 / ch);  // rows per tile of every launched fused shape
+  const int halo = p.kq ? ((p.kq == KQ_BOTH) ? 2 : 1) * (p.c_q - 1) : 0;
+  const int r_out = R - halo;
+  const long long tiles = (long long)p.B * (p.M / ch) * ((p.T - p.row_begin + r_out - 1) / r_out);
+  long long n = (TARGET_WORKGROUPS + tiles - 1) / tiles;
+  n = std::min<long long>(n, NSPLIT_MAX);
+  n = std::min<long long>(n, (p.T + 63) / 64);
+  if (n <= 1) return {1, 0};
+  const int keys = (int)(((p.T + n - 1) / n + 63) / 64 * 64);
+  return {(p.T + keys - 1) / keys, keys};
+}
+
+struct SplitLayout {
+  size_t nr, rows;  // rows of the partial buffers; B * nr * M
+  size_t shift, stats, o, total;
+};
+
+SplitLayout split_layout(const Problem& p, int n) {
+  SplitLayout l{};
+  l.nr = (size_t)(p.T - p.row_begin) + HPAD;
+  l.rows = (size_t)p.B * l.nr * p.M;
+  auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };
+  l.shift = 0;
+  l.stats = up(l.rows);
+  l.o = l.stats + up((size_t)n * l.rows * 2);
+  l.total = (l.o + (size_t)n * l.rows * p.d) * sizeof(float);
+  return l;
+}
+
+// statistics entries no workgroup writes stay (maximum -1e30, sum 0)
+__global__ void split_fill_kernel(float* stats, size_t n) {
+  const size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x < n) {
+    stats[2 * x] = -1e30f;
+    stats[2 * x + 1] = 0.0f;
+  }
+}
+
+// one log2 normaliser per (b, row, head): m + log2(sum_c 2^(m_c - m) l_c)
+__global__ void split_stats_kernel(const float* __restrict__ stats, float* __restrict__ shift, int nsplit,
+                                   size_t rows) {
+  const size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= rows) return;
+  float m = -1e30f;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, stats[(s * rows + x) * 2]);
+  float l = 0.0f;
+  for (int s = 0; s < nsplit; ++s) l += stats[(s * rows + x) * 2 + 1] * exp2f(stats[(s * rows + x) * 2] - m);
+  shift[x] = l > 0.0f ? m + log2f(l) : 1e30f;
+}
+
+// one wave per (b, output row, head): combine the AV partials, GroupNorm + gate, write out
+template <int D>
+__global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ stats, int weighted,
+                                                        int nsplit, int B, int nr, int M, int row_begin, int Tn,
+                                                        const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta, float lambda, int gn,
+                                                        __bf16* __restrict__ out) {
+  constexpr int CPL = (D + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const size_t wid = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nout = Tn - row_begin;
+  if (wid >= (size_t)B * nout * M) return;
+  const int m = (int)(wid % M), r = (int)((wid / M) % nout), b = (int)(wid / ((size_t)M * nout));
+  const size_t rows = (size_t)B * nr * M;
+  const size_t idx = ((size_t)b * nr + r + HPAD) * M + m;
+  float o[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) o[k] = 0.0f;
+  float mx = -1e30f, den = 0.0f;
+  if (weighted) {
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, stats[(s * rows + idx) * 2]);
+    for (int s = 0; s < nsplit; ++s) den += stats[(s * rows + idx) * 2 + 1] * exp2f(stats[(s * rows + idx) * 2] - mx);
+  }
+  for (int s = 0; s < nsplit; ++s) {
+    const float ws = weighted ? exp2f(stats[(s * rows + idx) * 2] - mx) : 1.0f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = lane + 64 * k;
+      if (c < D) o[k] += ws * part_o[(s * rows + idx) * D + c];
+    }
+  }
+  if (weighted) {
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o[k] *= inv;
+  }
+  float mean = 0.0f, rs = 1.0f;
+  if (gn) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) sum += (lane + 64 * k < D) ? o[k] : 0.0f;
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    mean = sum * (1.0f / D);
+    float sq = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const float dv = (lane + 64 * k < D) ? o[k] - mean : 0.0f;
+      sq += dv * dv;
+    }
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    rs = 1.0f / sqrtf(sq * (1.0f / D) + 1e-5f);
+  }
+  __bf16* dst = out + (((size_t)b * Tn + row_begin + r) * M + m) * D;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int c = lane + 64 * k;
+    if (c < D) {
+      float y = o[k];
+      if (gn) y = lambda * (gamma[(size_t)m * D + c] * (y - mean) * rs + beta[(size_t)m * D + c]);
+      dst[c] = (__bf16)y;
+    }
+  }
+}
+
+hipError_t launch_out(const Problem& p, const SplitLayout& l, float* ws, int n, bool weighted, hipStream_t st) {
+  const size_t waves = (size_t)p.B * (p.T - p.row_begin) * p.M;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  __bf16* out = reinterpret_cast<__bf16*>(p.out);
+  const int w = weighted ? 1 : 0;
+  switch (p.d) {
+#define MTA_D(DV)                                                                                                   \
+  case DV:                                                                                                        \
+    hipLaunchKernelGGL(split_out_kernel<DV>, grid, dim3(256), 0, st, ws + l.o, ws + l.stats, w, n, p.B, (int)l.nr, \
+                       p.M, p.row_begin, p.T, p.gamma, p.beta, p.lambda, p.gn, out);                              \
+    break;
+    MTA_D(32) MTA_D(64) MTA_D(96) MTA_D(128)
+#undef MTA_D
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t rows_split_workspace_bytes(const Problem& p) {
+  const SplitPlan plan = split_plan(p);
+  return plan.n <= 1 ? 0 : split_layout(p, plan.n).total;
+}
+
+hipError_t launch_rows_split(const Problem& p0, void* workspace, hipStream_t st, bool* unsupported) {
+  *unsupported = false;
+  const SplitPlan plan = split_plan(p0);
+  if (plan.n <= 1) return launch_fused(p0, st, unsupported);
+  if (!fused_supported(p0)) {
+    *unsupported = true;
+    return hipSuccess;
+  }
+  const SplitLayout l = split_layout(p0, plan.n);
+  float* ws = reinterpret_cast<float*>(workspace);
+  Problem p = p0;
+  p.split_n = plan.n;
+  p.split_keys = plan.keys;
+  p.part_stats = ws + l.stats;
+  p.part_o = ws + l.o;
+  p.split_shift = ws + l.shift;
+  hipError_t e;
+  const size_t nstat = (size_t)plan.n * l.rows;
+  hipLaunchKernelGGL(split_fill_kernel, dim3((unsigned)((nstat + 255) / 256)), dim3(256), 0, st, p.part_stats, nstat);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool normalised = (p.kq & KQ_POST) || (p.mix & MIX_POST);
+  if (normalised) {
+    p.split_mode = kmajor::SPLIT_STATS;
+    if ((e = launch_fused(p, st, unsupported)) != hipSuccess || *unsupported) return e;
+    hipLaunchKernelGGL(split_stats_kernel, dim3((unsigned)((l.rows + 255) / 256)), dim3(256), 0, st, p.part_stats,
+                       ws + l.shift, plan.n, l.rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  p.split_mode = kmajor::SPLIT_PARTIAL;
+  if ((e = launch_fused(p, st, unsupported)) != hipSuccess || *unsupported) return e;
+  return launch_out(p, l, ws, plan.n, !normalised, st);
+}
+
+}  // namespace mta

@@ -27,7 +27,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 EXPORTED = [
     "mta_forward", "mta_forward_rows", "mta_forward_materialized", "mta_materialized_workspace_bytes",
     "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
-    "mta_backward_materialized", "mta_backward_workspace_bytes",
+    "mta_backward_materialized", "mta_backward_workspace_bytes", "mta_forward_rows_split",
+    "mta_forward_rows_split_workspace_bytes",
 ]
 
 _lib = None
@@ -55,6 +56,11 @@ def lib() -> ctypes.CDLL:
         L.mta_forward.restype = i
         L.mta_forward_rows.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 8 + [u, vp]
         L.mta_forward_rows.restype = i
+        L.mta_forward_rows_split.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 8 + \
+            [u, vp, ctypes.c_size_t, vp]
+        L.mta_forward_rows_split.restype = i
+        L.mta_forward_rows_split_workspace_bytes.argtypes = [i] * 8 + [u]
+        L.mta_forward_rows_split_workspace_bytes.restype = ctypes.c_size_t
         L.mta_forward_materialized.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 7 + \
             [u, vp, ctypes.c_size_t, vp]
         L.mta_forward_materialized.restype = i
@@ -155,6 +161,36 @@ def forward_rows(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float 
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
         _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
         float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, int(row_begin), fl, _stream(stream)))
+    return out
+
+
+def rows_split_workspace_bytes(B: int, T: int, M: int, d: int, *, row_begin: int, c_q: int = 1, c_k: int = 1,
+                               c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None, gn: bool = False,
+                               fp32: bool = False) -> int:
+    return int(lib().mta_forward_rows_split_workspace_bytes(B, T, M, d, c_q, c_k, c_h, int(row_begin),
+                                                            placement_flags(kq, mix, gn, fp32)))
+
+
+def forward_rows_split(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, row_begin: int,
+                       c_q: int = 1, c_k: int = 1, c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None,
+                       gn: bool = False, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """``mta_forward_rows_split``: rows row_begin .. T-1 with the key range split over workgroups
+    (decode steps, short chunks); rows of ``out`` before row_begin are left as they are."""
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    fp32 = q.dtype == torch.float32
+    fl = placement_flags(kq, mix, gn, fp32)
+    need = rows_split_workspace_bytes(B, T, M, d, row_begin=row_begin, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix,
+                                      gn=gn, fp32=fp32)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().mta_forward_rows_split(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, int(row_begin), fl, ws_ptr, ws_bytes,
+        _stream(stream)))
     return out
 
 
