@@ -59,7 +59,7 @@ typedef enum mta_status {
   MTA_ERR_UNSUPPORTED = 2, /* valid but not built: d, dtype, c_q > 8, even c_k,
                               c_k > 17, c_h not in {1, 2, 4}, one batch of a
                               tensor (T*M*d elements) of 2 GiB or more, fused
-                              fp32 with a convolution or mixing on both sides    */
+                              fp32 with convolutions on both sides               */
   MTA_ERR_HIP = 3,         /* the HIP runtime reported an error                   */
   MTA_ERR_WORKSPACE = 4    /* workspace missing or smaller than required          */
 } mta_status;
@@ -88,8 +88,8 @@ typedef enum mta_status {
  *   c_h          head-group size; M % c_h == 0; c_h in {1,2,4}; ignored without MIX
  *   flags        MTA_* bits above
  * Supported head sizes: d in {32, 64, 96, 128} for bf16, d in {16, 32, 64} for fp32.
- * fp32 tensors: one side per operation (both-side placements return UNSUPPORTED;
- * mta_forward_materialized takes them).
+ * fp32 tensors: convolutions on both sides return UNSUPPORTED (mta_forward_materialized
+ * takes them); every other placement is built.
  */
 int mta_forward(const void* q, const void* k, const void* v, const float* theta_kq,
                 const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,

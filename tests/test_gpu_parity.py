@@ -186,15 +186,19 @@ def test_late_dominant_key(kq, mix, c_h, d):
     compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), want, what=f"late key {kq}/{mix}/{c_h} d={d}")
 
 
-@pytest.mark.parametrize("kq,mix", [(None, "pre"), (None, "post"), ("pre", "post"), ("post", "pre"), ("post", "post")])
+@pytest.mark.parametrize("kq,mix", [(None, "pre"), (None, "post"), ("pre", "post"), ("post", "pre"), ("post", "post"),
+                                    (None, "both")])
 @pytest.mark.parametrize("path", ["fused", "materialized"])
-def test_single_head_groups_scale(kq, mix, path):
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_single_head_groups_scale(kq, mix, path, dtype):
     """c_h = 1: each head is its own group and the mixing weight is a scalar per head;
     without GroupNorm a negative weight must show up as a scaled (pre: sharpened or
     flattened and reversed) output."""
-    cfg = mta_inputs.MTAConfig("ch1", 1, 90, 4, 64, 3, 5, 1, kq, mix, False, "bf16", 0.1, 0.0, seed=19)
+    cfg = mta_inputs.MTAConfig("ch1", 1, 90, 4, 64, 3, 5, 1, kq, mix, False, dtype, 0.1, 0.0, seed=19)
     inp = dict(case(cfg))
     inp["w"] = np.array([-0.7, 1.3, 0.4, -1.1], dtype=np.float32).reshape(4, 1, 1)
+    if mix == "both":
+        inp["w"] = np.stack([inp["w"], np.array([0.6, -1.2, 0.9, 1.4], dtype=np.float32).reshape(4, 1, 1)])
     # halved values keep the un-normalised outputs below 4, where half a bf16 ulp of the
     # stored output stays well inside the absolute bar
     inp["v"] = mta_inputs.round_bf16(inp["v"] * 0.5)
@@ -375,9 +379,17 @@ def test_both_sides_late_dominant_key(mix, c_h):
     compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), want, what=f"late key both/{mix}/{c_h}")
 
 
+@pytest.mark.parametrize("kq,c_h", [(None, 2), ("pre", 4), ("post", 2)])
+def test_mixing_both_sides_fp32_fused(kq, c_h):
+    cfg = mta_inputs.MTAConfig("mixboth_fp32", 1, 90, 4, 32, 3, 5, c_h, kq, "both", True, "fp32", 0.1, 0.2, 1.0, 0.0,
+                               0.8, seed=45)
+    inp = case(cfg)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"fp32 {kq}/both")
+
+
 def test_both_sides_fp32_materialized_and_fused_refusal():
     """fp32 tensors: the materialized chain takes every placement; the fp32 fused kernel
-    implements one side per convolution and reports both-side placements unsupported."""
+    implements one side per convolution and reports convolutions on both sides unsupported."""
     cfg = mta_inputs.MTAConfig("dual_fp32", 1, 64, 4, 16, 3, 5, 2, "both", "both", True, "fp32", 0.1, 0.1, 1.0,
                                0.0, 0.8, seed=26)
     inp = case(cfg)

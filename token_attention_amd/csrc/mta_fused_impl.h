@@ -45,7 +45,8 @@ struct FusedArgs {
   const void* k;
   const void* v;
   const float* theta;
-  const float* w;
+  const float* w_pre;   // mixing before softmax [M/c_h, c_h, c_h]
+  const float* w_post;  // mixing after softmax
   const float* gamma;
   const float* beta;
   float lambda;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
   const int last_row = min(i0 + A.r_out, T_) - 1;
   const int n_kt = last_row / C::BK + 1;
   const int m_head = g * C::CH + hu;
-  const bool mix_pre = A.mix == MIX_PRE;
+  const bool mix_pre = (A.mix & MIX_PRE) != 0;
 
   const size_t bstride = (size_t)T_ * M * C::D;
   const T* qb = reinterpret_cast<const T*>(A.q) + b * bstride;
@@ -253,9 +254,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
     }
   }
 
-  float wrow[C::CH];  // mixing weights w[g][hu][:]
+  float wrow[C::CH], wpost[C::CH];  // mixing weights w[g][hu][:] before / after softmax
 #pragma unroll
-  for (int u = 0; u < C::CH; ++u) wrow[u] = A.mix ? A.w[((size_t)g * C::CH + hu) * C::CH + u] : 0.0f;
+  for (int u = 0; u < C::CH; ++u) {
+    wrow[u] = (A.mix & MIX_PRE) ? A.w_pre[((size_t)g * C::CH + hu) * C::CH + u] : 0.0f;
+    wpost[u] = (A.mix & MIX_POST) ? A.w_post[((size_t)g * C::CH + hu) * C::CH + u] : 0.0f;
+  }
 
   f32x4 acc[C::NP][C::RB][C::NB];
 #pragma unroll
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
       for (int p = 0; p < C::NP; ++p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float sc = wrow[p];
+          float sc = wpost[p];
           if constexpr (!C::TWO) {
             const float l = St_l[p * C::R + ws * C::WR + rb * 16 + 4 * lg + i];
             sc = l > 0.0f ? sc / l : 0.0f;
@@ -563,13 +567,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
         for (int nb = 0; nb < C::NB; ++nb) o[nb] += acc[p][rb][nb] * coef;
       }
     } else {
+      // a one-head group mixed after softmax scales its head by the weight w[g][0][0]
+      const float wscale = (A.mix & MIX_POST) ? wpost[0] : 1.0f;
       f32x4 coef;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (!C::TWO)
-          coef[i] = l_run[rb][i] > 0.0f ? 1.0f / l_run[rb][i] : 0.0f;
+          coef[i] = l_run[rb][i] > 0.0f ? wscale / l_run[rb][i] : 0.0f;
         else
-          coef[i] = 1.0f;
+          coef[i] = wscale;
       }
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[0][rb][nb] * coef;
@@ -615,7 +621,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.k = p.k;
   a.v = p.v;
   a.theta = p.kq == KQ_PRE ? p.theta_pre : p.theta_post;
-  a.w = p.mix == MIX_PRE ? p.w_pre : p.w_post;
+  a.w_pre = p.w_pre;
+  a.w_post = p.w_post;
   a.gamma = p.gamma;
   a.beta = p.beta;
   a.lambda = p.lambda;
@@ -654,7 +661,7 @@ hipError_t launch_shape(const Problem& p, hipStream_t stream) {
 template <typename T, int D, int CH>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
   const bool two = p.kq == KQ_POST;
-  const bool pairs = p.mix == MIX_POST && CH > 1;
+  const bool pairs = (p.mix & MIX_POST) && CH > 1;
   if (two) {
     if (pairs) return launch_shape<T, D, CH, true, true>(p, stream);
     return launch_shape<T, D, CH, true, false>(p, stream);
