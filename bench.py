@@ -166,6 +166,30 @@ def cpu_baseline(cfg, inp, n_rows: int):
     }
 
 
+def cpu_single_thread():
+    """The fp64 oracle on one host thread, for scale: the tiny fp32 workload in full and a
+    seeded 64-row sample of the 880M-slice workload (batch 0, all heads)."""
+    from oracle import oracle  # the CPU baseline leg is the only product-side user of the oracle
+
+    rec = {}
+    for name, idx, n_rows in (("tiny_fp32", 0, 0), ("slice880m_bf16", 1, 64)):
+        cfg = mta_inputs.config(idx)
+        inp = mta_inputs.make_inputs(cfg)
+        c1 = cfg.replace(B=1)
+        sub_inp = dict(inp, **{n: inp[n][:1] for n in ("q", "k", "v")})
+        rows = None
+        if n_rows:
+            rng = np.random.default_rng(2025)
+            rows = np.sort(rng.choice(cfg.T, size=n_rows, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.forward_cfg(c1, sub_inp, rows=rows, n_threads=1)
+        dt = time.perf_counter() - t0
+        n_tok = cfg.T if rows is None else len(rows)
+        rec[name] = {"tokens_per_s": n_tok / dt, "seconds": dt,
+                     "sample": "every row of batch 0" if rows is None else f"{n_rows} seeded rows of batch 0"}
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +386,8 @@ def main():
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "gcn_arch": getattr(props, "gcnArchName", "")}
     result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(cfg, inp, args.cpu_rows)
+    if not args.no_cpu:
+        result["cpu_baseline"]["single_thread"] = cpu_single_thread()
     print(json.dumps(result))
 
 
