@@ -22,12 +22,17 @@ namespace {
 
 constexpr int HPAD = kmajor::SPLIT_HPAD;
 constexpr int NSPLIT_MAX = 64;
-constexpr int TARGET_WORKGROUPS = 512;  // two per compute unit
+constexpr int CUS = 256;                 // MI355X compute units; one fused workgroup fits per unit
+constexpr double WG_OVERHEAD = 0.04;     // fixed cost of a workgroup, relative to a whole row tile
 
 struct SplitPlan {
   int n, keys;
 };
 
+// Number of key chunks, when the row tiles alone leave compute units idle: workgroups run in
+// rounds of CUS, each costing the fixed overhead plus its share of the keys; the plan minimises
+// rounds * (overhead + 1/n) (chunks are whole multiples of 64 keys). A decode step at T=4096 with
+// 16 row tiles gets 16 chunks of 256 keys (one round), a 512-row chunk 5 chunks of 832 keys.
 SplitPlan split_plan(const Problem& p) {
   if (p.fp32) return {1, 0};
   const int ch = p.mix ? p.c_h : 1;
@@ -35,12 +40,22 @@ SplitPlan split_plan(const Problem& p) {
   const int halo = p.kq ? ((p.kq == KQ_BOTH) ? 2 : 1) * (p.c_q - 1) : 0;
   const int r_out = R - halo;
   const long long tiles = (long long)p.B * (p.M / ch) * ((p.T - p.row_begin + r_out - 1) / r_out);
-  long long n = (TARGET_WORKGROUPS + tiles - 1) / tiles;
-  n = std::min<long long>(n, NSPLIT_MAX);
-  n = std::min<long long>(n, (p.T + 63) / 64);
-  if (n <= 1) return {1, 0};
-  const int keys = (int)(((p.T + n - 1) / n + 63) / 64 * 64);
-  return {(p.T + keys - 1) / keys, keys};
+  // enough row tiles to occupy every compute unit: the unsplit kernel (heaviest tiles first)
+  if (tiles >= CUS) return {1, 0};
+  SplitPlan best{1, 0};
+  double best_cost = (double)((tiles + CUS - 1) / CUS) * (WG_OVERHEAD + 1.0);
+  const int nmax = std::min(NSPLIT_MAX, (p.T + 63) / 64);
+  for (int n = 2; n <= nmax; ++n) {
+    const int keys = ((p.T + n - 1) / n + 63) / 64 * 64;
+    const int neff = (p.T + keys - 1) / keys;
+    const double rounds = (double)((tiles * neff + CUS - 1) / CUS);
+    const double cost = rounds * (WG_OVERHEAD + 1.0 / neff);
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = {neff, keys};
+    }
+  }
+  return best.n <= 1 ? SplitPlan{1, 0} : best;
 }
 
 struct SplitLayout {
