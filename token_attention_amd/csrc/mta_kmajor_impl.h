@@ -43,10 +43,17 @@
 //   one pass   (no convolution after softmax, no mixing after softmax): weights against
 //              the reference, AV, division by the row sum in the epilogue;
 //   two passes (convolution or mixing after softmax): a statistics pass (row sums), then
-//              exact normalised weights -> [convolution -> Mask_0] -> [mixing] -> AV.
+//              exact normalised weights -> [convolution -> Mask_0] -> [mixing] -> AV;
+//   both sides (DUAL: convolutions before and after softmax): the two-pass schedule with a
+//              second ring; every tile convolves the logits (first ring) into softmax inputs
+//              8 keys ahead of the weights it convolves (second ring), after a lead-in tile.
 // Mixing exchanges fp16 blocks of the other heads of the group through a double-buffered
-// LDS buffer: logits before softmax (a wave's own head stays fp32), normalised weights
-// after softmax.
+// LDS buffer (one buffer with both convolutions, where ring barriers separate exchanges):
+// logits before softmax (a wave's own head stays fp32), normalised weights after softmax.
+//
+// SPLIT instantiations cover one chunk of the key range of a row tile and write partial
+// results (softmax statistics or AV sums) to a workspace for a combining kernel; they serve
+// short row ranges such as a decode step, where the row tiles alone would leave the GPU idle.
 //
 // K and V tiles are loaded with buffer loads whose range ends at the last key row, so rows
 // past the sequence read as zero (they are masked) without per-row clamping.
