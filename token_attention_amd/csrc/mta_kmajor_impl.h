@@ -388,7 +388,12 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // Regular tiles (BK rows per head, rows >= 0): chunk x of a team member is row r_x of
   // head thead + u_x, 16-byte column cc_x; its byte offset from the tile's first row and
   // its LDS element offsets do not change from tile to tile.
-  int goff[C::CPT], koff[C::CPT], voff[C::CPT];
+  // Two phases (one convolution): phase 1 double-buffers K, the second buffer (BK rows per
+  // head, stride LDK) in the V region, which phase 1 does not use.
+  constexpr bool K2BUF = C::TWO && !C::DUAL;
+  static_assert(!K2BUF || C::BK * C::LDK <= C::BK * C::LDV, "second K buffer fits the V region");
+  __bf16* const Ks2 = Vs;
+  int goff[C::CPT], koff[C::CPT], voff[C::CPT], koff2[K2BUF ? C::CPT : 1];
 #pragma unroll
   for (int x = 0; x < C::CPT; ++x) {
     // surplus team members of the last round repeat the last chunk (identical writes)
@@ -399,6 +404,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     goff[x] = ((r * M + g * C::CH + u) * C::D + cc * 8) * 2;
     koff[x] = (u * C::KROWS + r) * C::LDK + cc * 8;
     voff[x] = (u * C::BK + r) * C::LDV + cc * 8;
+    if constexpr (K2BUF) koff2[x] = (u * C::BK + r) * C::LDK + cc * 8;
   }
   // buffer resource over rows jfirst .. T-1 of a K or V tensor of batch b
   auto tile_rsrc = [&](const __bf16* base, int jfirst) {
@@ -407,30 +413,57 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
                                              rows * M * C::D * 2, 0x00020000);
   };
   u32x4 pk[C::CPT], pv[C::CPT];
-  auto prefetch = [&](int kfirst, int j0, bool with_v) {
+  auto prefetch_k = [&](int kfirst) {
     const auto rk = tile_rsrc(kb_, kfirst);
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x)
       pk[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[x], 0, 0));
-    if (with_v) {
-      const auto rv = tile_rsrc(vb_, j0);
-#pragma unroll
-      for (int x = 0; x < C::CPT; ++x)
-        pv[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[x], 0, 0));
-    }
   };
-  auto commit = [&](int lrow, bool with_v) {
+  auto prefetch_v = [&](int j0) {
+    const auto rv = tile_rsrc(vb_, j0);
+#pragma unroll
+    for (int x = 0; x < C::CPT; ++x)
+      pv[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[x], 0, 0));
+  };
+  auto prefetch = [&](int kfirst, int j0, bool with_v) {
+    prefetch_k(kfirst);
+    if (with_v) prefetch_v(j0);
+  };
+  auto commit_k = [&](int lrow) {
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks + koff[x] + lrow * C::LDK) = pk[x];
-    if (with_v) {
+  };
+  auto commit_k2 = [&]() {  // the second K buffer of phase 1
+    if constexpr (K2BUF) {
 #pragma unroll
-      for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Vs + voff[x]) = pv[x];
+      for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks2 + koff2[x]) = pk[x];
     }
+  };
+  auto commit_v = [&]() {
+#pragma unroll
+    for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Vs + voff[x]) = pv[x];
+  };
+  auto commit = [&](int lrow, bool with_v) {
+    commit_k(lrow);
+    if (with_v) commit_v();
   };
 
   // ---- compute helpers --------------------------------------------------------------------
   f32x4 s[C::LB][C::NQB];
-  // raw S^T of logit block lb (Ks rows 16*lb - kofs .. 16*lb - kofs + 15)
+  // raw S^T of logit block lb from rows 16*lb - kofs .. 16*lb - kofs + 15 of head hu's K rows
+  // (rph rows per head from kbuf; by default the Ks tile)
+  auto logit_block_from = [&](const __bf16* kbuf, int rph, int lb, int kofs) {
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const __bf16* kr = kbuf + ((size_t)hu * rph - kofs + lq) * C::LDK + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(kr + (size_t)lb * 16 * C::LDK + ks * 32);
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb)
+        s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
+    }
+  };
   auto logit_block = [&](int lb, int kofs = 0) {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -915,8 +948,20 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // ============================= two phase ============================================
     // phase 1: the row sums of head hu (after mixing) against a fixed reference, the
     // maximum of the row's first key tile; if a sum exceeds 2^64 the workgroup repeats the
-    // phase as an exact online pass (running maximum, rescaled sum). The K tile rows
-    // j0 .. j0+BK-1 sit at Ks rows 16 .. 16+BK-1 (logit blocks 1..NKB).
+    // phase as an exact online pass (running maximum, rescaled sum).
+    //
+    // Synchronisation: one workgroup barrier per tile in phase 1 and two in phase 2. The
+    // barrier after the logits (the exchange of the mixing before softmax, else an explicit
+    // one) is passed once every wave has read the K tile and finished the previous tile's
+    // AV and convolution, so the prefetched K and V rows are written to LDS right after it;
+    // the next barrier (phase 1: the next tile's; phase 2: the one before the convolution)
+    // publishes them. Phase 1 alternates between two K buffers: the Ks rows 16 .. 16+BK-1
+    // and a second one in the V region.
+    constexpr bool XBAR = mix_pre && C::CH > 1;  // the exchange itself is a workgroup barrier
+    auto after_logits = [&](auto lb0c) {
+      if constexpr (mix_pre) mix_blocks(s, wpre, lb0c, ILB{});
+      if constexpr (!XBAR) team_sync<C>();
+    };
     float lsum[C::NQB];
     // per-query normaliser folded into the exponent: p = exp2(x*sc - (m*sc + log2 l))
     float shift[C::NQB];
@@ -930,14 +975,24 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         l_run[qb] = 0.0f;
       }
       stage_k_direct(j0lo, C::BK, 16);
+      if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK);
       team_sync<C>();
       for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int j0 = kt * C::BK;
-        const bool more = kt + 1 < kt_hi;
-        if (more) prefetch(j0 + C::BK, 0, false);
+        const bool alt = ((kt - kt_lo) & 1) != 0;  // this tile's K rows are in the second buffer
+        if (kt + 1 < kt_hi) {
+          // K(kt + 1) into the other buffer, whose last reader (the logits of tile kt - 1)
+          // every wave finished before the previous barrier
+          if (alt) commit_k(16);
+          else commit_k2();
+          if (kt + 2 < kt_hi) prefetch_k(j0 + 2 * C::BK);
+        }
+        const __bf16* kbuf = alt ? Ks2 : Ks;
+        const int rph = alt ? C::BK : C::KROWS;
+        const int kofs = alt ? 16 : 0;
 #pragma unroll
-        for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-        if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
+        for (int lb = 1; lb < C::LB; ++lb) logit_block_from(kbuf, rph, lb, kofs);
+        after_logits(I1{});
         const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
         if (edge) {
 #pragma unroll
@@ -976,9 +1031,6 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             for (int i = 0; i < 4; ++i) sum += fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -mref));
           l_run[qb] += sum;
         }
-        team_sync<C>();
-        if (more) commit(16, false);
-        team_sync<C>();
       }
       bool big = false;
 #pragma unroll
@@ -1019,26 +1071,36 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int qb = 0; qb < C::NQB; ++qb) ring_store(kt, lb, qb, pv[qb]);
     };
 
-    // phase 2: exact weights (sliding key halo) -> convolution -> Mask_0 -> AV
+    // phase 2: exact weights (sliding key halo) -> convolution -> Mask_0 -> AV. The K tile
+    // rows j0 - 8 .. j0 + BK + 7 of the first tile sit at Ks rows 0 .. BK + 15; later tiles
+    // bring BK new rows to Ks rows 16 .. (logit blocks 1..NKB).
     if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
+    team_sync<C>();  // every wave is done with both phase-1 K buffers
     stage_k_direct(j0lo - 8, C::BK + 16, 0);
-    stage_v_direct(j0lo);
+    if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK + 8);
+    prefetch_v(j0lo);
     team_sync<C>();
     logit_block(0);
     if constexpr (mix_pre) mix_blocks(s, wpre, I0{}, I1{});
     weights(kt_lo, 0, true);
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
       const int j0 = kt * C::BK;
-      const bool more = kt + 1 < kt_hi;
-      if (more) prefetch(j0 + C::BK + 8, j0 + C::BK, true);
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-      if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
+      after_logits(I1{});
+      // every wave has read this K tile and finished the previous tile's AV: V(kt) and
+      // K(kt + 1) go to LDS, the loads of V(kt + 1) and K(kt + 2) are issued
+      commit_v();
+      if (kt + 1 < kt_hi) {
+        commit_k(16);
+        if (kt + 2 < kt_hi) prefetch_k(j0 + 2 * C::BK + 8);
+        prefetch_v(j0 + C::BK);
+      }
       const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) ||
                         (wrow_min + C::QW > T_);
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) weights(kt, lb, edge);
-      team_sync<C>();
+      team_sync<C>();  // ring, V(kt) and K(kt + 1) are visible
       convolve(kt);
       const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < cq1) || (wrow_min + C::QW > T_);
       if (edge2) {
@@ -1057,9 +1119,6 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
       if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
       av(cv, I0{});
-      team_sync<C>();
-      if (more) commit(16, true);
-      team_sync<C>();
     }
     }
   }
