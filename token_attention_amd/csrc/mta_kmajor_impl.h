@@ -388,9 +388,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // Regular tiles (BK rows per head, rows >= 0): chunk x of a team member is row r_x of
   // head thead + u_x, 16-byte column cc_x; its byte offset from the tile's first row and
   // its LDS element offsets do not change from tile to tile.
-  // Two phases (one convolution): phase 1 double-buffers K, the second buffer (BK rows per
-  // head, stride LDK) in the V region, which phase 1 does not use.
-  constexpr bool K2BUF = C::TWO && !C::DUAL;
+  // Two-phase schedules: phase 1 double-buffers K, the second buffer (BK rows per head,
+  // stride LDK) in the V region, which phase 1 does not use.
+  constexpr bool K2BUF = C::TWO;
   static_assert(!K2BUF || C::BK * C::LDK <= C::BK * C::LDV, "second K buffer fits the V region");
   __bf16* const Ks2 = Vs;
   int goff[C::CPT], koff[C::CPT], voff[C::CPT], koff2[K2BUF ? C::CPT : 1];
@@ -614,15 +614,29 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       pass = NORM;
       normalized = true;
     }
+    // Synchronisation. With a workgroup barrier between the logits and the weights (the
+    // convolution ring's, or the exchange of the mixing before softmax: MIDBAR), K(kt + 1)
+    // is written to LDS right after it (every wave has read K(kt)) and V(kt) at the start of
+    // the tile, after the tile's last barrier; that last barrier (TAIL) is the exchange of the
+    // mixing after softmax when a pass mixes (V(kt) then goes to LDS after the middle barrier
+    // instead), else an explicit one. Without a middle barrier a tile ends with two barriers
+    // around the LDS writes of the next tile's K and V.
+    constexpr bool MIDBAR = C::KQ || (mix_pre && C::CH > 1);
     for (;;) {
       const bool upd_first = pass == REF || pass == SUM;
       const bool weigh = pass != MAX;
       const bool with_av = pass == REF || pass == FIXED || pass == NORM;
+      const bool tail_mix = C::MIXPOST && C::CH > 1 && with_av;  // TAIL is the mixing exchange
       // prologue: tile 0's K rows (with the left halo block) and V rows; halo block 0 of
       // the convolution input computed here so that every tile computes blocks 1..NKB
       if constexpr (C::KQ) stage_k_direct(j0lo - 8, C::BK + 16, 0);
       else stage_k_direct(j0lo, C::BK, 0);
-      if (with_av) stage_v_direct(j0lo);
+      if constexpr (MIDBAR) {
+        if (kt_lo + 1 < kt_hi) prefetch_k(C::KQ ? j0lo + C::BK + 8 : j0lo + C::BK);
+        if (with_av) prefetch_v(j0lo);
+      } else {
+        if (with_av) stage_v_direct(j0lo);
+      }
       team_sync<C>();
       if constexpr (C::KQ) {
         logit_block(0);
@@ -642,10 +656,26 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int j0 = kt * C::BK;
         const bool more = kt + 1 < kt_hi;
-        if (more) prefetch(C::KQ ? j0 + C::BK + 8 : j0 + C::BK, j0 + C::BK, with_av);
+        auto next_v = [&]() {  // V(kt) to LDS, load V(kt + 1)
+          commit_v();
+          if (more) prefetch_v(j0 + C::BK);
+        };
+        if constexpr (MIDBAR) {
+          if (with_av && !tail_mix) next_v();  // every wave finished AV(kt - 1) before TAIL
+        } else {
+          if (more) prefetch(j0 + C::BK, j0 + C::BK, with_av);
+        }
 #pragma unroll
         for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
         if constexpr (mix_pre) mix_blocks(s, wpre, INEW{}, ILB{});
+        auto next_k = [&]() {  // after the middle barrier: K(kt + 1) to LDS, load K(kt + 2)
+          if (with_av && tail_mix) next_v();
+          if (more) {
+            commit_k(C::KQ ? 16 : 0);
+            if (kt + 2 < kt_hi) prefetch_k(C::KQ ? j0 + 2 * C::BK + 8 : j0 + 2 * C::BK);
+          }
+        };
+        if constexpr (MIDBAR && !C::KQ) next_k();
         // softmax input of this tile: cv (after the convolution) or the logits themselves
         auto& xw = [&]() -> auto& {
           if constexpr (C::KQ) return cv;
@@ -671,6 +701,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             }
           }
           team_sync<C>();  // rows of the neighbouring slab are read by the convolution
+          next_k();
           convolve(kt);
         }
         // Mask_-inf
@@ -722,9 +753,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           if constexpr (C::MIXPOST) mix_blocks(xw, wpost, I0{}, INKB{});
           av(xw, I0{});
         }
-        team_sync<C>();  // the team is done with Ks, Vs and the ring of this tile
-        if (more) commit(C::KQ ? 16 : 0, with_av);
-        team_sync<C>();
+        if constexpr (MIDBAR) {
+          if (!tail_mix) team_sync<C>();  // TAIL
+        } else {
+          team_sync<C>();  // the team is done with Ks and Vs of this tile
+          if (more) commit(0, with_av);
+          team_sync<C>();
+        }
       }
       if (pass == MAX) {
         pass = C::MIXPOST ? SUMFIX : FIXED;
@@ -786,12 +821,27 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // keys into weight-ring blocks 1..NKB (block b holds keys j0 - 8 + 16 b ..), then the
     // convolution after softmax of keys [j0, j0 + BK). The ring tile index is kt + 1. The K
     // tile of tile kt (rows j0 + 16 .. j0 + BK + 15) sits at Ks rows 0 .. BK - 1.
+    //
+    // Synchronisation: the barrier before the convolution before softmax (RING1) is passed
+    // once every wave has read the K tile and (phase 2) finished the previous AV, so the
+    // prefetched K and V rows go to LDS right after it (the hook); the barrier before the
+    // convolution after softmax (phase 2) or the next tile's RING1 (phase 1) publishes them.
+    // Phase 1 alternates between two K buffers (Ks and one in the V region) and needs a
+    // barrier between a tile's convolution and the next tile's logit-ring writes: the
+    // exchange of the mixing before softmax, else an explicit one. In phase 2 that role
+    // falls to the barrier before the convolution after softmax; only with mixing on both
+    // sides does a tile end with a barrier (the single exchange buffer is rewritten by the
+    // next tile's mixing before softmax).
+    constexpr bool XBAR = mix_pre && C::CH > 1;
     f32x4 cp[C::NKB][C::NQB];  // convolution before softmax, log2 units
-    auto front = [&](int kt) {
+    auto front = [&](int kt, const __bf16* kbuf, bool sync_before_ring, auto&& hook) {
       const int j0 = kt * C::BK, kr = kt + 1;
 #pragma unroll
-      for (int lb = 1; lb < C::LB; ++lb) logit_block(lb, 16);
+      for (int lb = 1; lb < C::LB; ++lb) logit_block_from(kbuf, C::BK, lb, 16);
       if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
+      if constexpr (!XBAR) {
+        if (sync_before_ring) team_sync<C>();
+      }
       // Mask_0 on keys j0 + 16 lb + 4 lg + i
       const bool edge0 = (j0 < 0) || (j0 + C::BK + 16 - 1 > wrow_min) || (wrow_min < 0);
 #pragma unroll
@@ -810,7 +860,8 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           ring_store(kr, lb, qb, z);
         }
       }
-      team_sync<C>();  // rows of the neighbouring slab are read by the convolution
+      team_sync<C>();  // RING1: rows of the neighbouring slab are read by the convolution
+      hook();
       convolve_ring(Zb, tz, cp, kr);
       // Mask_-inf: a softmax row needs all c_q logit rows of its convolution inside the
       // tile (t >= c_q - 1) and lies in the map; keys 0 .. gr
@@ -850,11 +901,18 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         l_run[qb] = 0.0f;
       }
       stage_k_direct(j0lo + 16 - C::BK, C::BK, 0);
+      if (kt_lo < kt_hi) prefetch_k(kt_lo * C::BK + 16);
       team_sync<C>();
       for (int kt = kt_lo - 1; kt < kt_hi; ++kt) {
-        const bool more = kt + 1 < kt_hi;
-        if (more) prefetch((kt + 1) * C::BK + 16, 0, false);
-        front(kt);
+        const bool alt = ((kt - kt_lo + 1) & 1) != 0;  // this tile's K rows are in the second buffer
+        if (kt + 1 < kt_hi) {
+          // K(kt + 1) into the other buffer, whose last reader (the logits of tile kt - 1)
+          // every wave finished before the previous RING1
+          if (alt) commit_k(0);
+          else commit_k2();
+          if (kt + 2 < kt_hi) prefetch_k((kt + 2) * C::BK + 16);
+        }
+        front(kt, alt ? Ks2 : Ks, true, [] {});
         const bool counted = kt >= kfirst;
         if (counted && (exact || kt == kfirst)) {
 #pragma unroll
@@ -880,9 +938,6 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
             l_run[qb] += sum;
           }
         }
-        team_sync<C>();
-        if (more) commit(0, false);
-        team_sync<C>();
       }
       bool big = false;
 #pragma unroll
@@ -902,13 +957,24 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 
     // phase 2: weights -> weight ring -> convolution after softmax -> Mask_0 -> [mixing] -> AV
     if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
+    team_sync<C>();  // every wave is done with both phase-1 K buffers
     stage_k_direct(j0lo + 16 - C::BK, C::BK, 0);
+    if (kt_lo < kt_hi) {
+      prefetch_k(kt_lo * C::BK + 16);
+      prefetch_v(kt_lo * C::BK);
+    }
     team_sync<C>();
     for (int kt = kt_lo - 1; kt < kt_hi; ++kt) {
       const int j0 = kt * C::BK, kr = kt + 1;
-      const bool more = kt + 1 < kt_hi;
-      if (more) prefetch((kt + 1) * C::BK + 16, (kt + 1) * C::BK, true);
-      front(kt);
+      front(kt, Ks, false, [&] {
+        // every wave has read K(kt) and finished AV(kt - 1): V(kt), K(kt + 1) to LDS
+        if (kt >= kt_lo) commit_v();
+        if (kt + 1 < kt_hi) {
+          commit_k(0);
+          if (kt + 2 < kt_hi) prefetch_k((kt + 2) * C::BK + 16);
+          if (kt >= kt_lo) prefetch_v((kt + 1) * C::BK);
+        }
+      });
 #pragma unroll
       for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
@@ -939,9 +1005,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
         av(cv, I0{});
       }
-      team_sync<C>();
-      if (more) commit(0, true);
-      team_sync<C>();
+      if constexpr (XBAR && C::MIXPOST && C::CH > 1) team_sync<C>();  // the exchange buffer is reused
     }
     }
   } else {
