@@ -65,6 +65,10 @@
 namespace mta {
 namespace kmajor {
 
+// every helper lambda of the kernel is inlined: one left out of line takes its array
+// arguments by reference, and those arrays then live in scratch memory
+#define MTA_INLINE __attribute__((always_inline))
+
 constexpr int ZPRE = 8;               // zero rows above the tile in the convolution input ring
 // Split key ranges: partial results of row gr live at row index gr - row_begin + SPLIT_HPAD of
 // the partial buffers (the rows before row_begin that a tile also computes, at most 2 (c_q - 1),
@@ -134,11 +138,14 @@ struct Cfg {
   static constexpr int KS = D / 32;            // k-steps of QK^T
   static constexpr int NB = D / 16;            // channel blocks
   static constexpr int NC = BK / 32;           // 32-key chunks of AV
-  // K rows in LDS: the one-convolution schedules stage a 16-key halo block in front
-  static constexpr int KROWS = (KQ && !DUAL) ? BK + 16 : BK;
+  // K rows in LDS: the one-pass convolution schedule stages a 16-key halo block in front
+  static constexpr int KROWS = (KQ && !TWO) ? BK + 16 : BK;
+  // convolution ring blocks per row: the window of a tile (LB blocks) and, in the pipelined
+  // two-phase schedule, the NKB new blocks of the next tile, written while the window is read
+  static constexpr int RB = (TWO && !DUAL) ? LB + NKB : LB;
   static constexpr int LDK = D + 8;            // K row stride (bf16): 16-byte reads conflict-free
   static constexpr int LDV = D + 16;           // V row stride (bf16): transposed reads conflict-free
-  static constexpr int ZW = LB * 16;           // ring width (keys)
+  static constexpr int ZW = RB * 16;           // ring width (keys)
   static constexpr int LDZ = ZW + 8;           // fp16 stride
   static constexpr int ZROWS = ZPRE + R;
   static constexpr int XW = NKB * 4;           // exchange halves per lane and query block
@@ -147,7 +154,7 @@ struct Cfg {
   // double buffered; with both convolutions every two exchanges are already separated by
   // a workgroup barrier (ring writes -> convolution reads), so one buffer suffices
   static constexpr int XBUFS = DUAL ? 1 : 2;
-  static constexpr size_t SX_BYTES = MIX ? XBUFS * SX_HALF * 2 : 0;
+  static constexpr size_t SX_BYTES = (MIX && CH > 1) ? XBUFS * SX_HALF * 2 : 0;  // one head: a scalar weight
   static constexpr size_t VS_BYTES = (size_t)CH * BK * LDV * 2;
   static constexpr size_t ZRING = (size_t)CH * ZROWS * LDZ;  // halves of one ring
   // rings: the convolution input; with both convolutions the logits and the weights
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // window key k is global key j0 - 8 + 16*ob + k; out key is j0 + 16*ob + n;
   // tap e = n - k + 8 + h0. Before softmax the logit scale is folded in.
   f16x8 tz[C::KQ ? C::CQM : 1], tz2[C::DUAL ? C::CQM : 1];
-  auto toeplitz = [&](f16x8 (&dst)[C::KQ ? C::CQM : 1], const float* theta, float tscale) {
+  auto toeplitz = [&](f16x8 (&dst)[C::KQ ? C::CQM : 1], const float* theta, float tscale) MTA_INLINE {
     const float* th = theta + (size_t)m_head * A.c_q * A.c_k;
 #pragma unroll
     for (int a = 0; a < C::CQM; ++a) {
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   }
 
   f32x4 acc[C::NB][C::NQB];
-  auto clear_acc = [&]() {
+  auto clear_acc = [&]() MTA_INLINE {
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -343,9 +350,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   const float NEG_INF = -__builtin_inff();
   // statistics written by SPLIT_STATS: row maximum in log2 units and the row sum against it
   float stat_m[C::NQB], stat_l[C::NQB];
-  auto split_row = [&](int gr) { return ((size_t)split_id * A.B + b) * A.nr + (gr - A.row_begin + SPLIT_HPAD); };
+  auto split_row = [&](int gr) MTA_INLINE { return ((size_t)split_id * A.B + b) * A.nr + (gr - A.row_begin + SPLIT_HPAD); };
   // normalised schedules in SPLIT_PARTIAL: the global normaliser of every tile row
-  auto load_shift = [&](float (&sh)[C::NQB]) {
+  auto load_shift = [&](float (&sh)[C::NQB]) MTA_INLINE {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       const int gr = row0 + qs0 + qb * 16 + lq;
@@ -356,31 +363,31 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   };
 
   // ---- staging (team = the wave itself when it owns its head, else the workgroup) ------
-  auto chunk_src = [&](const __bf16* base, int c, int rowfirst, int nrows_per_head) {
+  auto chunk_src = [&](const __bf16* base, int c, int rowfirst, int nrows_per_head) MTA_INLINE {
     const int u = thead + c / (nrows_per_head * (C::D / 8));
     const int rem = c % (nrows_per_head * (C::D / 8));
     const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
     const int j = min(max(rowfirst + r, 0), T_ - 1);  // rows outside the map are masked later
     return base + ((size_t)j * M + g * C::CH + u) * C::D + cc * 8;
   };
-  auto k_dst = [&](int c, int lrow, int nrows_per_head) {
+  auto k_dst = [&](int c, int lrow, int nrows_per_head) MTA_INLINE {
     const int u = thead + c / (nrows_per_head * (C::D / 8));
     const int rem = c % (nrows_per_head * (C::D / 8));
     const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
     return Ks + ((size_t)u * C::KROWS + lrow + r) * C::LDK + cc * 8;
   };
-  auto v_dst = [&](int c) {
+  auto v_dst = [&](int c) MTA_INLINE {
     const int u = thead + c / (C::BK * (C::D / 8));
     const int rem = c % (C::BK * (C::D / 8));
     const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
     return Vs + ((size_t)u * C::BK + r) * C::LDV + cc * 8;
   };
-  auto stage_k_direct = [&](int kfirst, int nrows, int lrow) {
+  auto stage_k_direct = [&](int kfirst, int nrows, int lrow) MTA_INLINE {
     const int total = C::HEADS * nrows * (C::D / 8);
     for (int c = trank; c < total; c += C::TEAM)
       *reinterpret_cast<u32x4*>(k_dst(c, lrow, nrows)) = *reinterpret_cast<const u32x4*>(chunk_src(kb_, c, kfirst, nrows));
   };
-  auto stage_v_direct = [&](int j0) {
+  auto stage_v_direct = [&](int j0) MTA_INLINE {
     constexpr int total = C::HEADS * C::BK * (C::D / 8);
     for (int c = trank; c < total; c += C::TEAM)
       *reinterpret_cast<u32x4*>(v_dst(c)) = *reinterpret_cast<const u32x4*>(chunk_src(vb_, c, j0, C::BK));
@@ -407,64 +414,64 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     if constexpr (K2BUF) koff2[x] = (u * C::BK + r) * C::LDK + cc * 8;
   }
   // buffer resource over rows jfirst .. T-1 of a K or V tensor of batch b
-  auto tile_rsrc = [&](const __bf16* base, int jfirst) {
+  auto tile_rsrc = [&](const __bf16* base, int jfirst) MTA_INLINE {
     const int rows = max(T_ - jfirst, 0);
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jfirst * M * C::D), (short)0,
                                              rows * M * C::D * 2, 0x00020000);
   };
   u32x4 pk[C::CPT], pv[C::CPT];
-  auto prefetch_k = [&](int kfirst) {
+  auto prefetch_k = [&](int kfirst) MTA_INLINE {
     const auto rk = tile_rsrc(kb_, kfirst);
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x)
       pk[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[x], 0, 0));
   };
-  auto prefetch_v = [&](int j0) {
+  auto prefetch_v = [&](int j0) MTA_INLINE {
     const auto rv = tile_rsrc(vb_, j0);
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x)
       pv[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[x], 0, 0));
   };
-  auto prefetch = [&](int kfirst, int j0, bool with_v) {
+  auto prefetch = [&](int kfirst, int j0, bool with_v) MTA_INLINE {
     prefetch_k(kfirst);
     if (with_v) prefetch_v(j0);
   };
-  auto commit_k = [&](int lrow) {
+  auto commit_k = [&](int lrow) MTA_INLINE {
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks + koff[x] + lrow * C::LDK) = pk[x];
   };
-  auto commit_k2 = [&]() {  // the second K buffer of phase 1
+  auto commit_k2 = [&]() MTA_INLINE {  // the second K buffer of phase 1
     if constexpr (K2BUF) {
 #pragma unroll
       for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks2 + koff2[x]) = pk[x];
     }
   };
-  auto commit_v = [&]() {
+  auto commit_v = [&]() MTA_INLINE {
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Vs + voff[x]) = pv[x];
   };
-  auto commit = [&](int lrow, bool with_v) {
+  auto commit = [&](int lrow, bool with_v) MTA_INLINE {
     commit_k(lrow);
     if (with_v) commit_v();
   };
 
   // ---- compute helpers --------------------------------------------------------------------
   f32x4 s[C::LB][C::NQB];
-  // raw S^T of logit block lb from rows 16*lb - kofs .. 16*lb - kofs + 15 of head hu's K rows
-  // (rph rows per head from kbuf; by default the Ks tile)
-  auto logit_block_from = [&](const __bf16* kbuf, int rph, int lb, int kofs) {
+  // raw S^T of logit block lb into dst[lb], from rows 16*lb - kofs .. 16*lb - kofs + 15 of
+  // head hu's K rows (rph rows per head from kbuf)
+  auto logit_block_from = [&](auto& dst, const __bf16* kbuf, int rph, int lb, int kofs) MTA_INLINE {
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < C::NQB; ++qb) dst[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const __bf16* kr = kbuf + ((size_t)hu * rph - kofs + lq) * C::LDK + lg * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(kr + (size_t)lb * 16 * C::LDK + ks * 32);
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb)
-        s[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], s[lb][qb], 0, 0, 0);
+        dst[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[qb][ks], dst[lb][qb], 0, 0, 0);
     }
   };
-  auto logit_block = [&](int lb, int kofs = 0) {
+  auto logit_block = [&](int lb, int kofs = 0) MTA_INLINE {
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) s[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -481,8 +488,26 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // lane-contiguous, and reads those of the other heads for the same rows. The buffer
   // alternates between two halves, so one barrier per exchange suffices: a half is
   // rewritten only after every wave has passed the barrier of the exchange in between.
-  int xbuf = 0;
-  auto mix_blocks = [&](auto& arr, const float (&wrot)[C::CH], auto lb0c, auto lb1c) {
+  // mix_write / mix_read: the two halves of an exchange through buffer xb, to be separated
+  // by a workgroup barrier.
+  auto xslot = [&](int xb, int u, int qb) MTA_INLINE {
+    return Sx + xb * C::SX_HALF + ((((size_t)u * C::WPH + slab) * C::NQB + qb) * 64 + lane) * C::XW;
+  };
+  auto mix_write = [&](auto& arr, int xb, auto lb0c, auto lb1c) MTA_INLINE {
+    constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value;
+    if constexpr (C::CH > 1) {
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+        for (int lb = LB0; lb < LB1; ++lb) {
+          const f16x4 h = {(_Float16)arr[lb][qb][0], (_Float16)arr[lb][qb][1], (_Float16)arr[lb][qb][2],
+                           (_Float16)arr[lb][qb][3]};
+          *reinterpret_cast<f16x4*>(xslot(xb, hu, qb) + (lb - LB0) * 4) = h;
+        }
+      }
+    }
+  };
+  auto mix_read = [&](auto& arr, int xb, const float (&wrot)[C::CH], auto lb0c, auto lb1c) MTA_INLINE {
     constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value, XB = LB1 - LB0;
     static_assert(XB >= 1 && XB <= C::NKB, "exchange width");
     if constexpr (C::CH == 1) {  // a group of one head: a scalar weight
@@ -490,43 +515,39 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int lb = LB0; lb < LB1; ++lb)
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) arr[lb][qb] = arr[lb][qb] * wrot[0];
+    } else {
+      f16x4 o[C::CH - 1][C::NQB][XB];
+#pragma unroll
+      for (int k = 1; k < C::CH; ++k) {
+        const int u = (hu + k) & (C::CH - 1);
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+          for (int x = 0; x < XB; ++x) o[k - 1][qb][x] = *reinterpret_cast<const f16x4*>(xslot(xb, u, qb) + x * 4);
+      }
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+        for (int lb = LB0; lb < LB1; ++lb) {
+          f32x4 x = arr[lb][qb] * wrot[0];
+#pragma unroll
+          for (int k = 1; k < C::CH; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(wrot[k], (float)o[k - 1][qb][lb - LB0][i], x[i]);
+          arr[lb][qb] = x;
+        }
+      }
+    }
+  };
+  int xbuf = 0;
+  auto mix_blocks = [&](auto& arr, const float (&wrot)[C::CH], auto lb0c, auto lb1c) MTA_INLINE {
+    if constexpr (C::CH == 1) {
+      mix_read(arr, 0, wrot, lb0c, lb1c);
       return;
     }
-    _Float16* X = Sx + xbuf * C::SX_HALF;
-    auto slot = [&](int u, int qb) {
-      return X + ((((size_t)u * C::WPH + slab) * C::NQB + qb) * 64 + lane) * C::XW;
-    };
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-#pragma unroll
-      for (int lb = LB0; lb < LB1; ++lb) {
-        const f16x4 h = {(_Float16)arr[lb][qb][0], (_Float16)arr[lb][qb][1], (_Float16)arr[lb][qb][2],
-                         (_Float16)arr[lb][qb][3]};
-        *reinterpret_cast<f16x4*>(slot(hu, qb) + (lb - LB0) * 4) = h;
-      }
-    }
+    mix_write(arr, xbuf, lb0c, lb1c);
     __syncthreads();
-    f16x4 o[C::CH > 1 ? C::CH - 1 : 1][C::NQB][XB];
-#pragma unroll
-    for (int k = 1; k < C::CH; ++k) {
-      const int u = (hu + k) & (C::CH - 1);
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb)
-#pragma unroll
-        for (int x = 0; x < XB; ++x) o[k - 1][qb][x] = *reinterpret_cast<const f16x4*>(slot(u, qb) + x * 4);
-    }
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-#pragma unroll
-      for (int lb = LB0; lb < LB1; ++lb) {
-        f32x4 x = arr[lb][qb] * wrot[0];
-#pragma unroll
-        for (int k = 1; k < C::CH; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(wrot[k], (float)o[k - 1][qb][lb - LB0][i], x[i]);
-        arr[lb][qb] = x;
-      }
-    }
+    mix_read(arr, xbuf, wrot, lb0c, lb1c);
     if constexpr (C::XBUFS == 2) xbuf ^= 1;
   };
 
@@ -534,9 +555,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // that start 8 keys after ring block ob, so it reads ring blocks ob and ob + 1.
   f32x4 cv[C::KQ ? C::NKB : 1][C::NQB];
   _Float16* const Zw = Zb + (C::DUAL ? C::ZRING : 0);  // ring of the weights (both convolutions)
-  auto ring_col = [&](int kt, int lb) { return ((kt * C::NKB + lb) % C::LB) * 16; };
+  auto ring_col = [&](int kt, int lb) MTA_INLINE { return ((kt * C::NKB + lb) % C::RB) * 16; };
   auto convolve_ring = [&](const _Float16* ring, const f16x8 (&tzs)[C::KQ ? C::CQM : 1],
-                           f32x4 (&res)[C::KQ ? C::NKB : 1][C::NQB], int kt) {
+                           f32x4 (&res)[C::KQ ? C::NKB : 1][C::NQB], int kt) MTA_INLINE {
 #pragma unroll
     for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
@@ -557,16 +578,16 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
     }
   };
-  auto convolve = [&](int kt) { convolve_ring(Zb, tz, cv, kt); };
-  auto ring_store_to = [&](_Float16* ring, int kt, int lb, int qb, const f32x4& val) {
+  auto convolve = [&](int kt) MTA_INLINE { convolve_ring(Zb, tz, cv, kt); };
+  auto ring_store_to = [&](_Float16* ring, int kt, int lb, int qb, const f32x4& val) MTA_INLINE {
     const f16x4 h = {(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
     *reinterpret_cast<f16x4*>(ring + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq) * C::LDZ +
                               ring_col(kt, lb) + lg * 4) = h;
   };
-  auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) { ring_store_to(Zb, kt, lb, qb, val); };
+  auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) MTA_INLINE { ring_store_to(Zb, kt, lb, qb, val); };
 
   // AV of the weights of key blocks ob0 .. ob0 + NKB - 1 against V of head hu
-  auto av = [&](auto& wts, auto ob0c) {
+  auto av = [&](auto& wts, auto ob0c) MTA_INLINE {
     constexpr int OB0 = decltype(ob0c)::value;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
@@ -656,7 +677,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int j0 = kt * C::BK;
         const bool more = kt + 1 < kt_hi;
-        auto next_v = [&]() {  // V(kt) to LDS, load V(kt + 1)
+        auto next_v = [&]() MTA_INLINE {  // V(kt) to LDS, load V(kt + 1)
           commit_v();
           if (more) prefetch_v(j0 + C::BK);
         };
@@ -668,7 +689,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
         for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
         if constexpr (mix_pre) mix_blocks(s, wpre, INEW{}, ILB{});
-        auto next_k = [&]() {  // after the middle barrier: K(kt + 1) to LDS, load K(kt + 2)
+        auto next_k = [&]() MTA_INLINE {  // after the middle barrier: K(kt + 1) to LDS, load K(kt + 2)
           if (with_av && tail_mix) next_v();
           if (more) {
             commit_k(C::KQ ? 16 : 0);
@@ -677,7 +698,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         };
         if constexpr (MIDBAR && !C::KQ) next_k();
         // softmax input of this tile: cv (after the convolution) or the logits themselves
-        auto& xw = [&]() -> auto& {
+        auto& xw = [&]() MTA_INLINE -> auto& {
           if constexpr (C::KQ) return cv;
           else return s;
         }();
@@ -834,10 +855,10 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // next tile's mixing before softmax).
     constexpr bool XBAR = mix_pre && C::CH > 1;
     f32x4 cp[C::NKB][C::NQB];  // convolution before softmax, log2 units
-    auto front = [&](int kt, const __bf16* kbuf, bool sync_before_ring, auto&& hook) {
+    auto front = [&](int kt, const __bf16* kbuf, bool sync_before_ring, auto&& hook) MTA_INLINE {
       const int j0 = kt * C::BK, kr = kt + 1;
 #pragma unroll
-      for (int lb = 1; lb < C::LB; ++lb) logit_block_from(kbuf, C::BK, lb, 16);
+      for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, kbuf, C::BK, lb, 16);
       if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
       if constexpr (!XBAR) {
         if (sync_before_ring) team_sync<C>();
@@ -912,7 +933,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           else commit_k2();
           if (kt + 2 < kt_hi) prefetch_k((kt + 2) * C::BK + 16);
         }
-        front(kt, alt ? Ks2 : Ks, true, [] {});
+        front(kt, alt ? Ks2 : Ks, true, []() MTA_INLINE {});
         const bool counted = kt >= kfirst;
         if (counted && (exact || kt == kfirst)) {
 #pragma unroll
@@ -966,7 +987,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     team_sync<C>();
     for (int kt = kt_lo - 1; kt < kt_hi; ++kt) {
       const int j0 = kt * C::BK, kr = kt + 1;
-      front(kt, Ks, false, [&] {
+      front(kt, Ks, false, [&]() MTA_INLINE {
         // every wave has read K(kt) and finished AV(kt - 1): V(kt), K(kt + 1) to LDS
         if (kt >= kt_lo) commit_v();
         if (kt + 1 < kt_hi) {
@@ -1013,88 +1034,126 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // phase 1: the row sums of head hu (after mixing) against a fixed reference, the
     // maximum of the row's first key tile; if a sum exceeds 2^64 the workgroup repeats the
     // phase as an exact online pass (running maximum, rescaled sum).
+    // phase 2: exact normalised weights -> ring -> convolution -> Mask_0 -> [mixing] -> AV.
     //
-    // Synchronisation: one workgroup barrier per tile in phase 1 and two in phase 2. The
-    // barrier after the logits (the exchange of the mixing before softmax, else an explicit
-    // one) is passed once every wave has read the K tile and finished the previous tile's
-    // AV and convolution, so the prefetched K and V rows are written to LDS right after it;
-    // the next barrier (phase 1: the next tile's; phase 2: the one before the convolution)
-    // publishes them. Phase 1 alternates between two K buffers: the Ks rows 16 .. 16+BK-1
-    // and a second one in the V region.
-    constexpr bool XBAR = mix_pre && C::CH > 1;  // the exchange itself is a workgroup barrier
-    auto after_logits = [&](auto lb0c) {
-      if constexpr (mix_pre) mix_blocks(s, wpre, lb0c, ILB{});
-      if constexpr (!XBAR) team_sync<C>();
-    };
+    // Both phases are software-pipelined so that every stretch between two workgroup
+    // barriers holds MFMA work and VALU work that do not depend on each other (the waves of
+    // a SIMD run in step, so a stretch of one kind alone leaves the other unit idle):
+    //   phase 1, one barrier per tile: the logits of tile kt + 1 (MFMA) beside the mixing,
+    //     masking and row sums of tile kt (VALU). K tiles alternate between two buffers (Ks
+    //     and one in the V region), mixing exchanges between the two exchange buffers.
+    //   phase 2, two barriers per tile: stretch A computes the logits of tile kt + 1 and
+    //     writes them to exchange buffer 0; stretch B convolves tile kt and multiplies it with
+    //     V (MFMA) beside the mixing and the normalised weights of tile kt + 1 (VALU), which
+    //     go to the ring's next NKB blocks (the ring holds LB + NKB blocks per row, so they
+    //     never overwrite the window being convolved). K(kt + 2) goes to LDS in stretch B,
+    //     V(kt) in stretch A; the mixing after softmax exchanges through buffer 1 inside B.
+    // In phase 2 the K tile of tile kt holds rows j0 + 8 .. j0 + BK + 7 (its logit blocks
+    // 1..NKB); block 0 of the first tile comes from the last block of a lead-in K tile.
+    constexpr bool XBAR = mix_pre && C::CH > 1;  // mixing before softmax exchanges through LDS
+    f32x4 sn[C::LB][C::NQB];  // phase 1: the logits of the other tile of a pair
     float lsum[C::NQB];
     // per-query normaliser folded into the exponent: p = exp2(x*sc - (m*sc + log2 l))
     float shift[C::NQB];
     if (C::SPLIT && A.split_mode == SPLIT_PARTIAL) {
       load_shift(shift);
     } else {
+    // tile kt: its logits are in cur and, mixing before softmax, in exchange buffer
+    // (kt - kt_lo) & 1, which also names its K buffer (0: Ks, 1: the V region)
+    auto p1_sums = [&](auto& cur) MTA_INLINE {
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const float mref = m_run[qb] * sc;
+        float sum = 0.0f;
+#pragma unroll
+        for (int lb = 1; lb < C::LB; ++lb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum += fast_exp2(__builtin_fmaf(cur[lb][qb][i], sc, -mref));
+        l_run[qb] += sum;
+      }
+    };
+    auto p1_step = [&](int kt, auto& cur, auto& nxt, bool exact) MTA_INLINE {
+      const int j0 = kt * C::BK;
+      const int pb = (kt - kt_lo) & 1;
+      const bool more = kt + 1 < kt_hi;
+      if (kt + 2 < kt_hi) {
+        // K(kt + 2) into tile kt's buffer, whose logits every wave finished before the last barrier
+        if (pb) commit_k2();
+        else commit_k(0);
+        if (kt + 3 < kt_hi) prefetch_k(j0 + 3 * C::BK);
+      }
+      const __bf16* kbuf = pb ? Ks : Ks2;
+      const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
+      if (!(exact || kt == kt_lo || edge)) {
+        // interior tile: one branch-free stretch, the next tile's logits (MFMA) beside this
+        // tile's mixing and row sums (VALU). After the last tile of a key range the next
+        // tile's logits and exchange are computed from stale rows and never used.
+#pragma unroll
+        for (int lb = 1; lb < C::LB; ++lb) logit_block_from(nxt, kbuf, C::BK, lb, 16);
+        if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
+        p1_sums(cur);
+        if constexpr (mix_pre) mix_write(nxt, pb ^ 1, I1{}, ILB{});
+        team_sync<C>();
+        return;
+      }
+      if (more) {
+#pragma unroll
+        for (int lb = 1; lb < C::LB; ++lb) logit_block_from(nxt, kbuf, C::BK, lb, 16);
+      }
+      if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
+      if (edge) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const int gr = row0 + qs0 + qb * 16 + lq;
+          const bool row_ok = (gr >= 0) & (gr < T_);
+#pragma unroll
+          for (int lb = 1; lb < C::LB; ++lb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = j0 + (lb - 1) * 16 + 4 * lg + i;
+              cur[lb][qb][i] = (row_ok & (j <= gr)) ? cur[lb][qb][i] : NEG_INF;
+            }
+        }
+      }
+      if (exact || kt == kt_lo) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          float mx = NEG_INF;
+#pragma unroll
+          for (int lb = 1; lb < C::LB; ++lb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, cur[lb][qb][i]);
+          const float m_new = fmaxf(m_run[qb], xgroup_max(mx));
+          l_run[qb] *= fast_exp2((m_run[qb] - m_new) * sc);
+          m_run[qb] = m_new;
+        }
+      }
+      p1_sums(cur);
+      if constexpr (mix_pre) {
+        if (more) mix_write(nxt, pb ^ 1, I1{}, ILB{});
+      }
+      team_sync<C>();
+    };
     for (int exact = 0;; exact = 1) {
 #pragma unroll
       for (int qb = 0; qb < C::NQB; ++qb) {
         m_run[qb] = -1e30f;
         l_run[qb] = 0.0f;
       }
-      stage_k_direct(j0lo, C::BK, 16);
-      if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK);
+      stage_k_direct(j0lo, C::BK, 0);  // K(kt_lo) into Ks, K(kt_lo + 1) into the second buffer
+      if (kt_lo + 1 < kt_hi) {
+        prefetch_k(j0lo + C::BK);
+        commit_k2();
+        if (kt_lo + 2 < kt_hi) prefetch_k(j0lo + 2 * C::BK);
+      }
       team_sync<C>();
-      for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int j0 = kt * C::BK;
-        const bool alt = ((kt - kt_lo) & 1) != 0;  // this tile's K rows are in the second buffer
-        if (kt + 1 < kt_hi) {
-          // K(kt + 1) into the other buffer, whose last reader (the logits of tile kt - 1)
-          // every wave finished before the previous barrier
-          if (alt) commit_k(16);
-          else commit_k2();
-          if (kt + 2 < kt_hi) prefetch_k(j0 + 2 * C::BK);
-        }
-        const __bf16* kbuf = alt ? Ks2 : Ks;
-        const int rph = alt ? C::BK : C::KROWS;
-        const int kofs = alt ? 16 : 0;
 #pragma unroll
-        for (int lb = 1; lb < C::LB; ++lb) logit_block_from(kbuf, rph, lb, kofs);
-        after_logits(I1{});
-        const bool edge = (j0 + C::BK - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
-        if (edge) {
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) {
-            const int gr = row0 + qs0 + qb * 16 + lq;
-            const bool row_ok = (gr >= 0) & (gr < T_);
-#pragma unroll
-            for (int lb = 1; lb < C::LB; ++lb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int j = j0 + (lb - 1) * 16 + 4 * lg + i;
-                s[lb][qb][i] = (row_ok & (j <= gr)) ? s[lb][qb][i] : NEG_INF;
-              }
-          }
-        }
-        if (exact || kt == kt_lo) {
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) {
-            float mx = NEG_INF;
-#pragma unroll
-            for (int lb = 1; lb < C::LB; ++lb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[lb][qb][i]);
-            const float m_new = fmaxf(m_run[qb], xgroup_max(mx));
-            l_run[qb] *= fast_exp2((m_run[qb] - m_new) * sc);
-            m_run[qb] = m_new;
-          }
-        }
-#pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) {
-          const float mref = m_run[qb] * sc;
-          float sum = 0.0f;
-#pragma unroll
-          for (int lb = 1; lb < C::LB; ++lb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sum += fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -mref));
-          l_run[qb] += sum;
-        }
+      for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, Ks, C::BK, lb, 16);
+      if constexpr (mix_pre) mix_write(s, 0, I1{}, ILB{});
+      team_sync<C>();
+      for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+        p1_step(kt, s, sn, exact != 0);
+        if (kt + 1 < kt_hi) p1_step(kt + 1, sn, s, exact != 0);
       }
       bool big = false;
 #pragma unroll
@@ -1112,77 +1171,128 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       stat_l[qb] = l;
     }
     }
-    auto weights = [&](int kt, int lb, bool edge) {
+
+    // normalised weights of blocks [L0, L1) of arr (tile kt: keys j0 - 8 + 16 lb ..) into the ring
+    auto weights_edge = [&](int kt) MTA_INLINE {
       const int j0 = kt * C::BK;
-      f32x4 pv[C::NQB];
+      return (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
+    };
+    auto weights_exp = [&](auto& arr, auto lb0c, auto lb1c) MTA_INLINE {
+      constexpr int L0 = decltype(lb0c)::value, L1 = decltype(lb1c)::value;
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb)
+      for (int lb = L0; lb < L1; ++lb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[qb][i] = fast_exp2(__builtin_fmaf(s[lb][qb][i], sc, -shift[qb]));
-      if (edge) {
+        for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) arr[lb][qb][i] = fast_exp2(__builtin_fmaf(arr[lb][qb][i], sc, -shift[qb]));
+    };
+    auto weights_store = [&](auto& arr, int kt, auto lb0c, auto lb1c) MTA_INLINE {
+      constexpr int L0 = decltype(lb0c)::value, L1 = decltype(lb1c)::value;
+#pragma unroll
+      for (int lb = L0; lb < L1; ++lb)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) ring_store(kt, lb, qb, arr[lb][qb]);
+    };
+    auto weights_to_ring = [&](auto& arr, int kt, auto lb0c, auto lb1c) MTA_INLINE {
+      constexpr int L0 = decltype(lb0c)::value, L1 = decltype(lb1c)::value;
+      const int j0 = kt * C::BK;
+      weights_exp(arr, lb0c, lb1c);
+      if (weights_edge(kt)) {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           const int gr = row0 + qs0 + qb * 16 + lq;
           const bool row_ok = (gr >= 0) & (gr < T_);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = j0 - 8 + lb * 16 + 4 * lg + i;
-            pv[qb][i] = (row_ok & (j >= 0) & (j <= gr)) ? pv[qb][i] : 0.0f;
-          }
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) ring_store(kt, lb, qb, pv[qb]);
-    };
-
-    // phase 2: exact weights (sliding key halo) -> convolution -> Mask_0 -> AV. The K tile
-    // rows j0 - 8 .. j0 + BK + 7 of the first tile sit at Ks rows 0 .. BK + 15; later tiles
-    // bring BK new rows to Ks rows 16 .. (logit blocks 1..NKB).
-    if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
-    team_sync<C>();  // every wave is done with both phase-1 K buffers
-    stage_k_direct(j0lo - 8, C::BK + 16, 0);
-    if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK + 8);
-    prefetch_v(j0lo);
-    team_sync<C>();
-    logit_block(0);
-    if constexpr (mix_pre) mix_blocks(s, wpre, I0{}, I1{});
-    weights(kt_lo, 0, true);
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-      const int j0 = kt * C::BK;
-#pragma unroll
-      for (int lb = 1; lb < C::LB; ++lb) logit_block(lb);
-      after_logits(I1{});
-      // every wave has read this K tile and finished the previous tile's AV: V(kt) and
-      // K(kt + 1) go to LDS, the loads of V(kt + 1) and K(kt + 2) are issued
-      commit_v();
-      if (kt + 1 < kt_hi) {
-        commit_k(16);
-        if (kt + 2 < kt_hi) prefetch_k(j0 + 2 * C::BK + 8);
-        prefetch_v(j0 + C::BK);
-      }
-      const bool edge = (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) ||
-                        (wrow_min + C::QW > T_);
-#pragma unroll
-      for (int lb = 1; lb < C::LB; ++lb) weights(kt, lb, edge);
-      team_sync<C>();  // ring, V(kt) and K(kt + 1) are visible
-      convolve(kt);
-      const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < cq1) || (wrow_min + C::QW > T_);
-      if (edge2) {
-#pragma unroll
-        for (int ob = 0; ob < C::NKB; ++ob)
-#pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) {
-            const int t = qs0 + qb * 16 + lq;
-            const int gr = row0 + t;
+          for (int lb = L0; lb < L1; ++lb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int j = j0 + ob * 16 + 4 * lg + i;
-              cv[ob][qb][i] = ((t >= cq1) & (gr < T_) & (j <= gr)) ? cv[ob][qb][i] : 0.0f;
+              const int j = j0 - 8 + lb * 16 + 4 * lg + i;
+              arr[lb][qb][i] = (row_ok & (j >= 0) & (j <= gr)) ? arr[lb][qb][i] : 0.0f;
             }
-          }
+        }
       }
-      if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
-      av(cv, I0{});
+      weights_store(arr, kt, lb0c, lb1c);
+    };
+
+    if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
+    team_sync<C>();  // every wave is done with both phase-1 K buffers
+    // lead-in K tile: rows j0lo - BK + 8 .. j0lo + 7, whose last block is block 0 of tile kt_lo
+    stage_k_direct(j0lo - C::BK + 8, C::BK, 0);
+    prefetch_k(j0lo + 8);
+    prefetch_v(j0lo);
+    team_sync<C>();
+    logit_block_from(s, Ks, C::BK, 0, 16 - C::BK);
+    if constexpr (XBAR) mix_write(s, 0, I0{}, I1{});
+    team_sync<C>();  // every wave has read the lead-in rows
+    if constexpr (mix_pre) mix_read(s, 0, wpre, I0{}, I1{});
+    weights_to_ring(s, kt_lo, I0{}, I1{});
+    commit_k(0);  // K(kt_lo)
+    if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK + 8);
+    team_sync<C>();
+    // stretches A and B of the lead-in: tile kt_lo's logits, mixing and weights
+#pragma unroll
+    for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, Ks, C::BK, lb, 16);
+    if constexpr (XBAR) mix_write(s, 0, I1{}, ILB{});
+    team_sync<C>();
+    if (kt_lo + 1 < kt_hi) {
+      commit_k(0);  // K(kt_lo + 1)
+      if (kt_lo + 2 < kt_hi) prefetch_k(j0lo + 2 * C::BK + 8);
+    }
+    if constexpr (mix_pre) mix_read(s, 0, wpre, I1{}, ILB{});
+    weights_to_ring(s, kt_lo, I1{}, ILB{});
+    team_sync<C>();
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+      const int j0 = kt * C::BK;
+      const bool more = kt + 1 < kt_hi;
+      // stretch A: V(kt) to LDS (every wave finished AV(kt - 1)); the logits of tile kt + 1
+      commit_v();
+      if (more) {
+        prefetch_v(j0 + C::BK);
+#pragma unroll
+        for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, Ks, C::BK, lb, 16);
+        if constexpr (XBAR) mix_write(s, 0, I1{}, ILB{});
+      }
+      team_sync<C>();
+      // stretch B: K(kt + 2) to LDS (every wave read K(kt + 1)); tile kt's convolution and
+      // AV beside tile kt + 1's mixing and weights
+      if (kt + 2 < kt_hi) {
+        commit_k(0);
+        if (kt + 3 < kt_hi) prefetch_k(j0 + 3 * C::BK + 8);
+      }
+      const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < cq1) || (wrow_min + C::QW > T_);
+      // tile kt's convolution and AV (MFMA), then tile kt + 1's mixing and weights (VALU)
+      auto conv_av = [&]() MTA_INLINE {
+        convolve(kt);
+        if (edge2) {
+#pragma unroll
+          for (int ob = 0; ob < C::NKB; ++ob)
+#pragma unroll
+            for (int qb = 0; qb < C::NQB; ++qb) {
+              const int t = qs0 + qb * 16 + lq;
+              const int gr = row0 + t;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int j = j0 + ob * 16 + 4 * lg + i;
+                cv[ob][qb][i] = ((t >= cq1) & (gr < T_) & (j <= gr)) ? cv[ob][qb][i] : 0.0f;
+              }
+            }
+        }
+        if constexpr (C::MIXPOST) {
+          mix_write(cv, 1, I0{}, INKB{});
+          if constexpr (C::CH > 1) team_sync<C>();
+          mix_read(cv, 1, wpost, I0{}, INKB{});
+        }
+        av(cv, I0{});
+      };
+      auto next_weights = [&]() MTA_INLINE {
+        if (more) {
+          if constexpr (mix_pre) mix_read(s, 0, wpre, I1{}, ILB{});
+          weights_to_ring(s, kt + 1, I1{}, ILB{});
+        }
+      };
+      conv_av();
+      next_weights();
+      team_sync<C>();
     }
     }
   }
