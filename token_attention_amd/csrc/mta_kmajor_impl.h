@@ -1026,7 +1026,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
         av(cv, I0{});
       }
-      if constexpr (XBAR && C::MIXPOST && C::CH > 1) team_sync<C>();  // the exchange buffer is reused
+      if constexpr (XBAR && C::MIXPOST && C::CH > 1) __syncthreads();  // the exchange buffer is reused
     }
     }
   } else {
@@ -1051,6 +1051,12 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // In phase 2 the K tile of tile kt holds rows j0 + 8 .. j0 + BK + 7 (its logit blocks
     // 1..NKB); block 0 of the first tile comes from the last block of a lead-in K tile.
     constexpr bool XBAR = mix_pre && C::CH > 1;  // mixing before softmax exchanges through LDS
+    // the barriers of this schedule also order the mixing exchanges, which span the workgroup
+    // even when a wave stages its own K and V
+    auto tsync = [&]() MTA_INLINE {
+      if constexpr (C::MIX && C::CH > 1) __syncthreads();
+      else team_sync<C>();
+    };
     f32x4 sn[C::LB][C::NQB];  // phase 1: the logits of the other tile of a pair
     float lsum[C::NQB];
     // per-query normaliser folded into the exponent: p = exp2(x*sc - (m*sc + log2 l))
@@ -1093,7 +1099,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
         p1_sums(cur);
         if constexpr (mix_pre) mix_write(nxt, pb ^ 1, I1{}, ILB{});
-        team_sync<C>();
+        tsync();
         return;
       }
       if (more) {
@@ -1132,7 +1138,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       if constexpr (mix_pre) {
         if (more) mix_write(nxt, pb ^ 1, I1{}, ILB{});
       }
-      team_sync<C>();
+      tsync();
     };
     for (int exact = 0;; exact = 1) {
 #pragma unroll
@@ -1146,11 +1152,11 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         commit_k2();
         if (kt_lo + 2 < kt_hi) prefetch_k(j0lo + 2 * C::BK);
       }
-      team_sync<C>();
+      tsync();
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, Ks, C::BK, lb, 16);
       if constexpr (mix_pre) mix_write(s, 0, I1{}, ILB{});
-      team_sync<C>();
+      tsync();
       for (int kt = kt_lo; kt < kt_hi; kt += 2) {
         p1_step(kt, s, sn, exact != 0);
         if (kt + 1 < kt_hi) p1_step(kt + 1, sn, s, exact != 0);
@@ -1215,32 +1221,32 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     };
 
     if (!C::SPLIT || A.split_mode != SPLIT_STATS) {
-    team_sync<C>();  // every wave is done with both phase-1 K buffers
+    tsync();  // every wave is done with both phase-1 K buffers
     // lead-in K tile: rows j0lo - BK + 8 .. j0lo + 7, whose last block is block 0 of tile kt_lo
     stage_k_direct(j0lo - C::BK + 8, C::BK, 0);
     prefetch_k(j0lo + 8);
     prefetch_v(j0lo);
-    team_sync<C>();
+    tsync();
     logit_block_from(s, Ks, C::BK, 0, 16 - C::BK);
     if constexpr (XBAR) mix_write(s, 0, I0{}, I1{});
-    team_sync<C>();  // every wave has read the lead-in rows
+    tsync();  // every wave has read the lead-in rows
     if constexpr (mix_pre) mix_read(s, 0, wpre, I0{}, I1{});
     weights_to_ring(s, kt_lo, I0{}, I1{});
     commit_k(0);  // K(kt_lo)
     if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK + 8);
-    team_sync<C>();
+    tsync();
     // stretches A and B of the lead-in: tile kt_lo's logits, mixing and weights
 #pragma unroll
     for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, Ks, C::BK, lb, 16);
     if constexpr (XBAR) mix_write(s, 0, I1{}, ILB{});
-    team_sync<C>();
+    tsync();
     if (kt_lo + 1 < kt_hi) {
       commit_k(0);  // K(kt_lo + 1)
       if (kt_lo + 2 < kt_hi) prefetch_k(j0lo + 2 * C::BK + 8);
     }
     if constexpr (mix_pre) mix_read(s, 0, wpre, I1{}, ILB{});
     weights_to_ring(s, kt_lo, I1{}, ILB{});
-    team_sync<C>();
+    tsync();
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
       const int j0 = kt * C::BK;
       const bool more = kt + 1 < kt_hi;
@@ -1252,7 +1258,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, Ks, C::BK, lb, 16);
         if constexpr (XBAR) mix_write(s, 0, I1{}, ILB{});
       }
-      team_sync<C>();
+      tsync();
       // stretch B: K(kt + 2) to LDS (every wave read K(kt + 1)); tile kt's convolution and
       // AV beside tile kt + 1's mixing and weights
       if (kt + 2 < kt_hi) {
@@ -1279,7 +1285,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         }
         if constexpr (C::MIXPOST) {
           mix_write(cv, 1, I0{}, INKB{});
-          if constexpr (C::CH > 1) team_sync<C>();
+          if constexpr (C::CH > 1) tsync();
           mix_read(cv, 1, wpost, I0{}, INKB{});
         }
         av(cv, I0{});
@@ -1292,7 +1298,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       };
       conv_av();
       next_weights();
-      team_sync<C>();
+      tsync();
     }
     }
   }
