@@ -98,19 +98,17 @@ def gpu_inputs(cfg, torch):
     return inp, d
 
 
-def clock_warmup(torch, seconds=0.5):
-    """Bring the GPU to its steady clock before any timed region: a loop of plain bf16 matrix
-    products (not the layer) for about `seconds`. Without it the first ~30 launches of a 1 ms
-    kernel run up to 25 % slower while the clock ramps up."""
-    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
-    b = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+def clock_warmup(fn, torch, seconds=0.5):
+    """Bring the GPU to its steady clock before any timed region: about `seconds` of back-to-back
+    calls of fn, the plain causal attention kernel on the workload's tensors (not the layer).
+    From a cold start the first ~30 launches of the 1 ms variant kernel ran up to 25 % slower
+    while the clock ramped up; a matrix-product load left it ~4 % slow, an attention load ~1 %."""
     torch.cuda.synchronize()
     t0 = time.time()
     while time.time() - t0 < seconds:
         for _ in range(8):
-            torch.mm(a, b)
+            fn()
         torch.cuda.synchronize()
-    del a, b
     return time.time() - t0
 
 
@@ -240,7 +238,6 @@ def main():
         return
 
     ta.lib()  # fail loudly if the HIP library is missing
-    warm_s = clock_warmup(torch)
     if args.workload != HEADLINE and not args.only:
         print(json.dumps({"error": "--workload selects a profiling workload and needs --only"}))
         sys.exit(2)
@@ -256,6 +253,8 @@ def main():
 
     def plain():
         ta.attention_plain(d["q"], d["k"], d["v"], out=out)
+
+    warm_s = clock_warmup(plain, torch)
 
     dflt = cfg.replace(kq="pre", mix="post")
     kw2 = dict(kw, kq="pre", mix="post")
