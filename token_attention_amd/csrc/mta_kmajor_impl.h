@@ -1094,10 +1094,67 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         // interior tile: one branch-free stretch, the next tile's logits (MFMA) beside this
         // tile's mixing and row sums (VALU). After the last tile of a key range the next
         // tile's logits and exchange are computed from stale rows and never used.
+        constexpr int NIT = C::NKB * C::KS;      // K operands of the next tile
+        constexpr int NEL = C::NKB * C::NQB * 4; // this tile's values per lane
+        if constexpr (NEL % NIT == 0) {
+          // Interleaved by hand (the scheduler keeps MFMAs together otherwise, and a wave
+          // issues in order): this tile's exchange reads first, then per K operand (loaded
+          // one step ahead) its MFMAs and an equal share of this tile's mixing and row sums;
+          // scheduling barriers keep the steps apart.
+          constexpr int EPI = NEL / NIT;
+          f16x4 xo[C::CH > 1 ? C::CH - 1 : 1][C::NQB][C::NKB];
+          if constexpr (XBAR) {
 #pragma unroll
-        for (int lb = 1; lb < C::LB; ++lb) logit_block_from(nxt, kbuf, C::BK, lb, 16);
-        if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
-        p1_sums(cur);
+            for (int k = 1; k < C::CH; ++k)
+#pragma unroll
+              for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+                for (int x = 0; x < C::NKB; ++x)
+                  xo[k - 1][qb][x] = *reinterpret_cast<const f16x4*>(xslot(pb, (hu + k) & (C::CH - 1), qb) + x * 4);
+          }
+          float mref[C::NQB], part[C::NQB];
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            mref[qb] = m_run[qb] * sc;
+            part[qb] = 0.0f;
+          }
+          const __bf16* kr = kbuf + ((size_t)hu * C::BK - 16 + lq) * C::LDK + lg * 8;
+          auto kop = [&](int it) MTA_INLINE {
+            return *reinterpret_cast<const bf16x8*>(kr + (size_t)(1 + it / C::KS) * 16 * C::LDK + (it % C::KS) * 32);
+          };
+          bf16x8 af = kop(0);
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const int lb = 1 + it / C::KS, ks = it % C::KS;
+            const bf16x8 a_it = af;
+            if (it + 1 < NIT) af = kop(it + 1);
+#pragma unroll
+            for (int qb = 0; qb < C::NQB; ++qb) {
+              if (ks == 0) nxt[lb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+              nxt[lb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_it, qf[qb][ks], nxt[lb][qb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < EPI; ++k) {
+              const int e = it * EPI + k;
+              const int clb = 1 + e / (C::NQB * 4), cqb = (e / 4) % C::NQB, ci = e % 4;
+              float x = cur[clb][cqb][ci];
+              if constexpr (mix_pre) {
+                x *= wpre[0];
+#pragma unroll
+                for (int kk = 1; kk < C::CH; ++kk) x = __builtin_fmaf(wpre[kk], (float)xo[kk - 1][cqb][clb - 1][ci], x);
+              }
+              part[cqb] += fast_exp2(__builtin_fmaf(x, sc, -mref[cqb]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) l_run[qb] += part[qb];
+        } else {
+#pragma unroll
+          for (int lb = 1; lb < C::LB; ++lb) logit_block_from(nxt, kbuf, C::BK, lb, 16);
+          if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
+          p1_sums(cur);
+        }
         if constexpr (mix_pre) mix_write(nxt, pb ^ 1, I1{}, ILB{});
         tsync();
         return;
