@@ -290,17 +290,26 @@ __global__ void transpose_w_kernel(const float* __restrict__ w, float* __restric
   wT[x] = w[((size_t)g * CH + v) * CH + u];
 }
 
-// ---- mixing-weight gradient partials: sum over a group's maps of G_u * E_u' ---------------------
-constexpr int PD_CHUNKS = 64;
+constexpr int PD_CHUNKS = 64;  // blocks per (batch, group) of the mixing backward
 
+// ---- mixing backward in one pass over a group's maps: the mixing-weight gradient partials
+// (sum over the maps of G_u * E_v per block, reduced deterministically afterwards) and
+// G_u <- sum_x wT[g][u][x] G_x in place (the gradient of the mixed map's input) --------------
 template <int CH>
-__global__ __launch_bounds__(MT_THREADS) void pairdot_kernel(const float* __restrict__ Gm, const float* __restrict__ Em,
-                                                            float* __restrict__ part, int M, size_t n4_per_map) {
+__global__ __launch_bounds__(MT_THREADS) void mix_backward_kernel(float* __restrict__ Gm, const float* __restrict__ Em,
+                                                                 const float* __restrict__ wT,
+                                                                 float* __restrict__ part, int M,
+                                                                 size_t n4_per_map) {
   __shared__ float red[4][CH * CH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int bg = blockIdx.y, G = M / CH, b = bg / G, g = bg % G;
-  const f32x4* gb = reinterpret_cast<const f32x4*>(Gm) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
+  f32x4* gb = reinterpret_cast<f32x4*>(Gm) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
   const f32x4* eb = reinterpret_cast<const f32x4*>(Em) + ((size_t)b * M + (size_t)g * CH) * n4_per_map;
+  float wl[CH][CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+#pragma unroll
+    for (int x = 0; x < CH; ++x) wl[u][x] = wT[((size_t)g * CH + u) * CH + x];
   float acc[CH][CH];
 #pragma unroll
   for (int u = 0; u < CH; ++u)
@@ -320,6 +329,13 @@ __global__ __launch_bounds__(MT_THREADS) void pairdot_kernel(const float* __rest
         const f32x4 pr = gv[u] * ev[v];
         acc[u][v] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      f32x4 o = gv[0] * wl[u][0];
+#pragma unroll
+      for (int x = 1; x < CH; ++x) o += gv[x] * wl[u][x];
+      gb[(size_t)u * n4_per_map + e] = o;
+    }
   }
 #pragma unroll
   for (int u = 0; u < CH; ++u)
@@ -623,25 +639,25 @@ hipError_t launch_softmax_bwd(const float* P, float* G, const Problem& p, hipStr
   return hipGetLastError();
 }
 
-// The gradient of one head mixing: dw (reduced into dw_out) and G <- mix with w^T, in place.
+// The gradient of one head mixing in one pass over the maps: dw (reduced into dw_out) and
+// G <- mix with w^T, in place.
 hipError_t mix_backward(float* G, const float* In, const float* w, float* wT, float* part, float* dw_out,
                         const Problem& p, hipStream_t st) {
   const int CH = p.c_h, NG = p.M / CH;
   const size_t n4 = (size_t)p.T * map_ld(p.T) / 4;
   const dim3 grid(PD_CHUNKS, p.B * NG);
-  switch (CH) {
-    case 1: hipLaunchKernelGGL(pairdot_kernel<1>, grid, dim3(MT_THREADS), 0, st, G, In, part, p.M, n4); break;
-    case 2: hipLaunchKernelGGL(pairdot_kernel<2>, grid, dim3(MT_THREADS), 0, st, G, In, part, p.M, n4); break;
-    case 4: hipLaunchKernelGGL(pairdot_kernel<4>, grid, dim3(MT_THREADS), 0, st, G, In, part, p.M, n4); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t e;
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = sum_rows(part, (size_t)p.B * PD_CHUNKS, (size_t)NG * CH * CH, dw_out, st)) != hipSuccess) return e;
   const int n = NG * CH * CH;
   hipLaunchKernelGGL(transpose_w_kernel, dim3((n + 255) / 256), dim3(256), 0, st, w, wT, NG, CH);
+  hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_mix(G, wT, p, st);
+  switch (CH) {
+    case 1: hipLaunchKernelGGL(mix_backward_kernel<1>, grid, dim3(MT_THREADS), 0, st, G, In, wT, part, p.M, n4); break;
+    case 2: hipLaunchKernelGGL(mix_backward_kernel<2>, grid, dim3(MT_THREADS), 0, st, G, In, wT, part, p.M, n4); break;
+    case 4: hipLaunchKernelGGL(mix_backward_kernel<4>, grid, dim3(MT_THREADS), 0, st, G, In, wT, part, p.M, n4); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return sum_rows(part, (size_t)p.B * PD_CHUNKS, (size_t)NG * CH * CH, dw_out, st);
 }
 
 // ---- workspace layout ------------------------------------------------------------------------
