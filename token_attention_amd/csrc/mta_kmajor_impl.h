@@ -1482,22 +1482,43 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Query halo rows of a tile: c_q - 1 per convolution.
+inline int tile_halo(const Problem& p) { return p.kq ? ((p.kq == KQ_BOTH) ? 2 : 1) * (p.c_q - 1) : 0; }
+// Rows per tile of the launched shape. A split key range whose output rows fit one 16-row tile
+// (a decode step) takes tiles of 16 rows with one wave per head of the group; everything else
+// takes 8 waves of 32 rows. The key-split plan uses the same figure.
+constexpr int SMALL_R = 16;
+inline bool short_rows(const Problem& p) { return p.T - p.row_begin <= SMALL_R - tile_halo(p); }
+inline bool small_tiles(const Problem& p) { return p.split_mode != 0 && short_rows(p); }
+inline int tile_rows(const Problem& p, bool split) {
+  const int ch = p.mix ? p.c_h : 1;
+  return (split && short_rows(p)) ? SMALL_R : 32 * (8 / ch);
+}
+
 // Tile shapes: 8 waves of 32 query rows (two waves per SIMD, so one wave's MFMA work
 // overlaps the other's LDS and VALU work). Key tiles of 64 keys, 32 when the LDS holds
 // four heads, the fp16 exchange of a mixing group, or (convolution before softmax) when
 // the ring, the convolution output and the logits are live in registers together.
-// SPLIT selects the instantiations that cover one chunk of a split key range.
+// SPLIT selects the instantiations that cover one chunk of a split key range; those also come
+// with 16-row tiles of one wave per head for short row ranges.
 template <int D, int CH, bool KQ, bool TWO, bool MIXPOST, int CQM, bool SPLIT>
 hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr bool small = CH == 4 || (CH > 1 && MIXPOST) || (KQ && !TWO);
   constexpr int BK = small ? 32 : 64;
-  if constexpr (!MIXPOST) {
-    if (p.mix == MIX_PRE)
-      return launch<Cfg<D, CH, 32, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true, 8, false, SPLIT>>(p, stream);
-  } else {
-    if (p.mix == MIX_BOTH) return launch<Cfg<D, CH, 32, BK, KQ, TWO, true, CQM, true, 8, false, SPLIT>>(p, stream);
+  auto go = [&](auto qwc, auto nwc) -> hipError_t {
+    constexpr int QW = decltype(qwc)::value, NW = decltype(nwc)::value;
+    if constexpr (!MIXPOST) {
+      if (p.mix == MIX_PRE)
+        return launch<Cfg<D, CH, QW, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true, NW, false, SPLIT>>(p, stream);
+    } else {
+      if (p.mix == MIX_BOTH) return launch<Cfg<D, CH, QW, BK, KQ, TWO, true, CQM, true, NW, false, SPLIT>>(p, stream);
+    }
+    return launch<Cfg<D, CH, QW, BK, KQ, TWO, MIXPOST, CQM, false, NW, false, SPLIT>>(p, stream);
+  };
+  if constexpr (SPLIT) {
+    if (small_tiles(p)) return go(std::integral_constant<int, SMALL_R>{}, std::integral_constant<int, CH>{});
   }
-  return launch<Cfg<D, CH, 32, BK, KQ, TWO, MIXPOST, CQM, false, 8, false, SPLIT>>(p, stream);
+  return go(std::integral_constant<int, 32>{}, std::integral_constant<int, 8>{});
 }
 
 template <int D, int CH, bool KQ, bool TWO, bool MIXPOST, bool SPLIT>
@@ -1515,8 +1536,15 @@ hipError_t launch_cq(const Problem& p, hipStream_t stream) {
 // Convolutions on both sides: 32-key tiles (two rings, two sets of Toeplitz operands).
 template <int D, int CH, bool MIXPOST, int CQM, bool SPLIT>
 hipError_t launch_dual_shape(const Problem& p, hipStream_t stream) {
-  if (p.mix & MIX_PRE) return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, true, 8, true, SPLIT>>(p, stream);
-  return launch<Cfg<D, CH, 32, 32, true, true, MIXPOST, CQM, false, 8, true, SPLIT>>(p, stream);
+  auto go = [&](auto qwc, auto nwc) -> hipError_t {
+    constexpr int QW = decltype(qwc)::value, NW = decltype(nwc)::value;
+    if (p.mix & MIX_PRE) return launch<Cfg<D, CH, QW, 32, true, true, MIXPOST, CQM, true, NW, true, SPLIT>>(p, stream);
+    return launch<Cfg<D, CH, QW, 32, true, true, MIXPOST, CQM, false, NW, true, SPLIT>>(p, stream);
+  };
+  if constexpr (SPLIT) {
+    if (small_tiles(p)) return go(std::integral_constant<int, SMALL_R>{}, std::integral_constant<int, CH>{});
+  }
+  return go(std::integral_constant<int, 32>{}, std::integral_constant<int, 8>{});
 }
 
 template <int D, int CH, bool MIXPOST, bool SPLIT>

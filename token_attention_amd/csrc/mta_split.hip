@@ -32,14 +32,18 @@ struct SplitPlan {
 // Number of key chunks, when the row tiles alone leave compute units idle: workgroups run in
 // rounds of CUS, each costing the fixed overhead plus its share of the keys; the plan minimises
 // rounds * (overhead + 1/n) (chunks are whole multiples of 64 keys). A decode step at T=4096 with
-// 16 row tiles gets 16 chunks of 256 keys (one round), a 512-row chunk 5 chunks of 832 keys.
+// 16 row tiles (of 16 rows) gets 16 chunks of 256 keys (one round), a 512-row chunk 5 chunks of
+// 832 keys.
 SplitPlan split_plan(const Problem& p) {
   if (p.fp32) return {1, 0};
+  // row tiles of the unsplit kernel and of the split instantiations (16-row tiles for a range
+  // that fits one, such as a decode step)
   const int ch = p.mix ? p.c_h : 1;
-  const int R = 32 * (8 / ch);  // rows per tile of every launched fused shape
-  const int halo = p.kq ? ((p.kq == KQ_BOTH) ? 2 : 1) * (p.c_q - 1) : 0;
-  const int r_out = R - halo;
-  const long long tiles = (long long)p.B * (p.M / ch) * ((p.T - p.row_begin + r_out - 1) / r_out);
+  const int halo = kmajor::tile_halo(p), rows = p.T - p.row_begin;
+  const int r_out = kmajor::tile_rows(p, false) - halo, r_split = kmajor::tile_rows(p, true) - halo;
+  const long long groups = (long long)p.B * (p.M / ch);
+  const long long tiles = groups * ((rows + r_out - 1) / r_out);
+  const long long tiles_split = groups * ((rows + r_split - 1) / r_split);
   // enough row tiles to occupy every compute unit: the unsplit kernel (heaviest tiles first)
   if (tiles >= CUS) return {1, 0};
   SplitPlan best{1, 0};
@@ -48,7 +52,7 @@ SplitPlan split_plan(const Problem& p) {
   for (int n = 2; n <= nmax; ++n) {
     const int keys = ((p.T + n - 1) / n + 63) / 64 * 64;
     const int neff = (p.T + keys - 1) / keys;
-    const double rounds = (double)((tiles * neff + CUS - 1) / CUS);
+    const double rounds = (double)((tiles_split * neff + CUS - 1) / CUS);
     const double cost = rounds * (WG_OVERHEAD + 1.0 / neff);
     if (cost < best_cost * 0.999) {
       best_cost = cost;
