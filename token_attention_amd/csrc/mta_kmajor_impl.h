@@ -16,20 +16,23 @@
 //     read with ds_read_b64_tr_b16, which transposes a 4 x 16 block of b16 values
 //     within each 16-lane group.
 //
-// Work split. One workgroup of NW waves (8 in every launched shape: two per SIMD, so one
-// wave's MFMA work overlaps the other's LDS and VALU work) owns batch b, head group g (c_h
-// heads) and a tile of R query rows; tile row t is global row i0 - (c_q - 1) + t (the first
-// c_q - 1 rows are the query halo of the convolution). Wave w owns head hu = w / (NW/c_h)
-// and a slab of QW = 32 rows. The workgroup stages the K and V tiles of all its heads
-// together (a wave that owned all rows of its head would stage them alone and synchronise
-// with a wavefront fence only; no launched shape uses that).
+// Work split. One workgroup of NW waves owns batch b, head group g (c_h heads) and a tile
+// of R query rows; tile row t is global row i0 - halo + t (the first rows are the query
+// halo of the convolutions). Wave w owns head hu = w / (NW/c_h) and a slab of QW rows.
+// The full-size shapes have 8 waves of 32 rows (two waves per SIMD, so one wave's MFMA work
+// overlaps the other's LDS and VALU work) and stage the K and V tiles of all heads of the
+// group together. The key-split instantiations for a range of at most 16 rows (a decode
+// step) have one wave of 16 rows per head; such a wave stages its own head's K and V and
+// synchronises those with a wavefront fence only (mixing exchanges stay workgroup-wide).
 //
-// Key tiles of BK keys stream through LDS; the next tile is loaded into registers
-// while the current one is computed (global -> VGPR prefetch) and written to LDS
-// afterwards. With a convolution the logits of a tile cover keys [j0 - 8, j0 + BK + 8):
-// 16-key blocks 0..BK/16, where block 0 equals the last block of the previous tile, so
-// each tile computes only BK new key columns (sliding key halo); the convolution
-// input lives in an LDS ring of BK/16 + 1 blocks per row.
+// Key tiles of BK keys stream through LDS. The K and V rows of a later tile are loaded
+// into registers (global -> VGPR prefetch) and written to LDS right after the first
+// workgroup barrier that follows the last read of the buffer they replace; a later barrier
+// of the same tile publishes them. With a convolution the logits of a tile cover keys
+// [j0 - 8, j0 + BK + 8): 16-key blocks 0..BK/16, where block 0 equals the last block of the
+// previous tile, so each tile computes only BK new key columns (sliding key halo); the
+// convolution input lives in an LDS ring of BK/16 + 1 blocks per row (BK/16 more in the
+// two-pass schedule, which writes the next tile's blocks while the current window is read).
 //
 // The c_q x c_k convolution runs on fp16 MFMA: output keys of one 16-key block read a
 // 32-key window (blocks ob, ob+1); for each query lag a the banded Toeplitz matrix of
@@ -43,7 +46,9 @@
 //   one pass   (no convolution after softmax, no mixing after softmax): weights against
 //              the reference, AV, division by the row sum in the epilogue;
 //   two passes (convolution or mixing after softmax): a statistics pass (row sums), then
-//              exact normalised weights -> [convolution -> Mask_0] -> [mixing] -> AV;
+//              exact normalised weights -> [convolution -> Mask_0] -> [mixing] -> AV; both
+//              passes are software-pipelined one tile deep (the next tile's logits are
+//              computed beside this tile's VALU work);
 //   both sides (DUAL: convolutions before and after softmax): the two-pass schedule with a
 //              second ring; every tile convolves the logits (first ring) into softmax inputs
 //              8 keys ahead of the weights it convolves (second ring), after a lead-in tile.
