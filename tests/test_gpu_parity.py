@@ -461,6 +461,34 @@ def test_rows_split_against_oracle(row_begin, kq, mix, c_h):
     assert diff <= 2e-2
 
 
+@pytest.mark.parametrize("kq,mix,c_h,c_q,c_k,nrows", [
+    ("both", "both", 4, 8, 17, 2), ("both", "both", 4, 8, 17, 3),  # halo 14: 16-row tiles hold 2 rows
+    ("post", "pre", 4, 4, 9, 13), ("post", "pre", 4, 4, 9, 14),    # halo 3
+    ("pre", "post", 2, 6, 11, 11), ("pre", "post", 2, 6, 11, 12),  # halo 5
+    (None, None, 1, 1, 1, 16), (None, None, 1, 1, 1, 17)])         # no halo
+def test_rows_split_sixteen_row_tiles(kq, mix, c_h, c_q, c_k, nrows):
+    """Key-split ranges that just fit one 16-row tile with its query halo (one wave per head)
+    and ranges one row longer (the 8-wave shapes), against the oracle and the unsplit range."""
+    cfg = mta_inputs.MTAConfig("rows_split16", 2, 200, 8, 128, c_q, c_k, c_h, kq, mix, True, "bf16", 0.1, 0.1, 1.0,
+                               0.0, 0.8, seed=43)
+    inp = case(cfg)
+    row_begin = cfg.T - nrows
+    dv = dev_inputs(cfg, inp)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    args = (dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"])
+    part = torch.full_like(dv["q"], 7.0)
+    ta.forward_rows_split(*args, row_begin=row_begin, out=part, **kw)
+    ref = ta.forward_rows(*args, row_begin=row_begin, **kw)
+    torch.cuda.synchronize()
+    p = part.float().cpu()
+    assert bool((p[:, :row_begin] == 7.0).all())
+    compare(cfg, p.numpy().astype(np.float64), oracle_full(cfg), rows=np.arange(row_begin, cfg.T),
+            what=f"split {nrows} rows {kq}/{mix}/{c_h} {c_q}x{c_k}")
+    diff = float((p[:, row_begin:] - ref.float().cpu()[:, row_begin:]).abs().max())
+    log(f"  vs unsplit: max diff {diff:.3e}")
+    assert diff <= 2e-2
+
+
 def test_rows_split_many_row_tiles():
     """Several row tiles per sequence, each split into key chunks (the statistics of the rows a
     tile shares with its neighbour are written once)."""
