@@ -148,10 +148,14 @@ struct Cfg {
   // convolution ring blocks per row: the window of a tile (LB blocks) and, in the pipelined
   // two-phase schedule, the NKB new blocks of the next tile, written while the window is read
   static constexpr int RB = (TWO && !DUAL) ? LB + NKB : LB;
-  static constexpr int LDK = D + 8;            // K row stride (bf16): 16-byte reads conflict-free
+  // K row stride (bf16) and ring row stride (fp16), chosen by measurement (LDS bank-conflict
+  // counter and time): at d = 128 the two-pass schedule with LDK = D + 8 and LDZ = ZW + 8 had
+  // 8.3e7 conflict cycles per launch, with D + 16 and ZW 2.8e7 and ran 5 % faster; an unpadded
+  // ring made the both-sides schedule 6 % faster; a ring stride of 64 halves was 50 % slower.
+  static constexpr int LDK = DUAL ? D + 8 : D + 16;
   static constexpr int LDV = D + 16;           // V row stride (bf16): transposed reads conflict-free
   static constexpr int ZW = RB * 16;           // ring width (keys)
-  static constexpr int LDZ = ZW + 8;           // fp16 stride
+  static constexpr int LDZ = ZW;
   static constexpr int ZROWS = ZPRE + R;
   static constexpr int XW = NKB * 4;           // exchange halves per lane and query block
   static constexpr size_t SX_HALF = (size_t)CH * R * BK;  // one exchange buffer (halves)
