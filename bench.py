@@ -220,8 +220,9 @@ def main():
                     help="only run a device-to-device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(the layer shards by batch and head group without communication)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 (multi-GPU runs "
+                                   "are not implemented; the layer would shard by batch and head group "
+                                   "without communication)"}))
         sys.exit(2)
 
     import torch
