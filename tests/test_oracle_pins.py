@@ -207,6 +207,43 @@ def test_mix_permutation_permutes_maps():
     np.testing.assert_array_equal(maps[:, [0, 1, 2, 3]], base[:, [2, 0, 3, 1]])
 
 
+# --- each head its own kernels, each group its own mixing weights ---------------------
+# The convolution kernels are per head and the mixing weights per group of c_h heads (§3.1,
+# §3.2). Closed forms that differ from head to head and from group to group fail when an index
+# lands on another head's kernel or another group's weights.
+@pytest.mark.parametrize("kq", ["pre", "post"])
+def test_each_head_uses_its_own_kernel(kq):
+    # head m's kernel alpha_m * delta(0, centre). Before softmax it scales head m's logits:
+    # softmax(alpha_m QK^T / sqrt(d)). After softmax it scales head m's weights: alpha_m times
+    # plain attention.
+    B, T, M, d, c_q, c_k, c_h = 2, 23, 4, 8, 3, 5, 2
+    q, k, v = _rand(B, T, M, d, 40)
+    alpha = np.array([0.5, 1.0, 1.7, 2.3])
+    th = _delta(M, c_q, c_k) * alpha[:, None, None]
+    out = oracle.forward(q, k, v, th, None, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq)
+    for m in range(M):
+        hq, hk, hv = q[:, :, m:m + 1], k[:, :, m:m + 1], v[:, :, m:m + 1]
+        if kq == "pre":
+            exp = _sdpa(hq, hk, hv, scale=alpha[m] / math.sqrt(d))
+        else:
+            exp = alpha[m] * _sdpa(hq, hk, hv)
+        np.testing.assert_allclose(out[:, :, m:m + 1], exp, atol=1e-12)
+
+
+@pytest.mark.parametrize("mix", ["pre", "post"])
+def test_each_group_uses_its_own_mixing_weights(mix):
+    # group 0 swaps its two heads, group 1 keeps them: w[g][u][u'] = 1 where u' = pi_g(u).
+    # Mixed logits (before softmax) or mixed weights (after it) of head u are those of head
+    # pi_g(u), so either way head u attends with the queries and keys of head pi_g(u) and its
+    # own values.
+    B, T, M, d, c_h = 2, 19, 4, 8, 2
+    q, k, v = _rand(B, T, M, d, 41)
+    w = np.stack([np.eye(2)[[1, 0]], np.eye(2)])
+    src = [1, 0, 2, 3]
+    out = oracle.forward(q, k, v, None, w, c_h=c_h, mix=mix)
+    np.testing.assert_allclose(out, _sdpa(q[:, :, src], k[:, :, src], v), atol=1e-12)
+
+
 # --- (b) row sums and (c) causality ------------------------------------------------
 def test_rows_sum_to_one_after_pre_conv():
     B, T, M, d, c_q, c_k, c_h = 1, 31, 4, 8, 4, 7, 2
