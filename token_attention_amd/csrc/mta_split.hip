@@ -31,9 +31,12 @@ struct SplitPlan {
 
 // Number of key chunks, when the row tiles alone leave compute units idle: workgroups run in
 // rounds of CUS, each costing the fixed overhead plus its share of the keys; the plan minimises
-// rounds * (overhead + 1/n) (chunks are whole multiples of 64 keys). A decode step at T=4096 with
-// 16 row tiles (of 16 rows) gets 16 chunks of 256 keys (one round), a 512-row chunk 5 chunks of
-// 832 keys.
+// rounds * (overhead + 1/n) (chunks are whole multiples of 64 keys). 16-row tiles of a group of
+// four heads (four waves whose LDS fills a compute unit) count a round as 7/8 of the units:
+// at exactly CUS such workgroups a launch took longer than at 13/16 of them (T=4096 decode
+// step: 16 chunks of 256 keys 76 us, 13 chunks of 320 keys 64 us). A decode step at T=4096
+// with 16 row tiles of a four-head group gets 13 chunks of 320 keys, a 512-row chunk 5 chunks
+// of 832 keys.
 SplitPlan split_plan(const Problem& p) {
   if (p.fp32) return {1, 0};
   // row tiles of the unsplit kernel and of the split instantiations (16-row tiles for a range
@@ -49,10 +52,11 @@ SplitPlan split_plan(const Problem& p) {
   SplitPlan best{1, 0};
   double best_cost = (double)((tiles + CUS - 1) / CUS) * (WG_OVERHEAD + 1.0);
   const int nmax = std::min(NSPLIT_MAX, (p.T + 63) / 64);
+  const long long per_round = (kmajor::short_rows(p) && ch >= 4) ? CUS - CUS / 8 : CUS;
   for (int n = 2; n <= nmax; ++n) {
     const int keys = ((p.T + n - 1) / n + 63) / 64 * 64;
     const int neff = (p.T + keys - 1) / keys;
-    const double rounds = (double)((tiles_split * neff + CUS - 1) / CUS);
+    const double rounds = (double)((tiles_split * neff + per_round - 1) / per_round);
     const double cost = rounds * (WG_OVERHEAD + 1.0 / neff);
     if (cost < best_cost * 0.999) {
       best_cost = cost;
