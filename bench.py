@@ -212,7 +212,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for cpu_baseline (0: the whole workload)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
-    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward"], default=None,
+    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward", "decode"],
+                    default=None,
                     help="run one path only (for counter collection); prints its timing")
     ap.add_argument("--workload", type=int, default=HEADLINE,
                     help="index of the workload in mta_inputs.CONFIGS for --only runs (profiling)")
@@ -326,6 +327,18 @@ def main():
 
     if args.only == "backward":
         print(json.dumps({"only": "backward", "workload": cfg.name, **backward_record(None)}))
+        return
+    if args.only == "decode":
+        # one decode step (the last row of every sequence) with the key range split over workgroups
+        rb = cfg.T - 1
+        need = ta.rows_split_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, row_begin=rb, **kw)
+        ws_dec = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+        def decode():
+            ta.forward_rows_split(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"],
+                                  row_begin=rb, out=out, workspace=ws_dec, **kw)
+        ms_dec = time_launches(decode, args.steps, args.warmup, torch)
+        print(json.dumps({"only": "decode", "workload": cfg.name, "row_begin": rb, "ms": ms_dec}))
         return
     if args.only:
         fn = {"fused": fused, "plain": plain, "default": fused_default, "both": fused_both}.get(args.only)
