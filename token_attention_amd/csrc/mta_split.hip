@@ -92,19 +92,39 @@ __global__ void split_fill_kernel(float* stats, size_t n) {
   }
 }
 
-// one log2 normaliser per (b, row, head): m + log2(sum_c 2^(m_c - m) l_c)
+// one log2 normaliser per (b, row, head): m + log2(sum_c 2^(m_c - m) l_c). The chunks' entries
+// are loaded in batches of 8 so that their memory latencies overlap.
+constexpr int SBATCH = 8;
+
 __global__ void split_stats_kernel(const float* __restrict__ stats, float* __restrict__ shift, int nsplit,
                                    size_t rows) {
   const size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (x >= rows) return;
   float m = -1e30f;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, stats[(s * rows + x) * 2]);
+  for (int s0 = 0; s0 < nsplit; s0 += SBATCH) {
+    float mv[SBATCH];
+#pragma unroll
+    for (int u = 0; u < SBATCH; ++u) mv[u] = (s0 + u < nsplit) ? stats[((s0 + u) * rows + x) * 2] : -1e30f;
+#pragma unroll
+    for (int u = 0; u < SBATCH; ++u) m = fmaxf(m, mv[u]);
+  }
   float l = 0.0f;
-  for (int s = 0; s < nsplit; ++s) l += stats[(s * rows + x) * 2 + 1] * exp2f(stats[(s * rows + x) * 2] - m);
+  for (int s0 = 0; s0 < nsplit; s0 += SBATCH) {
+    float mv[SBATCH], lv[SBATCH];
+#pragma unroll
+    for (int u = 0; u < SBATCH; ++u) {
+      const bool in = s0 + u < nsplit;
+      mv[u] = in ? stats[((s0 + u) * rows + x) * 2] : -1e30f;
+      lv[u] = in ? stats[((s0 + u) * rows + x) * 2 + 1] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < SBATCH; ++u) l += lv[u] * exp2f(mv[u] - m);
+  }
   shift[x] = l > 0.0f ? m + log2f(l) : 1e30f;
 }
 
-// one wave per (b, output row, head): combine the AV partials, GroupNorm + gate, write out
+// one wave per (b, output row, head): combine the AV partials, GroupNorm + gate, write out.
+// Lane s holds chunk s's statistics (at most 64 chunks); the partials are loaded in batches.
 template <int D>
 __global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict__ part_o,
                                                         const float* __restrict__ stats, int weighted,
@@ -123,17 +143,32 @@ __global__ __launch_bounds__(256) void split_out_kernel(const float* __restrict_
   float o[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) o[k] = 0.0f;
-  float mx = -1e30f, den = 0.0f;
+  // weight of chunk `lane` and the denominator (per-chunk references), else weight 1
+  float wl = 1.0f, den = 0.0f;
   if (weighted) {
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, stats[(s * rows + idx) * 2]);
-    for (int s = 0; s < nsplit; ++s) den += stats[(s * rows + idx) * 2 + 1] * exp2f(stats[(s * rows + idx) * 2] - mx);
+    const bool in = lane < nsplit;
+    const float ms = in ? stats[((size_t)lane * rows + idx) * 2] : -1e30f;
+    const float ls = in ? stats[((size_t)lane * rows + idx) * 2 + 1] : 0.0f;
+    float mx = ms;
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    wl = in ? exp2f(ms - mx) : 0.0f;
+    den = ls * wl;
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
   }
-  for (int s = 0; s < nsplit; ++s) {
-    const float ws = weighted ? exp2f(stats[(s * rows + idx) * 2] - mx) : 1.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += SBATCH) {
+    float pv[SBATCH][CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      if (c < D) o[k] += ws * part_o[(s * rows + idx) * D + c];
+    for (int u = 0; u < SBATCH; ++u)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int c = lane + 64 * k;
+        pv[u][k] = (s0 + u < nsplit && c < D) ? part_o[((size_t)(s0 + u) * rows + idx) * D + c] : 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < SBATCH; ++u) {
+      const float ws = __shfl(wl, (s0 + u) & 63);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) o[k] += ws * pv[u][k];
     }
   }
   if (weighted) {
