@@ -106,7 +106,7 @@ __global__ __launch_bounds__(MT_THREADS) void logits_kernel(const T* __restrict_
 // 16-byte loads in flight).
 template <int CH>
 __global__ __launch_bounds__(MT_THREADS) void mix_kernel(float* X, const float* Src, const float* __restrict__ w,
-                                                        int Tn, int M, size_t n4_per_map) {
+                                                        int M, size_t n4_per_map) {
   const int bg = blockIdx.y;  // b * (M/CH) + g
   const int G = M / CH;
   const int b = bg / G, g = bg % G;
@@ -714,9 +714,9 @@ hipError_t launch_mix(float* X, const float* w, const Problem& p, hipStream_t st
   const unsigned gx = (unsigned)(want < 4096 ? want : 4096);
   const dim3 grid(gx, p.B * G);
   switch (p.c_h) {
-    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.T, p.M, n4); break;
-    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.T, p.M, n4); break;
-    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.T, p.M, n4); break;
+    case 1: hipLaunchKernelGGL(mix_kernel<1>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.M, n4); break;
+    case 2: hipLaunchKernelGGL(mix_kernel<2>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.M, n4); break;
+    case 4: hipLaunchKernelGGL(mix_kernel<4>, grid, dim3(MT_THREADS), 0, st, X, S, w, p.M, n4); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

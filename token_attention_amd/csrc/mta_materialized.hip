@@ -22,8 +22,6 @@ template <typename T, int D>
 hipError_t run_chain(const Problem& p, float* X, float* Y, hipStream_t st) {
   const T* q = reinterpret_cast<const T*>(p.q);
   const T* k = reinterpret_cast<const T*>(p.k);
-  const T* v = reinterpret_cast<const T*>(p.v);
-  T* out = reinterpret_cast<T*>(p.out);
   hipError_t e;
   const float scale = (float)(1.0 / __builtin_sqrt((double)p.d));
   hipLaunchKernelGGL((logits_kernel<T, D>), dim3((p.T + 127) / 128, (p.T + 127) / 128, p.B * p.M),
