@@ -92,35 +92,24 @@ __global__ void split_fill_kernel(float* stats, size_t n) {
   }
 }
 
-// one log2 normaliser per (b, row, head): m + log2(sum_c 2^(m_c - m) l_c). The chunks' entries
-// are loaded in batches of 8 so that their memory latencies overlap.
+// Partials of up to SBATCH chunks are loaded together so that their memory latencies overlap.
 constexpr int SBATCH = 8;
 
-__global__ void split_stats_kernel(const float* __restrict__ stats, float* __restrict__ shift, int nsplit,
-                                   size_t rows) {
-  const size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+// one log2 normaliser per (b, row, head): m + log2(sum_c 2^(m_c - m) l_c); one wave per entry,
+// lane s holding chunk s's statistics (at most 64 chunks)
+__global__ __launch_bounds__(256) void split_stats_kernel(const float* __restrict__ stats, float* __restrict__ shift,
+                                                         int nsplit, size_t rows) {
+  const int lane = threadIdx.x & 63;
+  const size_t x = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (x >= rows) return;
-  float m = -1e30f;
-  for (int s0 = 0; s0 < nsplit; s0 += SBATCH) {
-    float mv[SBATCH];
-#pragma unroll
-    for (int u = 0; u < SBATCH; ++u) mv[u] = (s0 + u < nsplit) ? stats[((s0 + u) * rows + x) * 2] : -1e30f;
-#pragma unroll
-    for (int u = 0; u < SBATCH; ++u) m = fmaxf(m, mv[u]);
-  }
-  float l = 0.0f;
-  for (int s0 = 0; s0 < nsplit; s0 += SBATCH) {
-    float mv[SBATCH], lv[SBATCH];
-#pragma unroll
-    for (int u = 0; u < SBATCH; ++u) {
-      const bool in = s0 + u < nsplit;
-      mv[u] = in ? stats[((s0 + u) * rows + x) * 2] : -1e30f;
-      lv[u] = in ? stats[((s0 + u) * rows + x) * 2 + 1] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < SBATCH; ++u) l += lv[u] * exp2f(mv[u] - m);
-  }
-  shift[x] = l > 0.0f ? m + log2f(l) : 1e30f;
+  const bool in = lane < nsplit;
+  const float ms = in ? stats[((size_t)lane * rows + x) * 2] : -1e30f;
+  const float ls = in ? stats[((size_t)lane * rows + x) * 2 + 1] : 0.0f;
+  float m = ms;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float l = in ? ls * exp2f(ms - m) : 0.0f;
+  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  if (lane == 0) shift[x] = l > 0.0f ? m + log2f(l) : 1e30f;
 }
 
 // one wave per (b, output row, head): combine the AV partials, GroupNorm + gate, write out.
@@ -253,7 +242,8 @@ hipError_t launch_rows_split(const Problem& p0, void* workspace, hipStream_t st,
   if (normalised) {
     p.split_mode = kmajor::SPLIT_STATS;
     if ((e = launch_fused(p, st, unsupported)) != hipSuccess || *unsupported) return e;
-    hipLaunchKernelGGL(split_stats_kernel, dim3((unsigned)((l.rows + 255) / 256)), dim3(256), 0, st, p.part_stats,
+    static_assert(NSPLIT_MAX <= 64, "one chunk per lane");
+    hipLaunchKernelGGL(split_stats_kernel, dim3((unsigned)((l.rows + 3) / 4)), dim3(256), 0, st, p.part_stats,
                        ws + l.shift, plan.n, l.rows);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
