@@ -157,6 +157,37 @@ def test_rows_split_workspace_size():
     assert ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4096, **kw) == 0
 
 
+def _split_chunks(nbytes, B, T, M, d, row_begin):
+    """Key chunks of a split launch, read back from its workspace size: per (b, row, head) one
+    float of normaliser, two floats of statistics per chunk and d floats of AV partial per chunk
+    (row_begin - 16 .. T-1: 16 rows of query halo), each region rounded up to 64 floats."""
+    rows = B * (T - row_begin + 16) * M
+    up = lambda x: (x + 63) // 64 * 64
+    for n in range(2, 65):
+        if 4 * (up(rows) + up(2 * n * rows) + n * rows * d) == nbytes:
+            return n
+    raise AssertionError(f"{nbytes} bytes match no chunk count")
+
+
+def test_rows_split_plan_at_the_t4096_shape():
+    # decode step, convolution after and mixing before softmax: 16 row tiles of 16 rows, four
+    # waves each; 13 chunks of 320 keys (208 workgroups: a round of such workgroups is taken
+    # as 7/8 of the 256 compute units)
+    kw = dict(c_q=4, c_k=9, c_h=4, kq="post", mix="pre", gn=True)
+    assert _split_chunks(ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4095, **kw),
+                         2, 4096, 32, 128, 4095) == 13
+    # the default placement decodes the same way
+    kw_default = dict(c_q=4, c_k=9, c_h=4, kq="pre", mix="post", gn=True)
+    assert _split_chunks(ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4095, **kw_default),
+                         2, 4096, 32, 128, 4095) == 13
+    # no convolution or mixing: 64 one-wave row tiles, 4 chunks fill the 256 units once
+    assert _split_chunks(ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4095, gn=True),
+                         2, 4096, 32, 128, 4095) == 4
+    # 512-row prefill chunk: 144 row tiles of 64 rows, 5 chunks of 832 keys
+    assert _split_chunks(ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=3584, **kw),
+                         2, 4096, 32, 128, 3584) == 5
+
+
 @pytest.mark.parametrize("row_begin", [-1, 64])
 def test_rows_split_outside_the_sequence_is_rejected(row_begin):
     st = mta.lib().mta_forward_rows_split(P, P + 0x100, P + 0x200, P, P, P, P, 1.0, P + 0x300, 1, 64, 4, 128, 3, 5,
