@@ -74,6 +74,25 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def device_clock_mhz(dev: int = 0):
+    """Peak shader clock of the device in MHz (HIP attribute hipDeviceAttributeClockRate, in kHz),
+    read through the HIP runtime already loaded in this process; None if it cannot be read."""
+    import ctypes
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64.so" in ln}
+        if not paths:
+            return None
+        hip = ctypes.CDLL(sorted(paths)[0])
+        val = ctypes.c_int(0)
+        HIP_DEVICE_ATTRIBUTE_CLOCK_RATE = 5
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), HIP_DEVICE_ATTRIBUTE_CLOCK_RATE, dev) != 0:
+            return None
+        return val.value / 1000.0
+    except (OSError, AttributeError):
+        return None
+
+
 def measured_traffic():
     """HBM bytes per launch of the fused kernel from the committed counter summary,
     or None when the kernel sources changed since the counters were taken."""
@@ -415,7 +434,7 @@ def main():
         result["backward_materialized"] = backward_record(result["materialized"]["ms"])
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
-                        "gcn_arch": getattr(props, "gcnArchName", "")}
+                        "clock_mhz": device_clock_mhz(), "gcn_arch": getattr(props, "gcnArchName", "")}
     result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(cfg, inp, args.cpu_rows)
     if not args.no_cpu:
         result["cpu_baseline"]["single_thread"] = cpu_single_thread()
