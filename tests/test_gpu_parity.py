@@ -542,6 +542,39 @@ def test_rows_split_at_full_size(row_begin):
             what=f"split rows {row_begin}.. ({len(rows)} checked)")
 
 
+def _split_chunks(nbytes, B, T, M, d, row_begin):
+    """Key chunks of a split launch, read back from its workspace size (one normaliser, two
+    statistics floats and d partial floats per chunk for each (b, row, head) of rows
+    row_begin - 16 .. T-1, each region rounded up to 64 floats)."""
+    rows = B * (T - row_begin + 16) * M
+    up = lambda x: (x + 63) // 64 * 64
+    return next(n for n in range(2, 65) if 4 * (up(rows) + up(2 * n * rows) + n * rows * d) == nbytes)
+
+
+@pytest.mark.parametrize("row_begin", [4095, 3900])
+@pytest.mark.parametrize("kq,mix,c_h", [("post", "pre", 4), ("pre", "post", 4), (None, None, 1)])
+def test_rows_split_sixty_four_chunks(kq, mix, c_h, row_begin):
+    """The largest split: one head group at T=4096 takes 64 chunks of 64 keys, one per lane of
+    the combining kernels. From row 3900 with a convolution or mixing, the first 64-row tile
+    (output rows up to 3960) has no keys in the last two chunks."""
+    cfg = mta_inputs.MTAConfig("split64", 1, 4096, 4, 128, 4, 9, c_h, kq, mix, True, "bf16", 0.1, 0.1, 1.0, 0.0,
+                               0.8, seed=45)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=kq, mix=mix, gn=True)
+    need = ta.rows_split_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, row_begin=row_begin, **kw)
+    assert _split_chunks(need, cfg.B, cfg.T, cfg.M, cfg.d, row_begin) == 64
+    inp = case(cfg)
+    rows = np.unique(np.r_[np.arange(row_begin, min(row_begin + 4, cfg.T)), 3960, 3961, cfg.T - 1])
+    rows = rows[rows >= row_begin].astype(np.int32)
+    want = oracle.forward_cfg(cfg, inp, rows=rows)
+    dv = dev_inputs(cfg, inp)
+    out = ta.forward_rows_split(dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"],
+                                row_begin=row_begin, **kw)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got[:, row_begin:]).all()
+    compare(cfg, got, want, rows=rows, what=f"64 chunks rows {row_begin}.. {kq}/{mix}")
+
+
 def test_rows_split_fp32_runs_unsplit():
     cfg = mta_inputs.MTAConfig("split_fp32", 1, 90, 4, 32, 3, 5, 2, "pre", "post", True, "fp32", 0.1, 0.1, 1.0, 0.0,
                                0.8, seed=44)
