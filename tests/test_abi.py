@@ -158,13 +158,13 @@ def test_rows_split_workspace_size():
 
 
 def _split_chunks(nbytes, B, T, M, d, row_begin):
-    """Key chunks of a split launch, read back from its workspace size: per (b, row, head) one
-    float of normaliser, two floats of statistics per chunk and d floats of AV partial per chunk
-    (row_begin - 16 .. T-1: 16 rows of query halo), each region rounded up to 64 floats."""
+    """Key chunks of a split launch, read back from its workspace size: per (b, row, head) two
+    floats of statistics per chunk and d floats of AV partial per chunk (row_begin - 16 .. T-1:
+    16 rows of query halo), the statistics region rounded up to 64 floats."""
     rows = B * (T - row_begin + 16) * M
     up = lambda x: (x + 63) // 64 * 64
     for n in range(2, 65):
-        if 4 * (up(rows) + up(2 * n * rows) + n * rows * d) == nbytes:
+        if 4 * (up(2 * n * rows) + n * rows * d) == nbytes:
             return n
     raise AssertionError(f"{nbytes} bytes match no chunk count")
 

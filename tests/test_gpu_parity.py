@@ -543,12 +543,12 @@ def test_rows_split_at_full_size(row_begin):
 
 
 def _split_chunks(nbytes, B, T, M, d, row_begin):
-    """Key chunks of a split launch, read back from its workspace size (one normaliser, two
-    statistics floats and d partial floats per chunk for each (b, row, head) of rows
-    row_begin - 16 .. T-1, each region rounded up to 64 floats)."""
+    """Key chunks of a split launch, read back from its workspace size (two statistics floats
+    and d partial floats per chunk for each (b, row, head) of rows row_begin - 16 .. T-1, the
+    statistics region rounded up to 64 floats)."""
     rows = B * (T - row_begin + 16) * M
     up = lambda x: (x + 63) // 64 * 64
-    return next(n for n in range(2, 65) if 4 * (up(rows) + up(2 * n * rows) + n * rows * d) == nbytes)
+    return next(n for n in range(2, 65) if 4 * (up(2 * n * rows) + n * rows * d) == nbytes)
 
 
 @pytest.mark.parametrize("row_begin", [4095, 3900])

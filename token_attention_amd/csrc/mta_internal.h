@@ -37,7 +37,6 @@ struct Problem {
   int split_n = 1;
   float* part_stats = nullptr;   // partial buffers in the caller's workspace
   float* part_o = nullptr;
-  const float* split_shift = nullptr;
 };
 
 // Returns hipSuccess or the launch error; sets *unsupported when no kernel is

@@ -116,7 +116,7 @@ struct Args {
   int nr;              // rows of the partial buffers: T - row_begin + SPLIT_HPAD
   float* part_stats;   // [split][B][nr][M][2]: row maximum (log2 units) and row sum against it
   float* part_o;       // [split][B][nr][M][D]: AV partial
-  const float* shift;  // [B][nr][M]: global log2 normaliser (normalised schedules, SPLIT_PARTIAL)
+  int n_split;         // chunks whose statistics a normalised SPLIT_PARTIAL schedule combines
 };
 
 // KQ: a key-query convolution (TWO: after softmax); MIXPRE / MIXPOST: head mixing before /
@@ -360,14 +360,35 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   // statistics written by SPLIT_STATS: row maximum in log2 units and the row sum against it
   float stat_m[C::NQB], stat_l[C::NQB];
   auto split_row = [&](int gr) MTA_INLINE { return ((size_t)split_id * A.B + b) * A.nr + (gr - A.row_begin + SPLIT_HPAD); };
-  // normalised schedules in SPLIT_PARTIAL: the global normaliser of every tile row
+  // normalised schedules in SPLIT_PARTIAL: the global log2 normaliser of every tile row,
+  // m + log2(sum_c 2^(m_c - m) l_c) over the statistics every chunk wrote for that row
+  // (loaded 8 chunks at a time, combined with a running maximum)
   auto load_shift = [&](float (&sh)[C::NQB]) MTA_INLINE {
+    const size_t per_split = (size_t)A.B * A.nr * M * 2;
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
       const int gr = row0 + qs0 + qb * 16 + lq;
-      sh[qb] = (gr >= 0 && gr < T_)
-                   ? A.shift[((size_t)b * A.nr + (gr - A.row_begin + SPLIT_HPAD)) * M + m_head]
-                   : 1e30f;
+      sh[qb] = 1e30f;
+      if (gr >= 0 && gr < T_) {
+        const float* st = A.part_stats + (((size_t)b * A.nr + (gr - A.row_begin + SPLIT_HPAD)) * M + m_head) * 2;
+        float mx = -1e30f, l = 0.0f;
+        for (int s0 = 0; s0 < A.n_split; s0 += 8) {
+          float mv[8], lv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const bool in = s0 + u < A.n_split;
+            mv[u] = in ? st[(size_t)(s0 + u) * per_split] : -1e30f;
+            lv[u] = in ? st[(size_t)(s0 + u) * per_split + 1] : 0.0f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float mn = fmaxf(mx, mv[u]);
+            l = l * exp2f(mx - mn) + lv[u] * exp2f(mv[u] - mn);
+            mx = mn;
+          }
+        }
+        if (l > 0.0f) sh[qb] = mx + log2f(l);
+      }
     }
   };
 
@@ -1483,7 +1504,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.nr = p.T - p.row_begin + SPLIT_HPAD;
   a.part_stats = p.part_stats;
   a.part_o = p.part_o;
-  a.shift = p.split_shift;
+  a.n_split = p.split_mode ? p.split_n : 1;
   if (p.split_mode && (p.split_keys <= 0 || p.split_keys % C::BK != 0)) return hipErrorInvalidValue;
   const long long blocks = (long long)n_bg * a.n_tiles * (p.split_mode ? p.split_n : 1);
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;

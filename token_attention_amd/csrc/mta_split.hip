@@ -10,8 +10,9 @@
 //     writing (reference, row sum, AV partial) per chunk; the output is
 //     sum_c 2^(m_c - m) AV_c / sum_c 2^(m_c - m) l_c;
 //   * weights that must be exact first (a convolution or mixing after softmax): a statistics
-//     pass per chunk, their combination into one log2 normaliser per (row, head), then a
-//     weighted pass per chunk whose AV partials simply add up.
+//     pass per chunk, then a weighted pass per chunk that first combines every chunk's
+//     statistics of its rows into one log2 normaliser per (row, head); its AV partials simply
+//     add up.
 // GroupNorm and the gate follow in the combining kernel.
 #include <algorithm>
 
@@ -22,6 +23,7 @@ namespace {
 
 constexpr int HPAD = kmajor::SPLIT_HPAD;
 constexpr int NSPLIT_MAX = 64;
+static_assert(NSPLIT_MAX <= 64, "the output combination holds one chunk per lane");
 constexpr int CUS = 256;                 // MI355X compute units; one fused workgroup fits per unit
 constexpr double WG_OVERHEAD = 0.04;     // fixed cost of a workgroup, relative to a whole row tile
 
@@ -68,7 +70,7 @@ SplitPlan split_plan(const Problem& p) {
 
 struct SplitLayout {
   size_t nr, rows;  // rows of the partial buffers; B * nr * M
-  size_t shift, stats, o, total;
+  size_t stats, o, total;
 };
 
 SplitLayout split_layout(const Problem& p, int n) {
@@ -76,8 +78,7 @@ SplitLayout split_layout(const Problem& p, int n) {
   l.nr = (size_t)(p.T - p.row_begin) + HPAD;
   l.rows = (size_t)p.B * l.nr * p.M;
   auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };
-  l.shift = 0;
-  l.stats = up(l.rows);
+  l.stats = 0;
   l.o = l.stats + up((size_t)n * l.rows * 2);
   l.total = (l.o + (size_t)n * l.rows * p.d) * sizeof(float);
   return l;
@@ -94,23 +95,6 @@ __global__ void split_fill_kernel(float* stats, size_t n) {
 
 // Partials of up to SBATCH chunks are loaded together so that their memory latencies overlap.
 constexpr int SBATCH = 8;
-
-// one log2 normaliser per (b, row, head): m + log2(sum_c 2^(m_c - m) l_c); one wave per entry,
-// lane s holding chunk s's statistics (at most 64 chunks)
-__global__ __launch_bounds__(256) void split_stats_kernel(const float* __restrict__ stats, float* __restrict__ shift,
-                                                         int nsplit, size_t rows) {
-  const int lane = threadIdx.x & 63;
-  const size_t x = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (x >= rows) return;
-  const bool in = lane < nsplit;
-  const float ms = in ? stats[((size_t)lane * rows + x) * 2] : -1e30f;
-  const float ls = in ? stats[((size_t)lane * rows + x) * 2 + 1] : 0.0f;
-  float m = ms;
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float l = in ? ls * exp2f(ms - m) : 0.0f;
-  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-  if (lane == 0) shift[x] = l > 0.0f ? m + log2f(l) : 1e30f;
-}
 
 // one wave per (b, output row, head): combine the AV partials, GroupNorm + gate, write out.
 // Lane s holds chunk s's statistics (at most 64 chunks); the partials are loaded in batches.
@@ -233,7 +217,6 @@ hipError_t launch_rows_split(const Problem& p0, void* workspace, hipStream_t st,
   p.split_keys = plan.keys;
   p.part_stats = ws + l.stats;
   p.part_o = ws + l.o;
-  p.split_shift = ws + l.shift;
   hipError_t e;
   const size_t nstat = (size_t)plan.n * l.rows;
   hipLaunchKernelGGL(split_fill_kernel, dim3((unsigned)((nstat + 255) / 256)), dim3(256), 0, st, p.part_stats, nstat);
@@ -242,10 +225,6 @@ hipError_t launch_rows_split(const Problem& p0, void* workspace, hipStream_t st,
   if (normalised) {
     p.split_mode = kmajor::SPLIT_STATS;
     if ((e = launch_fused(p, st, unsupported)) != hipSuccess || *unsupported) return e;
-    static_assert(NSPLIT_MAX <= 64, "one chunk per lane");
-    hipLaunchKernelGGL(split_stats_kernel, dim3((unsigned)((l.rows + 3) / 4)), dim3(256), 0, st, p.part_stats,
-                       ws + l.shift, plan.n, l.rows);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   p.split_mode = kmajor::SPLIT_PARTIAL;
   if ((e = launch_fused(p, st, unsupported)) != hipSuccess || *unsupported) return e;
