@@ -429,20 +429,25 @@ def main():
         rows_rec[name + "_split"] = {"row_begin": rb, "ms": ms_split,
                                      "tokens_per_s": cfg.B * (cfg.T - rb) / (ms_split * 1e-3)}
         if name == "decode_step":
-            # the same step captured once in a HIP graph and replayed, as a serving loop would
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                part_split()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                part_split()
-            ms_graph = time_launches(graph.replay, args.steps, args.warmup, torch)
-            rows_rec[name + "_split_graph"] = {"row_begin": rb, "ms": ms_graph,
-                                               "tokens_per_s": cfg.B * (cfg.T - rb) / (ms_graph * 1e-3)}
-            del graph
+            # the same step captured once in a HIP graph and replayed, as a serving loop would;
+            # a capture error is recorded instead of ending the benchmark
+            try:
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    part_split()
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    part_split()
+                ms_graph = time_launches(graph.replay, args.steps, args.warmup, torch)
+                rows_rec[name + "_split_graph"] = {"row_begin": rb, "ms": ms_graph,
+                                                   "tokens_per_s": cfg.B * (cfg.T - rb) / (ms_graph * 1e-3)}
+                del graph
+            except RuntimeError as err:
+                torch.cuda.synchronize()
+                rows_rec[name + "_split_graph"] = {"row_begin": rb, "error": str(err)[:200]}
     result["rows_forward"] = rows_rec
     if not args.no_materialized:
         result["materialized"] = materialized_record(ms)
