@@ -34,8 +34,11 @@
  *               together they form one convolution over queries, keys and heads).
  *   Memory      every pointer is device memory owned by the caller. Nothing is
  *               retained after a call returns; buffers must stay alive until the
- *               queued work completes. q, k, v, out and workspace must be 16-byte
- *               aligned.
+ *               queued work completes. q, k, v, out, workspace and (with MTA_GN)
+ *               gn_gamma, gn_beta must be 16-byte aligned. The library cannot see the
+ *               extent of a parameter array: theta_kq, w_mix, gn_gamma and gn_beta must
+ *               hold the sizes given above for the flags passed, or the kernels read
+ *               past their end.
  *   Streams     stream is a hipStream_t (NULL = the default stream). Calls are
  *               asynchronous: they validate, enqueue and return. Launch errors are
  *               reported; faults during execution surface at the caller's sync.

@@ -57,6 +57,9 @@ int validate(const void* q, const void* k, const void* v, const float* theta, co
   }
   if ((flags & MTA_GN) && (!gamma || !beta))
     return fail(MTA_ERR_INVALID_ARG, "gn_gamma and gn_beta are required with MTA_GN");
+  // the GroupNorm epilogue reads gamma and beta four floats at a time
+  if ((flags & MTA_GN) && (!aligned16(gamma) || !aligned16(beta)))
+    return fail(MTA_ERR_INVALID_ARG, "gn_gamma and gn_beta must be 16-byte aligned");
   const bool fp32 = flags & MTA_FP32;
   if (fp32 ? !(d == 16 || d == 32 || d == 64) : !(d == 32 || d == 64 || d == 96 || d == 128))
     return fail(MTA_ERR_UNSUPPORTED, "head size d=%d is not built for %s", d, fp32 ? "fp32" : "bf16");

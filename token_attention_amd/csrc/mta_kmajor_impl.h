@@ -133,6 +133,13 @@ struct Cfg {
   static constexpr bool KQ = KQ_, TWO = TWO_, MIXPOST = MIXPOST_, MIXPRE = MIXPRE_, DUAL = DUAL_;
   static_assert(!DUAL || (KQ && TWO), "both convolutions use the two-phase schedule");
   static constexpr bool MIX = MIXPRE || MIXPOST;
+  // head mixing on MFMA (see mix_read): groups of four heads mixed after softmax only
+  // (before softmax the VALU mixing interleaved with the next tile's logits measured faster)
+  static constexpr bool XM = MIXPOST && !MIXPRE && CH == 4;
+  // mixing after softmax in groups of two heads without a convolution after softmax: one pass
+  // with an AV accumulator per (source head, head) pair of the group (the mixing weights and
+  // each source head's row sum are applied in the epilogue)
+  static constexpr bool PAIR = MIXPOST && !MIXPRE && !TWO && CH == 2 && !SPLIT;
   static constexpr int WPH = NW / CH;          // waves per head
   static constexpr bool PRIV = WPH == 1;       // a wave owns its head: private K/V staging
   static constexpr int TEAM = PRIV ? 64 : NT;  // threads staging one head set
@@ -342,11 +349,15 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   }
 
   f32x4 acc[C::NB][C::NQB];
+  f32x4 acc2[C::PAIR ? C::NB : 1][C::PAIR ? C::NQB : 1];  // the other head's weights times V of head hu
   auto clear_acc = [&]() MTA_INLINE {
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) acc[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        acc[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (C::PAIR) acc2[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
   };
   clear_acc();
 
@@ -523,6 +534,36 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   auto xslot = [&](int xb, int u, int qb) MTA_INLINE {
     return Sx + xb * C::SX_HALF + ((((size_t)u * C::WPH + slab) * C::NQB + qb) * 64 + lane) * C::XW;
   };
+  // Mixing on MFMA (C::XM, weights after softmax). The exchange holds, per (head, slab, query
+  // block, key block), a 16 x 16 fp16 tile stored query-major (a row of 16 keys per query; the
+  // two 8-key halves of a row swap places for queries 8..15, which keeps the 16-byte reads of
+  // a lane group on distinct banks). The mixed block of head hu is then one MFMA per pair of
+  // heads:
+  //   D[key][query] = sum over (head u, key k) of A[key][(u, k)] * B[(u, k)][query]
+  // with B the stacked tiles of the pair (lane group lg reads 8 keys of head 2m + lg/2) and A
+  // the constant operand w[hu][u] * delta(key, k) (zero for the wave's own head, whose fp32
+  // weights enter through the accumulator's initial value instead).
+  const int x_woff = lq * 16 + (((lg >> 1) ^ ((lq >> 3) & 1)) * 8) + (lg & 1) * 4;
+  const int x_roff = lq * 16 + (((lg & 1) ^ ((lq >> 3) & 1)) * 8);
+  auto xtile = [&](int xb, int u, int qb, int x) MTA_INLINE {
+    return Sx + xb * C::SX_HALF + ((((size_t)u * C::WPH + slab) * C::NQB + qb) * C::NKB + x) * 256;
+  };
+  constexpr int NPAIR = C::XM ? C::CH / 2 : 1;
+  f16x8 amx_pre[NPAIR], amx_post[NPAIR];
+  auto build_amix = [&](f16x8 (&dst)[NPAIR], const float* w, float wscale) MTA_INLINE {
+#pragma unroll
+    for (int m = 0; m < NPAIR; ++m) {
+      const int up = 2 * m + (lg >> 1);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int key = 8 * (lg & 1) + s;
+        float t = 0.0f;
+        if (key == lq && up != hu) t = w[((size_t)g * C::CH + hu) * C::CH + up] * wscale;
+        dst[m][s] = (_Float16)t;
+      }
+    }
+  };
+  if constexpr (C::XM) build_amix(amx_post, A.w_post, 1.0f);
   auto mix_write = [&](auto& arr, int xb, auto lb0c, auto lb1c) MTA_INLINE {
     constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value;
     if constexpr (C::CH > 1) {
@@ -532,19 +573,51 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         for (int lb = LB0; lb < LB1; ++lb) {
           const f16x4 h = {(_Float16)arr[lb][qb][0], (_Float16)arr[lb][qb][1], (_Float16)arr[lb][qb][2],
                            (_Float16)arr[lb][qb][3]};
-          *reinterpret_cast<f16x4*>(xslot(xb, hu, qb) + (lb - LB0) * 4) = h;
+          if constexpr (C::XM)
+            *reinterpret_cast<f16x4*>(xtile(xb, hu, qb, lb - LB0) + x_woff) = h;
+          else
+            *reinterpret_cast<f16x4*>(xslot(xb, hu, qb) + (lb - LB0) * 4) = h;
         }
       }
     }
   };
-  auto mix_read = [&](auto& arr, int xb, const float (&wrot)[C::CH], auto lb0c, auto lb1c) MTA_INLINE {
+  // Mixed blocks of arr: arr * w[hu][hu] + bias[qb] + the other heads' contributions. bias is
+  // folded into the accumulator's initial value on the MFMA path (used for the softmax offset).
+  auto mix_read_b = [&](auto& arr, int xb, const float (&wrot)[C::CH], const f16x8 (&amx)[NPAIR], const float* bias,
+                        auto lb0c, auto lb1c) MTA_INLINE {
     constexpr int LB0 = decltype(lb0c)::value, LB1 = decltype(lb1c)::value, XB = LB1 - LB0;
     static_assert(XB >= 1 && XB <= C::NKB, "exchange width");
+    if constexpr (C::XM) {
+      f16x8 bo[NPAIR][C::NQB][XB];
+#pragma unroll
+      for (int m = 0; m < NPAIR; ++m)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+          for (int x = 0; x < XB; ++x)
+            bo[m][qb][x] = *reinterpret_cast<const f16x8*>(xtile(xb, 2 * m + (lg >> 1), qb, x) + x_roff);
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+        for (int lb = LB0; lb < LB1; ++lb) {
+          f32x4 c;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[i] = bias ? __builtin_fmaf(arr[lb][qb][i], wrot[0], bias[qb]) : arr[lb][qb][i] * wrot[0];
+#pragma unroll
+          for (int m = 0; m < NPAIR; ++m) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(amx[m], bo[m][qb][lb - LB0], c, 0, 0, 0);
+          arr[lb][qb] = c;
+        }
+      }
+      return;
+    }
     if constexpr (C::CH == 1) {  // a group of one head: a scalar weight
 #pragma unroll
       for (int lb = LB0; lb < LB1; ++lb)
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) arr[lb][qb] = arr[lb][qb] * wrot[0];
+        for (int qb = 0; qb < C::NQB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            arr[lb][qb][i] = bias ? __builtin_fmaf(arr[lb][qb][i], wrot[0], bias[qb]) : arr[lb][qb][i] * wrot[0];
     } else {
       f16x4 o[C::CH - 1][C::NQB][XB];
 #pragma unroll
@@ -559,7 +632,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
         for (int lb = LB0; lb < LB1; ++lb) {
-          f32x4 x = arr[lb][qb] * wrot[0];
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = bias ? __builtin_fmaf(arr[lb][qb][i], wrot[0], bias[qb]) : arr[lb][qb][i] * wrot[0];
 #pragma unroll
           for (int k = 1; k < C::CH; ++k)
 #pragma unroll
@@ -569,15 +644,18 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
     }
   };
+  auto mix_read = [&](auto& arr, int xb, const float (&wrot)[C::CH], const f16x8 (&amx)[NPAIR], auto lb0c,
+                      auto lb1c) MTA_INLINE { mix_read_b(arr, xb, wrot, amx, nullptr, lb0c, lb1c); };
   int xbuf = 0;
-  auto mix_blocks = [&](auto& arr, const float (&wrot)[C::CH], auto lb0c, auto lb1c) MTA_INLINE {
+  auto mix_blocks = [&](auto& arr, const float (&wrot)[C::CH], const f16x8 (&amx)[NPAIR], auto lb0c,
+                        auto lb1c) MTA_INLINE {
     if constexpr (C::CH == 1) {
-      mix_read(arr, 0, wrot, lb0c, lb1c);
+      mix_read(arr, 0, wrot, amx, lb0c, lb1c);
       return;
     }
     mix_write(arr, xbuf, lb0c, lb1c);
     __syncthreads();
-    mix_read(arr, xbuf, wrot, lb0c, lb1c);
+    mix_read(arr, xbuf, wrot, amx, lb0c, lb1c);
     if constexpr (C::XBUFS == 2) xbuf ^= 1;
   };
 
@@ -638,6 +716,43 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
     }
   };
+  // Per-pair AV (C::PAIR): the wave's unnormalised bf16 weights go to the exchange buffer
+  // (lane-contiguous, 16 bytes per lane and 32-key chunk), and after one barrier the other
+  // head's weights for the same rows come back in the same B-operand layout; each V operand of
+  // head hu then feeds both products, P_hu V_hu into acc and P_other V_hu into acc2.
+  auto pair_av = [&](auto& wts) MTA_INLINE {
+    if constexpr (C::PAIR) {
+      bf16x8 bp[C::NC][C::NQB], bo[C::NC][C::NQB];
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          bp[c][qb] = pack_bf16(wts[2 * c][qb], wts[2 * c + 1][qb]);
+          *reinterpret_cast<bf16x8*>(xslot(xbuf, hu, qb) + c * 8) = bp[c][qb];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) bo[c][qb] = *reinterpret_cast<const bf16x8*>(xslot(xbuf, hu ^ 1, qb) + c * 8);
+      xbuf ^= 1;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const s16x4 lo = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 4 * lg, nb * 16, C::LDV, lane);
+          const s16x4 hi = vtr(Vs + (size_t)hu * C::BK * C::LDV, c * 32 + 16 + 4 * lg, nb * 16, C::LDV, lane);
+          s16x4 v8[2] = {lo, hi};
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(v8);
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            acc[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[c][qb], acc[nb][qb], 0, 0, 0);
+            acc2[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bo[c][qb], acc2[nb][qb], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
   typedef std::integral_constant<int, 0> I0;
   typedef std::integral_constant<int, 1> I1;
   typedef std::integral_constant<int, C::NKB> INKB;
@@ -658,7 +773,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     // mixed: SUM (row sums against the first-tile reference; if too large MAX then
     // SUMFIX), then NORM (exact weights, mixing, AV).
     enum { REF, MAX, FIXED, SUM, SUMFIX, NORM };
-    int pass = C::MIXPOST ? SUM : REF;
+    int pass = (C::MIXPOST && !C::PAIR) ? SUM : REF;
     float shift[C::NQB];  // NORM: m * ssc + log2(l) per row
     if (C::SPLIT && C::MIXPOST && A.split_mode == SPLIT_PARTIAL) {  // statistics of the whole key range given
       load_shift(shift);
@@ -691,7 +806,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       team_sync<C>();
       if constexpr (C::KQ) {
         logit_block(0);
-        if constexpr (mix_pre) mix_blocks(s, wpre, I0{}, I1{});
+        if constexpr (mix_pre) mix_blocks(s, wpre, amx_pre, I0{}, I1{});
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           const int gr = row0 + qs0 + qb * 16 + lq;
@@ -718,7 +833,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         }
 #pragma unroll
         for (int lb = INEW::value; lb < C::LB; ++lb) logit_block(lb);
-        if constexpr (mix_pre) mix_blocks(s, wpre, INEW{}, ILB{});
+        if constexpr (mix_pre) mix_blocks(s, wpre, amx_pre, INEW{}, ILB{});
         auto next_k = [&]() MTA_INLINE {  // after the middle barrier: K(kt + 1) to LDS, load K(kt + 2)
           if (with_av && tail_mix) next_v();
           if (more) {
@@ -801,8 +916,12 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
           }
         }
         if (with_av) {
-          if constexpr (C::MIXPOST) mix_blocks(xw, wpost, I0{}, INKB{});
-          av(xw, I0{});
+          if constexpr (C::PAIR) {
+            pair_av(xw);
+          } else {
+            if constexpr (C::MIXPOST) mix_blocks(xw, wpost, amx_post, I0{}, INKB{});
+            av(xw, I0{});
+          }
         }
         if constexpr (MIDBAR) {
           if (!tail_mix) team_sync<C>();  // TAIL
@@ -813,7 +932,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         }
       }
       if (pass == MAX) {
-        pass = C::MIXPOST ? SUMFIX : FIXED;
+        pass = (C::MIXPOST && !C::PAIR) ? SUMFIX : FIXED;
         clear_acc();
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) l_run[qb] = 0.0f;
@@ -889,7 +1008,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       const int j0 = kt * C::BK, kr = kt + 1;
 #pragma unroll
       for (int lb = 1; lb < C::LB; ++lb) logit_block_from(s, kbuf, C::BK, lb, 16);
-      if constexpr (mix_pre) mix_blocks(s, wpre, I1{}, ILB{});
+      if constexpr (mix_pre) mix_blocks(s, wpre, amx_pre, I1{}, ILB{});
       if constexpr (!XBAR) {
         if (sync_before_ring) team_sync<C>();
       }
@@ -1053,7 +1172,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
               }
             }
         }
-        if constexpr (C::MIXPOST) mix_blocks(cv, wpost, I0{}, INKB{});
+        if constexpr (C::MIXPOST) mix_blocks(cv, wpost, amx_post, I0{}, INKB{});
         av(cv, I0{});
       }
       if constexpr (XBAR && C::MIXPOST && C::CH > 1) __syncthreads();  // the exchange buffer is reused
@@ -1182,7 +1301,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         } else {
 #pragma unroll
           for (int lb = 1; lb < C::LB; ++lb) logit_block_from(nxt, kbuf, C::BK, lb, 16);
-          if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
+          if constexpr (mix_pre) mix_read(cur, pb, wpre, amx_pre, I1{}, ILB{});
           p1_sums(cur);
         }
         if constexpr (mix_pre) mix_write(nxt, pb ^ 1, I1{}, ILB{});
@@ -1193,7 +1312,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
         for (int lb = 1; lb < C::LB; ++lb) logit_block_from(nxt, kbuf, C::BK, lb, 16);
       }
-      if constexpr (mix_pre) mix_read(cur, pb, wpre, I1{}, ILB{});
+      if constexpr (mix_pre) mix_read(cur, pb, wpre, amx_pre, I1{}, ILB{});
       if (edge) {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
@@ -1270,6 +1389,11 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       const int j0 = kt * C::BK;
       return (j0 - 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (wrow_min < 0) || (wrow_min + C::QW > T_);
     };
+    // With mixing before softmax the mixing step already subtracts the normaliser (its
+    // accumulator starts at w[hu][hu] * x - shift), and the weights are exp2 of the result.
+    float nshift[C::NQB];
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) nshift[qb] = -shift[qb];
     auto weights_exp = [&](auto& arr, auto lb0c, auto lb1c) MTA_INLINE {
       constexpr int L0 = decltype(lb0c)::value, L1 = decltype(lb1c)::value;
 #pragma unroll
@@ -1277,7 +1401,8 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) arr[lb][qb][i] = fast_exp2(__builtin_fmaf(arr[lb][qb][i], sc, -shift[qb]));
+          for (int i = 0; i < 4; ++i)
+            arr[lb][qb][i] = fast_exp2(mix_pre ? arr[lb][qb][i] : __builtin_fmaf(arr[lb][qb][i], sc, -shift[qb]));
     };
     auto weights_store = [&](auto& arr, int kt, auto lb0c, auto lb1c) MTA_INLINE {
       constexpr int L0 = decltype(lb0c)::value, L1 = decltype(lb1c)::value;
@@ -1317,7 +1442,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     logit_block_from(s, Ks, C::BK, 0, 16 - C::BK);
     if constexpr (XBAR) mix_write(s, 0, I0{}, I1{});
     tsync();  // every wave has read the lead-in rows
-    if constexpr (mix_pre) mix_read(s, 0, wpre, I0{}, I1{});
+    if constexpr (mix_pre) mix_read_b(s, 0, wpre, amx_pre, nshift, I0{}, I1{});
     weights_to_ring(s, kt_lo, I0{}, I1{});
     commit_k(0);  // K(kt_lo)
     if (kt_lo + 1 < kt_hi) prefetch_k(j0lo + C::BK + 8);
@@ -1331,7 +1456,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       commit_k(0);  // K(kt_lo + 1)
       if (kt_lo + 2 < kt_hi) prefetch_k(j0lo + 2 * C::BK + 8);
     }
-    if constexpr (mix_pre) mix_read(s, 0, wpre, I1{}, ILB{});
+    if constexpr (mix_pre) mix_read_b(s, 0, wpre, amx_pre, nshift, I1{}, ILB{});
     weights_to_ring(s, kt_lo, I1{}, ILB{});
     tsync();
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
@@ -1373,13 +1498,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         if constexpr (C::MIXPOST) {
           mix_write(cv, 1, I0{}, INKB{});
           if constexpr (C::CH > 1) tsync();
-          mix_read(cv, 1, wpost, I0{}, INKB{});
+          mix_read(cv, 1, wpost, amx_post, I0{}, INKB{});
         }
         av(cv, I0{});
       };
       auto next_weights = [&]() MTA_INLINE {
         if (more) {
-          if constexpr (mix_pre) mix_read(s, 0, wpre, I1{}, ILB{});
+          if constexpr (mix_pre) mix_read_b(s, 0, wpre, amx_pre, nshift, I1{}, ILB{});
           weights_to_ring(s, kt + 1, I1{}, ILB{});
         }
       };
@@ -1424,6 +1549,18 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   }
 
   // ============================= epilogue =================================================
+  // per-pair accumulators: the other head's row sums of the same rows, through the exchange
+  // buffer the last tile did not use (its readers all passed that tile's barrier)
+  float l_oth[C::NQB];
+  if constexpr (C::PAIR) {
+    float* xl = reinterpret_cast<float*>(Sx + xbuf * C::SX_HALF);
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb)
+      if (lg == 0) xl[((hu * C::WPH + slab) * C::NQB + qb) * 16 + lq] = l_run[qb];
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) l_oth[qb] = xl[(((hu ^ 1) * C::WPH + slab) * C::NQB + qb) * 16 + lq];
+  }
   __bf16* ob_ = A.out + b * bstride;
 #pragma unroll
   for (int qb = 0; qb < C::NQB; ++qb) {
@@ -1431,8 +1568,16 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     const int gr = row0 + t;
     f32x4 o[C::NB];
     const float scl = (C::TWO || normalized) ? 1.0f : (l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f);
+    if constexpr (C::PAIR) {
+      // O = w[hu][hu] (P_hu V) / l_hu + w[hu][other] (P_other V) / l_other
+      const float s_own = wpost[0] * scl;
+      const float s_oth = l_oth[qb] > 0.0f ? wpost[1] / l_oth[qb] : 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[nb][qb] * scl;
+      for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[nb][qb] * s_own + acc2[nb][qb] * s_oth;
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) o[nb] = acc[nb][qb] * scl;
+    }
     float mean = 0.0f, inv = 1.0f;
     if (A.gn) {
       float sum = 0.0f;

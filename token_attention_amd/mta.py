@@ -121,6 +121,30 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+_SIDES = {None: 0, "pre": 1, "post": 1, "both": 2}
+
+
+def _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn):
+    """Check the parameter tensors against the sizes the library reads through their pointers
+    (the C ABI receives bare pointers and cannot see their extents): theta [sides, M, c_q, c_k],
+    w [sides, M/c_h, c_h, c_h] (sides = 2 for "both", the leading axis dropped for one side),
+    gamma and beta [M*d], all on the device of q."""
+    B, T, M, d = q.shape
+    want = {
+        "theta": (theta, _SIDES[kq] * M * c_q * c_k if kq else None),
+        "w": (w, _SIDES[mix] * M * c_h if mix else None),
+        "gamma": (gamma, M * d if gn else None),
+        "beta": (beta, M * d if gn else None),
+    }
+    for name, (t, n) in want.items():
+        if n is None or t is None:
+            continue
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}, got {t.device}")
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements; this placement reads {n}")
+
+
 def _common(q, k, v, out):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, M, d]")
@@ -141,6 +165,7 @@ def forward(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0
     """Fused forward (``mta_forward``). q, k, v: [B, T, M, d] bf16 or fp32 on the GPU."""
     out = _common(q, k, v, out)
     B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
     fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
     _check(lib().mta_forward(
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
@@ -156,6 +181,7 @@ def forward_rows(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float 
     rows of ``out`` before row_begin are left as they are."""
     out = _common(q, k, v, out)
     B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
     fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
     _check(lib().mta_forward_rows(
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
@@ -178,6 +204,7 @@ def forward_rows_split(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: 
     (decode steps, short chunks); rows of ``out`` before row_begin are left as they are."""
     out = _common(q, k, v, out)
     B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
     fp32 = q.dtype == torch.float32
     fl = placement_flags(kq, mix, gn, fp32)
     need = rows_split_workspace_bytes(B, T, M, d, row_begin=row_begin, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix,
@@ -205,6 +232,7 @@ def forward_materialized(q, k, v, theta=None, w=None, gamma=None, beta=None, lam
     """Unfused forward (``mta_forward_materialized``) with fp32 T x T maps in ``workspace``."""
     out = _common(q, k, v, out)
     B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
     need = materialized_workspace_bytes(B, T, M)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -233,6 +261,7 @@ def backward_materialized(q, k, v, theta=None, w=None, gamma=None, beta=None, la
     if dout.shape != q.shape or dout.dtype != q.dtype:
         raise ValueError("dout must match q in shape and dtype")
     B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
     fp32 = q.dtype == torch.float32
     fl = placement_flags(kq, mix, gn, fp32)
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q)}
