@@ -160,6 +160,14 @@ int mta_forward_rows_split(const void* q, const void* k, const void* v, const fl
 size_t mta_forward_rows_split_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k,
                                               int c_h, int row_begin, unsigned flags);
 
+/* The key split mta_forward_rows_split uses on a device with compute_units compute units
+ * (0: the current device, 256 when none can be queried): *n_chunks chunks of *chunk_keys keys
+ * (*n_chunks = 1 and *chunk_keys = T: no split). Host-only; returns MTA_OK or
+ * MTA_ERR_INVALID_ARG (invalid sizes, NULL outputs). */
+int mta_forward_rows_split_plan(int B, int T, int M, int d, int c_q, int c_k, int c_h,
+                                int row_begin, unsigned flags, int compute_units,
+                                int* n_chunks, int* chunk_keys);
+
 /* Workspace needed by mta_forward_materialized: two fp32 [B, M, T, LD] maps, LD = T
  * rounded up to a multiple of 4. Returns 0 for invalid sizes. */
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags);

@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports what include/mta.h
 declares, its flag values match the binding, and argument validation (host-only,
 ``mta_check_args``) returns the documented status codes."""
+import ctypes
 import os
 import re
 
@@ -193,3 +194,31 @@ def test_rows_split_outside_the_sequence_is_rejected(row_begin):
     st = mta.lib().mta_forward_rows_split(P, P + 0x100, P + 0x200, P, P, P, P, 1.0, P + 0x300, 1, 64, 4, 128, 3, 5,
                                           2, row_begin, mta.KQ_PRE | mta.MIX_POST | mta.GN, None, 0, None)
     assert st == mta.ERR_INVALID_ARG
+
+
+def test_rows_split_plan_reads_the_compute_unit_count():
+    # decode step at the T=4096 shape (16 row tiles of a four-head group, 16 rows each): with 256
+    # compute units a round holds 224 such workgroups, so 13 chunks of 320 keys fill one round;
+    # with 128 units (112 per round) 7 chunks of 640 keys do; with 64 units (56 per round) two
+    # rounds of 7 chunks cost less than one round of 3 chunks of 1408 keys
+    kw = dict(c_q=4, c_k=9, c_h=4, kq="post", mix="pre", gn=True)
+    assert ta.rows_split_plan(2, 4096, 32, 128, row_begin=4095, compute_units=256, **kw) == (13, 320)
+    assert ta.rows_split_plan(2, 4096, 32, 128, row_begin=4095, compute_units=128, **kw) == (7, 640)
+    assert ta.rows_split_plan(2, 4096, 32, 128, row_begin=4095, compute_units=64, **kw) == (7, 640)
+    # as many row tiles as compute units: no split
+    assert ta.rows_split_plan(2, 4096, 32, 128, row_begin=0, compute_units=256, **kw) == (1, 4096)
+    # the workspace query and the launch plan on the current device (256 units when none is
+    # present): the query's chunk count is the plan's
+    n, _ = ta.rows_split_plan(2, 4096, 32, 128, row_begin=4095, **kw)
+    assert _split_chunks(ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=4095, **kw),
+                         2, 4096, 32, 128, 4095) == n
+
+
+def test_rows_split_plan_rejects_bad_arguments():
+    n, keys = ctypes.c_int(0), ctypes.c_int(0)
+    lib = mta.lib()
+    assert lib.mta_forward_rows_split_plan(1, 64, 4, 128, 3, 5, 2, 64, mta.KQ_PRE, 0, ctypes.byref(n),
+                                           ctypes.byref(keys)) == mta.ERR_INVALID_ARG
+    assert lib.mta_forward_rows_split_plan(1, 64, 4, 128, 3, 5, 2, 0, mta.KQ_PRE, -1, ctypes.byref(n),
+                                           ctypes.byref(keys)) == mta.ERR_INVALID_ARG
+    assert lib.mta_forward_rows_split_plan(1, 64, 4, 128, 3, 5, 2, 0, mta.KQ_PRE, 0, None, None) == mta.ERR_INVALID_ARG

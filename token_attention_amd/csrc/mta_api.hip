@@ -195,6 +195,22 @@ int mta_forward_rows_split(const void* q, const void* k, const void* v, const fl
   return hip_status(e, "mta_forward_rows_split launch");
 }
 
+int mta_forward_rows_split_plan(int B, int T, int M, int d, int c_q, int c_k, int c_h, int row_begin, unsigned flags,
+                                int compute_units, int* n_chunks, int* chunk_keys) {
+  mta::Problem p{};
+  if (!n_chunks || !chunk_keys) return fail(MTA_ERR_INVALID_ARG, "n_chunks and chunk_keys must not be NULL");
+  if (!sizes_problem(B, T, M, d, c_q, c_k, c_h, flags, &p))
+    return fail(MTA_ERR_INVALID_ARG, "invalid sizes or flags");
+  if (row_begin < 0 || row_begin >= T)
+    return fail(MTA_ERR_INVALID_ARG, "row_begin=%d must lie in [0, T=%d)", row_begin, T);
+  if (compute_units < 0) return fail(MTA_ERR_INVALID_ARG, "compute_units must be >= 0");
+  p.row_begin = row_begin;
+  const mta::SplitPlan plan = mta::split_plan(p, compute_units ? compute_units : mta::device_compute_units());
+  *n_chunks = plan.n;
+  *chunk_keys = plan.n > 1 ? plan.keys : T;
+  return ok();
+}
+
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags) {
   (void)flags;
   return mta::materialized_workspace_bytes(B, T, M);

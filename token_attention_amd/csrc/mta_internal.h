@@ -47,6 +47,13 @@ bool fused_supported(const Problem& p);
 // Output rows row_begin .. T-1 with the key range split over workgroups (few row tiles: a
 // decode step or a short chunk); falls back to launch_fused when splitting does not pay.
 size_t rows_split_workspace_bytes(const Problem& p);
+// The key-split plan of a row range on a device with `cus` compute units: n chunks of `keys`
+// keys each (n = 1: no split), and the current device's compute-unit count the launches use.
+struct SplitPlan {
+  int n, keys;
+};
+SplitPlan split_plan(const Problem& p, int cus);
+int device_compute_units();
 hipError_t launch_rows_split(const Problem& p, void* workspace, hipStream_t stream, bool* unsupported);
 
 size_t materialized_workspace_bytes(int B, int T, int M);

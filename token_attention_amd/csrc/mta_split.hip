@@ -15,31 +15,52 @@
 //     add up.
 // GroupNorm and the gate follow in the combining kernel.
 #include <algorithm>
+#include <atomic>
 
 #include "mta_kmajor_impl.h"
 
 namespace mta {
+
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount), read once per
+// device; 256 (MI355X) when no device can be queried, so that size queries still answer on a
+// host without a GPU. The workspace-size query and the launch read the same value.
+int device_compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 namespace {
 
 constexpr int HPAD = kmajor::SPLIT_HPAD;
 constexpr int NSPLIT_MAX = 64;
 static_assert(NSPLIT_MAX <= 64, "the output combination holds one chunk per lane");
-constexpr int CUS = 256;                 // MI355X compute units; one fused workgroup fits per unit
 constexpr double WG_OVERHEAD = 0.04;     // fixed cost of a workgroup, relative to a whole row tile
 
-struct SplitPlan {
-  int n, keys;
-};
+}  // namespace
 
 // Number of key chunks, when the row tiles alone leave compute units idle: workgroups run in
-// rounds of CUS, each costing the fixed overhead plus its share of the keys; the plan minimises
+// rounds of cus (one fused workgroup fits per compute unit), each costing the fixed overhead
+// plus its share of the keys; the plan minimises
 // rounds * (overhead + 1/n) (chunks are whole multiples of 64 keys). 16-row tiles of a group of
 // four heads (four waves whose LDS fills a compute unit) count a round as 7/8 of the units:
-// at exactly CUS such workgroups a launch took longer than at 13/16 of them (T=4096 decode
+// at exactly one such workgroup per unit a launch took longer than at 13/16 of that (T=4096 decode
 // step: 16 chunks of 256 keys 76 us, 13 chunks of 320 keys 64 us). A decode step at T=4096
-// with 16 row tiles of a four-head group gets 13 chunks of 320 keys, a 512-row chunk 5 chunks
-// of 832 keys.
-SplitPlan split_plan(const Problem& p) {
+// with 16 row tiles of a four-head group gets 13 chunks of 320 keys (256 compute units), a
+// 512-row chunk 5 chunks of 832 keys.
+SplitPlan split_plan(const Problem& p, int cus) {
   if (p.fp32) return {1, 0};
   // row tiles of the unsplit kernel and of the split instantiations (16-row tiles for a range
   // that fits one, such as a decode step)
@@ -50,11 +71,12 @@ SplitPlan split_plan(const Problem& p) {
   const long long tiles = groups * ((rows + r_out - 1) / r_out);
   const long long tiles_split = groups * ((rows + r_split - 1) / r_split);
   // enough row tiles to occupy every compute unit: the unsplit kernel (heaviest tiles first)
-  if (tiles >= CUS) return {1, 0};
+  if (cus <= 0) cus = 1;
+  if (tiles >= cus) return {1, 0};
   SplitPlan best{1, 0};
-  double best_cost = (double)((tiles + CUS - 1) / CUS) * (WG_OVERHEAD + 1.0);
+  double best_cost = (double)((tiles + cus - 1) / cus) * (WG_OVERHEAD + 1.0);
   const int nmax = std::min(NSPLIT_MAX, (p.T + 63) / 64);
-  const long long per_round = (kmajor::short_rows(p) && ch >= 4) ? CUS - CUS / 8 : CUS;
+  const long long per_round = (kmajor::short_rows(p) && ch >= 4) ? cus - cus / 8 : cus;
   for (int n = 2; n <= nmax; ++n) {
     const int keys = ((p.T + n - 1) / n + 63) / 64 * 64;
     const int neff = (p.T + keys - 1) / keys;
@@ -67,6 +89,8 @@ SplitPlan split_plan(const Problem& p) {
   }
   return best.n <= 1 ? SplitPlan{1, 0} : best;
 }
+
+namespace {
 
 struct SplitLayout {
   size_t nr, rows;  // rows of the partial buffers; B * nr * M
@@ -198,13 +222,13 @@ hipError_t launch_out(const Problem& p, const SplitLayout& l, float* ws, int n, 
 }  // namespace
 
 size_t rows_split_workspace_bytes(const Problem& p) {
-  const SplitPlan plan = split_plan(p);
+  const SplitPlan plan = split_plan(p, device_compute_units());
   return plan.n <= 1 ? 0 : split_layout(p, plan.n).total;
 }
 
 hipError_t launch_rows_split(const Problem& p0, void* workspace, hipStream_t st, bool* unsupported) {
   *unsupported = false;
-  const SplitPlan plan = split_plan(p0);
+  const SplitPlan plan = split_plan(p0, device_compute_units());
   if (plan.n <= 1) return launch_fused(p0, st, unsupported);
   if (!fused_supported(p0)) {
     *unsupported = true;

@@ -28,7 +28,7 @@ EXPORTED = [
     "mta_forward", "mta_forward_rows", "mta_forward_materialized", "mta_materialized_workspace_bytes",
     "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
     "mta_backward_materialized", "mta_backward_workspace_bytes", "mta_forward_rows_split",
-    "mta_forward_rows_split_workspace_bytes",
+    "mta_forward_rows_split_workspace_bytes", "mta_forward_rows_split_plan",
 ]
 
 _lib = None
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.mta_forward_rows_split.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 8 + \
             [u, vp, ctypes.c_size_t, vp]
         L.mta_forward_rows_split.restype = i
+        L.mta_forward_rows_split_plan.argtypes = [i] * 8 + [u, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.mta_forward_rows_split_plan.restype = i
         L.mta_forward_rows_split_workspace_bytes.argtypes = [i] * 8 + [u]
         L.mta_forward_rows_split_workspace_bytes.restype = ctypes.c_size_t
         L.mta_forward_materialized.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 7 + \
@@ -195,6 +197,18 @@ def rows_split_workspace_bytes(B: int, T: int, M: int, d: int, *, row_begin: int
                                fp32: bool = False) -> int:
     return int(lib().mta_forward_rows_split_workspace_bytes(B, T, M, d, c_q, c_k, c_h, int(row_begin),
                                                             placement_flags(kq, mix, gn, fp32)))
+
+
+def rows_split_plan(B: int, T: int, M: int, d: int, *, row_begin: int, c_q: int = 1, c_k: int = 1, c_h: int = 1,
+                    kq: Optional[str] = None, mix: Optional[str] = None, gn: bool = False, fp32: bool = False,
+                    compute_units: int = 0):
+    """``mta_forward_rows_split_plan``: (number of key chunks, keys per chunk) of the split on a
+    device with ``compute_units`` compute units (0: the current device)."""
+    n, keys = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().mta_forward_rows_split_plan(B, T, M, d, c_q, c_k, c_h, int(row_begin),
+                                             placement_flags(kq, mix, gn, fp32), int(compute_units),
+                                             ctypes.byref(n), ctypes.byref(keys)))
+    return n.value, keys.value
 
 
 def forward_rows_split(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, row_begin: int,
