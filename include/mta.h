@@ -155,6 +155,26 @@ int mta_forward_rows_split(const void* q, const void* k, const void* v, const fl
                            int c_h, int row_begin, unsigned flags, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * mta_forward_rows_split_noalloc: mta_forward_rows_split for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The partial results live in a scratch array inside the library instead of a
+ * caller workspace: MTA_NOALLOC_SCRATCH_BYTES per device, held until the process ends. A row
+ * range whose mta_forward_rows_split_workspace_bytes() exceeds that size returns
+ * MTA_ERR_WORKSPACE (a decode step at B=2, T=4096, M=32, d=128 needs about 7 MiB). Every call
+ * on a device shares that device's scratch, so calls that overlap on one GPU (other streams,
+ * other threads) race; calls queued on one stream are ordered. The first call on a device
+ * looks up the scratch address with that device current (the caller's current device must be
+ * the one its stream and tensors belong to). Arguments, results and other errors as for
+ * mta_forward_rows_split; allocates nothing and copies nothing.
+ */
+#define MTA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mta_forward_rows_split_noalloc(const void* q, const void* k, const void* v,
+                                   const float* theta_kq, const float* w_mix,
+                                   const float* gn_gamma, const float* gn_beta, float lambda,
+                                   void* out, int B, int T, int M, int d, int c_q, int c_k,
+                                   int c_h, int row_begin, unsigned flags, void* stream);
+
 /* Workspace needed by mta_forward_rows_split (0: no splitting for this shape, or invalid
  * sizes): partial statistics and AV sums of up to 64 key chunks for rows row_begin-16 .. T-1. */
 size_t mta_forward_rows_split_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k,

@@ -222,3 +222,21 @@ def test_rows_split_plan_rejects_bad_arguments():
     assert lib.mta_forward_rows_split_plan(1, 64, 4, 128, 3, 5, 2, 0, mta.KQ_PRE, -1, ctypes.byref(n),
                                            ctypes.byref(keys)) == mta.ERR_INVALID_ARG
     assert lib.mta_forward_rows_split_plan(1, 64, 4, 128, 3, 5, 2, 0, mta.KQ_PRE, 0, None, None) == mta.ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_a_range_beyond_its_scratch():
+    # a 512-row chunk at the T=4096 shape needs about 86 MB of partial results, more than the
+    # library's scratch: refused before any GPU work
+    need = ta.rows_split_workspace_bytes(2, 4096, 32, 128, row_begin=3584, c_q=4, c_k=9, c_h=4, kq="post",
+                                         mix="pre", gn=True)
+    assert need > mta.NOALLOC_SCRATCH_BYTES
+    st = mta.lib().mta_forward_rows_split_noalloc(P, P + 0x100, P + 0x200, P, P, P, P, 1.0, P + 0x300, 2, 4096, 32,
+                                                  128, 4, 9, 4, 3584, mta.KQ_POST | mta.MIX_PRE | mta.GN, None)
+    assert st == mta.ERR_WORKSPACE
+    assert "scratch" in mta.last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MTA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mta.NOALLOC_SCRATCH_BYTES

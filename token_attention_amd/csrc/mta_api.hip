@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/mta.h"
@@ -209,6 +210,63 @@ int mta_forward_rows_split_plan(int B, int T, int M, int d, int c_q, int c_k, in
   *n_chunks = plan.n;
   *chunk_keys = plan.n > 1 ? plan.keys : T;
   return ok();
+}
+
+// ---- split row ranges without a caller workspace ---------------------------------------------
+// For callers that cannot allocate: the partial results of mta_forward_rows_split_noalloc live
+// in `scratch`, a file-scope device array of MTA_NOALLOC_SCRATCH_BYTES. Each device that runs
+// the library holds its own copy until the process ends. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the device symbol): the device
+// address is looked up once per device with hipGetSymbolAddress, with that device current, and
+// only that address reaches the kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[MTA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices];
+
+// Device address of the current device's scratch array; MTA_OK or an error status.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MTA_ERR_UNSUPPORTED, "device %d: scratch is kept for devices 0..%d", dev, kScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MTA_OK;
+}
+
+}  // namespace
+
+int mta_forward_rows_split_noalloc(const void* q, const void* k, const void* v, const float* theta_kq,
+                                   const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
+                                   void* out, int B, int T, int M, int d, int c_q, int c_k, int c_h, int row_begin,
+                                   unsigned flags, void* stream) {
+  mta::Problem p;
+  int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, out, B, T, M, d, c_q, c_k, c_h, flags, &p);
+  if (st != MTA_OK) return st;
+  if (row_begin < 0 || row_begin >= T)
+    return fail(MTA_ERR_INVALID_ARG, "row_begin=%d must lie in [0, T=%d)", row_begin, T);
+  p.row_begin = row_begin;
+  const size_t need = mta::rows_split_workspace_bytes(p);
+  if (need > (size_t)MTA_NOALLOC_SCRATCH_BYTES)
+    return fail(MTA_ERR_WORKSPACE, "this row range needs %zu bytes of partial results; the library's scratch holds %zu",
+                need, (size_t)MTA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_address(&ws)) != MTA_OK) return st;
+  bool unsupported = false;
+  const hipError_t e = mta::launch_rows_split(p, ws, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no fused kernel for this shape");
+  return hip_status(e, "mta_forward_rows_split_noalloc launch");
 }
 
 size_t mta_materialized_workspace_bytes(int B, int T, int M, unsigned flags) {

@@ -28,8 +28,10 @@ EXPORTED = [
     "mta_forward", "mta_forward_rows", "mta_forward_materialized", "mta_materialized_workspace_bytes",
     "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
     "mta_backward_materialized", "mta_backward_workspace_bytes", "mta_forward_rows_split",
-    "mta_forward_rows_split_workspace_bytes", "mta_forward_rows_split_plan",
+    "mta_forward_rows_split_workspace_bytes", "mta_forward_rows_split_plan", "mta_forward_rows_split_noalloc",
 ]
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MTA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -59,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.mta_forward_rows_split.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 8 + \
             [u, vp, ctypes.c_size_t, vp]
         L.mta_forward_rows_split.restype = i
+        L.mta_forward_rows_split_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp] + [i] * 8 + \
+            [u, vp]
+        L.mta_forward_rows_split_noalloc.restype = i
         L.mta_forward_rows_split_plan.argtypes = [i] * 8 + [u, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         L.mta_forward_rows_split_plan.restype = i
         L.mta_forward_rows_split_workspace_bytes.argtypes = [i] * 8 + [u]
@@ -232,6 +237,26 @@ def forward_rows_split(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: 
         _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
         float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, int(row_begin), fl, ws_ptr, ws_bytes,
         _stream(stream)))
+    return out
+
+
+def forward_rows_split_noalloc(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *,
+                               row_begin: int, out, c_q: int = 1, c_k: int = 1, c_h: int = 1,
+                               kq: Optional[str] = None, mix: Optional[str] = None, gn: bool = False,
+                               stream=None) -> torch.Tensor:
+    """``mta_forward_rows_split_noalloc``: ``forward_rows_split`` with the partial results in the
+    library's own device scratch (no workspace, no allocation; ``out`` must be given). Calls that
+    overlap on one GPU share that scratch and race."""
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
+    fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
+    _check(lib().mta_forward_rows_split_noalloc(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(out, "out"), B, T, M, d, c_q, c_k, c_h, int(row_begin), fl, _stream(stream)))
     return out
 
 
