@@ -158,15 +158,39 @@ def launch_spread(fn, reps, torch):
     return t[0], t[len(t) // 2]
 
 
-def cpu_model() -> str:
+def cpu_info() -> dict:
+    """Host CPU as ``lscpu`` reports it (model name, sockets, physical cores, threads), with
+    /proc/cpuinfo's model name when lscpu is not available."""
+    import subprocess
+    info = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in txt.splitlines():
+            key, _, val = line.partition(":")
+            info[key.strip()] = val.strip()
+    except (OSError, subprocess.SubprocessError):
         pass
-    return "unknown"
+    model = info.get("Model name")
+    if not model:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+
+    def num(key):
+        try:
+            return int(info.get(key, ""))
+        except ValueError:
+            return None
+    sockets, per_socket, tpc = num("Socket(s)"), num("Core(s) per socket"), num("Thread(s) per core")
+    return {"cpu_model": model or "unknown",
+            "physical_cores": sockets * per_socket if sockets and per_socket else None,
+            "threads_per_core": tpc, "logical_cpus": num("CPU(s)") or os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def cpu_baseline(cfg, inp, n_rows: int):
@@ -189,14 +213,15 @@ def cpu_baseline(cfg, inp, n_rows: int):
     n_tok = len(batches) * (cfg.T if rows is None else len(rows))
     what = (f"the whole workload ({cfg.B} x {cfg.T} query rows, all {cfg.M} heads)" if rows is None else
             f"{len(rows)} seeded random query rows of batch 0, all {cfg.M} heads, T={cfg.T}")
-    return {
+    rec = {
         "value": n_tok / dt,
         "unit": "tokens/s",
         "cores": oracle.max_threads(),
-        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{what} (fp64 C++ oracle, OpenMP); {dt:.1f} s",
     }
+    rec.update(cpu_info())
+    return rec
 
 
 def cpu_single_thread():
@@ -449,6 +474,34 @@ def main():
                 torch.cuda.synchronize()
                 rows_rec[name + "_split_graph"] = {"row_begin": rb, "error": str(err)[:200]}
     result["rows_forward"] = rows_rec
+    # the other bf16 workloads at their full shapes: the fused layer, and the library's plain
+    # causal attention at the same shape (the degenerate workload's kernels are identities, so
+    # its ratio is the overhead of the convolution and mixing machinery itself)
+    result["workloads"] = {}
+    for idx in (1, 2, 3):
+        wcfg = mta_inputs.config(idx)
+        _, wd = gpu_inputs(wcfg, torch)
+        wout = torch.empty_like(wd["q"])
+        wkw = dict(c_q=wcfg.c_q, c_k=wcfg.c_k, c_h=wcfg.c_h, kq=wcfg.kq, mix=wcfg.mix, gn=wcfg.gn)
+
+        def wfused(wd=wd, wout=wout, wkw=wkw):
+            ta.forward(wd["q"], wd["k"], wd["v"], wd["theta"], wd["w"], wd["gamma"], wd["beta"], wd["lam"], out=wout,
+                       **wkw)
+
+        def wplain(wd=wd, wout=wout):
+            ta.attention_plain(wd["q"], wd["k"], wd["v"], out=wout)
+        ms_w = time_launches(wfused, args.steps, args.warmup, torch)
+        ms_p = time_launches(wplain, args.steps, args.warmup, torch)
+        wn_c = wcfg.T * (wcfg.T + 1) // 2
+        tf = flops(wcfg) / (ms_w * 1e-3) / 1e12
+        result["workloads"][wcfg.name] = {
+            "shape": f"B={wcfg.B} T={wcfg.T} M={wcfg.M} d={wcfg.d} c_q={wcfg.c_q} c_k={wcfg.c_k} c_h={wcfg.c_h}, "
+                     f"conv {wcfg.kq} softmax, mixing {wcfg.mix} softmax, GroupNorm {'on' if wcfg.gn else 'off'}",
+            "ms": ms_w, "tokens_per_s": wcfg.B * wcfg.T / (ms_w * 1e-3), "tflops": tf,
+            "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS, "flops_per_call": flops(wcfg),
+            "plain_ms": ms_p, "plain_tflops": wcfg.B * wcfg.M * wn_c * 4 * wcfg.d / (ms_p * 1e-3) / 1e12,
+            "mta_slowdown_vs_plain": ms_w / ms_p}
+        del wd, wout
     if not args.no_materialized:
         result["materialized"] = materialized_record(ms)
         result["backward_materialized"] = backward_record(result["materialized"]["ms"])

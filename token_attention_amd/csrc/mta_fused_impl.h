@@ -1,4 +1,7 @@
-// Fused Multi-Token Attention forward for gfx950 (template implementation) (one launch, no T x T maps in HBM).
+// Fused Multi-Token Attention forward for fp32 tensors on gfx950 (template implementation; one
+// launch, no T x T maps in HBM). bf16 tensors run the key-major kernel of mta_kmajor_impl.h;
+// this template serves the fp32 head sizes 16, 32 and 64, with every product (logits,
+// Toeplitz convolution, AV) on the fp32 16x16x4 MFMA and fp32 operands in LDS.
 //
 // Method: page "Multi-Token Attention | Summary" (greeksharifa.github.io), §2 (logits,
 // causal softmax, AV), §3.1 (key-query convolution with Mask_0 / Mask_-inf), §3.2
@@ -11,9 +14,9 @@
 //
 // Two schedules, chosen at compile time:
 //  * one pass (no convolution, or convolution before softmax). Per key tile:
-//      logits of the tile plus a 16-column key halo (bf16 MFMA, fp32 accumulate)
-//      -> [mix before softmax, through LDS] -> Mask_0 -> fp16 in LDS
-//      -> c_q x c_k convolution as c_q banded-Toeplitz fp16 MFMAs per 16x16 block
+//      logits of the tile plus a 16-column key halo (fp32 MFMA)
+//      -> [mix before softmax, through LDS] -> Mask_0 -> fp32 in LDS
+//      -> c_q x c_k convolution as c_q banded-Toeplitz MFMAs per 16x16 block
 //      -> Mask_-inf -> online softmax per (row, head)
 //      -> AV. With mixing after softmax every wave keeps c_h accumulators
 //         Acc[u'][v] = sum_j exp(s_u' - m_u') V_v (one per input head u' of its output

@@ -167,9 +167,12 @@ struct Cfg {
   static constexpr int XW = NKB * 4;           // exchange halves per lane and query block
   static constexpr size_t SX_HALF = (size_t)CH * R * BK;  // one exchange buffer (halves)
   static constexpr size_t KS_BYTES = (size_t)CH * KROWS * LDK * 2;
-  // double buffered; with both convolutions every two exchanges are already separated by
-  // a workgroup barrier (ring writes -> convolution reads), so one buffer suffices
-  static constexpr int XBUFS = DUAL ? 1 : 2;
+  // Exchange buffers: double buffered, unless a workgroup barrier already separates every two
+  // exchanges: with both convolutions (ring writes -> convolution reads), and in the one-pass
+  // convolution schedule with mixing after softmax only (the ring barrier of the next tile
+  // comes between one tile's exchange reads and the next tile's writes).
+  static constexpr bool ONEPASS_CONV = KQ && !TWO;
+  static constexpr int XBUFS = (DUAL || (ONEPASS_CONV && !MIXPRE)) ? 1 : 2;
   static constexpr size_t SX_BYTES = (MIX && CH > 1) ? XBUFS * SX_HALF * 2 : 0;  // one head: a scalar weight
   static constexpr size_t VS_BYTES = (size_t)CH * BK * LDV * 2;
   static constexpr size_t ZRING = (size_t)CH * ZROWS * LDZ;  // halves of one ring
@@ -179,7 +182,17 @@ struct Cfg {
   static constexpr size_t OFF_SX = OFF_KS + KS_BYTES;
   static constexpr size_t OFF_VS = OFF_SX + SX_BYTES;
   static constexpr size_t OFF_ZB = OFF_VS + VS_BYTES;
-  static constexpr size_t LDS_BYTES = OFF_ZB + ZB_BYTES;
+  // Exact centre tap of the convolution before softmax (one-pass schedule): a second ring holds,
+  // for the tile's own rows, the fp16 residual z - fp16(z) of every logit in the ring, and the
+  // convolution adds the centre tap times that residual (one more MFMA per output block), so
+  // the dominant term of the convolution sees the fp32 logit (error ~2^-22 |z| instead of the
+  // fp16 rounding, ~2^-12 |z|, which grows with the logit's magnitude). Built where it fits the
+  // LDS budget.
+  static constexpr size_t ZR_RING = (size_t)CH * R * LDZ;  // halves
+  static constexpr bool XC = ONEPASS_CONV && (OFF_ZB + ZB_BYTES + ZR_RING * 2 <= 160 * 1024);
+  static constexpr size_t OFF_ZR = OFF_ZB + ZB_BYTES;
+  static constexpr size_t ZR_BYTES = XC ? ZR_RING * 2 : 0;
+  static constexpr size_t LDS_BYTES = OFF_ZR + ZR_BYTES;
   // staging: 16-byte chunks per team member for one regular tile
   static constexpr int HEADS = PRIV ? 1 : CH;
   static constexpr int CHUNKS = HEADS * BK * (D / 8);  // 16-byte chunks of one regular tile
@@ -244,6 +257,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   _Float16* Sx = reinterpret_cast<_Float16*>(smem + C::OFF_SX);
   __bf16* Vs = reinterpret_cast<__bf16*>(smem + C::OFF_VS);
   _Float16* Zb = reinterpret_cast<_Float16*>(smem + C::OFF_ZB);
+  _Float16* Zr = reinterpret_cast<_Float16*>(smem + C::OFF_ZR);  // residual ring (C::XC)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -327,6 +341,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
     }
   };
+  // the centre tap alone (lag 0, key offset 0): out key n reads window key n + 8
+  f16x8 tzc;
+  if constexpr (C::XC) {
+    const float c = A.theta[(size_t)m_head * A.c_q * A.c_k + h0] * (!mix_pre ? A.qk_scale : 1.0f);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) tzc[s] = (_Float16)((8 * lg + s == lq + 8) ? c : 0.0f);
+  }
   if constexpr (C::KQ) {
     // before softmax the logit scale is folded in (unless the mixing weights carry it)
     toeplitz(tz, A.theta, ((!C::TWO || C::DUAL) && !mix_pre) ? A.qk_scale : 1.0f);
@@ -441,19 +462,47 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   constexpr bool K2BUF = C::TWO;
   static_assert(!K2BUF || C::BK * C::LDK <= C::BK * C::LDV, "second K buffer fits the V region");
   __bf16* const Ks2 = Vs;
-  int goff[C::CPT], koff[C::CPT], voff[C::CPT], koff2[K2BUF ? C::CPT : 1];
+  // When the team's chunks advance by whole rows of one head (UNIFORM: the team covers a whole
+  // number of rows, and a head's tile a whole number of team rounds), chunk x of a member is
+  // its chunk 0 moved by a fixed number of rows and heads: one base offset per member plus
+  // per-x constants (and a wave-uniform global row step), instead of CPT offsets per array.
+  constexpr int PH = C::BK * (C::D / 8);  // chunks of one head's tile
+  constexpr bool UNIFORM = C::CHUNKS % C::TEAM == 0 && PH % C::TEAM == 0 && C::TEAM % (C::D / 8) == 0;
+  constexpr int NOFF = UNIFORM ? 1 : C::CPT;
+  int goff[NOFF], koff[NOFF], voff[NOFF], koff2[K2BUF ? NOFF : 1];
 #pragma unroll
-  for (int x = 0; x < C::CPT; ++x) {
+  for (int x = 0; x < NOFF; ++x) {
     // surplus team members of the last round repeat the last chunk (identical writes)
     const int c = min(trank + x * C::TEAM, C::CHUNKS - 1);
-    const int u = thead + c / (C::BK * (C::D / 8));
-    const int rem = c % (C::BK * (C::D / 8));
+    const int u = thead + c / PH;
+    const int rem = c % PH;
     const int r = rem / (C::D / 8), cc = rem % (C::D / 8);
     goff[x] = ((r * M + g * C::CH + u) * C::D + cc * 8) * 2;
     koff[x] = (u * C::KROWS + r) * C::LDK + cc * 8;
     voff[x] = (u * C::BK + r) * C::LDV + cc * 8;
     if constexpr (K2BUF) koff2[x] = (u * C::BK + r) * C::LDK + cc * 8;
   }
+  // chunk x of a UNIFORM team: du heads and dr rows after chunk 0
+  auto x_du = [](int x) { return UNIFORM ? x / (PH / C::TEAM) : 0; };
+  auto x_dr = [](int x) { return UNIFORM ? (x % (PH / C::TEAM)) * (C::TEAM / (C::D / 8)) : 0; };
+  auto g_off = [&](int x) MTA_INLINE {
+    if constexpr (UNIFORM) return goff[0];
+    else return goff[x];
+  };
+  // the uniform part of chunk x's global byte offset (a scalar operand of the load)
+  auto g_soff = [&](int x) MTA_INLINE { return UNIFORM ? (x_dr(x) * M + x_du(x)) * C::D * 2 : 0; };
+  auto k_off = [&](int x) MTA_INLINE {
+    if constexpr (UNIFORM) return koff[0] + (x_du(x) * C::KROWS + x_dr(x)) * C::LDK;
+    else return koff[x];
+  };
+  auto v_off = [&](int x) MTA_INLINE {
+    if constexpr (UNIFORM) return voff[0] + (x_du(x) * C::BK + x_dr(x)) * C::LDV;
+    else return voff[x];
+  };
+  auto k2_off = [&](int x) MTA_INLINE {
+    if constexpr (UNIFORM) return koff2[0] + (x_du(x) * C::BK + x_dr(x)) * C::LDK;
+    else return koff2[x];
+  };
   // buffer resource over rows jfirst .. T-1 of a K or V tensor of batch b
   auto tile_rsrc = [&](const __bf16* base, int jfirst) MTA_INLINE {
     const int rows = max(T_ - jfirst, 0);
@@ -465,13 +514,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     const auto rk = tile_rsrc(kb_, kfirst);
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x)
-      pk[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, goff[x], 0, 0));
+      pk[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, g_off(x), g_soff(x), 0));
   };
   auto prefetch_v = [&](int j0) MTA_INLINE {
     const auto rv = tile_rsrc(vb_, j0);
 #pragma unroll
     for (int x = 0; x < C::CPT; ++x)
-      pv[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, goff[x], 0, 0));
+      pv[x] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, g_off(x), g_soff(x), 0));
   };
   auto prefetch = [&](int kfirst, int j0, bool with_v) MTA_INLINE {
     prefetch_k(kfirst);
@@ -479,17 +528,17 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   };
   auto commit_k = [&](int lrow) MTA_INLINE {
 #pragma unroll
-    for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks + koff[x] + lrow * C::LDK) = pk[x];
+    for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks + k_off(x) + lrow * C::LDK) = pk[x];
   };
   auto commit_k2 = [&]() MTA_INLINE {  // the second K buffer of phase 1
     if constexpr (K2BUF) {
 #pragma unroll
-      for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks2 + koff2[x]) = pk[x];
+      for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Ks2 + k2_off(x)) = pk[x];
     }
   };
   auto commit_v = [&]() MTA_INLINE {
 #pragma unroll
-    for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Vs + voff[x]) = pv[x];
+    for (int x = 0; x < C::CPT; ++x) *reinterpret_cast<u32x4*>(Vs + v_off(x)) = pv[x];
   };
   auto commit = [&](int lrow, bool with_v) MTA_INLINE {
     commit_k(lrow);
@@ -664,8 +713,9 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
   f32x4 cv[C::KQ ? C::NKB : 1][C::NQB];
   _Float16* const Zw = Zb + (C::DUAL ? C::ZRING : 0);  // ring of the weights (both convolutions)
   auto ring_col = [&](int kt, int lb) MTA_INLINE { return ((kt * C::NKB + lb) % C::RB) * 16; };
+  // res_c: std::true_type adds the centre tap times the residual ring (C::XC)
   auto convolve_ring = [&](const _Float16* ring, const f16x8 (&tzs)[C::KQ ? C::CQM : 1],
-                           f32x4 (&res)[C::KQ ? C::NKB : 1][C::NQB], int kt) MTA_INLINE {
+                           f32x4 (&res)[C::KQ ? C::NKB : 1][C::NQB], int kt, auto res_c) MTA_INLINE {
 #pragma unroll
     for (int ob = 0; ob < C::NKB; ++ob)
 #pragma unroll
@@ -674,6 +724,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
     for (int ob = 0; ob < C::NKB; ++ob) {
       // slots of lane group lg: window keys 8*lg .. 8*lg+7 = block ob (lg < 2) or ob+1
       const int col = ring_col(kt, ob + (lg >> 1)) + (lg & 1) * 8;
+      if constexpr (decltype(res_c)::value) {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const f16x8 br = *reinterpret_cast<const f16x8*>(Zr + ((size_t)hu * C::R + qs0 + qb * 16 + lq) * C::LDZ + col);
+          res[ob][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(tzc, br, res[ob][qb], 0, 0, 0);
+        }
+      }
       // lags a >= c_q have an all-zero Toeplitz operand
 #pragma unroll
       for (int a = 0; a < C::CQM; ++a) {
@@ -686,13 +743,22 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
     }
   };
-  auto convolve = [&](int kt) MTA_INLINE { convolve_ring(Zb, tz, cv, kt); };
+  auto convolve = [&](int kt) MTA_INLINE { convolve_ring(Zb, tz, cv, kt, std::integral_constant<bool, C::XC>{}); };
   auto ring_store_to = [&](_Float16* ring, int kt, int lb, int qb, const f32x4& val) MTA_INLINE {
     const f16x4 h = {(_Float16)val[0], (_Float16)val[1], (_Float16)val[2], (_Float16)val[3]};
     *reinterpret_cast<f16x4*>(ring + ((size_t)hu * C::ZROWS + ZPRE + qs0 + qb * 16 + lq) * C::LDZ +
                               ring_col(kt, lb) + lg * 4) = h;
   };
-  auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) MTA_INLINE { ring_store_to(Zb, kt, lb, qb, val); };
+  auto ring_store = [&](int kt, int lb, int qb, const f32x4& val) MTA_INLINE {
+    ring_store_to(Zb, kt, lb, qb, val);
+    if constexpr (C::XC) {
+      // residual of the fp16 rounding, for the exact centre tap
+      f16x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (_Float16)(val[i] - (float)(_Float16)val[i]);
+      *reinterpret_cast<f16x4*>(Zr + ((size_t)hu * C::R + qs0 + qb * 16 + lq) * C::LDZ + ring_col(kt, lb) + lg * 4) = r;
+    }
+  };
 
   // AV of the weights of key blocks ob0 .. ob0 + NKB - 1 against V of head hu
   auto av = [&](auto& wts, auto ob0c) MTA_INLINE {
@@ -735,7 +801,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       for (int c = 0; c < C::NC; ++c)
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) bo[c][qb] = *reinterpret_cast<const bf16x8*>(xslot(xbuf, hu ^ 1, qb) + c * 8);
-      xbuf ^= 1;
+      if constexpr (C::XBUFS == 2) xbuf ^= 1;
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
 #pragma unroll
@@ -1032,7 +1098,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       }
       team_sync<C>();  // RING1: rows of the neighbouring slab are read by the convolution
       hook();
-      convolve_ring(Zb, tz, cp, kr);
+      convolve_ring(Zb, tz, cp, kr, std::false_type{});
       // Mask_-inf: a softmax row needs all c_q logit rows of its convolution inside the
       // tile (t >= c_q - 1) and lies in the map; keys 0 .. gr
       const bool edge1 = (j0 + 8 < 0) || (j0 + C::BK + 8 - 1 > wrow_min) || (qs0 < cq1) || (wrow_min < 0) ||
@@ -1156,7 +1222,7 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         }
       team_sync<C>();
       if (kt >= kt_lo) {
-        convolve_ring(Zw, tz2, cv, kr);
+        convolve_ring(Zw, tz2, cv, kr, std::false_type{});
         const bool edge2 = (j0 + C::BK - 1 > wrow_min) || (qs0 < halo) || (wrow_min + C::QW > T_);
         if (edge2) {
 #pragma unroll
@@ -1550,9 +1616,11 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
 
   // ============================= epilogue =================================================
   // per-pair accumulators: the other head's row sums of the same rows, through the exchange
-  // buffer the last tile did not use (its readers all passed that tile's barrier)
+  // buffer the last tile did not use (its readers all passed that tile's barrier), or after a
+  // barrier when there is one buffer
   float l_oth[C::NQB];
   if constexpr (C::PAIR) {
+    if constexpr (C::XBUFS == 1) __syncthreads();
     float* xl = reinterpret_cast<float*>(Sx + xbuf * C::SX_HALF);
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
