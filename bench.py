@@ -256,7 +256,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for cpu_baseline (0: the whole workload)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
-    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward", "decode"],
+    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward", "decode", "cpu"],
                     default=None,
                     help="run one path only (for counter collection); prints its timing")
     ap.add_argument("--workload", type=int, default=HEADLINE,
@@ -269,6 +269,14 @@ def main():
                                    "are not implemented; the layer would shard by batch and head group "
                                    "without communication)"}))
         sys.exit(2)
+
+    if args.only == "cpu":
+        # the fp64 oracle alone on the host cores: the workload of --workload, every row
+        # (--cpu-rows 0) or a seeded sample of rows of batch 0
+        cfg = mta_inputs.config(args.workload)
+        inp = mta_inputs.make_inputs(cfg)
+        print(json.dumps({"only": "cpu", "workload": cfg.name, **cpu_baseline(cfg, inp, args.cpu_rows)}))
+        return
 
     import torch
     import token_attention_amd as ta
