@@ -73,10 +73,21 @@ def oracle_full(cfg):
     return oracle.forward_cfg(cfg, case(cfg))
 
 
+def output_rows_per_tile(cfg):
+    """Output rows of one row tile of the fused bf16 kernel for this workload: 8 waves of 32 rows,
+    8/c_h waves per head of the group, less the query halo of c_q - 1 rows per convolution."""
+    c_h = cfg.c_h if cfg.mix else 1
+    halo = (cfg.c_q - 1) * {None: 0, "pre": 1, "post": 1, "both": 2}[cfg.kq]
+    return 32 * (8 // c_h) - halo
+
+
 @functools.lru_cache(maxsize=None)
 def oracle_rows(cfg):
-    rows = mta_inputs.sample_rows(cfg.T, row_tile=61, n_random=20)
-    rows = np.unique(np.concatenate([rows, mta_inputs.sample_rows(cfg.T, row_tile=59, n_random=0),
+    # both ends, seeded random rows, and both sides of every tile edge of this workload's own
+    # row tiles (and of the 59- and 27-row tiles of other shapes)
+    rows = mta_inputs.sample_rows(cfg.T, row_tile=output_rows_per_tile(cfg), n_random=20)
+    rows = np.unique(np.concatenate([rows, mta_inputs.sample_rows(cfg.T, row_tile=61, n_random=0),
+                                     mta_inputs.sample_rows(cfg.T, row_tile=59, n_random=0),
                                      mta_inputs.sample_rows(cfg.T, row_tile=27, n_random=0)]))
     return rows, oracle.forward_cfg(cfg, case(cfg), rows=rows)
 
