@@ -224,6 +224,49 @@ size_t mta_backward_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k
                                     unsigned flags);
 
 /*
+ * mta_forward_train: mta_forward (bf16 tensors; same arguments, placements and errors) that
+ * also keeps what mta_backward_fused needs, for training:
+ *   lse          [B, T, M] fp32, written: the natural log-sum-exp of every softmax row,
+ *                lse[b][i][m] = log sum_{j <= i} exp(C[i][j]) over the logits C that enter
+ *                the softmax of head m (§2; after the convolution and mixing before softmax
+ *                of §3.1-§3.2 where the placement has them). Required, 16-byte aligned.
+ *   out_pre_gn   [B, T, M, d] fp32, written, or NULL: the layer output before the GroupNorm
+ *                and gate of §3.3 (needed by mta_backward_fused with MTA_GN). 16-byte aligned.
+ * MTA_FP32 returns MTA_ERR_UNSUPPORTED. Allocates nothing.
+ */
+int mta_forward_train(const void* q, const void* k, const void* v, const float* theta_kq,
+                      const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
+                      void* out, float* lse, float* out_pre_gn, int B, int T, int M, int d, int c_q,
+                      int c_k, int c_h, unsigned flags, void* stream);
+
+/*
+ * mta_backward_fused: the gradients of mta_backward_materialized (same outputs, layouts and
+ * parameter-gradient order) without any T x T map in memory: every map of §2-§3.2 is
+ * recomputed on 16 x 16 tiles in on-chip memory, with the softmax rebuilt from the lse of
+ * mta_forward_train. bf16 tensors only.
+ *   lse, out_pre_gn  from mta_forward_train on the same inputs (out_pre_gn required with MTA_GN,
+ *                    ignored otherwise)
+ *   workspace        device buffer of at least mta_backward_fused_workspace_bytes(), 16-byte
+ *                    aligned: O(B*T*M*d) bytes (an fp32 dq accumulator, dO, per-row sums and
+ *                    per-tile partial sums of the parameter gradients)
+ * dq is accumulated with floating-point atomics, so its last bits may differ between calls;
+ * dk, dv and the parameter gradients are reduced in a fixed order. Errors as for
+ * mta_backward_materialized; MTA_ERR_UNSUPPORTED for MTA_FP32 and for placements whose tiles
+ * do not fit in the 160 KiB of LDS (the largest kernels on both sides with c_h = 4).
+ * Allocates nothing.
+ */
+int mta_backward_fused(const void* q, const void* k, const void* v, const float* theta_kq,
+                       const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
+                       const float* lse, const float* out_pre_gn, const void* dout, void* dq, void* dk,
+                       void* dv, float* dtheta_kq, float* dw_mix, float* dgn_gamma, float* dgn_beta,
+                       float* dlambda, int B, int T, int M, int d, int c_q, int c_k, int c_h,
+                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by mta_backward_fused; 0 for invalid sizes. */
+size_t mta_backward_fused_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k, int c_h,
+                                          unsigned flags);
+
+/*
  * mta_attention_plain: standard causal softmax attention softmax(QK^T/sqrt(d))V
  * (§2), computed by the same fused kernel with the convolution, mixing and
  * GroupNorm switched off. flags: 0 or MTA_FP32. Allocates nothing.

@@ -52,19 +52,29 @@ def _mix(X, w, c_h):
     return torch.einsum("guv,bgvij->bguij", w, Xg).reshape(B, M, T, T)
 
 
-def forward_torch(q, k, v, theta, w, gamma, beta, lam, *, c_q, c_k, c_h, kq, mix, gn):
-    """The layer on float64 torch tensors (q, k, v [B,T,M,d]); returns out [B,T,M,d]."""
-    B, T, M, d = q.shape
-    th_pre, th_post = _sides(kq, theta)
-    w_pre, w_post = _sides(mix, w)
-    qh, kh, vh = (x.permute(0, 2, 1, 3) for x in (q, k, v))  # [B,M,T,d]
+def _softmax_input(q, k, theta, w, *, c_h, kq, mix):
+    """The logits that enter the softmax, [B,M,T,T] with -inf above the diagonal (§2, §3.1, §3.2)."""
+    T, d = q.shape[1], q.shape[3]
+    th_pre, _ = _sides(kq, theta)
+    w_pre, _ = _sides(mix, w)
+    qh, kh = (x.permute(0, 2, 1, 3) for x in (q, k))  # [B,M,T,d]
     future = torch.triu(torch.ones(T, T, dtype=torch.bool), 1)
     L = qh @ kh.transpose(-1, -2) / math.sqrt(d)
     if w_pre is not None:
         L = _mix(L, w_pre, c_h)
     if th_pre is not None:
         L = _conv(L.masked_fill(future, 0.0), th_pre)
-    A = torch.softmax(L.masked_fill(future, -math.inf), dim=-1)
+    return L.masked_fill(future, -math.inf)
+
+
+def forward_torch(q, k, v, theta, w, gamma, beta, lam, *, c_q, c_k, c_h, kq, mix, gn):
+    """The layer on float64 torch tensors (q, k, v [B,T,M,d]); returns out [B,T,M,d]."""
+    B, T, M, d = q.shape
+    th_post = _sides(kq, theta)[1]
+    w_post = _sides(mix, w)[1]
+    vh = v.permute(0, 2, 1, 3)  # [B,M,T,d]
+    future = torch.triu(torch.ones(T, T, dtype=torch.bool), 1)
+    A = torch.softmax(_softmax_input(q, k, theta, w, c_h=c_h, kq=kq, mix=mix), dim=-1)
     if th_post is not None:
         A = _conv(A, th_post).masked_fill(future, 0.0)
     if w_post is not None:
@@ -75,6 +85,18 @@ def forward_torch(q, k, v, theta, w, gamma, beta, lam, *, c_q, c_k, c_h, kq, mix
         var = ((O - mu) ** 2).mean(dim=-1, keepdim=True)
         O = lam * (gamma.reshape(M, d) * (O - mu) / torch.sqrt(var + 1e-5) + beta.reshape(M, d))
     return O
+
+
+def row_logsumexp(q, k, theta=None, w=None, *, c_q=1, c_k=1, c_h=1, kq=None, mix=None):
+    """Natural log-sum-exp of every softmax row, [B,T,M] float64: log sum_{j<=i} exp(C[i][j])
+    over the logits C that enter the softmax (after the convolution and mixing before it)."""
+    del c_q, c_k  # the shapes of theta carry them
+
+    def t(x):
+        return None if x is None else torch.tensor(np.asarray(x, dtype=np.float64), dtype=_DT)
+
+    C = _softmax_input(t(q), t(k), t(theta) if kq else None, t(w) if mix else None, c_h=c_h, kq=kq, mix=mix)
+    return torch.logsumexp(C, dim=-1).permute(0, 2, 1).numpy().copy()
 
 
 def backward(q, k, v, theta, w, gamma, beta, lam, dout, *, c_q=1, c_k=1, c_h=1, kq=None, mix=None, gn=False):

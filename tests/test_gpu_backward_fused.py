@@ -1,0 +1,187 @@
+"""GPU parity of the training forward (mta_forward_train) and the fused backward
+(mta_backward_fused) against the fp64 oracles.
+
+The fused backward gets the lse and out_pre_gn that mta_forward_train wrote on the GPU, so
+its error includes theirs. Gradients are held to the materialized backward's bar (per tensor,
+relative to its scale: max |err| <= 2e-2 s, mean |err| <= 2e-3 s; the gate gradient's scale is
+the root-sum-square of its terms), see test_gpu_backward.py.
+
+The log-sum-exp bar: the fused forward rounds the logits that its convolutions and mixing
+read to fp16 (relative error 2^-11) and sums the softmax in fp32, so at logits of unit scale
+the log-sum-exp of a row is off by a few 1e-4; max |err| <= 5e-3 and mean |err| <= 5e-4 leave
+a margin of about ten. out_pre_gn is the layer output before GroupNorm: the bf16 output bar
+(2e-2 / 2e-3 on values of unit scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mta_inputs
+import token_attention_amd as ta
+from oracle import backward as obw
+from oracle import oracle
+from test_gpu_backward import NAMES, check, grads_case, log, oracle_grads
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = (5e-3, 5e-4)
+
+
+def to_gpu(cfg, inp):
+    d = {n: torch.from_numpy(inp[n]).cuda().to(torch.bfloat16).contiguous() for n in ("q", "k", "v")}
+    p = {n: torch.from_numpy(np.ascontiguousarray(inp[n], np.float32)).cuda() for n in ("theta", "w", "gamma", "beta")}
+    return d, p
+
+
+def train_forward(cfg, d, p, lam):
+    return ta.forward_train(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], lam, c_q=cfg.c_q,
+                            c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+
+
+def fused_grads(cfg, inp, dout):
+    d, p = to_gpu(cfg, inp)
+    _, lse, opre = train_forward(cfg, d, p, inp["lam"])
+    g = ta.backward_fused(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], inp["lam"],
+                          dout=torch.from_numpy(dout).cuda().to(torch.bfloat16), lse=lse, out_pre_gn=opre,
+                          c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    torch.cuda.synchronize()
+    return {n: (None if t is None else t.float().cpu().numpy().astype(np.float64)) for n, t in g.items()}
+
+
+PLACEMENTS = [("pre", "post"), ("post", "pre"), ("pre", None), ("post", None), (None, "post"), (None, "pre"),
+              ("pre", "pre"), ("post", "post"), (None, None), ("both", "both"), ("both", None), (None, "both")]
+
+
+@pytest.mark.parametrize("kq,mix", PLACEMENTS)
+def test_forward_train_outputs(kq, mix):
+    """out equals mta_forward bit for bit; lse and out_pre_gn against the oracle."""
+    cfg = mta_inputs.MTAConfig("train_fwd", 2, 97, 8, 64, 3, 7, 4, kq, mix, True, "bf16", 0.2, 0.3, 1.0, 0.0, 0.9,
+                               seed=41)
+    inp, _ = grads_case(cfg)
+    d, p = to_gpu(cfg, inp)
+    out, lse, opre = train_forward(cfg, d, p, inp["lam"])
+    ref_out = ta.forward(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], inp["lam"], c_q=cfg.c_q,
+                         c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    want = obw.row_logsumexp(inp["q"], inp["k"], inp["theta"] if kq else None, inp["w"] if mix else None,
+                             c_h=cfg.c_h, kq=kq, mix=mix)
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - want)
+    log(f"  {kq}/{mix} lse max {err.max():.2e} mean {err.mean():.2e}")
+    assert err.max() <= LSE_TOL[0] and err.mean() <= LSE_TOL[1]
+    o_want = oracle.forward(inp["q"], inp["k"], inp["v"], inp["theta"], inp["w"], kq=kq, mix=mix, c_q=cfg.c_q,
+                            c_k=cfg.c_k, c_h=cfg.c_h, gn=False)
+    oerr = np.abs(opre.cpu().numpy().astype(np.float64) - o_want)
+    log(f"  {kq}/{mix} out_pre_gn max {oerr.max():.2e} mean {oerr.mean():.2e}")
+    assert oerr.max() <= 2e-2 and oerr.mean() <= 2e-3
+
+
+def test_forward_train_lse_on_the_headline_shape():
+    """The log-sum-exp of the T=4096 variant (two-phase schedule) on sampled rows."""
+    cfg = mta_inputs.config("variant_bf16")
+    inp = mta_inputs.make_inputs(cfg)
+    d, p = to_gpu(cfg, inp)
+    _, lse, _ = train_forward(cfg, d, p, inp["lam"])
+    torch.cuda.synchronize()
+    rows = mta_inputs.sample_rows(cfg.T, row_tile=61, n_random=8)
+    # the oracle's log-sum-exp over the needed leading block of rows of one head group
+    T1 = int(rows.max()) + 1
+    sl = slice(0, cfg.c_h)
+    # pre-softmax mixing only (the convolution acts after softmax): rows of group 0, batch 0
+    want = obw.row_logsumexp(inp["q"][:1, :T1, sl], inp["k"][:1, :T1, sl], None, inp["w"][:1], c_h=cfg.c_h,
+                             kq=None, mix="pre")
+    got = lse[0, :T1, sl].cpu().numpy().astype(np.float64)
+    err = np.abs(got[rows] - want[0][rows])
+    log(f"  variant lse on {len(rows)} rows: max {err.max():.2e} mean {err.mean():.2e}")
+    assert err.max() <= LSE_TOL[0] and err.mean() <= LSE_TOL[1]
+
+
+@pytest.mark.parametrize("kq,mix", PLACEMENTS)
+def test_backward_fused_every_placement(kq, mix):
+    cfg = mta_inputs.MTAConfig("bwd", 2, 97, 8, 64, 3, 7, 4, kq, mix, True, "bf16", 0.2, 0.3, 1.0, 0.0, 0.9, seed=31)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what=f"fused {kq}/{mix}")
+
+
+@pytest.mark.parametrize("d,c_q,c_k,c_h", [(32, 4, 9, 2), (96, 6, 11, 2), (128, 8, 17, 4), (128, 1, 1, 1),
+                                           (64, 2, 3, 4)])
+@pytest.mark.parametrize("gn", [True, False])
+def test_backward_fused_shapes_and_sizes(d, c_q, c_k, c_h, gn):
+    mix = "pre" if c_h == 1 else "post"  # a one-head group mixed after softmax only rescales rows
+    cfg = mta_inputs.MTAConfig("bwd_shape", 1, 150, 4, d, c_q, c_k, c_h, "pre", mix, gn, "bf16", 0.2, 0.3, 1.0, 0.0,
+                               0.8, seed=32)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what=f"fused d={d} {c_q}x{c_k} c_h={c_h} gn={gn}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 200])
+def test_backward_fused_ragged_lengths(T):
+    cfg = mta_inputs.MTAConfig("bwd_T", 2, T, 4, 32, 4, 9, 2, "both", "both", T > 2, "bf16", 0.2, 0.2, 1.0, 0.0,
+                               0.8, seed=33)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what=f"fused T={T}")
+
+
+def test_backward_fused_medium_size():
+    """Many 16-tiles in both directions, every operation on both sides, four-head groups."""
+    cfg = mta_inputs.MTAConfig("bwd_mid", 1, 600, 8, 128, 4, 9, 4, "both", "both", True, "bf16", 0.05, 0.05, 1.0,
+                               0.0, 1.0 / 12 ** 0.5, seed=36)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what="fused T=600")
+
+
+def test_backward_fused_matches_materialized_at_t1024():
+    """The headline placement at T=1024 against the materialized backward (itself oracle-checked)."""
+    from test_gpu_backward import gpu_grads
+    cfg = mta_inputs.MTAConfig("bwd_1k", 1, 1024, 8, 128, 4, 9, 4, "post", "pre", True, "bf16", 0.05, 0.05, 1.0, 0.0,
+                               1.0 / 12 ** 0.5, seed=37)
+    inp, dout = grads_case(cfg)
+    got, want = fused_grads(cfg, inp, dout), gpu_grads(cfg, inp, dout)
+    for n in NAMES:
+        if want[n] is None:
+            continue
+        w = np.asarray(want[n]).reshape(np.shape(got[n]))
+        err = np.abs(got[n] - w)
+        scale = max(float(np.max(np.abs(w))), 1e-30)
+        log(f"  T=1024 {n}: max|err|/scale {err.max() / scale:.2e} mean {err.mean() / scale:.2e}")
+        assert err.max() <= 2e-2 * scale
+        if err.size > 1:
+            assert err.mean() <= 2e-3 * scale
+
+
+def test_backward_fused_parameter_gradients_are_deterministic():
+    cfg = mta_inputs.MTAConfig("bwd_det", 2, 130, 8, 64, 4, 9, 4, "post", "pre", True, "bf16", 0.1, 0.1, seed=34)
+    inp, dout = grads_case(cfg)
+    a, b = fused_grads(cfg, inp, dout), fused_grads(cfg, inp, dout)
+    for n in ("dk", "dv", "dtheta", "dw", "dgamma", "dbeta", "dlambda"):
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
+
+
+def test_backward_fused_rejections():
+    cfg = mta_inputs.MTAConfig("bwd_ws", 1, 64, 4, 64, 3, 5, 2, "pre", "post", True, "bf16", 0.1, 0.1, seed=35)
+    inp, dout = grads_case(cfg)
+    d, p = to_gpu(cfg, inp)
+    _, lse, opre = train_forward(cfg, d, p, inp["lam"])
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    kw = dict(c_q=3, c_k=5, c_h=2, kq="pre", mix="post", gn=True)
+    with pytest.raises(ta.MTAError) as e:
+        ta.backward_fused(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], 0.8, dout=d["q"].clone(),
+                          lse=lse, out_pre_gn=opre, workspace=ws, **kw)
+    assert e.value.status == ta.mta.ERR_WORKSPACE
+    with pytest.raises(ta.MTAError) as e:  # GroupNorm needs the output before it
+        ta.backward_fused(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], 0.8, dout=d["q"].clone(),
+                          lse=lse, out_pre_gn=None, **kw)
+    assert e.value.status == ta.mta.ERR_INVALID_ARG
+    # the largest kernels on both sides with four-head groups do not fit the LDS of one tile
+    q = torch.zeros((1, 32, 4, 128), dtype=torch.bfloat16, device="cuda")
+    th = torch.zeros((2, 4, 8, 17), device="cuda")
+    w = torch.zeros((2, 1, 4, 4), device="cuda")
+    with pytest.raises(ta.MTAError) as e:
+        ta.backward_fused(q, q.clone(), q.clone(), th, w, None, None, 1.0, dout=q.clone(),
+                          lse=torch.zeros((1, 32, 4), device="cuda"), c_q=8, c_k=17, c_h=4, kq="both", mix="both")
+    assert e.value.status == ta.mta.ERR_UNSUPPORTED

@@ -6,7 +6,7 @@
   copy with a planted out-of-bounds read shows that the sanitizer is live in that setup.
 * The C ABI's host code: argument validation, the key-split plan and the dispatch
   (`mta_api.hip`, `mta_split.hip`, `mta_fused.hip`, `mta_materialized.hip`,
-  `mta_backward.hip`) built with the sanitizers on the host side only (device code is built as
+  `mta_backward.hip`, `mta_bwd_fused.hip`) built with the sanitizers on the host side only (device code is built as
   usual and never runs here); the per-shape kernel instantiation units are replaced by stubs.
   The C-ABI tests (`tests/test_abi.py`) run against that library.
 
@@ -94,6 +94,7 @@ _STUB = """// Stand-ins for the per-shape kernel instantiation units: the host-s
 // never reach them (no device is present), and a launch through them reports an error.
 #include <hip/hip_runtime.h>
 #include "mta_internal.h"
+#include "mta_bwd_tile.h"
 namespace mta {{
 {decls}
 }}
@@ -107,6 +108,11 @@ def _stub_source():
             names.append("launch_" + fn[len("mta_"):-len(".hip")])
     decls = "\n".join(f"hipError_t {n}(const Problem&, hipStream_t) {{ return hipErrorInvalidValue; }}"
                       for n in names)
+    tiles = [fn[len("mta_bwd_tile_"):-len(".hip")] for fn in sorted(os.listdir(CSRC))
+             if fn.startswith("mta_bwd_tile_d") and fn.endswith(".hip")]
+    decls += "\n" + "\n".join(
+        f"hipError_t launch_bwd_tiles_{n}(const bwt::BwArgs&, int, int, size_t, unsigned, hipStream_t) "
+        "{ return hipErrorInvalidValue; }" for n in tiles)
     return _STUB.format(decls=decls)
 
 
@@ -119,7 +125,7 @@ def abi_san_lib(tmp_path_factory):
     stub = work / "stubs.hip"
     stub.write_text(_stub_source())
     srcs = [os.path.join(CSRC, n) for n in ("mta_api.hip", "mta_split.hip", "mta_fused.hip", "mta_materialized.hip",
-                                            "mta_backward.hip")] + [str(stub)]
+                                            "mta_backward.hip", "mta_bwd_fused.hip")] + [str(stub)]
     # sanitizers on the host side only: each -fsanitize follows -Xarch_host
     host_san = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
     flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",

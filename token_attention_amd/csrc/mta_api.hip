@@ -331,6 +331,73 @@ int mta_backward_materialized(const void* q, const void* k, const void* v, const
   return hip_status(e, "mta_backward_materialized launch");
 }
 
+int mta_forward_train(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                      const float* gn_gamma, const float* gn_beta, float lambda, void* out, float* lse,
+                      float* out_pre_gn, int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags,
+                      void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, out, B, T, M, d, c_q, c_k, c_h,
+                          flags, &p);
+  if (st != MTA_OK) return st;
+  if (p.fp32) return fail(MTA_ERR_UNSUPPORTED, "mta_forward_train is built for bf16 tensors");
+  if (!lse) return fail(MTA_ERR_INVALID_ARG, "lse must not be NULL");
+  if (!aligned16(lse) || (out_pre_gn && !aligned16(out_pre_gn)))
+    return fail(MTA_ERR_INVALID_ARG, "lse and out_pre_gn must be 16-byte aligned");
+  p.lse = lse;
+  p.o32 = out_pre_gn;
+  bool unsupported = false;
+  const hipError_t e = mta::launch_fused(p, reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no fused kernel for this shape");
+  return hip_status(e, "mta_forward_train launch");
+}
+
+size_t mta_backward_fused_workspace_bytes(int B, int T, int M, int d, int c_q, int c_k, int c_h, unsigned flags) {
+  mta::Problem p{};
+  if (!sizes_problem(B, T, M, d, c_q, c_k, c_h, flags, &p)) return 0;
+  return mta::backward_fused_workspace_bytes(p);
+}
+
+int mta_backward_fused(const void* q, const void* k, const void* v, const float* theta_kq, const float* w_mix,
+                       const float* gn_gamma, const float* gn_beta, float lambda, const float* lse,
+                       const float* out_pre_gn, const void* dout, void* dq, void* dk, void* dv, float* dtheta_kq,
+                       float* dw_mix, float* dgn_gamma, float* dgn_beta, float* dlambda, int B, int T, int M, int d,
+                       int c_q, int c_k, int c_h, unsigned flags, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  mta::Problem p;
+  const int st = validate(q, k, v, theta_kq, w_mix, gn_gamma, gn_beta, lambda, dq, B, T, M, d, c_q, c_k, c_h, flags,
+                          &p);
+  if (st != MTA_OK) return st;
+  if (p.fp32) return fail(MTA_ERR_UNSUPPORTED, "mta_backward_fused is built for bf16 tensors");
+  if (!dout || !dk || !dv) return fail(MTA_ERR_INVALID_ARG, "dout, dq, dk and dv must not be NULL");
+  if (!aligned16(dout) || !aligned16(dk) || !aligned16(dv))
+    return fail(MTA_ERR_INVALID_ARG, "dout, dq, dk and dv must be 16-byte aligned");
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (void* o : outs)
+    for (const void* in : ins)
+      if (o == in) return fail(MTA_ERR_INVALID_ARG, "dq, dk and dv may not alias q, k, v or dout");
+  if (dq == dk || dq == dv || dk == dv) return fail(MTA_ERR_INVALID_ARG, "dq, dk and dv must be distinct");
+  if (!lse) return fail(MTA_ERR_INVALID_ARG, "lse (from mta_forward_train) must not be NULL");
+  if (p.gn && !out_pre_gn) return fail(MTA_ERR_INVALID_ARG, "out_pre_gn (from mta_forward_train) is required with MTA_GN");
+  if (p.gn && !aligned16(out_pre_gn)) return fail(MTA_ERR_INVALID_ARG, "out_pre_gn must be 16-byte aligned");
+  if (p.kq && !dtheta_kq) return fail(MTA_ERR_INVALID_ARG, "dtheta_kq is required with a KQ flag");
+  if (p.mix && !dw_mix) return fail(MTA_ERR_INVALID_ARG, "dw_mix is required with a MIX flag");
+  if (p.gn && (!dgn_gamma || !dgn_beta || !dlambda))
+    return fail(MTA_ERR_INVALID_ARG, "dgn_gamma, dgn_beta and dlambda are required with MTA_GN");
+  if (!mta::backward_fused_supported(p))
+    return fail(MTA_ERR_UNSUPPORTED, "the fused backward's tiles of this placement do not fit in LDS");
+  const size_t need = mta::backward_fused_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(MTA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(MTA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  mta::BwdGrads g{dout, dq, dk, dv, dtheta_kq, dw_mix, dgn_gamma, dgn_beta, dlambda};
+  bool unsupported = false;
+  const hipError_t e = mta::launch_backward_fused(p, g, lse, out_pre_gn, workspace,
+                                                  reinterpret_cast<hipStream_t>(stream), &unsupported);
+  if (unsupported) return fail(MTA_ERR_UNSUPPORTED, "no fused backward for this shape");
+  return hip_status(e, "mta_backward_fused launch");
+}
+
 int mta_attention_plain(const void* q, const void* k, const void* v, void* out, int B, int T, int M, int d,
                         unsigned flags, void* stream) {
   if (flags & ~MTA_FP32) return fail(MTA_ERR_INVALID_ARG, "mta_attention_plain accepts only MTA_FP32");

@@ -23,4 +23,11 @@ bool backward_supported(const Problem& p);
 hipError_t launch_backward(const Problem& p, const BwdGrads& g, void* workspace, hipStream_t stream,
                            bool* unsupported);
 
+// Fused backward (mta_bwd_fused.hip): no T x T map in memory. lse [B,T,M] and o32 [B,T,M,d]
+// (needed with GroupNorm) come from the forward (Problem::lse, Problem::o32).
+size_t backward_fused_workspace_bytes(const Problem& p);
+bool backward_fused_supported(const Problem& p);
+hipError_t launch_backward_fused(const Problem& p, const BwdGrads& g, const float* lse, const float* o32,
+                                 void* workspace, hipStream_t stream, bool* unsupported);
+
 }  // namespace mta

@@ -23,106 +23,11 @@
 #include <utility>
 
 #include "mta_backward.h"
+#include "mta_bwd_common.h"
 #include "mta_map_kernels.h"
 
 namespace mta {
 namespace {
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// ---- GroupNorm + gate backward, one wave per (b, token, head) row ----------------------------
-// xhat = (O - mean) / sqrt(var + eps); Y = lambda (gamma xhat + beta). With g = lambda gamma dY:
-// dO = (g - mean(g) - xhat mean(g xhat)) / sqrt(var + eps). Partial sums of dgamma, dbeta
-// (over the rows of the block) and dlambda go to part_*.
-constexpr int GN_RB = 64;  // rows of one (b, m) per workgroup
-
-template <typename T, int D>
-__global__ __launch_bounds__(MT_THREADS) void gn_backward_kernel(const float* __restrict__ O, const T* __restrict__ dY,
-                                                                const float* __restrict__ gamma,
-                                                                const float* __restrict__ beta, float lambda,
-                                                                T* __restrict__ dO, float* __restrict__ part_g,
-                                                                float* __restrict__ part_b, float* __restrict__ part_l,
-                                                                int Tn, int M) {
-  constexpr int CPL = (D + 63) / 64;  // channels per lane
-  __shared__ float red[4][2 * D + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bm = blockIdx.y, b = bm / M, m = bm % M;
-  const int chunk = blockIdx.x, nch = gridDim.x;
-  const int i0 = chunk * GN_RB;
-  float gam[CPL], bet[CPL], pg[CPL], pb[CPL];
-  float pl = 0.0f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const int c = lane + 64 * k;
-    gam[k] = c < D ? gamma[(size_t)m * D + c] : 0.0f;
-    bet[k] = c < D ? beta[(size_t)m * D + c] : 0.0f;
-    pg[k] = pb[k] = 0.0f;
-  }
-  for (int r = wave; r < GN_RB; r += 4) {
-    const int i = i0 + r;
-    if (i >= Tn) break;
-    const size_t row = ((size_t)b * Tn + i) * M + m;
-    float o[CPL], dy[CPL];
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      o[k] = c < D ? O[row * D + c] : 0.0f;
-      dy[k] = c < D ? (float)dY[row * D + c] : 0.0f;
-      s += o[k];
-    }
-    const float mean = wave_sum(s) * (1.0f / D);
-    float sq = 0.0f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      const float dv = c < D ? o[k] - mean : 0.0f;
-      sq += dv * dv;
-    }
-    const float rs = 1.0f / sqrtf(wave_sum(sq) * (1.0f / D) + 1e-5f);
-    float xh[CPL], g[CPL], sg = 0.0f, sgx = 0.0f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      xh[k] = c < D ? (o[k] - mean) * rs : 0.0f;
-      pl += dy[k] * (gam[k] * xh[k] + bet[k]);
-      pg[k] += lambda * dy[k] * xh[k];
-      pb[k] += lambda * dy[k];
-      g[k] = lambda * gam[k] * dy[k];
-      sg += g[k];
-      sgx += g[k] * xh[k];
-    }
-    const float mg = wave_sum(sg) * (1.0f / D), mgx = wave_sum(sgx) * (1.0f / D);
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      if (c < D) dO[row * D + c] = T((g[k] - mg - xh[k] * mgx) * rs);
-    }
-  }
-  // per-channel partials over the four waves, the gate partial over the workgroup
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const int c = lane + 64 * k;
-    if (c < D) {
-      red[wave][c] = pg[k];
-      red[wave][D + c] = pb[k];
-    }
-  }
-  pl = wave_sum(pl);
-  if (lane == 0) red[wave][2 * D] = pl;
-  __syncthreads();
-  const size_t prow = (size_t)b * nch + chunk;
-  for (int x = threadIdx.x; x < 2 * D; x += MT_THREADS) {
-    const float v = (red[0][x] + red[1][x]) + (red[2][x] + red[3][x]);
-    if (x < D) part_g[(prow * M + m) * D + x] = v;
-    else part_b[(prow * M + m) * D + (x - D)] = v;
-  }
-  if (threadIdx.x == 0) part_l[prow * M + m] = (red[0][2 * D] + red[1][2 * D]) + (red[2][2 * D] + red[3][2 * D]);
-}
 
 // ---- out[j][c] = scale * sum_i Map[i][j] X[i][c] (Map^T X; Map is zero for i < j) --------------
 // fp32 tensors (VALU): 64 output rows j of one (b, m) per workgroup; thread (j, channel quarter). Chunks of 32 map rows
@@ -575,20 +480,6 @@ __global__ __launch_bounds__(MT_THREADS) void conv_dtheta_kernel(const float* __
   __syncthreads();
   float* dst = part + (((size_t)b * nty + ty) * M + m) * c_q * CK;
   for (int x = threadIdx.x; x < c_q * CK; x += MT_THREADS) dst[x] = (red[0][x] + red[1][x]) + (red[2][x] + red[3][x]);
-}
-
-// ---- out[k] = sum_r part[r * K + k], rows added in order ------------------------------------------
-__global__ void sum_rows_kernel(const float* __restrict__ part, size_t R, size_t K, float* __restrict__ out) {
-  const size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
-  float s = 0.0f;
-  for (size_t r = 0; r < R; ++r) s += part[r * K + k];
-  out[k] = s;
-}
-
-hipError_t sum_rows(const float* part, size_t R, size_t K, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(sum_rows_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, part, R, K, out);
-  return hipGetLastError();
 }
 
 template <int CK>

@@ -1,0 +1,10 @@
+// Fused backward tile kernels for head size 32 (one translation unit per head size).
+#include "mta_bwd_tile.h"
+
+namespace mta {
+
+hipError_t launch_bwd_tiles_d32(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st) {
+  return bwt::launch_tiles<32>(a, ch, mode, lds, grid, st);
+}
+
+}  // namespace mta

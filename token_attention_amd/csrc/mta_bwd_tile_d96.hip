@@ -1,0 +1,10 @@
+// Fused backward tile kernels for head size 96 (one translation unit per head size).
+#include "mta_bwd_tile.h"
+
+namespace mta {
+
+hipError_t launch_bwd_tiles_d96(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st) {
+  return bwt::launch_tiles<96>(a, ch, mode, lds, grid, st);
+}
+
+}  // namespace mta

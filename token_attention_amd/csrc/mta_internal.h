@@ -37,6 +37,9 @@ struct Problem {
   int split_n = 1;
   float* part_stats = nullptr;   // partial buffers in the caller's workspace
   float* part_o = nullptr;
+  // fused bf16 path, unsplit, optional: what a backward pass keeps from the forward
+  float* lse = nullptr;          // [B, T, M] natural log-sum-exp of every softmax row
+  float* o32 = nullptr;          // [B, T, M, d] output before GroupNorm, fp32
 };
 
 // Returns hipSuccess or the launch error; sets *unsupported when no kernel is

@@ -117,6 +117,8 @@ struct Args {
   float* part_stats;   // [split][B][nr][M][2]: row maximum (log2 units) and row sum against it
   float* part_o;       // [split][B][nr][M][D]: AV partial
   int n_split;         // chunks whose statistics a normalised SPLIT_PARTIAL schedule combines
+  float* lse;          // unsplit, optional: [B][T][M] natural log-sum-exp of each softmax row
+  float* o32;          // unsplit, optional: [B][T][M][D] output before GroupNorm, fp32
 };
 
 // KQ: a key-query convolution (TWO: after softmax); MIXPRE / MIXPOST: head mixing before /
@@ -1048,6 +1050,13 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
         stat_l[qb] = l_run[qb];
       }
     }
+    if constexpr (!C::SPLIT) {  // the row statistics the epilogue reports (log-sum-exp output)
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        stat_m[qb] = normalized ? shift[qb] : m_run[qb] * ssc;
+        stat_l[qb] = normalized ? 1.0f : l_run[qb];
+      }
+    }
   } else if constexpr (C::DUAL) {
     // ===================== convolutions before and after softmax ========================
     // Tile kt (j0 = kt * BK; kt = -1 is a lead-in tile that only fills the rings) computes
@@ -1663,6 +1672,15 @@ __global__ __launch_bounds__(C::NT, 1) void kmajor_kernel(Args A) {
       inv = 1.0f / sqrtf(xgroup_sum(sq) * (1.0f / C::D) + 1e-5f);
     }
     if (t >= halo && gr < T_) {
+      // for a backward pass: the output before GroupNorm (fp32) and the row's natural
+      // log-sum-exp of the softmax input, m + log2(l) in log2 units times ln 2
+      if (A.o32) {
+        float* d32 = A.o32 + ((b * (size_t)T_ + gr) * M + m_head) * C::D;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) *reinterpret_cast<f32x4*>(d32 + nb * 16 + 4 * lg) = o[nb];
+      }
+      if (A.lse && lg == 0)
+        A.lse[(b * (size_t)T_ + gr) * M + m_head] = (stat_m[qb] + __builtin_log2f(stat_l[qb])) * 0.6931471805599453f;
       __bf16* dst = ob_ + ((size_t)gr * M + m_head) * C::D;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
@@ -1718,6 +1736,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.part_stats = p.part_stats;
   a.part_o = p.part_o;
   a.n_split = p.split_mode ? p.split_n : 1;
+  a.lse = p.split_mode ? nullptr : p.lse;
+  a.o32 = p.split_mode ? nullptr : p.o32;
   if (p.split_mode && (p.split_keys <= 0 || p.split_keys % C::BK != 0)) return hipErrorInvalidValue;
   const long long blocks = (long long)n_bg * a.n_tiles * (p.split_mode ? p.split_n : 1);
   if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;

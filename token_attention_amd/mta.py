@@ -29,6 +29,7 @@ EXPORTED = [
     "mta_attention_plain", "mta_check_args", "mta_status_string", "mta_last_error", "mta_version",
     "mta_backward_materialized", "mta_backward_workspace_bytes", "mta_forward_rows_split",
     "mta_forward_rows_split_workspace_bytes", "mta_forward_rows_split_plan", "mta_forward_rows_split_noalloc",
+    "mta_forward_train", "mta_backward_fused", "mta_backward_fused_workspace_bytes",
 ]
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # MTA_NOALLOC_SCRATCH_BYTES
@@ -78,6 +79,13 @@ def lib() -> ctypes.CDLL:
         L.mta_backward_materialized.restype = i
         L.mta_backward_workspace_bytes.argtypes = [i] * 7 + [u]
         L.mta_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.mta_forward_train.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp, vp, vp] + [i] * 7 + [u, vp]
+        L.mta_forward_train.restype = i
+        L.mta_backward_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, ctypes.c_float, vp, vp, vp, vp, vp, vp, fp, fp,
+                                         fp, fp, fp] + [i] * 7 + [u, vp, ctypes.c_size_t, vp]
+        L.mta_backward_fused.restype = i
+        L.mta_backward_fused_workspace_bytes.argtypes = [i] * 7 + [u]
+        L.mta_backward_fused_workspace_bytes.restype = ctypes.c_size_t
         L.mta_attention_plain.argtypes = [vp, vp, vp, vp, i, i, i, i, u, vp]
         L.mta_attention_plain.restype = i
         L.mta_check_args.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [u]
@@ -316,6 +324,67 @@ def backward_materialized(q, k, v, theta=None, w=None, gamma=None, beta=None, la
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
         _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
         float(lam), _dev(dout, "dout"), _dev(g["dq"], "dq"), _dev(g["dk"], "dk"), _dev(g["dv"], "dv"),
+        _dev(g["dtheta"], "dtheta"), _dev(g["dw"], "dw"), _dev(g["dgamma"], "dgamma"), _dev(g["dbeta"], "dbeta"),
+        _dev(g["dlambda"], "dlambda"), B, T, M, d, c_q, c_k, c_h, fl, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return g
+
+
+def forward_train(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, c_q: int = 1,
+                  c_k: int = 1, c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None,
+                  gn: bool = False, out=None, lse=None, out_pre_gn=None, stream=None):
+    """``mta_forward_train``: the fused forward (bf16) that also keeps what ``backward_fused``
+    needs. Returns (out, lse [B, T, M] fp32, out_pre_gn [B, T, M, d] fp32 or None without
+    GroupNorm)."""
+    out = _common(q, k, v, out)
+    B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
+    if lse is None:
+        lse = torch.empty((B, T, M), dtype=torch.float32, device=q.device)
+    if out_pre_gn is None and gn:
+        out_pre_gn = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if lse.shape != (B, T, M) or (out_pre_gn is not None and out_pre_gn.shape != q.shape):
+        raise ValueError("lse must be [B, T, M] and out_pre_gn [B, T, M, d]")
+    fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
+    _check(lib().mta_forward_train(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(out, "out"), _dev(lse, "lse", torch.float32), _dev(out_pre_gn, "out_pre_gn", torch.float32),
+        B, T, M, d, c_q, c_k, c_h, fl, _stream(stream)))
+    return out, lse, out_pre_gn
+
+
+def backward_fused_workspace_bytes(B: int, T: int, M: int, d: int, *, c_q: int = 1, c_k: int = 1, c_h: int = 1,
+                                   kq: Optional[str] = None, mix: Optional[str] = None, gn: bool = False) -> int:
+    return int(lib().mta_backward_fused_workspace_bytes(B, T, M, d, c_q, c_k, c_h, placement_flags(kq, mix, gn, False)))
+
+
+def backward_fused(q, k, v, theta=None, w=None, gamma=None, beta=None, lam: float = 1.0, *, dout, lse,
+                   out_pre_gn=None, c_q: int = 1, c_k: int = 1, c_h: int = 1, kq: Optional[str] = None,
+                   mix: Optional[str] = None, gn: bool = False, workspace=None, stream=None) -> dict:
+    """Gradients of sum(out * dout) by the fused backward (``mta_backward_fused``), from the
+    ``lse`` and ``out_pre_gn`` of ``forward_train``. Returns the same dict as
+    ``backward_materialized``."""
+    _common(q, k, v, None)
+    if dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must match q in shape and dtype")
+    B, T, M, d = q.shape
+    _params(q, theta, w, gamma, beta, c_q, c_k, c_h, kq, mix, gn)
+    fl = placement_flags(kq, mix, gn, q.dtype == torch.float32)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q)}
+    g["dtheta"] = torch.empty_like(theta) if kq else None
+    g["dw"] = torch.empty_like(w) if mix else None
+    g["dgamma"] = torch.empty_like(gamma) if gn else None
+    g["dbeta"] = torch.empty_like(beta) if gn else None
+    g["dlambda"] = torch.empty(1, dtype=torch.float32, device=q.device) if gn else None
+    need = backward_fused_workspace_bytes(B, T, M, d, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().mta_backward_fused(
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(theta, "theta", torch.float32),
+        _dev(w, "w", torch.float32), _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32),
+        float(lam), _dev(lse, "lse", torch.float32), _dev(out_pre_gn, "out_pre_gn", torch.float32),
+        _dev(dout, "dout"), _dev(g["dq"], "dq"), _dev(g["dk"], "dk"), _dev(g["dv"], "dv"),
         _dev(g["dtheta"], "dtheta"), _dev(g["dw"], "dw"), _dev(g["dgamma"], "dgamma"), _dev(g["dbeta"], "dbeta"),
         _dev(g["dlambda"], "dlambda"), B, T, M, d, c_q, c_k, c_h, fl, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
