@@ -101,3 +101,61 @@ def test_groupnorm_gate_gradients_match_layer_norm():
     for n, t in (("dq", tq), ("dk", tk), ("dv", tv), ("dgamma", tg), ("dbeta", tb)):
         np.testing.assert_allclose(g[n], t.grad.numpy(), atol=1e-12, err_msg=n)
     assert math.isclose(g["dlambda"], float(tl.grad), rel_tol=1e-12, abs_tol=1e-12)
+
+
+# ---- the per-row log-sum-exp that the training forward reports and the fused backward uses
+def _brute_lse(S, i):
+    """log sum_{j <= i} exp(S[j]) by a plain loop."""
+    return math.log(math.fsum(math.exp(S[j]) for j in range(i + 1)))
+
+
+def _dots(x, b, i, m):
+    """q_i . k_j / sqrt(d) for every j, by plain loops."""
+    d = x["q"].shape[3]
+    return [sum(x["q"][b, i, m, t] * x["k"][b, j, m, t] for t in range(d)) / math.sqrt(d)
+            for j in range(x["q"].shape[1])]
+
+
+def test_row_logsumexp_plain_attention_by_brute_force():
+    x, _, _ = _problem(None, None, False, 6, B=2, T=7, M=2, d=4)
+    got = bw.row_logsumexp(x["q"], x["k"])
+    for b in range(2):
+        for m in range(2):
+            for i in range(7):
+                assert math.isclose(got[b, i, m], _brute_lse(_dots(x, b, i, m), i), rel_tol=0, abs_tol=1e-12)
+
+
+def test_row_logsumexp_closed_forms_of_the_convolution():
+    # theta = alpha delta(0, h0): the logits scaled by alpha. theta = delta(1, h0): row i sees the
+    # previous row's logits at keys j < i and a zero-padded logit at j = i; row 0 sees one zero.
+    B, T, M, d, c_q, c_k = 1, 6, 2, 4, 2, 3
+    x, _, _ = _problem(None, None, False, 7, B=B, T=T, M=M, d=d)
+    h0 = (c_k - 1) // 2
+    th = np.zeros((M, c_q, c_k))
+    th[:, 0, h0] = 1.7
+    got = bw.row_logsumexp(x["q"], x["k"], th, c_q=c_q, c_k=c_k, kq="pre")
+    lag = np.zeros((M, c_q, c_k))
+    lag[:, 1, h0] = 1.0
+    got_lag = bw.row_logsumexp(x["q"], x["k"], lag, c_q=c_q, c_k=c_k, kq="pre")
+    for m in range(M):
+        for i in range(T):
+            S = _dots(x, 0, i, m)
+            assert math.isclose(got[0, i, m], _brute_lse([1.7 * s for s in S], i), abs_tol=1e-12)
+            row = (_dots(x, 0, i - 1, m)[:i] if i > 0 else []) + [0.0]
+            assert math.isclose(got_lag[0, i, m], _brute_lse(row, i), abs_tol=1e-12)
+
+
+def test_row_logsumexp_permutation_mixing_and_post_steps():
+    # Mixing before softmax by a permutation renames the heads' logits; the steps after softmax
+    # do not change the softmax input at all.
+    x, _, _ = _problem(None, None, False, 8, B=1, T=9, M=4, d=4)
+    perm = [2, 0, 3, 1]
+    w = np.zeros((1, 4, 4))
+    for u, v in enumerate(perm):
+        w[0, u, v] = 1.0
+    plain = bw.row_logsumexp(x["q"], x["k"])
+    mixed = bw.row_logsumexp(x["q"], x["k"], None, w, c_h=4, mix="pre")
+    np.testing.assert_allclose(mixed, plain[:, :, perm], atol=1e-12)
+    th = np.random.default_rng(9).standard_normal((4, 3, 5))
+    post = bw.row_logsumexp(x["q"], x["k"], th, w, c_q=3, c_k=5, c_h=4, kq="post", mix="post")
+    np.testing.assert_allclose(post, plain, atol=1e-12)
