@@ -256,7 +256,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for cpu_baseline (0: the whole workload)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-materialized", action="store_true")
-    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward", "decode", "cpu"],
+    ap.add_argument("--only", choices=["fused", "plain", "default", "both", "materialized", "backward",
+                                       "backward_fused", "decode", "cpu"],
                     default=None,
                     help="run one path only (for counter collection); prints its timing")
     ap.add_argument("--workload", type=int, default=HEADLINE,
@@ -377,8 +378,40 @@ def main():
         del ws
         return rec
 
+    def fused_backward_record(ms_fwd):
+        """A training step's layer work at this workload: mta_forward_train, then
+        mta_backward_fused (no T x T map in memory), each timed on its own."""
+        kwb = dict(kw)
+        need = ta.backward_fused_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h,
+                                                 kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        lse = torch.empty((cfg.B, cfg.T, cfg.M), dtype=torch.float32, device="cuda")
+        opre = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda") if cfg.gn else None
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        dout = torch.randn(d["q"].shape, generator=gen, device="cuda").to(d["q"].dtype)
+
+        def fwd_train():
+            ta.forward_train(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"], out=out,
+                             lse=lse, out_pre_gn=opre, **kwb)
+
+        def bwd():
+            ta.backward_fused(d["q"], d["k"], d["v"], d["theta"], d["w"], d["gamma"], d["beta"], d["lam"],
+                              dout=dout, lse=lse, out_pre_gn=opre, workspace=ws, **kwb)
+        ms_f = time_launches(fwd_train, max(2, args.steps // 2), 1, torch)
+        ms_b = time_launches(bwd, max(2, args.steps // 4), 1, torch)
+        kept = lse.numel() * 4 + (opre.numel() * 4 if opre is not None else 0)
+        rec = {"ms": ms_b, "forward_train_ms": ms_f, "train_step_ms": ms_f + ms_b,
+               "train_tokens_per_s": tokens / ((ms_f + ms_b) * 1e-3),
+               "workspace_gib": need / 2 ** 30, "kept_from_forward_gib": kept / 2 ** 30,
+               "vs_fused_forward": ms_b / ms_fwd if ms_fwd else None}
+        del ws, lse, opre
+        return rec
+
     if args.only == "backward":
         print(json.dumps({"only": "backward", "workload": cfg.name, **backward_record(None)}))
+        return
+    if args.only == "backward_fused":
+        print(json.dumps({"only": "backward_fused", "workload": cfg.name, **fused_backward_record(None)}))
         return
     if args.only == "decode":
         # one decode step (the last row of every sequence) with the key range split over workgroups
@@ -523,6 +556,7 @@ def main():
             "plain_ms": ms_p, "plain_tflops": wcfg.B * wcfg.M * wn_c * 4 * wcfg.d / (ms_p * 1e-3) / 1e12,
             "mta_slowdown_vs_plain": ms_w / ms_p}
         del wd, wout
+    result["backward_fused"] = fused_backward_record(ms)
     if not args.no_materialized:
         result["materialized"] = materialized_record(ms)
         result["backward_materialized"] = backward_record(result["materialized"]["ms"])

@@ -111,7 +111,7 @@ def _stub_source():
     tiles = [fn[len("mta_bwd_tile_"):-len(".hip")] for fn in sorted(os.listdir(CSRC))
              if fn.startswith("mta_bwd_tile_d") and fn.endswith(".hip")]
     decls += "\n" + "\n".join(
-        f"hipError_t launch_bwd_tiles_{n}(const bwt::BwArgs&, int, int, size_t, unsigned, hipStream_t) "
+        f"hipError_t launch_bwd_tiles_{n}(const bwt::BwArgs&, int, int, int, size_t, unsigned, hipStream_t) "
         "{ return hipErrorInvalidValue; }" for n in tiles)
     return _STUB.format(decls=decls)
 

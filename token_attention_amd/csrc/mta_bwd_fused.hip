@@ -8,81 +8,39 @@
 
 namespace mta {
 
-hipError_t launch_bwd_tiles_d32(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st);
-hipError_t launch_bwd_tiles_d64(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st);
-hipError_t launch_bwd_tiles_d96(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st);
-hipError_t launch_bwd_tiles_d128(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st);
+hipError_t launch_bwd_tiles_d32(const bwt::BwArgs& a, int ch, int mode, int spec, size_t lds, unsigned grid,
+                                 hipStream_t st);
+hipError_t launch_bwd_tiles_d64(const bwt::BwArgs& a, int ch, int mode, int spec, size_t lds, unsigned grid,
+                                 hipStream_t st);
+hipError_t launch_bwd_tiles_d96(const bwt::BwArgs& a, int ch, int mode, int spec, size_t lds, unsigned grid,
+                                 hipStream_t st);
+hipError_t launch_bwd_tiles_d128(const bwt::BwArgs& a, int ch, int mode, int spec, size_t lds, unsigned grid,
+                                 hipStream_t st);
 
 namespace {
 
 constexpr size_t LDS_LIMIT = 160 * 1024;
 
-int r4(int x) { return (x + 3) & ~3; }
-int r16(int x) { return (x + 15) & ~15; }
+// The placement bits of a problem as the plan takes them: 1 before softmax, 2 after.
+int kq_bits(const Problem& p) { return ((p.kq & KQ_PRE) ? 1 : 0) | ((p.kq & KQ_POST) ? 2 : 0); }
+int mix_bits(const Problem& p) { return ((p.mix & MIX_PRE) ? 1 : 0) | ((p.mix & MIX_POST) ? 2 : 0); }
 
-// The regions a tile step computes and their LDS storage (see the stage comments in
-// mta_bwd_tile.h). Returns the LDS bytes, 0 if the placement does not fit.
+// The plan of one pass (mta_bwd_tile.h); returns the LDS bytes, 0 if the tiles do not fit.
 size_t plan_tiles(const Problem& p, int mode, bwt::BwArgs& a) {
-  using bwt::Geo;
-  using bwt::Reg;
-  const bool pre = (p.kq & KQ_PRE) != 0, post = (p.kq & KQ_POST) != 0;
-  const int ch = p.c_h;
-  a.cq = p.kq ? p.c_q : 1;
-  a.ck = p.kq ? p.c_k : 1;
-  a.a1 = pre ? p.c_q - 1 : 0;
-  a.h1 = pre ? (p.c_k - 1) / 2 : 0;
-  a.a2 = post ? p.c_q - 1 : 0;
-  a.h2 = post ? (p.c_k - 1) / 2 : 0;
-  const int a1 = a.a1, h1 = a.h1, a2 = a.a2, h2 = a.h2;
-  const Reg core{0, 0, bwt::TB, bwt::TB};
-  if (mode == bwt::PASS_K) {
-    a.rdC = Reg{0, -h1, bwt::TB + a1, r4(bwt::TB + 2 * h1)};
-    const int hc = std::max(h1, h2);
-    const int c_end = std::max(a.rdC.c0 + a.rdC.nc, bwt::TB + h2);
-    a.rP = Reg{-a2, -hc, bwt::TB + a1 + a2, r4(c_end + hc)};
-  } else {
-    a.rdC = core;
-    a.rP = core;
-  }
-  a.rS = Reg{a.rP.r0 - a1, a.rP.c0 - h1, r16(a.rP.nr + a1), r16(a.rP.nc + 2 * h1)};
-  a.rdA = Reg{0, a.rdC.c0 - h2, r16(a.rdC.nr + a2), r16(a.rdC.nc + 2 * h2)};
-
-  int pool = 0;  // floats
-  auto own = [&](const Reg& R) {
-    Geo G{R.r0, R.c0, r4(R.nc) + 4, 0, pool};
-    G.hs = R.nr * G.ld;
-    pool += ch * G.hs;
-    pool = r4(pool);
-    return G;
-  };
-  a.gS = own(a.rS);
-  a.gZ = (p.mix & MIX_PRE) ? own(a.rS) : a.gS;
-  a.gP = pre ? own(a.rP) : a.gZ;
-  if (mode == bwt::PASS_K) {
-    a.gE = post ? own(core) : a.gP;
-    a.gAc = (p.mix & MIX_POST) ? own(core) : a.gE;
-  } else {
-    a.gE = a.gAc = a.gP;
-  }
-  a.gdA = own(a.rdA);
-  a.gdC = post ? own(a.rdC) : a.gdA;
-  a.gdL = (mode == bwt::PASS_K && pre) ? own(core) : a.gdC;
-  a.off_lse = pool;
-  pool = r4(pool + ch * a.rP.nr);
-  a.off_d = pool;
-  pool = r4(pool + ch * a.rdC.nr);
-  a.off_th = pool;
-  pool = r4(pool + 2 * ch * a.cq * a.ck);
-  a.off_w = pool;
-  pool = r4(pool + 2 * ch * ch);
-  a.ldk = p.d + 8;
-  a.off_bf = pool;
-  if (mode == bwt::PASS_K) pool += (3 * ch * bwt::TB * a.ldk + 2 * ch * bwt::TB * 24) / 2;
-  // the end-of-sweep reductions reuse the pool from its start
-  a.off_red = 0;
-  pool = std::max(pool, std::max(ch * a.cq * a.ck * bwt::NRQ, (bwt::NTH / 64) * ch * ch));
-  const size_t bytes = (size_t)r4(pool) * sizeof(float);
+  a.P = bwt::make_plan(mode, kq_bits(p), mix_bits(p), p.c_q, p.c_k, p.c_h, p.d);
+  const size_t bytes = (size_t)a.P.lds_floats * sizeof(float);
   return bytes <= LDS_LIMIT ? bytes : 0;
+}
+
+// The specialised kernel of this shape, 0 for the generic one.
+int spec_of(const Problem& p) {
+  for (int s = 1; s < bwt::NSPEC; ++s) {
+    const bwt::SpecShape sh = bwt::spec_shape(s);
+    if (sh.kq == kq_bits(p) && sh.mix == mix_bits(p) && sh.cq == p.c_q && sh.ck == p.c_k &&
+        bwt::spec_built(s, p.c_h, p.d))
+      return s;
+  }
+  return 0;
 }
 
 __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
@@ -131,11 +89,12 @@ FusedLayout fused_layout(const Problem& p) {
 
 hipError_t launch_tiles(const Problem& p, const bwt::BwArgs& a, int mode, size_t lds, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)p.B * (p.M / p.c_h) * a.n_tiles);
+  const int spec = spec_of(p);
   switch (p.d) {
-    case 32: return launch_bwd_tiles_d32(a, p.c_h, mode, lds, grid, st);
-    case 64: return launch_bwd_tiles_d64(a, p.c_h, mode, lds, grid, st);
-    case 96: return launch_bwd_tiles_d96(a, p.c_h, mode, lds, grid, st);
-    case 128: return launch_bwd_tiles_d128(a, p.c_h, mode, lds, grid, st);
+    case 32: return launch_bwd_tiles_d32(a, p.c_h, mode, spec, lds, grid, st);
+    case 64: return launch_bwd_tiles_d64(a, p.c_h, mode, spec, lds, grid, st);
+    case 96: return launch_bwd_tiles_d96(a, p.c_h, mode, spec, lds, grid, st);
+    case 128: return launch_bwd_tiles_d128(a, p.c_h, mode, spec, lds, grid, st);
   }
   return hipErrorInvalidValue;
 }
@@ -214,8 +173,6 @@ hipError_t launch_backward_fused(const Problem& p, const BwdGrads& g, const floa
   a.T = p.T;
   a.M = p.M;
   a.G = p.M / p.c_h;
-  a.premix = (p.mix & MIX_PRE) ? 1 : 0;
-  a.postmix = (p.mix & MIX_POST) ? 1 : 0;
   a.scale = (float)(1.0 / __builtin_sqrt((double)p.d));
   a.n_tiles = (p.T + bwt::TB - 1) / bwt::TB;
   bwt::BwArgs ad = a, ak = a;

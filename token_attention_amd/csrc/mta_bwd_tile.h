@@ -56,6 +56,107 @@ struct Geo {
   int r0, c0, ld, hs, off;
 };
 
+// The regions a tile step computes and their LDS storage. Maps that are not needed alias
+// the storage of the map they are computed from.
+struct Plan {
+  int cq, ck, a1, h1, a2, h2;  // reach of the convolution before (1) / after (2) softmax, 0 if absent
+  int pre, post, premix, postmix;
+  Reg rS, rP, rdC, rdA;  // regions computed: S / Z, P, dP / dC, dA / dE
+  Geo gS, gSc, gZ, gP, gE, gAc, gdA, gdC, gdL;  // gSc: PASS_K core copy of S (mixing before softmax)
+  int off_lse, off_d, off_th, off_w, off_red;  // small LDS arrays (floats)
+  int off_bf;            // bf16 staging, in floats from the pool start
+  int ldk;               // leading dimension of the staged operand rows (bf16 elements)
+  int nx1, nx2;          // staged rows per head: rows (PASS_K) or columns (PASS_D) of rS and rdA
+  int lds_floats;        // pool size
+};
+
+__host__ __device__ constexpr int r4c(int x) { return (x + 3) & ~3; }
+__host__ __device__ constexpr int r16c(int x) { return (x + 15) & ~15; }
+__host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ constexpr Geo own_geo(const Reg& R, int ch, int& pool) {
+  Geo G{R.r0, R.c0, r4c(R.nc) + 4, 0, pool};
+  G.hs = R.nr * G.ld;
+  pool = r4c(pool + ch * G.hs);
+  return G;
+}
+
+// kq, mix: placement bits, 1 before softmax, 2 after. The regions, from the core tile outwards:
+// PASS_K: dC on the rows the adjoint of the convolution before softmax reads; P there and
+// where the convolution after softmax reads for the core; S around P; dA around dC.
+// PASS_D: P and dP on the core tile only.
+__host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q, int c_k, int ch, int d) {
+  Plan p{};
+  p.pre = (kq & 1) != 0;
+  p.post = (kq & 2) != 0;
+  p.premix = (mix & 1) != 0;
+  p.postmix = (mix & 2) != 0;
+  p.cq = kq ? c_q : 1;
+  p.ck = kq ? c_k : 1;
+  p.a1 = p.pre ? c_q - 1 : 0;
+  p.h1 = p.pre ? (c_k - 1) / 2 : 0;
+  p.a2 = p.post ? c_q - 1 : 0;
+  p.h2 = p.post ? (c_k - 1) / 2 : 0;
+  const Reg core{0, 0, TB, TB};
+  if (mode == PASS_K) {
+    p.rdC = Reg{0, -p.h1, TB + p.a1, r4c(TB + 2 * p.h1)};
+    const int hc = imax(p.h1, p.h2);
+    const int c_end = imax(p.rdC.c0 + p.rdC.nc, TB + p.h2);
+    p.rP = Reg{-p.a2, -hc, TB + p.a1 + p.a2, r4c(c_end + hc)};
+  } else {
+    p.rdC = core;
+    p.rP = core;
+  }
+  p.rS = Reg{p.rP.r0 - p.a1, p.rP.c0 - p.h1, r16c(p.rP.nr + p.a1), r16c(p.rP.nc + 2 * p.h1)};
+  p.rdA = Reg{0, p.rdC.c0 - p.h2, r16c(p.rdC.nr + p.a2), r16c(p.rdC.nc + 2 * p.h2)};
+  int pool = 0;
+  p.gS = own_geo(p.rS, ch, pool);
+  p.gZ = p.gS;  // Z is formed in place
+  p.gSc = (mode == PASS_K && p.premix) ? own_geo(core, ch, pool) : p.gS;
+  p.gP = p.pre ? own_geo(p.rP, ch, pool) : p.gZ;
+  if (mode == PASS_K) {
+    p.gE = p.post ? own_geo(core, ch, pool) : p.gP;
+    p.gAc = p.postmix ? own_geo(core, ch, pool) : p.gE;
+  } else {
+    p.gE = p.gP;
+    p.gAc = p.gP;
+  }
+  p.gdA = own_geo(p.rdA, ch, pool);
+  p.gdC = p.post ? own_geo(p.rdC, ch, pool) : p.gdA;
+  p.gdL = (mode == PASS_K && p.pre) ? own_geo(core, ch, pool) : p.gdC;
+  p.off_lse = pool;
+  pool = r4c(pool + ch * p.rP.nr);
+  p.off_d = pool;
+  pool = r4c(pool + ch * p.rdC.nr);
+  p.off_th = pool;
+  pool = r4c(pool + 2 * ch * p.cq * p.ck);
+  p.off_w = pool;
+  pool = r4c(pool + 2 * ch * ch);
+  p.ldk = d + 8;
+  p.nx1 = mode == PASS_K ? p.rS.nr : p.rS.nc;
+  p.nx2 = mode == PASS_K ? p.rdA.nr : p.rdA.nc;
+  p.off_bf = pool;
+  pool += (ch * (p.nx1 + p.nx2) * p.ldk) / 2;
+  if (mode == PASS_K) pool += (2 * ch * TB * 24) / 2;
+  p.off_red = 0;  // the end-of-sweep reductions reuse the pool from its start
+  pool = imax(pool, imax(ch * p.cq * p.ck * NRQ, ch * ch * TB));
+  p.lds_floats = r4c(pool);
+  return p;
+}
+
+// Shapes with kernels specialised at compile time (the placements and kernel sizes of the
+// benchmark workloads); spec 0 is the generic kernel that reads its plan from the arguments.
+struct SpecShape {
+  int kq, mix, cq, ck;
+};
+__host__ __device__ constexpr SpecShape spec_shape(int spec) {
+  return spec == 1 ? SpecShape{2, 1, 4, 9}     // convolution after softmax, mixing before (4 x 9)
+       : spec == 2 ? SpecShape{1, 2, 4, 9}     // convolution before softmax, mixing after (4 x 9)
+       : spec == 3 ? SpecShape{3, 3, 4, 9}     // both on both sides (4 x 9)
+       : spec == 4 ? SpecShape{1, 2, 6, 11}    // convolution before softmax, mixing after (6 x 11)
+                   : SpecShape{0, 0, 1, 1};
+}
+constexpr int NSPEC = 5;
+
 struct BwArgs {
   const __bf16* q;
   const __bf16* k;
@@ -76,16 +177,9 @@ struct BwArgs {
   float* part_wpre;      // [B * n_tiles][M][CH]
   float* part_wpost;
   int B, T, M, G;
-  int cq, ck;
-  int a1, h1, a2, h2;    // reach of the convolution before (1) / after (2) softmax, 0 if absent
-  int premix, postmix;
   float scale;           // 1 / sqrt(d)
   int n_tiles;           // ceil(T / TB)
-  Reg rS, rP, rdC, rdA;  // regions computed: S / Z, P, dP / dC, dA / dE
-  Geo gS, gZ, gP, gE, gAc, gdA, gdC, gdL;
-  int off_lse, off_d, off_th, off_w, off_red;  // small LDS arrays (floats)
-  int off_bf;            // bf16 staging (PASS_K), in floats from the pool start
-  int ldk;               // leading dimension of the staged Q, dO, K rows (bf16 elements)
+  Plan P;                // the generic kernel's plan (the specialised ones carry their own)
 };
 
 #define BWT_INLINE __attribute__((always_inline))
@@ -166,9 +260,19 @@ __device__ __forceinline__ s16x4 tr_read(const __bf16* base, int row0, int col0,
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-template <int D, int CH, int MODE>
+template <int D, int CH, int MODE, int SPEC>
 __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
+  // the plan: compile-time constants for a specialised shape, so that loop bounds, divisors and
+  // LDS offsets fold away
+  Plan P;
+  if constexpr (SPEC != 0) {
+    constexpr SpecShape sh = spec_shape(SPEC);
+    constexpr Plan KP = make_plan(MODE, sh.kq, sh.mix, sh.cq, sh.ck, CH, D);
+    P = KP;
+  } else {
+    P = A.P;
+  }
   constexpr int NB = D / 16;
   constexpr int NKV = (2 * CH * NB + NTH / 64 - 1) / (NTH / 64);  // dK / dV blocks per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -179,15 +283,14 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   const int tile_rank = (int)blockIdx.x / nbg;  // workgroups with the longest sweeps first
   const int b = bg / A.G, g = bg % A.G;
   const int tile = MODE == PASS_D ? A.n_tiles - 1 - tile_rank : tile_rank;
-  const bool pre = A.th_pre != nullptr;
-  const bool post = A.th_post != nullptr;
+  const bool pre = P.pre, post = P.post;
   const size_t bT = (size_t)b * T;
 
-  float* th_s = lds + A.off_th;  // [2][CH][cq][ck]: before softmax, then after
-  float* w_s = lds + A.off_w;    // [2][CH][CH]
-  float* lse_s = lds + A.off_lse;
-  float* d_s = lds + A.off_d;
-  const int thn = CH * A.cq * A.ck;
+  float* th_s = lds + P.off_th;  // [2][CH][cq][ck]: before softmax, then after
+  float* w_s = lds + P.off_w;    // [2][CH][CH]
+  float* lse_s = lds + P.off_lse;
+  float* d_s = lds + P.off_d;
+  const int thn = CH * P.cq * P.ck;
   for (int x = tid; x < 2 * thn; x += NTH) {
     const float* src = x < thn ? A.th_pre : A.th_post;
     const int y = x < thn ? x : x - thn;
@@ -201,10 +304,9 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
 
   // staged bf16 rows (PASS_K): K of the workgroup's keys, Q and dO of the step's query rows,
   // and the step's dS and A tiles
-  __bf16* Ks = reinterpret_cast<__bf16*>(lds + A.off_bf);
-  __bf16* Qs = Ks + CH * TB * A.ldk;
-  __bf16* Os = Qs + CH * TB * A.ldk;
-  __bf16* dSb = Os + CH * TB * A.ldk;
+  __bf16* X1 = reinterpret_cast<__bf16*>(lds + P.off_bf);  // [CH][nx1] rows: Q (PASS_K) or K (PASS_D)
+  __bf16* X2 = X1 + CH * P.nx1 * P.ldk;                        // [CH][nx2] rows: dO (PASS_K) or V (PASS_D)
+  __bf16* dSb = X2 + CH * P.nx2 * P.ldk;
   __bf16* Ab = dSb + CH * TB * 24;
   constexpr int LDT = 24;  // leading dimension of the 16 x 16 bf16 tiles
 
@@ -216,25 +318,37 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
       const int i = r0 + rr;
       uint4 val = make_uint4(0u, 0u, 0u, 0u);
       if (i < T) val = *reinterpret_cast<const uint4*>(X + ((bT + i) * M + g * CH + u) * D + c * 8);
-      *reinterpret_cast<uint4*>(dst + (u * TB + rr) * A.ldk + c * 8) = val;
+      *reinterpret_cast<uint4*>(dst + (u * TB + rr) * P.ldk + c * 8) = val;
     }
   };
 
   // persistent accumulators
-  float acc_thpre[MAXR], acc_thpost[MAXR], acc_w[CH * CH], acc_w2[CH * CH], acc_d = 0.0f, acc_l = 0.0f;
+  // acc_wpre / acc_wpost: task (u, v, r) = thread CH TB u + TB v + r < CH^2 TB of the mixing gradients,
+  // row r of the core tile
+  float acc_thpre[MAXR], acc_thpost[MAXR], acc_wpre = 0.0f, acc_wpost = 0.0f, acc_d = 0.0f, acc_l = 0.0f;
+  const int wu = tid / (CH * TB), wv = (tid / TB) % CH, wr = tid % TB;
+  const bool wtask = tid < CH * CH * TB;
 #pragma unroll
   for (int x = 0; x < MAXR; ++x) acc_thpre[x] = acc_thpost[x] = 0.0f;
-#pragma unroll
-  for (int x = 0; x < CH * CH; ++x) acc_w[x] = acc_w2[x] = 0.0f;
   f32x4 acc_kv[NKV];
 #pragma unroll
   for (int x = 0; x < NKV; ++x) acc_kv[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // PASS_K: the dQ tasks of this wave (head u, 16 channels nb) and their K operand, K rows of
+  // the workgroup's keys read transposed once for the whole sweep (staged through X1)
+  constexpr int NQT = (CH * NB + NTH / 64 - 1) / (NTH / 64);
+  s16x4 kfrag[NQT];
   int i0, j0;
   if (MODE == PASS_K) {
     j0 = tile * TB;
     i0 = j0;
-    stage_rows(Ks, A.k, j0);
+    stage_rows(X1, A.k, j0);
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NQT; ++x) {
+      const int t = wave + x * (NTH / 64);
+      if (t < CH * NB) kfrag[x] = tr_read(X1 + (t / NB) * TB * P.ldk, 4 * lg, (t % NB) * 16, P.ldk, lane);
+    }
   } else {
     i0 = tile * TB;
     j0 = 0;
@@ -247,68 +361,125 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
       const int i = i0 + r, j = j0 + c;
       return (j >= 0) & (j <= i) & (i < T);
     };
-    // ---- (1) row statistics; S = Q K^T / sqrt(d) and dA = dO V^T on MFMA
-    for (int x = tid; x < CH * A.rP.nr; x += NTH) {
-      const int u = x / A.rP.nr, r = A.rP.r0 + x % A.rP.nr;
+    // ---- (1) the operand rows that change from step to step (PASS_K: Q and dO of the query
+    // rows, PASS_D: K and V of the keys) into LDS in one round of loads, with the row
+    // statistics; then S = Q K^T / sqrt(d) and dA = dO V^T on MFMA, the operand that is fixed for
+    // the sweep read from global memory (it stays in the caches)
+    {
+      constexpr int PER = D / 8;  // 16-byte pieces per row
+      const int n1 = CH * P.nx1 * PER, n2 = CH * P.nx2 * PER;
+      const int o1 = MODE == PASS_K ? i0 + P.rS.r0 : j0 + P.rS.c0;
+      const int o2 = MODE == PASS_K ? i0 + P.rdA.r0 : j0 + P.rdA.c0;
+      const __bf16* s1 = MODE == PASS_K ? A.q : A.k;
+      const __bf16* s2 = MODE == PASS_K ? A.dO : A.v;
+      for (int x = tid; x < n1 + n2; x += NTH) {
+        const bool first = x < n1;
+        const int y = first ? x : x - n1;
+        const int row = y / PER, c = y % PER;  // row of [CH][n] rows
+        const int n = first ? P.nx1 : P.nx2;
+        const int u = row / n, rr = row - u * n;
+        const int gi = (first ? o1 : o2) + rr;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (gi >= 0 && gi < T) val = *reinterpret_cast<const uint4*>((first ? s1 : s2) + ((bT + gi) * M + g * CH + u) * D + c * 8);
+        *reinterpret_cast<uint4*>((first ? X1 : X2) + (u * n + rr) * P.ldk + c * 8) = val;
+      }
+    }
+    for (int x = tid; x < CH * P.rP.nr; x += NTH) {
+      const int u = x / P.rP.nr, r = P.rP.r0 + x % P.rP.nr;
       const int i = i0 + r;
       lse_s[x] = (i >= 0 && i < T) ? (MODE == PASS_D ? A.lse : A.lse_c)[(bT + i) * M + g * CH + u] : 0.0f;
     }
     if (MODE == PASS_K) {
-      for (int x = tid; x < CH * A.rdC.nr; x += NTH) {
-        const int u = x / A.rdC.nr, r = A.rdC.r0 + x % A.rdC.nr;
+      for (int x = tid; x < CH * P.rdC.nr; x += NTH) {
+        const int u = x / P.rdC.nr, r = P.rdC.r0 + x % P.rdC.nr;
         const int i = i0 + r;
         d_s[x] = (i >= 0 && i < T) ? A.dvec[(bT + i) * M + g * CH + u] : 0.0f;
       }
     }
+    __syncthreads();
     {
-      const int nbS = (A.rS.nr / 16) * (A.rS.nc / 16), nbA = (A.rdA.nr / 16) * (A.rdA.nc / 16);
+      const int nbS = (P.rS.nr / 16) * (P.rS.nc / 16), nbA = (P.rdA.nr / 16) * (P.rdA.nc / 16);
       const int ntask = CH * (nbS + nbA);
-      for (int t = wave; t < ntask; t += NTH / 64) {
-        const bool isS = t < CH * nbS;
+      // task t: map (S or dA), head, 16 x 16 block; two tasks per wave at a time so that their
+      // global loads are in flight together
+      auto task = [&](int t, int& u, int& rb, int& cb, bool& isS) BWT_INLINE {
+        isS = t < CH * nbS;
         const int tt = isS ? t : t - CH * nbS;
-        const Reg& R = isS ? A.rS : A.rdA;
+        const Reg& R = isS ? P.rS : P.rdA;
         const int nbc = R.nc / 16;
-        const int u = tt / (isS ? nbS : nbA), blk = tt % (isS ? nbS : nbA);
-        const int rb = R.r0 + 16 * (blk / nbc), cb = R.c0 + 16 * (blk % nbc);
+        u = tt / (isS ? nbS : nbA);
+        const int blk = tt % (isS ? nbS : nbA);
+        rb = R.r0 + 16 * (blk / nbc);
+        cb = R.c0 + 16 * (blk % nbc);
+      };
+      // operand rows: the staged side from LDS, the fixed side from global memory
+      auto frags = [&](int u, int rb, int cb, bool isS, bf16x8 (&fa)[D / 32], bf16x8 (&fb)[D / 32]) BWT_INLINE {
         const int m = g * CH + u;
-        const int ia = min(max(i0 + rb + lq, 0), T - 1);
-        const int jb = min(max(j0 + cb + lq, 0), T - 1);
-        const __bf16* pa = (isS ? A.q : A.dO) + ((bT + ia) * M + m) * D + lg * 8;
-        const __bf16* pb = (isS ? A.k : A.v) + ((bT + jb) * M + m) * D + lg * 8;
-        bf16x8 fa[D / 32], fb[D / 32];
+        const __bf16* pa;
+        const __bf16* pb;
+        if (MODE == PASS_K) {
+          pa = (isS ? X1 + (u * P.nx1 + rb - P.rS.r0 + lq) * P.ldk : X2 + (u * P.nx2 + rb - P.rdA.r0 + lq) * P.ldk) + lg * 8;
+          const int jb = min(max(j0 + cb + lq, 0), T - 1);
+          pb = (isS ? A.k : A.v) + ((bT + jb) * M + m) * D + lg * 8;
+        } else {
+          const int ia = min(max(i0 + rb + lq, 0), T - 1);
+          pa = (isS ? A.q : A.dO) + ((bT + ia) * M + m) * D + lg * 8;
+          pb = (isS ? X1 + (u * P.nx1 + cb - P.rS.c0 + lq) * P.ldk : X2 + (u * P.nx2 + cb - P.rdA.c0 + lq) * P.ldk) + lg * 8;
+        }
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
           fa[kk] = *reinterpret_cast<const bf16x8*>(pa + kk * 32);
           fb[kk] = *reinterpret_cast<const bf16x8*>(pb + kk * 32);
         }
+      };
+      auto finish = [&](int u, int rb, int cb, bool isS, const bf16x8 (&fa)[D / 32], const bf16x8 (&fb)[D / 32]) BWT_INLINE {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk], fb[kk], c, 0, 0, 0);
-        const Geo& G = isS ? A.gS : A.gdA;
+        const Geo& G = isS ? P.gS : P.gdA;
         const float sc = isS ? A.scale : 1.0f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) *at(lds, G, u, rb + 4 * lg + x, cb + lq) = c[x] * sc;
+      };
+      constexpr int NW = NTH / 64;
+      for (int t = wave; t < ntask; t += 2 * NW) {
+        int u0, rb0, cb0, u1 = 0, rb1 = 0, cb1 = 0;
+        bool s0, s1 = false;
+        bf16x8 fa0[D / 32], fb0[D / 32], fa1[D / 32], fb1[D / 32];
+        const bool two = t + NW < ntask;
+        task(t, u0, rb0, cb0, s0);
+        frags(u0, rb0, cb0, s0, fa0, fb0);
+        if (two) {
+          task(t + NW, u1, rb1, cb1, s1);
+          frags(u1, rb1, cb1, s1, fa1, fb1);
+        }
+        finish(u0, rb0, cb0, s0, fa0, fb0);
+        if (two) finish(u1, rb1, cb1, s1, fa1, fb1);
       }
     }
     __syncthreads();
-    // ---- (2) Z = Mask_0(mix_pre(S)) over rS
+    // ---- (2) Z = Mask_0(mix_pre(S)) over rS, in place (PASS_K keeps the core of S for dw_pre)
     {
-      const int n = A.rS.nr * A.rS.nc;
+      const int n = P.rS.nr * P.rS.nc;
       for (int x = tid; x < n; x += NTH) {
-        const int r = A.rS.r0 + x / A.rS.nc, c = A.rS.c0 + x % A.rS.nc;
+        const int r = P.rS.r0 + x / P.rS.nc, c = P.rS.c0 + x % P.rS.nc;
         const bool ok = valid(r, c);
         float s[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) s[u] = *at(lds, A.gS, u, r, c);
+        for (int u = 0; u < CH; ++u) s[u] = *at(lds, P.gS, u, r, c);
+        if (MODE == PASS_K && P.premix && r >= 0 && r < TB && c >= 0 && c < TB) {
+#pragma unroll
+          for (int u = 0; u < CH; ++u) *at(lds, P.gSc, u, r, c) = s[u];
+        }
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
           float z = s[u];
-          if (A.premix) {
+          if (P.premix) {
             z = 0.0f;
 #pragma unroll
             for (int v = 0; v < CH; ++v) z = __builtin_fmaf(w_s[u * CH + v], s[v], z);
           }
-          *at(lds, A.gZ, u, r, c) = ok ? z : 0.0f;
+          *at(lds, P.gZ, u, r, c) = ok ? z : 0.0f;
         }
       }
     }
@@ -316,87 +487,92 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
     // ---- (3) P = exp(C - lse) over rP (C = conv_pre(Z), or Z); zero where masked
     {
       auto finP = [&](int u, int r, int c, float cv) BWT_INLINE {
-        const float l = lse_s[u * A.rP.nr + (r - A.rP.r0)];
-        *at(lds, A.gP, u, r, c) = valid(r, c) ? __builtin_amdgcn_exp2f((cv - l) * 1.4426950408889634f) : 0.0f;
+        const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
+        *at(lds, P.gP, u, r, c) = valid(r, c) ? __builtin_amdgcn_exp2f((cv - l) * 1.4426950408889634f) : 0.0f;
       };
       if (pre) {
-        conv_region<CH>(lds, A.gZ, A.rP, th_s, A.cq, A.ck, A.h1, false, finP);
+        conv_region<CH>(lds, P.gZ, P.rP, th_s, P.cq, P.ck, P.h1, false, finP);
       } else {
-        const int n = CH * A.rP.nr * A.rP.nc;
+        const int n = CH * P.rP.nr * P.rP.nc;
         for (int x = tid; x < n; x += NTH) {
-          const int u = x / (A.rP.nr * A.rP.nc), rem = x % (A.rP.nr * A.rP.nc);
-          const int r = A.rP.r0 + rem / A.rP.nc, c = A.rP.c0 + rem % A.rP.nc;
-          finP(u, r, c, *at(lds, A.gZ, u, r, c));
+          const int u = x / (P.rP.nr * P.rP.nc), rem = x % (P.rP.nr * P.rP.nc);
+          const int r = P.rP.r0 + rem / P.rP.nc, c = P.rP.c0 + rem % P.rP.nc;
+          finP(u, r, c, *at(lds, P.gZ, u, r, c));
         }
       }
     }
     __syncthreads();
     // ---- (4) PASS_K: E = Mask_0(conv_post(P)) and A = mix_post(E) on the core tile
-    if (MODE == PASS_K && (post || A.postmix)) {
+    if (MODE == PASS_K && (post || P.postmix)) {
       const Reg core{0, 0, TB, TB};
       if (post) {
-        conv_region<CH>(lds, A.gP, core, th_s + thn, A.cq, A.ck, A.h2, false,
-                        [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, A.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
-        if (A.postmix) __syncthreads();
+        conv_region<CH>(lds, P.gP, core, th_s + thn, P.cq, P.ck, P.h2, false,
+                        [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, P.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
+        if (P.postmix) __syncthreads();
       }
-      if (A.postmix) {
+      if (P.postmix) {
         for (int x = tid; x < TB * TB; x += NTH) {
           const int r = x / TB, c = x % TB;
           float e[CH];
 #pragma unroll
-          for (int u = 0; u < CH; ++u) e[u] = *at(lds, A.gE, u, r, c);
+          for (int u = 0; u < CH; ++u) e[u] = *at(lds, P.gE, u, r, c);
 #pragma unroll
           for (int u = 0; u < CH; ++u) {
             float s = 0.0f;
 #pragma unroll
             for (int v = 0; v < CH; ++v) s = __builtin_fmaf(w_s[CH * CH + u * CH + v], e[v], s);
-            *at(lds, A.gAc, u, r, c) = s;
+            *at(lds, P.gAc, u, r, c) = s;
           }
         }
       }
       __syncthreads();
+      if (P.postmix) {  // dw_post partials: sum over the core row of dA_u E_v (before dA turns into dE)
+        if (wtask) {
+          const float* pa = at(lds, P.gdA, wu, wr, 0);
+          const float* pe = at(lds, P.gE, wv, wr, 0);
+          float s = 0.0f;
+#pragma unroll
+          for (int c = 0; c < TB; ++c) s = __builtin_fmaf(pa[c], pe[c], s);
+          acc_wpost += s;
+        }
+        __syncthreads();
+      }
     }
     // ---- (5) dE = Mask_0(mix_post^T(dA)) over rdA, in place; PASS_K: dw_post partials
     {
-      const int n = A.rdA.nr * A.rdA.nc;
+      const int n = P.rdA.nr * P.rdA.nc;
       for (int x = tid; x < n; x += NTH) {
-        const int r = A.rdA.r0 + x / A.rdA.nc, c = A.rdA.c0 + x % A.rdA.nc;
+        const int r = P.rdA.r0 + x / P.rdA.nc, c = P.rdA.c0 + x % P.rdA.nc;
         const bool ok = valid(r, c);
         float da[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) da[u] = *at(lds, A.gdA, u, r, c);
-        if (MODE == PASS_K && A.postmix && r >= 0 && r < TB && c >= 0 && c < TB) {
-#pragma unroll
-          for (int u = 0; u < CH; ++u)
-#pragma unroll
-            for (int v = 0; v < CH; ++v) acc_w2[u * CH + v] = __builtin_fmaf(da[u], *at(lds, A.gE, v, r, c), acc_w2[u * CH + v]);
-        }
+        for (int u = 0; u < CH; ++u) da[u] = *at(lds, P.gdA, u, r, c);
 #pragma unroll
         for (int v = 0; v < CH; ++v) {
           float s = da[v];
-          if (A.postmix) {
+          if (P.postmix) {
             s = 0.0f;
 #pragma unroll
             for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[CH * CH + u * CH + v], da[u], s);
           }
-          *at(lds, A.gdA, v, r, c) = ok ? s : 0.0f;
+          *at(lds, P.gdA, v, r, c) = ok ? s : 0.0f;
         }
       }
     }
     __syncthreads();
     // ---- (6) dP = conv_post^T(dE) over rdC; PASS_K: dtheta_post partials
     if (post) {
-      conv_region<CH>(lds, A.gdA, A.rdC, th_s + thn, A.cq, A.ck, A.h2, true,
-                      [&](int u, int r, int c, float pv) BWT_INLINE { *at(lds, A.gdC, u, r, c) = pv; });
-      if (MODE == PASS_K) dtheta_tasks<CH>(lds, A.gdA, A.gP, A.cq, A.ck, A.h2, acc_thpost);
+      conv_region<CH>(lds, P.gdA, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
+                      [&](int u, int r, int c, float pv) BWT_INLINE { *at(lds, P.gdC, u, r, c) = pv; });
+      if (MODE == PASS_K) dtheta_tasks<CH>(lds, P.gdA, P.gP, P.cq, P.ck, P.h2, acc_thpost);
       __syncthreads();
     }
     if (MODE == PASS_D) {
       // ---- D_i partials: sum over the tile's keys of P dP
       if (tid < CH * TB) {
         const int u = tid / TB, r = tid % TB;
-        const float* pr = at(lds, A.gP, u, r, 0);
-        const float* dr = at(lds, A.gdC, u, r, 0);
+        const float* pr = at(lds, P.gP, u, r, 0);
+        const float* dr = at(lds, P.gdC, u, r, 0);
         float s = 0.0f, l = 0.0f;
 #pragma unroll
         for (int c = 0; c < TB; ++c) {
@@ -411,20 +587,20 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
     }
     // ---- (7) dC = P (dP - D) over rdC, in place
     {
-      const int n = CH * A.rdC.nr * A.rdC.nc;
+      const int n = CH * P.rdC.nr * P.rdC.nc;
       for (int x = tid; x < n; x += NTH) {
-        const int u = x / (A.rdC.nr * A.rdC.nc), rem = x % (A.rdC.nr * A.rdC.nc);
-        const int r = A.rdC.r0 + rem / A.rdC.nc, c = A.rdC.c0 + rem % A.rdC.nc;
-        float* pd = at(lds, A.gdC, u, r, c);
-        *pd = *at(lds, A.gP, u, r, c) * (*pd - d_s[u * A.rdC.nr + (r - A.rdC.r0)]);
+        const int u = x / (P.rdC.nr * P.rdC.nc), rem = x % (P.rdC.nr * P.rdC.nc);
+        const int r = P.rdC.r0 + rem / P.rdC.nc, c = P.rdC.c0 + rem % P.rdC.nc;
+        float* pd = at(lds, P.gdC, u, r, c);
+        *pd = *at(lds, P.gP, u, r, c) * (*pd - d_s[u * P.rdC.nr + (r - P.rdC.r0)]);
       }
     }
     __syncthreads();
     // ---- (8) dL = Mask_0(conv_pre^T(dC)) on the core tile; dtheta_pre partials
     if (pre) {
-      conv_region<CH>(lds, A.gdC, Reg{0, 0, TB, TB}, th_s, A.cq, A.ck, A.h1, true,
-                      [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, A.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
-      dtheta_tasks<CH>(lds, A.gdC, A.gZ, A.cq, A.ck, A.h1, acc_thpre);
+      conv_region<CH>(lds, P.gdC, Reg{0, 0, TB, TB}, th_s, P.cq, P.ck, P.h1, true,
+                      [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, P.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
+      dtheta_tasks<CH>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, acc_thpre);
       __syncthreads();
     }
     // ---- (9) dS = mix_pre^T(dL) (dw_pre partials) and A as bf16 tiles; stage Q and dO rows
@@ -432,27 +608,27 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
       const int r = x / TB, c = x % TB;
       float dl[CH];
 #pragma unroll
-      for (int u = 0; u < CH; ++u) dl[u] = *at(lds, A.gdL, u, r, c);
-      if (A.premix) {
-#pragma unroll
-        for (int u = 0; u < CH; ++u)
-#pragma unroll
-          for (int v = 0; v < CH; ++v) acc_w[u * CH + v] = __builtin_fmaf(dl[u], *at(lds, A.gS, v, r, c), acc_w[u * CH + v]);
-      }
+      for (int u = 0; u < CH; ++u) dl[u] = *at(lds, P.gdL, u, r, c);
 #pragma unroll
       for (int v = 0; v < CH; ++v) {
         float s = dl[v];
-        if (A.premix) {
+        if (P.premix) {
           s = 0.0f;
 #pragma unroll
           for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[u * CH + v], dl[u], s);
         }
         dSb[(v * TB + r) * LDT + c] = (__bf16)s;
-        Ab[(v * TB + r) * LDT + c] = (__bf16)*at(lds, A.gAc, v, r, c);
+        Ab[(v * TB + r) * LDT + c] = (__bf16)*at(lds, P.gAc, v, r, c);
       }
     }
-    stage_rows(Qs, A.q, i0);
-    stage_rows(Os, A.dO, i0);
+    if (P.premix && wtask) {  // dw_pre partials: sum over the core row of dL_u S_v
+      const float* pl = at(lds, P.gdL, wu, wr, 0);
+      const float* ps = at(lds, P.gSc, wv, wr, 0);
+      float s = 0.0f;
+#pragma unroll
+      for (int c = 0; c < TB; ++c) s = __builtin_fmaf(pl[c], ps[c], s);
+      acc_wpre += s;
+    }
     __syncthreads();
     // ---- (10) dK += dS^T Q, dV += A^T dO (registers); dQ += dS K (atomics)
 #pragma unroll
@@ -461,15 +637,19 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
       if (kv < 2 * CH * NB) {
         const int kind = kv / (CH * NB), u = (kv / NB) % CH, nb = kv % NB;
         const s16x4 fa = tr_read((kind ? Ab : dSb) + u * TB * LDT, 4 * lg, 0, LDT, lane);
-        const s16x4 fb = tr_read((kind ? Os : Qs) + u * TB * A.ldk, 4 * lg, nb * 16, A.ldk, lane);
+        // the step's core query rows inside the staged Q (from row -rS.r0) and dO (from row 0)
+        const __bf16* xb = kind ? X2 + u * P.nx2 * P.ldk : X1 + (u * P.nx1 - P.rS.r0) * P.ldk;
+        const s16x4 fb = tr_read(xb, 4 * lg, nb * 16, P.ldk, lane);
         acc_kv[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, acc_kv[x], 0, 0, 0);
       }
     }
-    for (int t = wave; t < CH * NB; t += NTH / 64) {
+#pragma unroll
+    for (int y = 0; y < NQT; ++y) {
+      const int t = wave + y * (NTH / 64);
+      if (t >= CH * NB) break;
       const int u = t / NB, nb = t % NB;
       const s16x4 fa = *reinterpret_cast<const s16x4*>(dSb + (u * TB + lq) * LDT + 4 * lg);
-      const s16x4 fb = tr_read(Ks + u * TB * A.ldk, 4 * lg, nb * 16, A.ldk, lane);
-      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, kfrag[y], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int i = i0 + 4 * lg + x;
@@ -507,14 +687,11 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   }
   // ---- parameter-gradient partials of this workgroup: [b * n_tiles + tile][m][...]
   __syncthreads();
-  float* red = lds + A.off_red;
+  float* red = lds + P.off_red;
   const size_t prow = (size_t)b * A.n_tiles + tile;
-  const int ntap = CH * A.cq * A.ck;
-#pragma unroll
-  for (int side = 0; side < 2; ++side) {
-    float* part = side == 0 ? A.part_thpre : A.part_thpost;
-    if (!part) continue;
-    const float(&acc)[MAXR] = side == 0 ? acc_thpre : acc_thpost;
+  const int ntap = CH * P.cq * P.ck;
+  // dtheta: the row groups of each tap added in order
+  auto emit_theta = [&](const float (&acc)[MAXR], float* part) BWT_INLINE {
 #pragma unroll
     for (int rr = 0; rr < MAXR; ++rr) {
       const int t = tid + rr * NTH;
@@ -527,50 +704,61 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
       part[(prow * A.G + g) * ntap + x] = s;
     }
     __syncthreads();
-  }
-#pragma unroll
-  for (int side = 0; side < 2; ++side) {
-    float* part = side == 0 ? A.part_wpre : A.part_wpost;
-    if (!part) continue;
-    const float(&acc)[CH * CH] = side == 0 ? acc_w : acc_w2;
-    // sum over the workgroup's threads in a fixed order: wave sums, then the waves in turn
-#pragma unroll
-    for (int x = 0; x < CH * CH; ++x) {
-      float s = acc[x];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-      if (lane == 0) red[wave * CH * CH + x] = s;
-    }
+  };
+  // mixing weights: the rows of each (u, v) added in order
+  auto emit_w = [&](float acc, float* part) BWT_INLINE {
+    if (wtask) red[tid] = acc;
     __syncthreads();
     if (tid < CH * CH) {
       float s = 0.0f;
-      for (int w = 0; w < NTH / 64; ++w) s += red[w * CH * CH + tid];
+      for (int r = 0; r < TB; ++r) s += red[tid * TB + r];
       part[(prow * A.G + g) * CH * CH + tid] = s;
     }
     __syncthreads();
-  }
+  };
+  if (A.part_thpre) emit_theta(acc_thpre, A.part_thpre);
+  if (A.part_thpost) emit_theta(acc_thpost, A.part_thpost);
+  if (A.part_wpre) emit_w(acc_wpre, A.part_wpre);
+  if (A.part_wpost) emit_w(acc_wpost, A.part_wpost);
 }
 
 // Launch of one pass for a head group of ch heads; lds = dynamic LDS bytes of the plan.
-template <int D, int CH, int MODE>
+template <int D, int CH, int MODE, int SPEC>
 hipError_t launch_one(const BwArgs& a, size_t lds, unsigned grid, hipStream_t st) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_tile_kernel<D, CH, MODE>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_tile_kernel<D, CH, MODE, SPEC>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_tile_kernel<D, CH, MODE>), dim3(grid), dim3(NTH), lds, st, a);
+  hipLaunchKernelGGL((bwd_tile_kernel<D, CH, MODE, SPEC>), dim3(grid), dim3(NTH), lds, st, a);
   return hipGetLastError();
 }
 
+// Specialised shapes instantiated per (head size, heads per group): 1-3 for four-head groups of
+// 128 channels, 4 for two- and four-head groups of 96 or 128 channels.
+__host__ __device__ constexpr bool spec_built(int spec, int ch, int d) {
+  return (spec >= 1 && spec <= 3 && ch == 4 && d == 128) || (spec == 4 && d >= 96 && (ch == 2 || ch == 4));
+}
+
+template <int D, int CH, int MODE>
+hipError_t launch_spec(const BwArgs& a, int spec, size_t lds, unsigned grid, hipStream_t st) {
+  switch (spec) {
+    case 1: if constexpr (spec_built(1, CH, D)) return launch_one<D, CH, MODE, 1>(a, lds, grid, st); break;
+    case 2: if constexpr (spec_built(2, CH, D)) return launch_one<D, CH, MODE, 2>(a, lds, grid, st); break;
+    case 3: if constexpr (spec_built(3, CH, D)) return launch_one<D, CH, MODE, 3>(a, lds, grid, st); break;
+    case 4: if constexpr (spec_built(4, CH, D)) return launch_one<D, CH, MODE, 4>(a, lds, grid, st); break;
+  }
+  return launch_one<D, CH, MODE, 0>(a, lds, grid, st);
+}
+
 template <int D>
-hipError_t launch_tiles(const BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st) {
+hipError_t launch_tiles(const BwArgs& a, int ch, int mode, int spec, size_t lds, unsigned grid, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   switch (ch * 2 + mode) {
-    case 2: return launch_one<D, 1, PASS_D>(a, lds, grid, st);
-    case 3: return launch_one<D, 1, PASS_K>(a, lds, grid, st);
-    case 4: return launch_one<D, 2, PASS_D>(a, lds, grid, st);
-    case 5: return launch_one<D, 2, PASS_K>(a, lds, grid, st);
-    case 8: return launch_one<D, 4, PASS_D>(a, lds, grid, st);
-    case 9: return launch_one<D, 4, PASS_K>(a, lds, grid, st);
+    case 2: return launch_spec<D, 1, PASS_D>(a, spec, lds, grid, st);
+    case 3: return launch_spec<D, 1, PASS_K>(a, spec, lds, grid, st);
+    case 4: return launch_spec<D, 2, PASS_D>(a, spec, lds, grid, st);
+    case 5: return launch_spec<D, 2, PASS_K>(a, spec, lds, grid, st);
+    case 8: return launch_spec<D, 4, PASS_D>(a, spec, lds, grid, st);
+    case 9: return launch_spec<D, 4, PASS_K>(a, spec, lds, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -3,8 +3,9 @@
 
 namespace mta {
 
-hipError_t launch_bwd_tiles_d64(const bwt::BwArgs& a, int ch, int mode, size_t lds, unsigned grid, hipStream_t st) {
-  return bwt::launch_tiles<64>(a, ch, mode, lds, grid, st);
+hipError_t launch_bwd_tiles_d64(const bwt::BwArgs& a, int ch, int mode, int spec, size_t lds, unsigned grid,
+                                 hipStream_t st) {
+  return bwt::launch_tiles<64>(a, ch, mode, spec, lds, grid, st);
 }
 
 }  // namespace mta
