@@ -177,11 +177,13 @@ def test_backward_fused_rejections():
         ta.backward_fused(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], 0.8, dout=d["q"].clone(),
                           lse=lse, out_pre_gn=None, **kw)
     assert e.value.status == ta.mta.ERR_INVALID_ARG
-    # the largest kernels on both sides with four-head groups do not fit the LDS of one tile
-    q = torch.zeros((1, 32, 4, 128), dtype=torch.bfloat16, device="cuda")
-    th = torch.zeros((2, 4, 8, 17), device="cuda")
-    w = torch.zeros((2, 1, 4, 4), device="cuda")
-    with pytest.raises(ta.MTAError) as e:
-        ta.backward_fused(q, q.clone(), q.clone(), th, w, None, None, 1.0, dout=q.clone(),
-                          lse=torch.zeros((1, 32, 4), device="cuda"), c_q=8, c_k=17, c_h=4, kq="both", mix="both")
-    assert e.value.status == ta.mta.ERR_UNSUPPORTED
+
+
+def test_backward_fused_largest_kernels_on_both_sides():
+    """8 x 17 kernels before and after softmax with four-head groups mixed on both sides: the
+    largest tile regions, which still fit the LDS of one workgroup."""
+    cfg = mta_inputs.MTAConfig("bwd_big", 1, 70, 4, 128, 8, 17, 4, "both", "both", True, "bf16", 0.1, 0.1, 1.0, 0.0,
+                               0.8, seed=38)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what="fused 8x17 both sides")

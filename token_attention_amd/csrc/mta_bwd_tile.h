@@ -23,10 +23,15 @@
 // sums each row of that P (the forward reached its lse through fp16-rounded logits, so the sum
 // is 1 only to about 1e-4) and hands PASS_K lse + log(sum) and D / sum: the normalisation then
 // matches this recomputation to fp32 rounding, which a row with one key (exact gradient zero)
-// needs. A tile
-// step recomputes each map on the region its adjoint needs (the core 16 x 16 tile grown by the
-// convolutions' reach): S = QK^T and dA = dO V^T on MFMA (bf16 operands read from global
-// memory), the masks, mixing, convolutions and softmax gradient in fp32 on the VALU from LDS.
+// needs.
+//
+// A tile step recomputes each map on the region its adjoint needs (the core 16 x 16 tile grown
+// by the convolutions' reach). S = QK^T and dA = dO V^T run on MFMA, one 16 x 16 block of every
+// head of the group per task, so that the mixing, the masks and (without a convolution before
+// softmax) the exponential happen in registers on the MFMA result; the convolutions, the
+// softmax gradient and the parameter-gradient sums run in fp32 on the VALU from LDS, the
+// softmax gradient folded into the convolutions' epilogues. A step has three to five
+// workgroup barriers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,36 +42,38 @@
 namespace mta {
 namespace bwt {
 
-constexpr int TB = 16;           // core tile: TB query rows x TB keys
-constexpr int NTH = 512;         // threads per workgroup
-constexpr int CKM = 17;          // largest key extent of a convolution
-constexpr int NRQ = 4;           // the rows of a parameter-gradient task split in NRQ groups
-constexpr int MAXR = 5;          // rounds of those tasks per thread: 5 * NTH >= 4 * 8 * 17 * NRQ
+constexpr int TB = 16;   // core tile: TB query rows x TB keys
+constexpr int CKM = 17;  // largest key extent of a convolution
+constexpr int NRQ = 4;   // the rows of a parameter-gradient task split in NRQ groups
+constexpr int LDT = 20;  // leading dimension of the 16 x 16 bf16 tiles
 enum { PASS_D = 0, PASS_K = 1 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// A rectangle of a map, relative to the tile origin (i0, j0).
+// A rectangle of a map, relative to the tile origin (i0, j0): rows [r0, r0 + nr), columns
+// [c0, c0 + nc).
 struct Reg {
   int r0, c0, nr, nc;
 };
-// Storage of a map in LDS: rows from r0 and columns from c0 (tile-relative), leading
-// dimension ld, head stride hs, offset off (floats). Maps that alias share one storage.
+// Storage of a map in LDS: the rectangle it holds, leading dimension ld, head stride hs,
+// offset off (floats). Maps that are not needed alias the storage they would be made from.
 struct Geo {
   int r0, c0, ld, hs, off;
 };
 
-// The regions a tile step computes and their LDS storage. Maps that are not needed alias
-// the storage of the map they are computed from.
 struct Plan {
   int cq, ck, a1, h1, a2, h2;  // reach of the convolution before (1) / after (2) softmax, 0 if absent
   int pre, post, premix, postmix;
-  Reg rS, rP, rdC, rdA;  // regions computed: S / Z, P, dP / dC, dA / dE
-  Geo gS, gSc, gZ, gP, gE, gAc, gdA, gdC, gdL;  // gSc: PASS_K core copy of S (mixing before softmax)
-  int off_lse, off_d, off_th, off_w, off_red;  // small LDS arrays (floats)
-  int off_bf;            // bf16 staging, in floats from the pool start
-  int ldk;               // leading dimension of the staged operand rows (bf16 elements)
-  int nx1, nx2;          // staged rows per head: rows (PASS_K) or columns (PASS_D) of rS and rdA
+  Reg rZ, rP, rdC, rdE;        // regions: Z (with a convolution before softmax), P, dC, dE
+  Reg mS, mA;                  // MFMA regions (16 x 16 blocks) covering Z or P, and dE
+  Geo gZ, gP, gSc, gdE, gdAc, gE, gdC, gdL;
+  int off_lse, off_d, off_th, off_w;  // small arrays (floats): lse and D double-buffered per step
+  int ldk;               // leading dimension of the staged rows (bf16 elements)
+  // operand rows resident for the whole sweep (bf16): PASS_K the keys' K (over the columns of
+  // mS) and V (columns of mA), PASS_D the query rows' Q (rows of mS) and dO (rows of mA)
+  int off_x, off_y, nrx, nry;
+  int resident;          // 0: those rows did not fit; they are read from global memory instead
+  int off_bf;            // PASS_K bf16 staging: Q and dO of the core rows, dS and A tiles
   int lds_floats;        // pool size
 };
 
@@ -74,17 +81,21 @@ __host__ __device__ constexpr int r4c(int x) { return (x + 3) & ~3; }
 __host__ __device__ constexpr int r16c(int x) { return (x + 15) & ~15; }
 __host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
 __host__ __device__ constexpr Geo own_geo(const Reg& R, int ch, int& pool) {
-  Geo G{R.r0, R.c0, r4c(R.nc) + 4, 0, pool};
+  Geo G{R.r0, R.c0, r4c(R.nc) + 1, 0, pool};
   G.hs = R.nr * G.ld;
   pool = r4c(pool + ch * G.hs);
   return G;
 }
+__host__ __device__ constexpr Reg grow(const Reg& R, int up, int down, int side) {
+  return Reg{R.r0 - up, R.c0 - side, R.nr + up + down, r4c(R.nc + 2 * side)};
+}
 
-// kq, mix: placement bits, 1 before softmax, 2 after. The regions, from the core tile outwards:
-// PASS_K: dC on the rows the adjoint of the convolution before softmax reads; P there and
-// where the convolution after softmax reads for the core; S around P; dA around dC.
-// PASS_D: P and dP on the core tile only.
-__host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q, int c_k, int ch, int d) {
+// kq, mix: placement bits, 1 before softmax, 2 after.
+// PASS_K: dC on the rows and columns the adjoint of the convolution before softmax reads for
+// the core tile; P there and where the convolution after softmax reads for the core; Z around
+// P; dE around dC. PASS_D: P and dP on the core tile, Z and dE around them.
+__host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q, int c_k, int ch, int d,
+                                             bool resident = true) {
   Plan p{};
   p.pre = (kq & 1) != 0;
   p.post = (kq & 2) != 0;
@@ -97,49 +108,51 @@ __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q,
   p.a2 = p.post ? c_q - 1 : 0;
   p.h2 = p.post ? (c_k - 1) / 2 : 0;
   const Reg core{0, 0, TB, TB};
-  if (mode == PASS_K) {
-    p.rdC = Reg{0, -p.h1, TB + p.a1, r4c(TB + 2 * p.h1)};
+  const bool K = mode == PASS_K;
+  p.rdC = K ? Reg{0, -p.h1, TB + p.a1, r4c(TB + 2 * p.h1)} : core;
+  if (K) {
     const int hc = imax(p.h1, p.h2);
-    const int c_end = imax(p.rdC.c0 + p.rdC.nc, TB + p.h2);
-    p.rP = Reg{-p.a2, -hc, TB + p.a1 + p.a2, r4c(c_end + hc)};
+    p.rP = Reg{-p.a2, -hc, TB + p.a1 + p.a2, r4c(TB + 2 * hc)};
   } else {
-    p.rdC = core;
     p.rP = core;
   }
-  p.rS = Reg{p.rP.r0 - p.a1, p.rP.c0 - p.h1, r16c(p.rP.nr + p.a1), r16c(p.rP.nc + 2 * p.h1)};
-  p.rdA = Reg{0, p.rdC.c0 - p.h2, r16c(p.rdC.nr + p.a2), r16c(p.rdC.nc + 2 * p.h2)};
+  p.rZ = grow(p.rP, p.a1, 0, p.h1);
+  p.rdE = Reg{p.rdC.r0, p.rdC.c0 - p.h2, p.rdC.nr + p.a2, r4c(p.rdC.nc + 2 * p.h2)};
+  const Reg& cover = p.pre ? p.rZ : p.rP;
+  p.mS = Reg{cover.r0, cover.c0, r16c(cover.nr), r16c(cover.nc)};
+  p.mA = Reg{p.rdE.r0, p.rdE.c0, r16c(p.rdE.nr), r16c(p.rdE.nc)};
   int pool = 0;
-  p.gS = own_geo(p.rS, ch, pool);
-  p.gZ = p.gS;  // Z is formed in place
-  p.gSc = (mode == PASS_K && p.premix) ? own_geo(core, ch, pool) : p.gS;
-  p.gP = p.pre ? own_geo(p.rP, ch, pool) : p.gZ;
-  if (mode == PASS_K) {
-    p.gE = p.post ? own_geo(core, ch, pool) : p.gP;
-    p.gAc = p.postmix ? own_geo(core, ch, pool) : p.gE;
-  } else {
-    p.gE = p.gP;
-    p.gAc = p.gP;
-  }
-  p.gdA = own_geo(p.rdA, ch, pool);
-  p.gdC = p.post ? own_geo(p.rdC, ch, pool) : p.gdA;
-  p.gdL = (mode == PASS_K && p.pre) ? own_geo(core, ch, pool) : p.gdC;
+  p.gP = own_geo(p.rP, ch, pool);
+  p.gZ = p.pre ? own_geo(p.rZ, ch, pool) : p.gP;
+  p.gSc = (K && p.premix) ? own_geo(core, ch, pool) : p.gP;
+  p.gdE = own_geo(p.rdE, ch, pool);
+  p.gdAc = (K && p.postmix) ? own_geo(core, ch, pool) : p.gdE;
+  p.gE = (K && p.post) ? own_geo(core, ch, pool) : p.gP;
+  // dC: its own storage after a convolution (dP is made from dE), else in place over dE
+  p.gdC = (K && p.post) ? own_geo(p.rdC, ch, pool) : p.gdE;
+  p.gdL = (K && p.pre) ? own_geo(core, ch, pool) : p.gdC;
   p.off_lse = pool;
-  pool = r4c(pool + ch * p.rP.nr);
+  pool = r4c(pool + 2 * ch * p.rP.nr);
   p.off_d = pool;
-  pool = r4c(pool + ch * p.rdC.nr);
+  pool = r4c(pool + 2 * ch * p.rdC.nr);
   p.off_th = pool;
   pool = r4c(pool + 2 * ch * p.cq * p.ck);
   p.off_w = pool;
   pool = r4c(pool + 2 * ch * ch);
   p.ldk = d + 8;
-  p.nx1 = mode == PASS_K ? p.rS.nr : p.rS.nc;
-  p.nx2 = mode == PASS_K ? p.rdA.nr : p.rdA.nc;
+  p.nrx = K ? p.mS.nc : p.mS.nr;
+  p.nry = K ? p.mA.nc : p.mA.nr;
+  p.resident = resident;
+  p.off_x = pool;
+  if (resident) pool += (ch * p.nrx * p.ldk) / 2;
+  p.off_y = pool;
+  if (resident) pool += (ch * p.nry * p.ldk) / 2;
   p.off_bf = pool;
-  pool += (ch * (p.nx1 + p.nx2) * p.ldk) / 2;
-  if (mode == PASS_K) pool += (2 * ch * TB * 24) / 2;
-  p.off_red = 0;  // the end-of-sweep reductions reuse the pool from its start
+  if (K) pool += (2 * ch * TB * p.ldk + 2 * ch * TB * LDT) / 2;
+  // the end-of-sweep reductions reuse the pool from its start
   pool = imax(pool, imax(ch * p.cq * p.ck * NRQ, ch * ch * TB));
   p.lds_floats = r4c(pool);
+  if (resident && p.lds_floats * 4 > 160 * 1024) return make_plan(mode, kq, mix, c_q, c_k, ch, d, false);
   return p;
 }
 
@@ -156,6 +169,10 @@ __host__ __device__ constexpr SpecShape spec_shape(int spec) {
                    : SpecShape{0, 0, 1, 1};
 }
 constexpr int NSPEC = 5;
+
+// Threads per workgroup: 256 when two workgroups fit the LDS of a CU (their barriers then
+// overlap), else 512.
+__host__ __device__ constexpr int threads_for(const Plan& p) { return p.lds_floats * 4 <= 80 * 1024 ? 256 : 512; }
 
 struct BwArgs {
   const __bf16* q;
@@ -187,16 +204,19 @@ struct BwArgs {
 __device__ __forceinline__ float* at(float* lds, const Geo& G, int u, int r, int c) {
   return lds + G.off + u * G.hs + (r - G.r0) * G.ld + (c - G.c0);
 }
+__device__ __forceinline__ bool inside(const Reg& R, int r, int c) {
+  return r >= R.r0 && r < R.r0 + R.nr && c >= R.c0 && c < R.c0 + R.nc;
+}
 
-// dst[u][r][c] over region R of every head: sum_{a, e} th[u][a][e] * src[u][r + sa a][c + sa (e - h)],
-// sa = -1 for the convolution, +1 for its adjoint; then fin(u, r, c, value). Each thread makes four
-// consecutive columns of one row from a window of 4 + 2h source values per lag.
-template <int CH, class Fin>
+// dst over region R of every head: sum_{a, e} th[u][a][e] * src[u][r + sa a][c + sa (e - h)],
+// sa = -1 for the convolution, +1 for its adjoint; fin(u, r, c, value) stores it. Each thread
+// makes four consecutive columns of one row from a window of 4 + 2h source values per lag.
+template <int CH, int NT, class Fin>
 __device__ __forceinline__ void conv_region(float* lds, const Geo& src, const Reg& R, const float* th, int cq,
                                             int ck, int h, bool adjoint, Fin fin) {
-  const int ncb = (R.nc + 3) >> 2;
+  const int ncb = R.nc >> 2;  // R.nc is a multiple of 4
   const int n = CH * R.nr * ncb;
-  for (int t = threadIdx.x; t < n; t += NTH) {
+  for (int t = threadIdx.x; t < n; t += NT) {
     const int u = t / (R.nr * ncb);
     const int rem = t - u * R.nr * ncb;
     const int r = R.r0 + rem / ncb;
@@ -223,20 +243,19 @@ __device__ __forceinline__ void conv_region(float* lds, const Geo& src, const Re
       }
     }
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-      if (c4 + qq < R.c0 + R.nc) fin(u, r, c4 + qq, o[qq]);
+    for (int qq = 0; qq < 4; ++qq) fin(u, r, c4 + qq, o[qq]);
   }
 }
 
 // Partial sums of dtheta[u][a][e] over the core tile: sum_{r, c} G[u][r][c] X[u][r - a][c - e + h],
 // for task t = ((u * cq + a) * ck + e) * NRQ + rq covering rows rq, rq + NRQ, ...
-template <int CH>
+template <int CH, int NT, int MAXR>
 __device__ __forceinline__ void dtheta_tasks(float* lds, const Geo& gG, const Geo& gX, int cq, int ck, int h,
                                              float (&acc)[MAXR]) {
   const int n = CH * cq * ck * NRQ;
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
-    const int t = threadIdx.x + rr * NTH;
+    const int t = threadIdx.x + rr * NT;
     if (t < n) {
       const int rq = t % NRQ;
       const int e = (t / NRQ) % ck;
@@ -260,8 +279,8 @@ __device__ __forceinline__ s16x4 tr_read(const __bf16* base, int row0, int col0,
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-template <int D, int CH, int MODE, int SPEC>
-__global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
+template <int D, int CH, int MODE, int SPEC, int NT>
+__global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   // the plan: compile-time constants for a specialised shape, so that loop bounds, divisors and
   // LDS offsets fold away
@@ -273,8 +292,11 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   } else {
     P = A.P;
   }
+  constexpr int NW = NT / 64;
   constexpr int NB = D / 16;
-  constexpr int NKV = (2 * CH * NB + NTH / 64 - 1) / (NTH / 64);  // dK / dV blocks per wave
+  constexpr int NKV = (2 * CH * NB + NW - 1) / NW;  // dK / dV blocks per wave
+  constexpr int NQT = (CH * NB + NW - 1) / NW;      // dQ blocks per wave
+  constexpr int MAXR = (4 * 8 * CKM * NRQ + NT - 1) / NT;  // dtheta task rounds
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
   const int T = A.T, M = A.M;
@@ -285,46 +307,61 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   const int tile = MODE == PASS_D ? A.n_tiles - 1 - tile_rank : tile_rank;
   const bool pre = P.pre, post = P.post;
   const size_t bT = (size_t)b * T;
+  const Reg core{0, 0, TB, TB};
 
   float* th_s = lds + P.off_th;  // [2][CH][cq][ck]: before softmax, then after
   float* w_s = lds + P.off_w;    // [2][CH][CH]
-  float* lse_s = lds + P.off_lse;
-  float* d_s = lds + P.off_d;
   const int thn = CH * P.cq * P.ck;
-  for (int x = tid; x < 2 * thn; x += NTH) {
+  for (int x = tid; x < 2 * thn; x += NT) {
     const float* src = x < thn ? A.th_pre : A.th_post;
     const int y = x < thn ? x : x - thn;
     th_s[x] = src ? src[(size_t)g * thn + y] : 0.0f;
   }
-  for (int x = tid; x < 2 * CH * CH; x += NTH) {
+  for (int x = tid; x < 2 * CH * CH; x += NT) {
     const float* src = x < CH * CH ? A.w_pre : A.w_post;
     const int y = x < CH * CH ? x : x - CH * CH;
     w_s[x] = src ? src[(size_t)g * CH * CH + y] : 0.0f;
   }
+  // resident operand rows (see Plan::off_x); PASS_K bf16 staging: Q and dO of the step's core
+  // rows, the dS and A tiles
+  __bf16* Xr = reinterpret_cast<__bf16*>(lds + P.off_x);
+  __bf16* Yr = reinterpret_cast<__bf16*>(lds + P.off_y);
+  __bf16* Qc = reinterpret_cast<__bf16*>(lds + P.off_bf);
+  __bf16* Oc = Qc + CH * TB * P.ldk;
+  __bf16* dSb = Oc + CH * TB * P.ldk;
+  __bf16* Ab = dSb + CH * TB * LDT;
 
-  // staged bf16 rows (PASS_K): K of the workgroup's keys, Q and dO of the step's query rows,
-  // and the step's dS and A tiles
-  __bf16* X1 = reinterpret_cast<__bf16*>(lds + P.off_bf);  // [CH][nx1] rows: Q (PASS_K) or K (PASS_D)
-  __bf16* X2 = X1 + CH * P.nx1 * P.ldk;                        // [CH][nx2] rows: dO (PASS_K) or V (PASS_D)
-  __bf16* dSb = X2 + CH * P.nx2 * P.ldk;
-  __bf16* Ab = dSb + CH * TB * 24;
-  constexpr int LDT = 24;  // leading dimension of the 16 x 16 bf16 tiles
-
-  // stage rows r0 .. r0 + 15 of head u of X (bf16) into dst[u][16][ldk]; zeros past T
-  auto stage_rows = [&](__bf16* dst, const __bf16* X, int r0) BWT_INLINE {
+  // rows r0 .. r0 + n - 1 of every head of X (bf16) into dst[u][n][ldk]; zeros outside [0, T)
+  auto stage_rows = [&](__bf16* dst, const __bf16* X, int r0, int n) BWT_INLINE {
     constexpr int PER = D / 8;  // 16-byte pieces per row
-    for (int x = tid; x < CH * TB * PER; x += NTH) {
-      const int u = x / (TB * PER), rr = (x / PER) % TB, c = x % PER;
+    for (int x = tid; x < CH * n * PER; x += NT) {
+      const int row = x / PER, c = x % PER;
+      const int u = row / n, rr = row - u * n;
       const int i = r0 + rr;
       uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (i < T) val = *reinterpret_cast<const uint4*>(X + ((bT + i) * M + g * CH + u) * D + c * 8);
-      *reinterpret_cast<uint4*>(dst + (u * TB + rr) * P.ldk + c * 8) = val;
+      if (i >= 0 && i < T) val = *reinterpret_cast<const uint4*>(X + ((bT + i) * M + g * CH + u) * D + c * 8);
+      *reinterpret_cast<uint4*>(dst + (u * n + rr) * P.ldk + c * 8) = val;
+    }
+  };
+  // the step's row statistics (lse over rP rows, D over rdC rows) into buffer slot `buf`
+  auto load_stats = [&](int i_base, int buf) BWT_INLINE {
+    float* ls = lds + P.off_lse + buf * CH * P.rP.nr;
+    for (int x = tid; x < CH * P.rP.nr; x += NT) {
+      const int u = x / P.rP.nr, i = i_base + P.rP.r0 + x % P.rP.nr;
+      ls[x] = (i >= 0 && i < T) ? (MODE == PASS_D ? A.lse : A.lse_c)[(bT + i) * M + g * CH + u] : 0.0f;
+    }
+    if (MODE == PASS_K) {
+      float* ds = lds + P.off_d + buf * CH * P.rdC.nr;
+      for (int x = tid; x < CH * P.rdC.nr; x += NT) {
+        const int u = x / P.rdC.nr, i = i_base + P.rdC.r0 + x % P.rdC.nr;
+        ds[x] = (i >= 0 && i < T) ? A.dvec[(bT + i) * M + g * CH + u] : 0.0f;
+      }
     }
   };
 
-  // persistent accumulators
-  // acc_wpre / acc_wpost: task (u, v, r) = thread CH TB u + TB v + r < CH^2 TB of the mixing gradients,
-  // row r of the core tile
+  // persistent accumulators. acc_wpre / acc_wpost: task (u, v, r) = thread CH TB u + TB v + r
+  // < CH^2 TB of the mixing gradients, row r of the core tile. acc_d, acc_l (PASS_D): the
+  // thread's share of D and of the row sum of P for its (head, row).
   float acc_thpre[MAXR], acc_thpost[MAXR], acc_wpre = 0.0f, acc_wpost = 0.0f, acc_d = 0.0f, acc_l = 0.0f;
   const int wu = tid / (CH * TB), wv = (tid / TB) % CH, wr = tid % TB;
   const bool wtask = tid < CH * CH * TB;
@@ -334,334 +371,328 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
 #pragma unroll
   for (int x = 0; x < NKV; ++x) acc_kv[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // PASS_K: the dQ tasks of this wave (head u, 16 channels nb) and their K operand, K rows of
-  // the workgroup's keys read transposed once for the whole sweep (staged through X1)
-  constexpr int NQT = (CH * NB + NTH / 64 - 1) / (NTH / 64);
+  // PASS_K: the dQ tasks of this wave (head u, 16 channels nb) and their K operand, the K rows
+  // of the workgroup's keys (inside the resident K rows) read transposed once for the sweep
   s16x4 kfrag[NQT];
   int i0, j0;
   if (MODE == PASS_K) {
     j0 = tile * TB;
     i0 = j0;
-    stage_rows(X1, A.k, j0);
+    if (P.resident) {
+      stage_rows(Xr, A.k, j0 + P.mS.c0, P.nrx);
+      stage_rows(Yr, A.v, j0 + P.mA.c0, P.nry);
+    } else {
+      stage_rows(Qc, A.k, j0, TB);  // the K rows of the keys, for the transposed reads below
+    }
+    load_stats(i0, 0);
     __syncthreads();
+    const __bf16* kc = P.resident ? Xr - P.mS.c0 * P.ldk : Qc;  // K row j0 of head 0
+    const int kstride = P.resident ? P.nrx : TB;                  // rows per head
 #pragma unroll
     for (int x = 0; x < NQT; ++x) {
-      const int t = wave + x * (NTH / 64);
-      if (t < CH * NB) kfrag[x] = tr_read(X1 + (t / NB) * TB * P.ldk, 4 * lg, (t % NB) * 16, P.ldk, lane);
+      const int t = wave + x * NW;
+      if (t < CH * NB) kfrag[x] = tr_read(kc + (t / NB) * kstride * P.ldk, 4 * lg, (t % NB) * 16, P.ldk, lane);
     }
+    if (!P.resident) __syncthreads();  // Qc is rewritten by the first step
   } else {
     i0 = tile * TB;
     j0 = 0;
+    if (P.resident) {
+      stage_rows(Xr, A.q, i0 + P.mS.r0, P.nrx);
+      stage_rows(Yr, A.dO, i0 + P.mA.r0, P.nry);
+    }
+    load_stats(i0, 0);
+    __syncthreads();
   }
 
-  for (;;) {
+  for (int step = 0;; ++step) {
     if (MODE == PASS_K ? i0 >= T : j0 > i0) break;
-    __syncthreads();  // the previous step is done with every LDS map
+    const int buf = MODE == PASS_K ? (step & 1) : 0;
+    const float* lse_s = lds + P.off_lse + buf * CH * P.rP.nr;
+    const float* d_s = lds + P.off_d + buf * CH * P.rdC.nr;
     auto valid = [&](int r, int c) BWT_INLINE {
       const int i = i0 + r, j = j0 + c;
       return (j >= 0) & (j <= i) & (i < T);
     };
-    // ---- (1) the operand rows that change from step to step (PASS_K: Q and dO of the query
-    // rows, PASS_D: K and V of the keys) into LDS in one round of loads, with the row
-    // statistics; then S = Q K^T / sqrt(d) and dA = dO V^T on MFMA, the operand that is fixed for
-    // the sweep read from global memory (it stays in the caches)
+    // ---- (1) MFMA: S over mS and dA over mA for every head of the group. A task is one row of
+    // 16 x 16 blocks (PASS_K: its Q or dO rows from global memory, once per step; K or V rows
+    // from the resident LDS copy) or one column of blocks (PASS_D, the other way round).
+    // S block: mixing before softmax, Mask_0, and Z into gZ (with a convolution before softmax)
+    // or P = exp(Z - lse) into gP; PASS_K keeps the core of S (dw_pre). dA block: PASS_K keeps
+    // the core (dw_post), then dE = Mask_0(mix_post^T(dA)) into gdE. PASS_K also copies the core
+    // rows of Q and dO into Qc and Oc.
+    if (MODE == PASS_K && step > 0) __syncthreads();  // the previous step's MFMAs read Qc and Oc
     {
-      constexpr int PER = D / 8;  // 16-byte pieces per row
-      const int n1 = CH * P.nx1 * PER, n2 = CH * P.nx2 * PER;
-      const int o1 = MODE == PASS_K ? i0 + P.rS.r0 : j0 + P.rS.c0;
-      const int o2 = MODE == PASS_K ? i0 + P.rdA.r0 : j0 + P.rdA.c0;
-      const __bf16* s1 = MODE == PASS_K ? A.q : A.k;
-      const __bf16* s2 = MODE == PASS_K ? A.dO : A.v;
-      for (int x = tid; x < n1 + n2; x += NTH) {
-        const bool first = x < n1;
-        const int y = first ? x : x - n1;
-        const int row = y / PER, c = y % PER;  // row of [CH][n] rows
-        const int n = first ? P.nx1 : P.nx2;
-        const int u = row / n, rr = row - u * n;
-        const int gi = (first ? o1 : o2) + rr;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (gi >= 0 && gi < T) val = *reinterpret_cast<const uint4*>((first ? s1 : s2) + ((bT + gi) * M + g * CH + u) * D + c * 8);
-        *reinterpret_cast<uint4*>((first ? X1 : X2) + (u * n + rr) * P.ldk + c * 8) = val;
-      }
-    }
-    for (int x = tid; x < CH * P.rP.nr; x += NTH) {
-      const int u = x / P.rP.nr, r = P.rP.r0 + x % P.rP.nr;
-      const int i = i0 + r;
-      lse_s[x] = (i >= 0 && i < T) ? (MODE == PASS_D ? A.lse : A.lse_c)[(bT + i) * M + g * CH + u] : 0.0f;
-    }
-    if (MODE == PASS_K) {
-      for (int x = tid; x < CH * P.rdC.nr; x += NTH) {
-        const int u = x / P.rdC.nr, r = P.rdC.r0 + x % P.rdC.nr;
-        const int i = i0 + r;
-        d_s[x] = (i >= 0 && i < T) ? A.dvec[(bT + i) * M + g * CH + u] : 0.0f;
-      }
-    }
-    __syncthreads();
-    {
-      const int nbS = (P.rS.nr / 16) * (P.rS.nc / 16), nbA = (P.rdA.nr / 16) * (P.rdA.nc / 16);
-      const int ntask = CH * (nbS + nbA);
-      // task t: map (S or dA), head, 16 x 16 block; two tasks per wave at a time so that their
-      // global loads are in flight together
-      auto task = [&](int t, int& u, int& rb, int& cb, bool& isS) BWT_INLINE {
-        isS = t < CH * nbS;
-        const int tt = isS ? t : t - CH * nbS;
-        const Reg& R = isS ? P.rS : P.rdA;
-        const int nbc = R.nc / 16;
-        u = tt / (isS ? nbS : nbA);
-        const int blk = tt % (isS ? nbS : nbA);
-        rb = R.r0 + 16 * (blk / nbc);
-        cb = R.c0 + 16 * (blk % nbc);
-      };
-      // operand rows: the staged side from LDS, the fixed side from global memory
-      auto frags = [&](int u, int rb, int cb, bool isS, bf16x8 (&fa)[D / 32], bf16x8 (&fb)[D / 32]) BWT_INLINE {
-        const int m = g * CH + u;
-        const __bf16* pa;
-        const __bf16* pb;
-        if (MODE == PASS_K) {
-          pa = (isS ? X1 + (u * P.nx1 + rb - P.rS.r0 + lq) * P.ldk : X2 + (u * P.nx2 + rb - P.rdA.r0 + lq) * P.ldk) + lg * 8;
-          const int jb = min(max(j0 + cb + lq, 0), T - 1);
-          pb = (isS ? A.k : A.v) + ((bT + jb) * M + m) * D + lg * 8;
-        } else {
-          const int ia = min(max(i0 + rb + lq, 0), T - 1);
-          pa = (isS ? A.q : A.dO) + ((bT + ia) * M + m) * D + lg * 8;
-          pb = (isS ? X1 + (u * P.nx1 + cb - P.rS.c0 + lq) * P.ldk : X2 + (u * P.nx2 + cb - P.rdA.c0 + lq) * P.ldk) + lg * 8;
-        }
+      auto epilogue = [&](bool isS, int rb, int cb, const f32x4 (&c)[CH]) BWT_INLINE {
+        // lane holds rows rb + 4 lg + x, column cb + lq of every head
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          fa[kk] = *reinterpret_cast<const bf16x8*>(pa + kk * 32);
-          fb[kk] = *reinterpret_cast<const bf16x8*>(pb + kk * 32);
-        }
-      };
-      auto finish = [&](int u, int rb, int cb, bool isS, const bf16x8 (&fa)[D / 32], const bf16x8 (&fb)[D / 32]) BWT_INLINE {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < 4; ++x) {
+          const int r = rb + 4 * lg + x, cc = cb + lq;
+          const bool ok = valid(r, cc);
+          const bool in_core = r >= 0 && r < TB && cc >= 0 && cc < TB;
+          float v[CH];
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk], fb[kk], c, 0, 0, 0);
-        const Geo& G = isS ? P.gS : P.gdA;
-        const float sc = isS ? A.scale : 1.0f;
+          for (int u = 0; u < CH; ++u) v[u] = isS ? c[u][x] * A.scale : c[u][x];
+          if (isS) {
+            if (MODE == PASS_K && P.premix && in_core) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) *at(lds, G, u, rb + 4 * lg + x, cb + lq) = c[x] * sc;
-      };
-      constexpr int NW = NTH / 64;
-      for (int t = wave; t < ntask; t += 2 * NW) {
-        int u0, rb0, cb0, u1 = 0, rb1 = 0, cb1 = 0;
-        bool s0, s1 = false;
-        bf16x8 fa0[D / 32], fb0[D / 32], fa1[D / 32], fb1[D / 32];
-        const bool two = t + NW < ntask;
-        task(t, u0, rb0, cb0, s0);
-        frags(u0, rb0, cb0, s0, fa0, fb0);
-        if (two) {
-          task(t + NW, u1, rb1, cb1, s1);
-          frags(u1, rb1, cb1, s1, fa1, fb1);
-        }
-        finish(u0, rb0, cb0, s0, fa0, fb0);
-        if (two) finish(u1, rb1, cb1, s1, fa1, fb1);
-      }
-    }
-    __syncthreads();
-    // ---- (2) Z = Mask_0(mix_pre(S)) over rS, in place (PASS_K keeps the core of S for dw_pre)
-    {
-      const int n = P.rS.nr * P.rS.nc;
-      for (int x = tid; x < n; x += NTH) {
-        const int r = P.rS.r0 + x / P.rS.nc, c = P.rS.c0 + x % P.rS.nc;
-        const bool ok = valid(r, c);
-        float s[CH];
+              for (int u = 0; u < CH; ++u) *at(lds, P.gSc, u, r, cc) = v[u];
+            }
+            if (pre ? inside(P.rZ, r, cc) : inside(P.rP, r, cc)) {
 #pragma unroll
-        for (int u = 0; u < CH; ++u) s[u] = *at(lds, P.gS, u, r, c);
-        if (MODE == PASS_K && P.premix && r >= 0 && r < TB && c >= 0 && c < TB) {
+              for (int u = 0; u < CH; ++u) {
+                float z = v[u];
+                if (P.premix) {
+                  z = 0.0f;
 #pragma unroll
-          for (int u = 0; u < CH; ++u) *at(lds, P.gSc, u, r, c) = s[u];
-        }
+                  for (int w = 0; w < CH; ++w) z = __builtin_fmaf(w_s[u * CH + w], v[w], z);
+                }
+                if (pre) {
+                  *at(lds, P.gZ, u, r, cc) = ok ? z : 0.0f;
+                } else {
+                  const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
+                  *at(lds, P.gP, u, r, cc) = ok ? __builtin_amdgcn_exp2f((z - l) * 1.4426950408889634f) : 0.0f;
+                }
+              }
+            }
+          } else {
+            if (MODE == PASS_K && P.postmix && in_core) {
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-          float z = s[u];
-          if (P.premix) {
-            z = 0.0f;
+              for (int u = 0; u < CH; ++u) *at(lds, P.gdAc, u, r, cc) = v[u];
+            }
+            if (inside(P.rdE, r, cc)) {
 #pragma unroll
-            for (int v = 0; v < CH; ++v) z = __builtin_fmaf(w_s[u * CH + v], s[v], z);
+              for (int w = 0; w < CH; ++w) {
+                float s = v[w];
+                if (P.postmix) {
+                  s = 0.0f;
+#pragma unroll
+                  for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[CH * CH + u * CH + w], v[u], s);
+                }
+                *at(lds, P.gdE, w, r, cc) = ok ? s : 0.0f;
+              }
+            }
           }
-          *at(lds, P.gZ, u, r, c) = ok ? z : 0.0f;
         }
-      }
-    }
-    __syncthreads();
-    // ---- (3) P = exp(C - lse) over rP (C = conv_pre(Z), or Z); zero where masked
-    {
-      auto finP = [&](int u, int r, int c, float cv) BWT_INLINE {
-        const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
-        *at(lds, P.gP, u, r, c) = valid(r, c) ? __builtin_amdgcn_exp2f((cv - l) * 1.4426950408889634f) : 0.0f;
       };
-      if (pre) {
-        conv_region<CH>(lds, P.gZ, P.rP, th_s, P.cq, P.ck, P.h1, false, finP);
-      } else {
-        const int n = CH * P.rP.nr * P.rP.nc;
-        for (int x = tid; x < n; x += NTH) {
-          const int u = x / (P.rP.nr * P.rP.nc), rem = x % (P.rP.nr * P.rP.nc);
-          const int r = P.rP.r0 + rem / P.rP.nc, c = P.rP.c0 + rem % P.rP.nc;
-          finP(u, r, c, *at(lds, P.gZ, u, r, c));
-        }
-      }
-    }
-    __syncthreads();
-    // ---- (4) PASS_K: E = Mask_0(conv_post(P)) and A = mix_post(E) on the core tile
-    if (MODE == PASS_K && (post || P.postmix)) {
-      const Reg core{0, 0, TB, TB};
-      if (post) {
-        conv_region<CH>(lds, P.gP, core, th_s + thn, P.cq, P.ck, P.h2, false,
-                        [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, P.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
-        if (P.postmix) __syncthreads();
-      }
-      if (P.postmix) {
-        for (int x = tid; x < TB * TB; x += NTH) {
-          const int r = x / TB, c = x % TB;
-          float e[CH];
+      const int nS = MODE == PASS_K ? P.mS.nr / 16 : P.mS.nc / 16;  // tasks of each map
+      const int nA = MODE == PASS_K ? P.mA.nr / 16 : P.mA.nc / 16;
+      for (int t = wave; t < nS + nA; t += NW) {
+        const bool isS = t < nS;
+        const int blk = isS ? t : t - nS;
+        const Reg& R = isS ? P.mS : P.mA;
+        const __bf16* res = isS ? Xr : Yr;  // resident rows of this map
+        const int nres = isS ? P.nrx : P.nry;
+        // the global operand: rows (PASS_K) or columns (PASS_D) blk of the map, every head
+        bf16x8 fg[CH][D / 32];
+        {
+          const int gi = MODE == PASS_K ? min(max(i0 + R.r0 + 16 * blk + lq, 0), T - 1)
+                                        : min(max(j0 + R.c0 + 16 * blk + lq, 0), T - 1);
+          const __bf16* src = MODE == PASS_K ? (isS ? A.q : A.dO) : (isS ? A.k : A.v);
+          const __bf16* pg = src + ((bT + gi) * M + g * CH) * D + lg * 8;
 #pragma unroll
-          for (int u = 0; u < CH; ++u) e[u] = *at(lds, P.gE, u, r, c);
+          for (int u = 0; u < CH; ++u)
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) fg[u][kk] = *reinterpret_cast<const bf16x8*>(pg + u * D + kk * 32);
+        }
+        if (MODE == PASS_K) {
+          // the core rows of Q (S rows) and dO (dA rows), for the step's dK and dV products
+          const int row = R.r0 + 16 * blk + lq;
+          if (row >= 0 && row < TB) {
+            __bf16* dst = isS ? Qc : Oc;
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+#pragma unroll
+              for (int kk = 0; kk < D / 32; ++kk)
+                *reinterpret_cast<bf16x8*>(dst + (u * TB + row) * P.ldk + kk * 32 + lg * 8) = fg[u][kk];
+          }
+        }
+        const int nother = MODE == PASS_K ? R.nc / 16 : R.nr / 16;
+        for (int o = 0; o < nother; ++o) {
+          f32x4 c[CH];
+          // the other operand's rows: resident in LDS, or from global memory
+          const __bf16* pr0;
+          size_t ustride;
+          if (P.resident) {
+            pr0 = res + (16 * o + lq) * P.ldk + lg * 8;
+            ustride = (size_t)nres * P.ldk;
+          } else {
+            const int oi = MODE == PASS_K ? min(max(j0 + R.c0 + 16 * o + lq, 0), T - 1)
+                                          : min(max(i0 + R.r0 + 16 * o + lq, 0), T - 1);
+            const __bf16* src = MODE == PASS_K ? (isS ? A.k : A.v) : (isS ? A.q : A.dO);
+            pr0 = src + ((bT + oi) * M + g * CH) * D + lg * 8;
+            ustride = D;
+          }
 #pragma unroll
           for (int u = 0; u < CH; ++u) {
-            float s = 0.0f;
+            const __bf16* pr = pr0 + u * ustride;
+            c[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int v = 0; v < CH; ++v) s = __builtin_fmaf(w_s[CH * CH + u * CH + v], e[v], s);
-            *at(lds, P.gAc, u, r, c) = s;
+            for (int kk = 0; kk < D / 32; ++kk) {
+              const bf16x8 fr = *reinterpret_cast<const bf16x8*>(pr + kk * 32);
+              c[u] = MODE == PASS_K ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fg[u][kk], fr, c[u], 0, 0, 0)
+                                    : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr, fg[u][kk], c[u], 0, 0, 0);
+            }
           }
-        }
-      }
-      __syncthreads();
-      if (P.postmix) {  // dw_post partials: sum over the core row of dA_u E_v (before dA turns into dE)
-        if (wtask) {
-          const float* pa = at(lds, P.gdA, wu, wr, 0);
-          const float* pe = at(lds, P.gE, wv, wr, 0);
-          float s = 0.0f;
-#pragma unroll
-          for (int c = 0; c < TB; ++c) s = __builtin_fmaf(pa[c], pe[c], s);
-          acc_wpost += s;
-        }
-        __syncthreads();
-      }
-    }
-    // ---- (5) dE = Mask_0(mix_post^T(dA)) over rdA, in place; PASS_K: dw_post partials
-    {
-      const int n = P.rdA.nr * P.rdA.nc;
-      for (int x = tid; x < n; x += NTH) {
-        const int r = P.rdA.r0 + x / P.rdA.nc, c = P.rdA.c0 + x % P.rdA.nc;
-        const bool ok = valid(r, c);
-        float da[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) da[u] = *at(lds, P.gdA, u, r, c);
-#pragma unroll
-        for (int v = 0; v < CH; ++v) {
-          float s = da[v];
-          if (P.postmix) {
-            s = 0.0f;
-#pragma unroll
-            for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[CH * CH + u * CH + v], da[u], s);
-          }
-          *at(lds, P.gdA, v, r, c) = ok ? s : 0.0f;
+          const int rb = MODE == PASS_K ? R.r0 + 16 * blk : R.r0 + 16 * o;
+          const int cb = MODE == PASS_K ? R.c0 + 16 * o : R.c0 + 16 * blk;
+          epilogue(isS, rb, cb, c);
         }
       }
     }
     __syncthreads();
-    // ---- (6) dP = conv_post^T(dE) over rdC; PASS_K: dtheta_post partials
-    if (post) {
-      conv_region<CH>(lds, P.gdA, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
-                      [&](int u, int r, int c, float pv) BWT_INLINE { *at(lds, P.gdC, u, r, c) = pv; });
-      if (MODE == PASS_K) dtheta_tasks<CH>(lds, P.gdA, P.gP, P.cq, P.ck, P.h2, acc_thpost);
+    // the softmax gradient at (u, r, c) of rdC, from dP there: dC = P (dP - D_r)
+    auto dC_of = [&](int u, int r, int c, float dp) BWT_INLINE {
+      return *at(lds, P.gP, u, r, c) * (dp - d_s[u * P.rdC.nr + (r - P.rdC.r0)]);
+    };
+    // ---- (2) with a convolution before softmax: P = exp(conv_pre(Z) - lse) over rP; PASS_K
+    // without one after softmax also dC there (dP = dE)
+    if (pre) {
+      conv_region<CH, NT>(lds, P.gZ, P.rP, th_s, P.cq, P.ck, P.h1, false, [&](int u, int r, int c, float cv) BWT_INLINE {
+        const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
+        const float pv = valid(r, c) ? __builtin_amdgcn_exp2f((cv - l) * 1.4426950408889634f) : 0.0f;
+        *at(lds, P.gP, u, r, c) = pv;
+        if (MODE == PASS_K && !post && inside(P.rdC, r, c)) {
+          float* pd = at(lds, P.gdC, u, r, c);
+          *pd = pv * (*pd - d_s[u * P.rdC.nr + (r - P.rdC.r0)]);
+        }
+      });
       __syncthreads();
     }
     if (MODE == PASS_D) {
-      // ---- D_i partials: sum over the tile's keys of P dP
-      if (tid < CH * TB) {
-        const int u = tid / TB, r = tid % TB;
-        const float* pr = at(lds, P.gP, u, r, 0);
-        const float* dr = at(lds, P.gdC, u, r, 0);
-        float s = 0.0f, l = 0.0f;
+      // ---- D_i and the row sum of P: dP = conv_post^T(dE) (or dE) on the core tile; the four
+      // threads of a row (consecutive lanes) combine their columns
+      if (post) {
+        conv_region<CH, NT>(lds, P.gdE, core, th_s + thn, P.cq, P.ck, P.h2, true, [&](int u, int r, int c, float dp) BWT_INLINE {
+          const float pv = *at(lds, P.gP, u, r, c);
+          acc_d = __builtin_fmaf(pv, dp, acc_d);
+          acc_l += pv;
+        });
+      } else {
+        for (int t = tid; t < CH * TB * 4; t += NT) {
+          const int u = t / (TB * 4), r = (t / 4) % TB, c4 = 4 * (t % 4);
 #pragma unroll
-        for (int c = 0; c < TB; ++c) {
-          s = __builtin_fmaf(pr[c], dr[c], s);
-          l += pr[c];
+          for (int qq = 0; qq < 4; ++qq) {
+            const float pv = *at(lds, P.gP, u, r, c4 + qq);
+            acc_d = __builtin_fmaf(pv, *at(lds, P.gdE, u, r, c4 + qq), acc_d);
+            acc_l += pv;
+          }
         }
-        acc_d += s;
-        acc_l += l;
       }
       j0 += TB;
+      __syncthreads();  // the next step rewrites gP and gdE
       continue;
     }
-    // ---- (7) dC = P (dP - D) over rdC, in place
-    {
-      const int n = CH * P.rdC.nr * P.rdC.nc;
-      for (int x = tid; x < n; x += NTH) {
-        const int u = x / (P.rdC.nr * P.rdC.nc), rem = x % (P.rdC.nr * P.rdC.nc);
+    // ---- (3) PASS_K: E = Mask_0(conv_post(P)) on the core; dP = conv_post^T(dE) over rdC
+    // and dC = P (dP - D) there; dtheta_post partials. Without a convolution after softmax and
+    // before it either, dC = P (dE - D) in place. Q and dO of the core rows into LDS.
+    if (post) {
+      conv_region<CH, NT>(lds, P.gP, core, th_s + thn, P.cq, P.ck, P.h2, false,
+                          [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, P.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
+      conv_region<CH, NT>(lds, P.gdE, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
+                          [&](int u, int r, int c, float dp) BWT_INLINE { *at(lds, P.gdC, u, r, c) = dC_of(u, r, c, dp); });
+      dtheta_tasks<CH, NT, MAXR>(lds, P.gdE, P.gP, P.cq, P.ck, P.h2, acc_thpost);
+    } else if (!pre) {
+      for (int t = tid; t < CH * P.rdC.nr * P.rdC.nc; t += NT) {
+        const int u = t / (P.rdC.nr * P.rdC.nc), rem = t % (P.rdC.nr * P.rdC.nc);
         const int r = P.rdC.r0 + rem / P.rdC.nc, c = P.rdC.c0 + rem % P.rdC.nc;
         float* pd = at(lds, P.gdC, u, r, c);
-        *pd = *at(lds, P.gP, u, r, c) * (*pd - d_s[u * P.rdC.nr + (r - P.rdC.r0)]);
+        *pd = dC_of(u, r, c, *pd);
       }
     }
     __syncthreads();
-    // ---- (8) dL = Mask_0(conv_pre^T(dC)) on the core tile; dtheta_pre partials
+    // ---- (4) with a convolution before softmax: dL = Mask_0(conv_pre^T(dC)) on the core;
+    // dtheta_pre partials
     if (pre) {
-      conv_region<CH>(lds, P.gdC, Reg{0, 0, TB, TB}, th_s, P.cq, P.ck, P.h1, true,
-                      [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, P.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
-      dtheta_tasks<CH>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, acc_thpre);
+      conv_region<CH, NT>(lds, P.gdC, core, th_s, P.cq, P.ck, P.h1, true,
+                          [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, P.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
+      dtheta_tasks<CH, NT, MAXR>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, acc_thpre);
       __syncthreads();
     }
-    // ---- (9) dS = mix_pre^T(dL) (dw_pre partials) and A as bf16 tiles; stage Q and dO rows
-    for (int x = tid; x < TB * TB; x += NTH) {
+    // ---- (5) dS = mix_pre^T(dL) and A = mix_post(E) on the core as bf16 tiles; the mixing
+    // gradients' partials; the next step's row statistics
+    for (int x = tid; x < TB * TB; x += NT) {
       const int r = x / TB, c = x % TB;
-      float dl[CH];
+      float dl[CH], e[CH];
 #pragma unroll
-      for (int u = 0; u < CH; ++u) dl[u] = *at(lds, P.gdL, u, r, c);
+      for (int u = 0; u < CH; ++u) {
+        dl[u] = *at(lds, P.gdL, u, r, c);
+        e[u] = *at(lds, P.gE, u, r, c);
+      }
 #pragma unroll
-      for (int v = 0; v < CH; ++v) {
-        float s = dl[v];
+      for (int w = 0; w < CH; ++w) {
+        float s = dl[w], av = e[w];
         if (P.premix) {
           s = 0.0f;
 #pragma unroll
-          for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[u * CH + v], dl[u], s);
+          for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[u * CH + w], dl[u], s);
         }
-        dSb[(v * TB + r) * LDT + c] = (__bf16)s;
-        Ab[(v * TB + r) * LDT + c] = (__bf16)*at(lds, P.gAc, v, r, c);
+        if (P.postmix) {
+          av = 0.0f;
+#pragma unroll
+          for (int u = 0; u < CH; ++u) av = __builtin_fmaf(w_s[CH * CH + w * CH + u], e[u], av);
+        }
+        dSb[(w * TB + r) * LDT + c] = (__bf16)s;
+        Ab[(w * TB + r) * LDT + c] = (__bf16)av;
       }
     }
-    if (P.premix && wtask) {  // dw_pre partials: sum over the core row of dL_u S_v
-      const float* pl = at(lds, P.gdL, wu, wr, 0);
-      const float* ps = at(lds, P.gSc, wv, wr, 0);
-      float s = 0.0f;
+    if (wtask) {
+      if (P.premix) {  // dw_pre: the core row of dL_u S_v
+        const float* pl = at(lds, P.gdL, wu, wr, 0);
+        const float* ps = at(lds, P.gSc, wv, wr, 0);
+        float s = 0.0f;
 #pragma unroll
-      for (int c = 0; c < TB; ++c) s = __builtin_fmaf(pl[c], ps[c], s);
-      acc_wpre += s;
+        for (int c = 0; c < TB; ++c) s = __builtin_fmaf(pl[c], ps[c], s);
+        acc_wpre += s;
+      }
+      if (P.postmix) {  // dw_post: the core row of dA_u E_v
+        const float* pa = at(lds, P.gdAc, wu, wr, 0);
+        const float* pe = at(lds, P.gE, wv, wr, 0);
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < TB; ++c) s = __builtin_fmaf(pa[c], pe[c], s);
+        acc_wpost += s;
+      }
     }
+    if (i0 + TB < T) load_stats(i0 + TB, buf ^ 1);
     __syncthreads();
-    // ---- (10) dK += dS^T Q, dV += A^T dO (registers); dQ += dS K (atomics)
+    // ---- (6) dK += dS^T Q, dV += A^T dO (registers); dQ += dS K (atomics). The next step's
+    // first stage writes none of what this one reads, so no barrier follows.
 #pragma unroll
     for (int x = 0; x < NKV; ++x) {
-      const int kv = wave + x * (NTH / 64);
+      const int kv = wave + x * NW;
       if (kv < 2 * CH * NB) {
         const int kind = kv / (CH * NB), u = (kv / NB) % CH, nb = kv % NB;
         const s16x4 fa = tr_read((kind ? Ab : dSb) + u * TB * LDT, 4 * lg, 0, LDT, lane);
-        // the step's core query rows inside the staged Q (from row -rS.r0) and dO (from row 0)
-        const __bf16* xb = kind ? X2 + u * P.nx2 * P.ldk : X1 + (u * P.nx1 - P.rS.r0) * P.ldk;
-        const s16x4 fb = tr_read(xb, 4 * lg, nb * 16, P.ldk, lane);
+        const s16x4 fb = tr_read((kind ? Oc : Qc) + u * TB * P.ldk, 4 * lg, nb * 16, P.ldk, lane);
         acc_kv[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, fb, acc_kv[x], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int y = 0; y < NQT; ++y) {
-      const int t = wave + y * (NTH / 64);
-      if (t >= CH * NB) break;
-      const int u = t / NB, nb = t % NB;
-      const s16x4 fa = *reinterpret_cast<const s16x4*>(dSb + (u * TB + lq) * LDT + 4 * lg);
-      const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, kfrag[y], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const int t = wave + y * NW;
+      if (t < CH * NB) {
+        const int u = t / NB, nb = t % NB;
+        const s16x4 fa = *reinterpret_cast<const s16x4*>(dSb + (u * TB + lq) * LDT + 4 * lg);
+        const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa, kfrag[y], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int i = i0 + 4 * lg + x;
-        if (i < T) unsafeAtomicAdd(A.dq_acc + ((bT + i) * M + g * CH + u) * D + nb * 16 + lq, c[x]);
+        for (int x = 0; x < 4; ++x) {
+          const int i = i0 + 4 * lg + x;
+          if (i < T) unsafeAtomicAdd(A.dq_acc + ((bT + i) * M + g * CH + u) * D + nb * 16 + lq, c[x]);
+        }
       }
     }
     i0 += TB;
   }
 
   if (MODE == PASS_D) {
-    if (tid < CH * TB) {
-      const int u = tid / TB, i = i0 + tid % TB;
+    // the threads of a (head, row) are four consecutive lanes; the first adds their shares
+    acc_d += __shfl_xor(acc_d, 1);
+    acc_l += __shfl_xor(acc_l, 1);
+    acc_d += __shfl_xor(acc_d, 2);
+    acc_l += __shfl_xor(acc_l, 2);
+    if (tid < CH * TB * 4 && (tid & 3) == 0) {
+      const int u = tid / (TB * 4), i = i0 + (tid / 4) % TB;
       if (i < T) {
         const size_t x = (bT + i) * M + g * CH + u;
         A.dvec[x] = acc_d / acc_l;
@@ -673,7 +704,7 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   // ---- dK, dV of the workgroup's keys
 #pragma unroll
   for (int x = 0; x < NKV; ++x) {
-    const int kv = wave + x * (NTH / 64);
+    const int kv = wave + x * NW;
     if (kv < 2 * CH * NB) {
       const int kind = kv / (CH * NB), u = (kv / NB) % CH, nb = kv % NB;
       __bf16* dst = kind ? A.dv : A.dk;
@@ -687,18 +718,18 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   }
   // ---- parameter-gradient partials of this workgroup: [b * n_tiles + tile][m][...]
   __syncthreads();
-  float* red = lds + P.off_red;
+  float* red = lds;
   const size_t prow = (size_t)b * A.n_tiles + tile;
   const int ntap = CH * P.cq * P.ck;
   // dtheta: the row groups of each tap added in order
   auto emit_theta = [&](const float (&acc)[MAXR], float* part) BWT_INLINE {
 #pragma unroll
     for (int rr = 0; rr < MAXR; ++rr) {
-      const int t = tid + rr * NTH;
+      const int t = tid + rr * NT;
       if (t < ntap * NRQ) red[t] = acc[rr];
     }
     __syncthreads();
-    for (int x = tid; x < ntap; x += NTH) {
+    for (int x = tid; x < ntap; x += NT) {
       float s = 0.0f;
       for (int rq = 0; rq < NRQ; ++rq) s += red[x * NRQ + rq];
       part[(prow * A.G + g) * ntap + x] = s;
@@ -722,13 +753,13 @@ __global__ __launch_bounds__(NTH) void bwd_tile_kernel(BwArgs A) {
   if (A.part_wpost) emit_w(acc_wpost, A.part_wpost);
 }
 
-// Launch of one pass for a head group of ch heads; lds = dynamic LDS bytes of the plan.
-template <int D, int CH, int MODE, int SPEC>
+// Launch of one pass for a head group of CH heads; lds = dynamic LDS bytes of the plan.
+template <int D, int CH, int MODE, int SPEC, int NT>
 hipError_t launch_one(const BwArgs& a, size_t lds, unsigned grid, hipStream_t st) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_tile_kernel<D, CH, MODE, SPEC>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_tile_kernel<D, CH, MODE, SPEC, NT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_tile_kernel<D, CH, MODE, SPEC>), dim3(grid), dim3(NTH), lds, st, a);
+  hipLaunchKernelGGL((bwd_tile_kernel<D, CH, MODE, SPEC, NT>), dim3(grid), dim3(NT), lds, st, a);
   return hipGetLastError();
 }
 
@@ -738,15 +769,26 @@ __host__ __device__ constexpr bool spec_built(int spec, int ch, int d) {
   return (spec >= 1 && spec <= 3 && ch == 4 && d == 128) || (spec == 4 && d >= 96 && (ch == 2 || ch == 4));
 }
 
+template <int D, int CH, int MODE, int SPEC>
+hipError_t launch_nt(const BwArgs& a, size_t lds, unsigned grid, hipStream_t st) {
+  if constexpr (SPEC != 0) {
+    constexpr SpecShape sh = spec_shape(SPEC);
+    constexpr int NT = threads_for(make_plan(MODE, sh.kq, sh.mix, sh.cq, sh.ck, CH, D));
+    return launch_one<D, CH, MODE, SPEC, NT>(a, lds, grid, st);
+  } else {
+    return launch_one<D, CH, MODE, 0, 512>(a, lds, grid, st);
+  }
+}
+
 template <int D, int CH, int MODE>
 hipError_t launch_spec(const BwArgs& a, int spec, size_t lds, unsigned grid, hipStream_t st) {
   switch (spec) {
-    case 1: if constexpr (spec_built(1, CH, D)) return launch_one<D, CH, MODE, 1>(a, lds, grid, st); break;
-    case 2: if constexpr (spec_built(2, CH, D)) return launch_one<D, CH, MODE, 2>(a, lds, grid, st); break;
-    case 3: if constexpr (spec_built(3, CH, D)) return launch_one<D, CH, MODE, 3>(a, lds, grid, st); break;
-    case 4: if constexpr (spec_built(4, CH, D)) return launch_one<D, CH, MODE, 4>(a, lds, grid, st); break;
+    case 1: if constexpr (spec_built(1, CH, D)) return launch_nt<D, CH, MODE, 1>(a, lds, grid, st); break;
+    case 2: if constexpr (spec_built(2, CH, D)) return launch_nt<D, CH, MODE, 2>(a, lds, grid, st); break;
+    case 3: if constexpr (spec_built(3, CH, D)) return launch_nt<D, CH, MODE, 3>(a, lds, grid, st); break;
+    case 4: if constexpr (spec_built(4, CH, D)) return launch_nt<D, CH, MODE, 4>(a, lds, grid, st); break;
   }
-  return launch_one<D, CH, MODE, 0>(a, lds, grid, st);
+  return launch_nt<D, CH, MODE, 0>(a, lds, grid, st);
 }
 
 template <int D>
