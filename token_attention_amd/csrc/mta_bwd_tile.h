@@ -405,6 +405,28 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     __syncthreads();
   }
 
+  // stage-1 tasks: one row (PASS_K) or column (PASS_D) of 16 x 16 blocks of S, then of dA
+  const int nS = MODE == PASS_K ? P.mS.nr / 16 : P.mS.nc / 16;
+  const int nA = MODE == PASS_K ? P.mA.nr / 16 : P.mA.nc / 16;
+  const bool prefetch = nS + nA <= NW;  // a wave per task: its global operand is loaded ahead
+  bf16x8 fg[CH][D / 32];
+  // task t's global operand at the tile origin (ti, tj): rows (PASS_K) or columns (PASS_D) of
+  // its blocks, 16 bytes per lane and 32 channels, every head
+  auto load_global = [&](int t, int ti, int tj, bf16x8 (&dst)[CH][D / 32]) BWT_INLINE {
+    const bool isS = t < nS;
+    const int blk = isS ? t : t - nS;
+    const Reg& R = isS ? P.mS : P.mA;
+    const int gi = MODE == PASS_K ? min(max(ti + R.r0 + 16 * blk + lq, 0), T - 1)
+                                  : min(max(tj + R.c0 + 16 * blk + lq, 0), T - 1);
+    const __bf16* src = MODE == PASS_K ? (isS ? A.q : A.dO) : (isS ? A.k : A.v);
+    const __bf16* pg = src + ((bT + gi) * M + g * CH) * D + lg * 8;
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) dst[u][kk] = *reinterpret_cast<const bf16x8*>(pg + u * D + kk * 32);
+  };
+  if (prefetch && wave < nS + nA) load_global(wave, i0, j0, fg);
+
   for (int step = 0;; ++step) {
     if (MODE == PASS_K ? i0 >= T : j0 > i0) break;
     const int buf = MODE == PASS_K ? (step & 1) : 0;
@@ -475,26 +497,15 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
           }
         }
       };
-      const int nS = MODE == PASS_K ? P.mS.nr / 16 : P.mS.nc / 16;  // tasks of each map
-      const int nA = MODE == PASS_K ? P.mA.nr / 16 : P.mA.nc / 16;
       for (int t = wave; t < nS + nA; t += NW) {
         const bool isS = t < nS;
         const int blk = isS ? t : t - nS;
         const Reg& R = isS ? P.mS : P.mA;
         const __bf16* res = isS ? Xr : Yr;  // resident rows of this map
         const int nres = isS ? P.nrx : P.nry;
-        // the global operand: rows (PASS_K) or columns (PASS_D) blk of the map, every head
-        bf16x8 fg[CH][D / 32];
-        {
-          const int gi = MODE == PASS_K ? min(max(i0 + R.r0 + 16 * blk + lq, 0), T - 1)
-                                        : min(max(j0 + R.c0 + 16 * blk + lq, 0), T - 1);
-          const __bf16* src = MODE == PASS_K ? (isS ? A.q : A.dO) : (isS ? A.k : A.v);
-          const __bf16* pg = src + ((bT + gi) * M + g * CH) * D + lg * 8;
-#pragma unroll
-          for (int u = 0; u < CH; ++u)
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) fg[u][kk] = *reinterpret_cast<const bf16x8*>(pg + u * D + kk * 32);
-        }
+        // the global operand: rows (PASS_K) or columns (PASS_D) blk of the map, every head;
+        // prefetched by the previous step when every task has a wave of its own
+        if (!prefetch) load_global(t, i0, j0, fg);
         if (MODE == PASS_K) {
           // the core rows of Q (S rows) and dO (dA rows), for the step's dK and dV products
           const int row = R.r0 + 16 * blk + lq;
@@ -537,6 +548,10 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
           const int rb = MODE == PASS_K ? R.r0 + 16 * blk : R.r0 + 16 * o;
           const int cb = MODE == PASS_K ? R.c0 + 16 * o : R.c0 + 16 * blk;
           epilogue(isS, rb, cb, c);
+        }
+        if (prefetch) {  // the next step's operand, in flight through the stages that follow
+          if (MODE == PASS_K ? i0 + TB < T : j0 + TB <= i0) load_global(t, MODE == PASS_K ? i0 + TB : i0,
+                                                                        MODE == PASS_K ? j0 : j0 + TB, fg);
         }
       }
     }
