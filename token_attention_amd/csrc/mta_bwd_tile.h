@@ -44,7 +44,6 @@ namespace bwt {
 
 constexpr int TB = 16;   // core tile: TB query rows x TB keys
 constexpr int CKM = 17;  // largest key extent of a convolution
-constexpr int NRQ = 4;   // the rows of a parameter-gradient task split in NRQ groups
 constexpr int LDT = 20;  // leading dimension of the 16 x 16 bf16 tiles
 enum { PASS_D = 0, PASS_K = 1 };
 
@@ -150,7 +149,7 @@ __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q,
   p.off_bf = pool;
   if (K) pool += (2 * ch * TB * p.ldk + 2 * ch * TB * LDT) / 2;
   // the end-of-sweep reductions reuse the pool from its start
-  pool = imax(pool, imax(ch * p.cq * p.ck * NRQ, ch * ch * TB));
+  pool = imax(pool, imax(3 * 512, ch * ch * TB));  // dtheta partials: at most EB per thread
   p.lds_floats = r4c(pool);
   if (resident && p.lds_floats * 4 > 160 * 1024) return make_plan(mode, kq, mix, c_q, c_k, ch, d, false);
   return p;
@@ -213,10 +212,10 @@ __device__ __forceinline__ bool inside(const Reg& R, int r, int c) {
 // makes four consecutive columns of one row from a window of 4 + 2h source values per lag.
 template <int CH, int NT, class Fin>
 __device__ __forceinline__ void conv_region(float* lds, const Geo& src, const Reg& R, const float* th, int cq,
-                                            int ck, int h, bool adjoint, Fin fin) {
+                                            int ck, int h, bool adjoint, Fin fin, int t0 = -1, int nthreads = NT) {
   const int ncb = R.nc >> 2;  // R.nc is a multiple of 4
   const int n = CH * R.nr * ncb;
-  for (int t = threadIdx.x; t < n; t += NT) {
+  for (int t = t0 < 0 ? (int)threadIdx.x : t0; t < n; t += nthreads) {
     const int u = t / (R.nr * ncb);
     const int rem = t - u * R.nr * ncb;
     const int r = R.r0 + rem / ncb;
@@ -247,28 +246,36 @@ __device__ __forceinline__ void conv_region(float* lds, const Geo& src, const Re
   }
 }
 
-// Partial sums of dtheta[u][a][e] over the core tile: sum_{r, c} G[u][r][c] X[u][r - a][c - e + h],
-// for task t = ((u * cq + a) * ck + e) * NRQ + rq covering rows rq, rq + NRQ, ...
-template <int CH, int NT, int MAXR>
-__device__ __forceinline__ void dtheta_tasks(float* lds, const Geo& gG, const Geo& gX, int cq, int ck, int h,
-                                             float (&acc)[MAXR]) {
-  const int n = CH * cq * ck * NRQ;
+// Partial sums of dtheta[u][a][e] over the core tile: sum_{r, c} G[u][r][c] X[u][r - a][c - e + h].
+// Task t = ((u * cq + a) * neb + eb) * nrq + rq makes taps e = 3 eb .. 3 eb + 2 from one window of
+// X per row (rows rq, rq + nrq, ...; nrq row groups keep the tasks within one round).
+constexpr int EB = 3;  // taps per task
+template <int CH, int NT>
+__device__ __forceinline__ void dtheta_tasks(float* lds, const Geo& gG, const Geo& gX, int cq, int ck, int h, int nrq,
+                                             float (&acc)[EB]) {
+  const int neb = (ck + EB - 1) / EB;
+  const int t = threadIdx.x;
+  if (t < CH * cq * neb * nrq) {
+    const int rq = t % nrq;
+    const int eb = (t / nrq) % neb;
+    const int a = (t / (nrq * neb)) % cq;
+    const int u = t / (nrq * neb * cq);
+    const int e0 = EB * eb;
+    // window slot k holds column k + h - e0 - (EB - 1); tap e0 + j reads slot c + EB - 1 - j.
+    // Slots left of column -h serve only taps beyond ck and are not read.
+    const int kmin = e0 + EB - 1 - 2 * h;
+    for (int r = rq; r < TB; r += nrq) {
+      const float* gr = at(lds, gG, u, r, 0);
+      const float* xr = at(lds, gX, u, r - a, h - e0 - (EB - 1));
+      float xw[TB + EB - 1];
 #pragma unroll
-  for (int rr = 0; rr < MAXR; ++rr) {
-    const int t = threadIdx.x + rr * NT;
-    if (t < n) {
-      const int rq = t % NRQ;
-      const int e = (t / NRQ) % ck;
-      const int a = (t / (NRQ * ck)) % cq;
-      const int u = t / (NRQ * ck * cq);
-      float s = 0.0f;
-      for (int r = rq; r < TB; r += NRQ) {
-        const float* gr = at(lds, gG, u, r, 0);
-        const float* xr = at(lds, gX, u, r - a, h - e);
+      for (int k = 0; k < TB + EB - 1; ++k) xw[k] = k >= kmin ? xr[k] : 0.0f;
 #pragma unroll
-        for (int c = 0; c < TB; ++c) s = __builtin_fmaf(gr[c], xr[c], s);
+      for (int c = 0; c < TB; ++c) {
+        const float gv = gr[c];
+#pragma unroll
+        for (int j = 0; j < EB; ++j) acc[j] = __builtin_fmaf(gv, xw[c + EB - 1 - j], acc[j]);
       }
-      acc[rr] += s;
     }
   }
 }
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   constexpr int NB = D / 16;
   constexpr int NKV = (2 * CH * NB + NW - 1) / NW;  // dK / dV blocks per wave
   constexpr int NQT = (CH * NB + NW - 1) / NW;      // dQ blocks per wave
-  constexpr int MAXR = (4 * 8 * CKM * NRQ + NT - 1) / NT;  // dtheta task rounds
+  const int nrq = imax(1, min(TB, NT / (CH * P.cq * ((P.ck + EB - 1) / EB))));  // dtheta row groups
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
   const int T = A.T, M = A.M;
@@ -362,11 +369,11 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   // persistent accumulators. acc_wpre / acc_wpost: task (u, v, r) = thread CH TB u + TB v + r
   // < CH^2 TB of the mixing gradients, row r of the core tile. acc_d, acc_l (PASS_D): the
   // thread's share of D and of the row sum of P for its (head, row).
-  float acc_thpre[MAXR], acc_thpost[MAXR], acc_wpre = 0.0f, acc_wpost = 0.0f, acc_d = 0.0f, acc_l = 0.0f;
+  float acc_thpre[EB], acc_thpost[EB], acc_wpre = 0.0f, acc_wpost = 0.0f, acc_d = 0.0f, acc_l = 0.0f;
   const int wu = tid / (CH * TB), wv = (tid / TB) % CH, wr = tid % TB;
   const bool wtask = tid < CH * CH * TB;
 #pragma unroll
-  for (int x = 0; x < MAXR; ++x) acc_thpre[x] = acc_thpost[x] = 0.0f;
+  for (int x = 0; x < EB; ++x) acc_thpre[x] = acc_thpost[x] = 0.0f;
   f32x4 acc_kv[NKV];
 #pragma unroll
   for (int x = 0; x < NKV; ++x) acc_kv[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -606,7 +613,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
                           [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, P.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
       conv_region<CH, NT>(lds, P.gdE, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
                           [&](int u, int r, int c, float dp) BWT_INLINE { *at(lds, P.gdC, u, r, c) = dC_of(u, r, c, dp); });
-      dtheta_tasks<CH, NT, MAXR>(lds, P.gdE, P.gP, P.cq, P.ck, P.h2, acc_thpost);
+      dtheta_tasks<CH, NT>(lds, P.gdE, P.gP, P.cq, P.ck, P.h2, nrq, acc_thpost);
     } else if (!pre) {
       for (int t = tid; t < CH * P.rdC.nr * P.rdC.nc; t += NT) {
         const int u = t / (P.rdC.nr * P.rdC.nc), rem = t % (P.rdC.nr * P.rdC.nc);
@@ -621,7 +628,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     if (pre) {
       conv_region<CH, NT>(lds, P.gdC, core, th_s, P.cq, P.ck, P.h1, true,
                           [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, P.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
-      dtheta_tasks<CH, NT, MAXR>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, acc_thpre);
+      dtheta_tasks<CH, NT>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, nrq, acc_thpre);
       __syncthreads();
     }
     // ---- (5) dS = mix_pre^T(dL) and A = mix_post(E) on the core as bf16 tiles; the mixing
@@ -737,16 +744,18 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   const size_t prow = (size_t)b * A.n_tiles + tile;
   const int ntap = CH * P.cq * P.ck;
   // dtheta: the row groups of each tap added in order
-  auto emit_theta = [&](const float (&acc)[MAXR], float* part) BWT_INLINE {
+  auto emit_theta = [&](const float (&acc)[EB], float* part) BWT_INLINE {
+    const int neb = (P.ck + EB - 1) / EB;
+    if (tid < CH * P.cq * neb * nrq) {
+      const int rq = tid % nrq, eb = (tid / nrq) % neb, ua = tid / (nrq * neb);  // ua = u * cq + a
 #pragma unroll
-    for (int rr = 0; rr < MAXR; ++rr) {
-      const int t = tid + rr * NT;
-      if (t < ntap * NRQ) red[t] = acc[rr];
+      for (int j = 0; j < EB; ++j)
+        if (EB * eb + j < P.ck) red[(ua * P.ck + EB * eb + j) * nrq + rq] = acc[j];
     }
     __syncthreads();
     for (int x = tid; x < ntap; x += NT) {
       float s = 0.0f;
-      for (int rq = 0; rq < NRQ; ++rq) s += red[x * NRQ + rq];
+      for (int rq = 0; rq < nrq; ++rq) s += red[x * nrq + rq];
       part[(prow * A.G + g) * ntap + x] = s;
     }
     __syncthreads();
