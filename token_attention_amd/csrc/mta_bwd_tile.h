@@ -317,17 +317,18 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   const Reg core{0, 0, TB, TB};
 
   float* th_s = lds + P.off_th;  // [2][CH][cq][ck]: before softmax, then after
-  float* w_s = lds + P.off_w;    // [2][CH][CH]
   const int thn = CH * P.cq * P.ck;
   for (int x = tid; x < 2 * thn; x += NT) {
     const float* src = x < thn ? A.th_pre : A.th_post;
     const int y = x < thn ? x : x - thn;
     th_s[x] = src ? src[(size_t)g * thn + y] : 0.0f;
   }
-  for (int x = tid; x < 2 * CH * CH; x += NT) {
-    const float* src = x < CH * CH ? A.w_pre : A.w_post;
-    const int y = x < CH * CH ? x : x - CH * CH;
-    w_s[x] = src ? src[(size_t)g * CH * CH + y] : 0.0f;
+  // the group's mixing weights, uniform across the workgroup: scalar registers
+  float wm1[CH * CH], wm2[CH * CH];
+#pragma unroll
+  for (int x = 0; x < CH * CH; ++x) {
+    wm1[x] = P.premix ? A.w_pre[(size_t)g * CH * CH + x] : 0.0f;
+    wm2[x] = P.postmix ? A.w_post[(size_t)g * CH * CH + x] : 0.0f;
   }
   // resident operand rows (see Plan::off_x); PASS_K bf16 staging: Q and dO of the step's core
   // rows, the dS and A tiles
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
                 if (P.premix) {
                   z = 0.0f;
 #pragma unroll
-                  for (int w = 0; w < CH; ++w) z = __builtin_fmaf(w_s[u * CH + w], v[w], z);
+                  for (int w = 0; w < CH; ++w) z = __builtin_fmaf(wm1[u * CH + w], v[w], z);
                 }
                 if (pre) {
                   *at(lds, P.gZ, u, r, cc) = ok ? z : 0.0f;
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
                 if (P.postmix) {
                   s = 0.0f;
 #pragma unroll
-                  for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[CH * CH + u * CH + w], v[u], s);
+                  for (int u = 0; u < CH; ++u) s = __builtin_fmaf(wm2[u * CH + w], v[u], s);
                 }
                 *at(lds, P.gdE, w, r, cc) = ok ? s : 0.0f;
               }
@@ -647,12 +648,12 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
         if (P.premix) {
           s = 0.0f;
 #pragma unroll
-          for (int u = 0; u < CH; ++u) s = __builtin_fmaf(w_s[u * CH + w], dl[u], s);
+          for (int u = 0; u < CH; ++u) s = __builtin_fmaf(wm1[u * CH + w], dl[u], s);
         }
         if (P.postmix) {
           av = 0.0f;
 #pragma unroll
-          for (int u = 0; u < CH; ++u) av = __builtin_fmaf(w_s[CH * CH + w * CH + u], e[u], av);
+          for (int u = 0; u < CH; ++u) av = __builtin_fmaf(wm2[w * CH + u], e[u], av);
         }
         dSb[(w * TB + r) * LDT + c] = (__bf16)s;
         Ab[(w * TB + r) * LDT + c] = (__bf16)av;
