@@ -116,6 +116,19 @@ def test_backward_fused_shapes_and_sizes(d, c_q, c_k, c_h, gn):
           what=f"fused d={d} {c_q}x{c_k} c_h={c_h} gn={gn}")
 
 
+@pytest.mark.parametrize("kq,mix,c_q,c_k,c_h,d", [("post", "pre", 4, 9, 4, 128), ("pre", "post", 4, 9, 4, 128),
+                                                  ("both", "both", 4, 9, 4, 128), ("pre", "post", 6, 11, 2, 96),
+                                                  ("pre", "post", 6, 11, 4, 128)])
+def test_backward_fused_specialised_kernels(kq, mix, c_q, c_k, c_h, d):
+    """Each kernel shape compiled with its plan as constants (the benchmark workloads' placements
+    and kernel sizes), over several tiles and a ragged tail."""
+    cfg = mta_inputs.MTAConfig("bwd_spec", 1, 130, 8, d, c_q, c_k, c_h, kq, mix, True, "bf16", 0.1, 0.1, 1.0, 0.0,
+                               1.0 / 12 ** 0.5, seed=38)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what=f"fused {kq}/{mix} {c_q}x{c_k} c_h={c_h} d={d}")
+
+
 @pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 200])
 def test_backward_fused_ragged_lengths(T):
     cfg = mta_inputs.MTAConfig("bwd_T", 2, T, 4, 32, 4, 9, 2, "both", "both", T > 2, "bf16", 0.2, 0.2, 1.0, 0.0,

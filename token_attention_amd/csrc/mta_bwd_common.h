@@ -105,17 +105,35 @@ __global__ __launch_bounds__(MT_THREADS) void gn_backward_kernel(const float* __
   if (threadIdx.x == 0) part_l[prow * M + m] = (red[0][2 * D] + red[1][2 * D]) + (red[2][2 * D] + red[3][2 * D]);
 }
 
-// ---- out[k] = sum_r part[r * K + k], rows added in order ------------------------------------------
-__global__ void sum_rows_kernel(const float* __restrict__ part, size_t R, size_t K, float* __restrict__ out) {
-  const size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
+// ---- out[k] = sum_r part[r * K + k] in a fixed order ---------------------------------------------
+// A workgroup owns SR_W columns (fewer where K is smaller); its SR_THREADS / W row groups each add
+// every (SR_THREADS / W)-th row in order, and a fixed pairwise tree adds the groups: the result
+// does not depend on timing, so repeated calls agree bit for bit.
+constexpr int SR_THREADS = 256;
+constexpr int SR_W = 16;
+
+__global__ __launch_bounds__(SR_THREADS) void sum_rows_kernel(const float* __restrict__ part, size_t R, size_t K,
+                                                              int W, float* __restrict__ out) {
+  __shared__ float red[SR_THREADS];
+  const int t = threadIdx.x, ng = SR_THREADS / W, rg = t / W;
+  const size_t k = (size_t)blockIdx.x * W + t % W;
   float s = 0.0f;
-  for (size_t r = 0; r < R; ++r) s += part[r * K + k];
-  out[k] = s;
+  if (k < K)
+    for (size_t r = rg; r < R; r += ng) s += part[r * K + k];
+  red[t] = s;
+  __syncthreads();
+  for (int h = ng / 2; h > 0; h >>= 1) {
+    if (rg < h) red[t] += red[t + h * W];
+    __syncthreads();
+  }
+  if (rg == 0 && k < K) out[k] = red[t];
 }
 
 hipError_t sum_rows(const float* part, size_t R, size_t K, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(sum_rows_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, part, R, K, out);
+  if (K == 0) return hipSuccess;
+  int W = 1;
+  while (W < SR_W && (size_t)W < K) W *= 2;
+  hipLaunchKernelGGL(sum_rows_kernel, dim3((unsigned)((K + W - 1) / W)), dim3(SR_THREADS), 0, st, part, R, K, W, out);
   return hipGetLastError();
 }
 

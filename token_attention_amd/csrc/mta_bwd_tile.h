@@ -173,6 +173,20 @@ constexpr int NSPEC = 5;
 // overlap), else 512.
 __host__ __device__ constexpr int threads_for(const Plan& p) { return p.lds_floats * 4 <= 80 * 1024 ? 256 : 512; }
 
+// Heads per stage-1 MFMA task: the whole group, or (HS = 2) half of it. Halved tasks give the
+// waves that would otherwise idle a share of the products, and the mixing, which needs every
+// head of a position, then runs as a pointwise pass of its own after them. Used where both
+// mixings are present and the halved tasks still give every wave at most one (the specialised
+// PASS_K kernel with everything on both sides: 42.0 -> 37.9 ms at T=4096); with one mixing the
+// extra pass and barrier cost what the shorter products save (post 4 x 9 with mixing before:
+// 20.5 -> 21.8 ms; pre 4 x 9 with mixing after: unchanged).
+__host__ __device__ constexpr int head_split(int mode, int spec, int ch, int d, int nt) {
+  if (spec == 0 || mode != PASS_K || ch % 2 != 0) return 1;
+  const SpecShape sh = spec_shape(spec);
+  const Plan p = make_plan(mode, sh.kq, sh.mix, sh.cq, sh.ck, ch, d);
+  return p.premix && p.postmix && 2 * (p.mS.nr / 16 + p.mA.nr / 16) <= nt / 64 ? 2 : 1;
+}
+
 struct BwArgs {
   const __bf16* q;
   const __bf16* k;
@@ -303,6 +317,8 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   constexpr int NB = D / 16;
   constexpr int NKV = (2 * CH * NB + NW - 1) / NW;  // dK / dV blocks per wave
   constexpr int NQT = (CH * NB + NW - 1) / NW;      // dQ blocks per wave
+  constexpr int HS = head_split(MODE, SPEC, CH, D, NT);
+  constexpr int CHT = CH / HS;  // heads per stage-1 task
   const int nrq = imax(1, min(TB, NT / (CH * P.cq * ((P.ck + EB - 1) / EB))));  // dtheta row groups
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
@@ -413,27 +429,30 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     __syncthreads();
   }
 
-  // stage-1 tasks: one row (PASS_K) or column (PASS_D) of 16 x 16 blocks of S, then of dA
+  // stage-1 tasks: one row (PASS_K) or column (PASS_D) of 16 x 16 blocks of S, then of dA, for
+  // CHT heads of the group: task t is block row (column) t / HS, heads CHT (t % HS) ..
   const int nS = MODE == PASS_K ? P.mS.nr / 16 : P.mS.nc / 16;
   const int nA = MODE == PASS_K ? P.mA.nr / 16 : P.mA.nc / 16;
-  const bool prefetch = nS + nA <= NW;  // a wave per task: its global operand is loaded ahead
-  bf16x8 fg[CH][D / 32];
+  const int ntask = (nS + nA) * HS;
+  const bool prefetch = ntask <= NW;  // a wave per task: its global operand is loaded ahead
+  bf16x8 fg[CHT][D / 32];
   // task t's global operand at the tile origin (ti, tj): rows (PASS_K) or columns (PASS_D) of
-  // its blocks, 16 bytes per lane and 32 channels, every head
-  auto load_global = [&](int t, int ti, int tj, bf16x8 (&dst)[CH][D / 32]) BWT_INLINE {
-    const bool isS = t < nS;
-    const int blk = isS ? t : t - nS;
+  // its blocks, 16 bytes per lane and 32 channels, each of its heads
+  auto load_global = [&](int t, int ti, int tj, bf16x8 (&dst)[CHT][D / 32]) BWT_INLINE {
+    const int tb = t / HS, u0 = (t % HS) * CHT;
+    const bool isS = tb < nS;
+    const int blk = isS ? tb : tb - nS;
     const Reg& R = isS ? P.mS : P.mA;
     const int gi = MODE == PASS_K ? min(max(ti + R.r0 + 16 * blk + lq, 0), T - 1)
                                   : min(max(tj + R.c0 + 16 * blk + lq, 0), T - 1);
     const __bf16* src = MODE == PASS_K ? (isS ? A.q : A.dO) : (isS ? A.k : A.v);
-    const __bf16* pg = src + ((bT + gi) * M + g * CH) * D + lg * 8;
+    const __bf16* pg = src + ((bT + gi) * M + g * CH + u0) * D + lg * 8;
 #pragma unroll
-    for (int u = 0; u < CH; ++u)
+    for (int u = 0; u < CHT; ++u)
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) dst[u][kk] = *reinterpret_cast<const bf16x8*>(pg + u * D + kk * 32);
   };
-  if (prefetch && wave < nS + nA) load_global(wave, i0, j0, fg);
+  if (prefetch && wave < ntask) load_global(wave, i0, j0, fg);
 
   for (int step = 0;; ++step) {
     if (MODE == PASS_K ? i0 >= T : j0 > i0) break;
@@ -453,66 +472,82 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     // rows of Q and dO into Qc and Oc.
     if (MODE == PASS_K && step > 0) __syncthreads();  // the previous step's MFMAs read Qc and Oc
     {
-      auto epilogue = [&](bool isS, int rb, int cb, const f32x4 (&c)[CH]) BWT_INLINE {
-        // lane holds rows rb + 4 lg + x, column cb + lq of every head
+      auto epilogue = [&](bool isS, int rb, int cb, int u0, const f32x4 (&c)[CHT]) BWT_INLINE {
+        // lane holds rows rb + 4 lg + x, column cb + lq of heads u0 .. u0 + CHT - 1. With HS > 1
+        // a mixed map is stored as the plain product here and mixed by the pass after the barrier.
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = rb + 4 * lg + x, cc = cb + lq;
           const bool ok = valid(r, cc);
           const bool in_core = r >= 0 && r < TB && cc >= 0 && cc < TB;
-          float v[CH];
+          float v[CHT];
 #pragma unroll
-          for (int u = 0; u < CH; ++u) v[u] = isS ? c[u][x] * A.scale : c[u][x];
+          for (int u = 0; u < CHT; ++u) v[u] = isS ? c[u][x] * A.scale : c[u][x];
           if (isS) {
             if (MODE == PASS_K && P.premix && in_core) {
 #pragma unroll
-              for (int u = 0; u < CH; ++u) *at(lds, P.gSc, u, r, cc) = v[u];
+              for (int u = 0; u < CHT; ++u) *at(lds, P.gSc, u0 + u, r, cc) = v[u];
             }
             if (pre ? inside(P.rZ, r, cc) : inside(P.rP, r, cc)) {
 #pragma unroll
-              for (int u = 0; u < CH; ++u) {
+              for (int u = 0; u < CHT; ++u) {
                 float z = v[u];
-                if (P.premix) {
-                  z = 0.0f;
+                if constexpr (HS > 1) {
+                  if (P.premix) {
+                    *at(lds, pre ? P.gZ : P.gP, u0 + u, r, cc) = z;
+                    continue;
+                  }
+                } else {
+                  if (P.premix) {
+                    z = 0.0f;
 #pragma unroll
-                  for (int w = 0; w < CH; ++w) z = __builtin_fmaf(wm1[u * CH + w], v[w], z);
+                    for (int w = 0; w < CH; ++w) z = __builtin_fmaf(wm1[u * CH + w], v[w], z);
+                  }
                 }
                 if (pre) {
-                  *at(lds, P.gZ, u, r, cc) = ok ? z : 0.0f;
+                  *at(lds, P.gZ, u0 + u, r, cc) = ok ? z : 0.0f;
                 } else {
-                  const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
-                  *at(lds, P.gP, u, r, cc) = ok ? __builtin_amdgcn_exp2f((z - l) * 1.4426950408889634f) : 0.0f;
+                  const float l = lse_s[(u0 + u) * P.rP.nr + (r - P.rP.r0)];
+                  *at(lds, P.gP, u0 + u, r, cc) = ok ? __builtin_amdgcn_exp2f((z - l) * 1.4426950408889634f) : 0.0f;
                 }
               }
             }
           } else {
             if (MODE == PASS_K && P.postmix && in_core) {
 #pragma unroll
-              for (int u = 0; u < CH; ++u) *at(lds, P.gdAc, u, r, cc) = v[u];
+              for (int u = 0; u < CHT; ++u) *at(lds, P.gdAc, u0 + u, r, cc) = v[u];
             }
             if (inside(P.rdE, r, cc)) {
 #pragma unroll
-              for (int w = 0; w < CH; ++w) {
+              for (int w = 0; w < CHT; ++w) {
                 float s = v[w];
-                if (P.postmix) {
-                  s = 0.0f;
+                if constexpr (HS > 1) {
+                  if (P.postmix) {
+                    *at(lds, P.gdE, u0 + w, r, cc) = s;
+                    continue;
+                  }
+                } else {
+                  if (P.postmix) {
+                    s = 0.0f;
 #pragma unroll
-                  for (int u = 0; u < CH; ++u) s = __builtin_fmaf(wm2[u * CH + w], v[u], s);
+                    for (int u = 0; u < CH; ++u) s = __builtin_fmaf(wm2[u * CH + w], v[u], s);
+                  }
                 }
-                *at(lds, P.gdE, w, r, cc) = ok ? s : 0.0f;
+                *at(lds, P.gdE, u0 + w, r, cc) = ok ? s : 0.0f;
               }
             }
           }
         }
       };
-      for (int t = wave; t < nS + nA; t += NW) {
-        const bool isS = t < nS;
-        const int blk = isS ? t : t - nS;
+      for (int t = wave; t < ntask; t += NW) {
+        const int tb = t / HS, u0 = (t % HS) * CHT;
+        const bool isS = tb < nS;
+        const int blk = isS ? tb : tb - nS;
         const Reg& R = isS ? P.mS : P.mA;
         const __bf16* res = isS ? Xr : Yr;  // resident rows of this map
         const int nres = isS ? P.nrx : P.nry;
-        // the global operand: rows (PASS_K) or columns (PASS_D) blk of the map, every head;
-        // prefetched by the previous step when every task has a wave of its own
+        // the global operand: rows (PASS_K) or columns (PASS_D) blk of the map, the task's
+        // heads; prefetched by the previous step when every task has a wave of its own
         if (!prefetch) load_global(t, i0, j0, fg);
         if (MODE == PASS_K) {
           // the core rows of Q (S rows) and dO (dA rows), for the step's dK and dV products
@@ -520,30 +555,30 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
           if (row >= 0 && row < TB) {
             __bf16* dst = isS ? Qc : Oc;
 #pragma unroll
-            for (int u = 0; u < CH; ++u)
+            for (int u = 0; u < CHT; ++u)
 #pragma unroll
               for (int kk = 0; kk < D / 32; ++kk)
-                *reinterpret_cast<bf16x8*>(dst + (u * TB + row) * P.ldk + kk * 32 + lg * 8) = fg[u][kk];
+                *reinterpret_cast<bf16x8*>(dst + ((u0 + u) * TB + row) * P.ldk + kk * 32 + lg * 8) = fg[u][kk];
           }
         }
         const int nother = MODE == PASS_K ? R.nc / 16 : R.nr / 16;
         for (int o = 0; o < nother; ++o) {
-          f32x4 c[CH];
+          f32x4 c[CHT];
           // the other operand's rows: resident in LDS, or from global memory
           const __bf16* pr0;
           size_t ustride;
           if (P.resident) {
-            pr0 = res + (16 * o + lq) * P.ldk + lg * 8;
+            pr0 = res + ((size_t)u0 * nres + 16 * o + lq) * P.ldk + lg * 8;
             ustride = (size_t)nres * P.ldk;
           } else {
             const int oi = MODE == PASS_K ? min(max(j0 + R.c0 + 16 * o + lq, 0), T - 1)
                                           : min(max(i0 + R.r0 + 16 * o + lq, 0), T - 1);
             const __bf16* src = MODE == PASS_K ? (isS ? A.k : A.v) : (isS ? A.q : A.dO);
-            pr0 = src + ((bT + oi) * M + g * CH) * D + lg * 8;
+            pr0 = src + ((bT + oi) * M + g * CH + u0) * D + lg * 8;
             ustride = D;
           }
 #pragma unroll
-          for (int u = 0; u < CH; ++u) {
+          for (int u = 0; u < CHT; ++u) {
             const __bf16* pr = pr0 + u * ustride;
             c[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -555,7 +590,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
           }
           const int rb = MODE == PASS_K ? R.r0 + 16 * blk : R.r0 + 16 * o;
           const int cb = MODE == PASS_K ? R.c0 + 16 * o : R.c0 + 16 * blk;
-          epilogue(isS, rb, cb, c);
+          epilogue(isS, rb, cb, u0, c);
         }
         if (prefetch) {  // the next step's operand, in flight through the stages that follow
           if (MODE == PASS_K ? i0 + TB < T : j0 + TB <= i0) load_global(t, MODE == PASS_K ? i0 + TB : i0,
@@ -564,6 +599,52 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
       }
     }
     __syncthreads();
+    if constexpr (HS > 1) {
+      // ---- (1b) the mixing of the halved tasks, position by position over every head: before
+      // softmax with Mask_0 into Z, or with the exponential into P; after softmax, dE
+      if (P.premix || P.postmix) {
+        if (P.premix) {
+          const Reg& R = pre ? P.rZ : P.rP;
+          const Geo& G = pre ? P.gZ : P.gP;
+          for (int x = tid; x < R.nr * R.nc; x += NT) {
+            const int r = R.r0 + x / R.nc, c = R.c0 + x % R.nc;
+            const bool ok = valid(r, c);
+            float v[CH];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) v[u] = *at(lds, G, u, r, c);
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+              float z = 0.0f;
+#pragma unroll
+              for (int w = 0; w < CH; ++w) z = __builtin_fmaf(wm1[u * CH + w], v[w], z);
+              if (pre) {
+                *at(lds, G, u, r, c) = ok ? z : 0.0f;
+              } else {
+                const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
+                *at(lds, G, u, r, c) = ok ? __builtin_amdgcn_exp2f((z - l) * 1.4426950408889634f) : 0.0f;
+              }
+            }
+          }
+        }
+        if (P.postmix) {
+          for (int x = tid; x < P.rdE.nr * P.rdE.nc; x += NT) {
+            const int r = P.rdE.r0 + x / P.rdE.nc, c = P.rdE.c0 + x % P.rdE.nc;
+            const bool ok = valid(r, c);
+            float v[CH];
+#pragma unroll
+            for (int u = 0; u < CH; ++u) v[u] = *at(lds, P.gdE, u, r, c);
+#pragma unroll
+            for (int w = 0; w < CH; ++w) {
+              float s = 0.0f;
+#pragma unroll
+              for (int u = 0; u < CH; ++u) s = __builtin_fmaf(wm2[u * CH + w], v[u], s);
+              *at(lds, P.gdE, w, r, c) = ok ? s : 0.0f;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
     // the softmax gradient at (u, r, c) of rdC, from dP there: dC = P (dP - D_r)
     auto dC_of = [&](int u, int r, int c, float dp) BWT_INLINE {
       return *at(lds, P.gP, u, r, c) * (dp - d_s[u * P.rdC.nr + (r - P.rdC.r0)]);
