@@ -463,8 +463,8 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
       const int i = i0 + r, j = j0 + c;
       return (j >= 0) & (j <= i) & (i < T);
     };
-    // ---- (1) MFMA: S over mS and dA over mA for every head of the group. A task is one row of
-    // 16 x 16 blocks (PASS_K: its Q or dO rows from global memory, once per step; K or V rows
+    // ---- (1) MFMA: S over mS and dA over mA for every head of the group (a task takes CHT of
+    // them). A task is one row of 16 x 16 blocks (PASS_K: its Q or dO rows from global memory, once per step; K or V rows
     // from the resident LDS copy) or one column of blocks (PASS_D, the other way round).
     // S block: mixing before softmax, Mask_0, and Z into gZ (with a convolution before softmax)
     // or P = exp(Z - lse) into gP; PASS_K keeps the core of S (dw_pre). dA block: PASS_K keeps
