@@ -1,4 +1,5 @@
-"""The fused forward and the split decode step captured in a HIP graph (torch.cuda.CUDAGraph).
+"""The fused forward, the split decode step and a training step (forward_train + the fused
+backward) captured in a HIP graph (torch.cuda.CUDAGraph).
 
 The library only launches kernels on the caller's stream (no memset, allocation or
 synchronisation), so a serving loop can capture a step once and replay it. Between replays the
@@ -69,3 +70,60 @@ def test_step_replays_in_a_graph(split):
     got = out_g.float().cpu().numpy().astype(np.float64)
     err = np.abs(got[:, rows] - want[:, rows])
     assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("kq,mix", [("post", "pre"), ("both", "both")])
+def test_training_step_replays_in_a_graph(kq, mix):
+    """mta_forward_train and mta_backward_fused captured together (a layer's training step) and
+    replayed with new inputs written in place between replays: every replay equals the eager
+    step; the fixed-order gradients bit for bit, dQ (summed with atomics in no fixed order) to
+    rounding."""
+    cfg = mta_inputs.MTAConfig("graph_train", 2, 600, 8, 128, 4, 9, 4, kq, mix, True, "bf16", 0.1, 0.1, 1.0, 0.0,
+                               0.8, seed=47)
+    inp = mta_inputs.make_inputs(cfg)
+    d = {n: torch.from_numpy(inp[n]).cuda().to(torch.bfloat16).contiguous() for n in ("q", "k", "v")}
+    p = {n: torch.from_numpy(np.ascontiguousarray(inp[n], np.float32)).cuda() for n in ("theta", "w", "gamma", "beta")}
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    gen = torch.Generator(device="cuda").manual_seed(8)
+    dout = torch.randn(d["q"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    need = ta.backward_fused_workspace_bytes(cfg.B, cfg.T, cfg.M, cfg.d, **kw)
+
+    def buffers():
+        return {"out": torch.empty_like(d["q"]),
+                "lse": torch.empty((cfg.B, cfg.T, cfg.M), dtype=torch.float32, device="cuda"),
+                "opre": torch.empty(d["q"].shape, dtype=torch.float32, device="cuda"),
+                "ws": torch.empty(need, dtype=torch.uint8, device="cuda")}
+
+    def step(bf):
+        args = (d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], inp["lam"])
+        ta.forward_train(*args, out=bf["out"], lse=bf["lse"], out_pre_gn=bf["opre"], **kw)
+        return ta.backward_fused(*args, dout=dout, lse=bf["lse"], out_pre_gn=bf["opre"], workspace=bf["ws"], **kw)
+
+    bg, be = buffers(), buffers()
+    side = torch.cuda.Stream()  # warm-up off the default stream before capture
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(bg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got = step(bg)
+    torch.cuda.synchronize()
+
+    shape = (cfg.B, 16, cfg.M, cfg.d)
+    for rep in range(3):
+        for n in ("q", "k", "v"):
+            d[n][:, 100 * rep:100 * rep + 16] = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        dout[:, -16:] = torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = step(be)
+        torch.cuda.synchronize()
+        for n in ("out", "lse", "opre"):
+            assert torch.equal(bg[n], be[n]), f"replay {rep}: {n} differs from the eager step"
+        for n in ("dk", "dv", "dtheta", "dw", "dgamma", "dbeta", "dlambda"):
+            assert torch.equal(got[n], want[n]), f"replay {rep}: {n} differs from the eager step"
+        err = (got["dq"].float() - want["dq"].float()).abs().max()
+        assert float(err) <= 1e-2 * float(want["dq"].float().abs().max()), f"replay {rep}: dq {float(err)}"
