@@ -129,6 +129,23 @@ def test_backward_fused_specialised_kernels(kq, mix, c_q, c_k, c_h, d):
           what=f"fused {kq}/{mix} {c_q}x{c_k} c_h={c_h} d={d}")
 
 
+@pytest.mark.parametrize("sigma", [2.0, 3.0])
+@pytest.mark.parametrize("base", ["slice880m_bf16", "longctx_bf16", "variant_bf16", "both_sides_bf16"])
+def test_backward_fused_large_logits(base, sigma):
+    """q and k scaled by sigma (logit standard deviation sigma^2: rows with several competing large
+    logits), on each benchmark placement and kernel size: the forward's log-sum-exp comes from
+    fp16-held logits whose error grows with their magnitude, and the backward renormalises its
+    recomputed softmax against it."""
+    c = mta_inputs.config(base)
+    over = dict(plant_block=0) if base == "longctx_bf16" else {}
+    cfg = c.replace(B=1, T=256, M=2 * c.c_h, **over)
+    inp, dout = grads_case(cfg)
+    for n in ("q", "k"):
+        inp[n] = mta_inputs.round_bf16(inp[n] * sigma)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what=f"fused {base} sigma={sigma}")
+
+
 @pytest.mark.parametrize("T", [1, 2, 15, 16, 17, 63, 200])
 def test_backward_fused_ragged_lengths(T):
     cfg = mta_inputs.MTAConfig("bwd_T", 2, T, 4, 32, 4, 9, 2, "both", "both", T > 2, "bf16", 0.2, 0.2, 1.0, 0.0,
