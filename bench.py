@@ -146,6 +146,30 @@ def time_launches(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps
 
 
+def training_step_record(ta, torch, wcfg, wd, steps):
+    """mta_forward_train and mta_backward_fused on one workload's device tensors, each timed on its
+    own (ms per call); the output gradient is a seeded N(0,1) tensor in the input dtype."""
+    wkw = dict(c_q=wcfg.c_q, c_k=wcfg.c_k, c_h=wcfg.c_h, kq=wcfg.kq, mix=wcfg.mix, gn=wcfg.gn)
+    need = ta.backward_fused_workspace_bytes(wcfg.B, wcfg.T, wcfg.M, wcfg.d, **wkw)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(wd["q"])
+    lse = torch.empty((wcfg.B, wcfg.T, wcfg.M), dtype=torch.float32, device="cuda")
+    opre = torch.empty(wd["q"].shape, dtype=torch.float32, device="cuda") if wcfg.gn else None
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn(wd["q"].shape, generator=gen, device="cuda").to(wd["q"].dtype)
+    args = (wd["q"], wd["k"], wd["v"], wd["theta"], wd["w"], wd["gamma"], wd["beta"], wd["lam"])
+
+    def fwd():
+        ta.forward_train(*args, out=out, lse=lse, out_pre_gn=opre, **wkw)
+
+    def bwd():
+        ta.backward_fused(*args, dout=dout, lse=lse, out_pre_gn=opre, workspace=ws, **wkw)
+    ms_f = time_launches(fwd, max(2, steps // 2), 1, torch)
+    ms_b = time_launches(bwd, max(2, steps // 4), 1, torch)
+    return {"forward_train_ms": ms_f, "backward_fused_ms": ms_b, "train_step_ms": ms_f + ms_b,
+            "train_tokens_per_s": wcfg.B * wcfg.T / ((ms_f + ms_b) * 1e-3), "workspace_gib": need / 2 ** 30}
+
+
 def launch_spread(fn, reps, torch):
     """Min and median ms of reps individually timed calls (an event pair around each)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -471,9 +495,12 @@ def main():
     result["plain_attention"] = plain_record(ms_plain, ms)
     result["default_placement_same_shape"] = default_record(
         time_launches(fused_default, args.steps, args.warmup, torch), ms_plain)
+    result["default_placement_same_shape"]["training_step"] = training_step_record(ta, torch, dflt, d, args.steps)
     if cfg.T == both_cfg.T and cfg.B == both_cfg.B and cfg.M == both_cfg.M and cfg.d == both_cfg.d:
         result["both_sides_same_shape"] = both_record(time_launches(fused_both, args.steps, args.warmup, torch),
                                                       ms_plain)
+        result["both_sides_same_shape"]["training_step"] = training_step_record(ta, torch, both_cfg, both_d,
+                                                                                args.steps)
         both_d.clear()
     # a suffix of rows against all keys: one decode step (the last row of every sequence) and
     # a 512-row prefill chunk, both at the headline placement
@@ -554,7 +581,8 @@ def main():
             "ms": ms_w, "tokens_per_s": wcfg.B * wcfg.T / (ms_w * 1e-3), "tflops": tf,
             "pct_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS, "flops_per_call": flops(wcfg),
             "plain_ms": ms_p, "plain_tflops": wcfg.B * wcfg.M * wn_c * 4 * wcfg.d / (ms_p * 1e-3) / 1e12,
-            "mta_slowdown_vs_plain": ms_w / ms_p}
+            "mta_slowdown_vs_plain": ms_w / ms_p,
+            "training_step": training_step_record(ta, torch, wcfg, wd, args.steps)}
         del wd, wout
     result["backward_fused"] = fused_backward_record(ms)
     if not args.no_materialized:
