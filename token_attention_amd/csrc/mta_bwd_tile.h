@@ -71,7 +71,7 @@ struct Plan {
   // operand rows resident for the whole sweep (bf16): PASS_K the keys' K (over the columns of
   // mS) and V (columns of mA), PASS_D the query rows' Q (rows of mS) and dO (rows of mA)
   int off_x, off_y, nrx, nry;
-  int resident;          // 0: those rows did not fit; they are read from global memory instead
+  int resident;          // 2: both; 1: the first (X) only; 0: neither (read from global memory)
   int off_bf;            // PASS_K bf16 staging: Q and dO of the core rows, dS and A tiles
   int lds_floats;        // pool size
 };
@@ -104,7 +104,7 @@ __host__ __device__ constexpr Reg grow(const Reg& R, int up, int down, int side)
 // the core tile; P there and where the convolution after softmax reads for the core; Z around
 // P; dE around dC. PASS_D: P and dP on the core tile, Z and dE around them.
 __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q, int c_k, int ch, int d,
-                                             bool resident = true) {
+                                             int resident = 2) {
   Plan p{};
   p.pre = (kq & 1) != 0;
   p.post = (kq & 2) != 0;
@@ -153,15 +153,17 @@ __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q,
   p.nry = K ? p.mA.nc : p.mA.nr;
   p.resident = resident;
   p.off_x = pool;
-  if (resident) pool += (ch * p.nrx * p.ldk) / 2;
+  if (resident >= 1) pool += (ch * p.nrx * p.ldk) / 2;
   p.off_y = pool;
-  if (resident) pool += (ch * p.nry * p.ldk) / 2;
+  if (resident >= 2) pool += (ch * p.nry * p.ldk) / 2;
   p.off_bf = pool;
   if (K) pool += (2 * ch * TB * p.ldk + 2 * ch * TB * LDT) / 2;
   // the end-of-sweep reductions reuse the pool from its start
   pool = imax(pool, imax(3 * 512, ch * ch * TB));  // dtheta partials: at most EB per thread
   p.lds_floats = r4c(pool);
-  if (resident && p.lds_floats * 4 > 160 * 1024) return make_plan(mode, kq, mix, c_q, c_k, ch, d, false);
+  // what does not fit the 160 KiB of a CU is read from global memory: first Y (fewer MFMA operand
+  // reads: the dA map is the smaller one), then X
+  if (resident > 0 && p.lds_floats * 4 > 160 * 1024) return make_plan(mode, kq, mix, c_q, c_k, ch, d, resident - 1);
   return p;
 }
 
@@ -412,29 +414,27 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   if (MODE == PASS_K) {
     j0 = tile * TB;
     i0 = j0;
-    if (P.resident) {
+    if (P.resident >= 1) {
       stage_rows(Xr, A.k, j0 + P.mS.c0, P.nrx);
-      stage_rows(Yr, A.v, j0 + P.mA.c0, P.nry);
+      if (P.resident >= 2) stage_rows(Yr, A.v, j0 + P.mA.c0, P.nry);
     } else {
       stage_rows(Qc, A.k, j0, TB);  // the K rows of the keys, for the transposed reads below
     }
     load_stats(i0, 0);
     __syncthreads();
-    const __bf16* kc = P.resident ? Xr - P.mS.c0 * P.ldk : Qc;  // K row j0 of head 0
-    const int kstride = P.resident ? P.nrx : TB;                  // rows per head
+    const __bf16* kc = P.resident >= 1 ? Xr - P.mS.c0 * P.ldk : Qc;  // K row j0 of head 0
+    const int kstride = P.resident >= 1 ? P.nrx : TB;                  // rows per head
 #pragma unroll
     for (int x = 0; x < NQT; ++x) {
       const int t = wave + x * NW;
       if (t < CH * NB) kfrag[x] = tr_read(kc + (t / NB) * kstride * P.ldk, 4 * lg, (t % NB) * 16, P.ldk, lane);
     }
-    if (!P.resident) __syncthreads();  // Qc is rewritten by the first step
+    if (P.resident == 0) __syncthreads();  // Qc is rewritten by the first step
   } else {
     i0 = tile * TB;
     j0 = 0;
-    if (P.resident) {
-      stage_rows(Xr, A.q, i0 + P.mS.r0, P.nrx);
-      stage_rows(Yr, A.dO, i0 + P.mA.r0, P.nry);
-    }
+    if (P.resident >= 1) stage_rows(Xr, A.q, i0 + P.mS.r0, P.nrx);
+    if (P.resident >= 2) stage_rows(Yr, A.dO, i0 + P.mA.r0, P.nry);
     load_stats(i0, 0);
     __syncthreads();
   }
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
           // the other operand's rows: resident in LDS, or from global memory
           const __bf16* pr0;
           size_t ustride;
-          if (P.resident) {
+          if (isS ? P.resident >= 1 : P.resident >= 2) {
             pr0 = res + ((size_t)u0 * nres + 16 * o + lq) * P.ldk + lg * 8;
             ustride = (size_t)nres * P.ldk;
           } else {
