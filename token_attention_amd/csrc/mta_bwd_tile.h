@@ -187,16 +187,17 @@ __host__ __device__ constexpr int threads_for(const Plan& p) { return p.lds_floa
 
 // Heads per stage-1 MFMA task: the whole group, or (HS = 2) half of it. Halved tasks give the
 // waves that would otherwise idle a share of the products, and the mixing, which needs every
-// head of a position, then runs as a pointwise pass of its own after them. Used where both
-// mixings are present and the halved tasks still give every wave at most one (the specialised
-// PASS_K kernel with everything on both sides: 42.0 -> 37.9 ms at T=4096); with one mixing the
-// extra pass and barrier cost what the shorter products save (post 4 x 9 with mixing before:
-// 20.5 -> 21.8 ms; pre 4 x 9 with mixing after: unchanged).
+// head of a position, then runs as a pointwise pass of its own after them. Chosen per
+// specialised PASS_K shape by measurement of the whole fused backward (the halved tasks must
+// still give every wave at most one): used with mixing after softmax and 4 x 9 kernels (before
+// softmax, T=4096: 28.5 -> 27.2 ms; both sides, T=4096: 42.0 -> 37.1 ms); not with mixing before
+// softmax only (4 x 9 after softmax, T=4096: 19.5 -> 21.5 ms) nor with 6 x 11 kernels before
+// softmax and four-head groups (T=16384: 126 -> 133 ms).
 __host__ __device__ constexpr int head_split(int mode, int spec, int ch, int d, int nt) {
-  if (spec == 0 || mode != PASS_K || ch % 2 != 0) return 1;
+  if (!(spec == 2 || spec == 3) || mode != PASS_K || ch % 2 != 0) return 1;
   const SpecShape sh = spec_shape(spec);
   const Plan p = make_plan(mode, sh.kq, sh.mix, sh.cq, sh.ck, ch, d);
-  return p.premix && p.postmix && 2 * (p.mS.nr / 16 + p.mA.nr / 16) <= nt / 64 ? 2 : 1;
+  return 2 * (p.mS.nr / 16 + p.mA.nr / 16) <= nt / 64 ? 2 : 1;
 }
 
 struct BwArgs {
