@@ -236,40 +236,43 @@ __device__ __forceinline__ bool inside(const Reg& R, int r, int c) {
 
 // dst over region R of every head: sum_{a, e} th[u][a][e] * src[u][r + sa a][c + sa (e - h)],
 // sa = -1 for the convolution, +1 for its adjoint; fin(u, r, c, value) stores it. Each thread
-// makes four consecutive columns of one row from a window of 4 + 2h source values per lag.
-template <int CH, int NT, class Fin>
+// makes CPT consecutive columns of one row from a window of CPT + 2h source values per lag.
+template <int CH, int NT, int CPT = 4, class Fin>
 __device__ __forceinline__ void conv_region(float* lds, const Geo& src, const Reg& R, const float* th, int cq,
                                             int ck, int h, bool adjoint, Fin fin, int t0 = -1, int nthreads = NT) {
-  const int ncb = R.nc >> 2;  // R.nc is a multiple of 4
+  static_assert(CPT == 1 || CPT == 2 || CPT == 4, "R.nc is a multiple of 4");
+  const int ncb = R.nc / CPT;
   const int n = CH * R.nr * ncb;
   for (int t = t0 < 0 ? (int)threadIdx.x : t0; t < n; t += nthreads) {
     const int u = t / (R.nr * ncb);
     const int rem = t - u * R.nr * ncb;
     const int r = R.r0 + rem / ncb;
-    const int c4 = R.c0 + 4 * (rem % ncb);
+    const int c0 = R.c0 + CPT * (rem % ncb);
     const float* thu = th + u * cq * ck;
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    float o[CPT];
+#pragma unroll
+    for (int qq = 0; qq < CPT; ++qq) o[qq] = 0.0f;
     for (int a = 0; a < cq; ++a) {
       const int sr = adjoint ? r + a : r - a;
-      const float* row = at(lds, src, u, sr, c4 - h);
-      float xr[4 + CKM - 1];
+      const float* row = at(lds, src, u, sr, c0 - h);
+      float xr[CPT + CKM - 1];
 #pragma unroll
-      for (int x = 0; x < 4 + CKM - 1; ++x)
-        if (x < 4 + 2 * h) xr[x] = row[x];
+      for (int x = 0; x < CPT + CKM - 1; ++x)
+        if (x < CPT + 2 * h) xr[x] = row[x];
       const float* tha = thu + a * ck;
 #pragma unroll
       for (int e = 0; e < CKM; ++e) {
         if (e < ck) {
-          // window slot x holds column c4 - h + x: the adjoint reads c + e - h (slot q + e),
+          // window slot x holds column c0 - h + x: the adjoint reads c + e - h (slot q + e),
           // the convolution reads c - e' + h with e' = ck - 1 - e (slot q + e)
           const float w = tha[adjoint ? e : ck - 1 - e];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) o[qq] = __builtin_fmaf(w, xr[qq + e], o[qq]);
+          for (int qq = 0; qq < CPT; ++qq) o[qq] = __builtin_fmaf(w, xr[qq + e], o[qq]);
         }
       }
     }
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) fin(u, r, c4 + qq, o[qq]);
+    for (int qq = 0; qq < CPT; ++qq) fin(u, r, c0 + qq, o[qq]);
   }
 }
 
@@ -330,6 +333,10 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   constexpr int NB = D / 16;
   constexpr int NKV = (2 * CH * NB + NW - 1) / NW;  // dK / dV blocks per wave
   constexpr int NQT = (CH * NB + NW - 1) / NW;      // dQ blocks per wave
+  // columns per thread of the convolutions (PASS_D's D accumulation keeps four): two for 4 x 9
+  // before softmax with mixing after (fused backward at T=4096: 27.4 -> 24.3 ms), four elsewhere
+  // (two measured slower: +4 % after softmax, +7 % on both sides, twice the time with 6 x 11)
+  constexpr int CPC = SPEC == 2 ? 2 : 4;
   constexpr int HS = head_split(MODE, SPEC, CH, D, NT);
   constexpr int CHT = CH / HS;  // heads per stage-1 task
   const int nrq = imax(1, min(TB, NT / (CH * P.cq * ((P.ck + EB - 1) / EB))));  // dtheta row groups
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     // ---- (2) with a convolution before softmax: P = exp(conv_pre(Z) - lse) over rP; PASS_K
     // without one after softmax also dC there (dP = dE)
     if (pre) {
-      conv_region<CH, NT>(lds, P.gZ, P.rP, th_s, P.cq, P.ck, P.h1, false, [&](int u, int r, int c, float cv) BWT_INLINE {
+      conv_region<CH, NT, CPC>(lds, P.gZ, P.rP, th_s, P.cq, P.ck, P.h1, false, [&](int u, int r, int c, float cv) BWT_INLINE {
         const float l = lse_s[u * P.rP.nr + (r - P.rP.r0)];
         const float pv = valid(r, c) ? __builtin_amdgcn_exp2f((cv - l) * 1.4426950408889634f) : 0.0f;
         *at(lds, P.gP, u, r, c) = pv;
@@ -702,9 +709,9 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     // and dC = P (dP - D) there; dtheta_post partials. Without a convolution after softmax and
     // before it either, dC = P (dE - D) in place. Q and dO of the core rows into LDS.
     if (post) {
-      conv_region<CH, NT>(lds, P.gP, core, th_s + thn, P.cq, P.ck, P.h2, false,
+      conv_region<CH, NT, CPC>(lds, P.gP, core, th_s + thn, P.cq, P.ck, P.h2, false,
                           [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, P.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
-      conv_region<CH, NT>(lds, P.gdE, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
+      conv_region<CH, NT, CPC>(lds, P.gdE, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
                           [&](int u, int r, int c, float dp) BWT_INLINE { *at(lds, P.gdC, u, r, c) = dC_of(u, r, c, dp); });
       dtheta_tasks<CH, NT>(lds, P.gdE, P.gP, P.cq, P.ck, P.h2, nrq, acc_thpost);
     } else if (!pre) {
@@ -719,7 +726,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     // ---- (4) with a convolution before softmax: dL = Mask_0(conv_pre^T(dC)) on the core;
     // dtheta_pre partials
     if (pre) {
-      conv_region<CH, NT>(lds, P.gdC, core, th_s, P.cq, P.ck, P.h1, true,
+      conv_region<CH, NT, CPC>(lds, P.gdC, core, th_s, P.cq, P.ck, P.h1, true,
                           [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, P.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
       dtheta_tasks<CH, NT>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, nrq, acc_thpre);
       __syncthreads();
