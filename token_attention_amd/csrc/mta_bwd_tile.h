@@ -131,7 +131,9 @@ __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q,
   const Reg& cover = p.pre ? p.rZ : p.rP;
   p.mS = Reg{cover.r0, cover.c0, r16c(cover.nr), r16c(cover.nc)};
   p.mA = Reg{p.rdE.r0, p.rdE.c0, r16c(p.rdE.nr), r16c(p.rdE.nc)};
-  int pool = 0;
+  // four floats before the first map: the dtheta windows of taps beyond c_k (the last group of EB
+  // taps) start up to EB - 1 columns left of the map they read and discard those values
+  int pool = 4;
   p.gP = own_geo(p.rP, ch, pool);
   p.gZ = p.pre ? own_geo(p.rZ, ch, pool) : p.gP;
   p.gSc = (K && p.premix) ? own_geo(core, ch, pool) : p.gP;
