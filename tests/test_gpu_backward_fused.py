@@ -129,6 +129,17 @@ def test_backward_fused_specialised_kernels(kq, mix, c_q, c_k, c_h, d):
           what=f"fused {kq}/{mix} {c_q}x{c_k} c_h={c_h} d={d}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 12, 13, 14, 16, 17, 26, 27, 40])
+def test_backward_fused_variant_kernel_ragged_lengths(T):
+    """The specialised kernel of the convolution after softmax with mixing before (its key-major
+    pass steps 13 query rows at a time): lengths around one and two steps and one 16-key tile."""
+    cfg = mta_inputs.MTAConfig("bwd_var_T", 1, T, 4, 128, 4, 9, 4, "post", "pre", T > 2, "bf16", 0.2, 0.2, 1.0,
+                               0.0, 0.8, seed=39)
+    inp, dout = grads_case(cfg)
+    check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
+          what=f"fused variant kernel T={T}")
+
+
 @pytest.mark.parametrize("sigma", [2.0, 3.0])
 @pytest.mark.parametrize("base", ["slice880m_bf16", "longctx_bf16", "variant_bf16", "both_sides_bf16"])
 def test_backward_fused_large_logits(base, sigma):

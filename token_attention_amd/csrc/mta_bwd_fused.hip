@@ -25,13 +25,6 @@ constexpr size_t LDS_LIMIT = 160 * 1024;
 int kq_bits(const Problem& p) { return ((p.kq & KQ_PRE) ? 1 : 0) | ((p.kq & KQ_POST) ? 2 : 0); }
 int mix_bits(const Problem& p) { return ((p.mix & MIX_PRE) ? 1 : 0) | ((p.mix & MIX_POST) ? 2 : 0); }
 
-// The plan of one pass (mta_bwd_tile.h); returns the LDS bytes, 0 if the tiles do not fit.
-size_t plan_tiles(const Problem& p, int mode, bwt::BwArgs& a) {
-  a.P = bwt::make_plan(mode, kq_bits(p), mix_bits(p), p.c_q, p.c_k, p.c_h, p.d);
-  const size_t bytes = (size_t)a.P.lds_floats * sizeof(float);
-  return bytes <= LDS_LIMIT ? bytes : 0;
-}
-
 // The specialised kernel of this shape, 0 for the generic one.
 int spec_of(const Problem& p) {
   for (int s = 1; s < bwt::NSPEC; ++s) {
@@ -41,6 +34,16 @@ int spec_of(const Problem& p) {
       return s;
   }
   return 0;
+}
+
+// The plan of one pass (mta_bwd_tile.h): a specialised kernel's own, else the generic kernel's,
+// which it reads from its arguments; returns the LDS bytes, 0 if the tiles do not fit.
+size_t plan_tiles(const Problem& p, int mode, bwt::BwArgs& a) {
+  const int spec = spec_of(p);
+  a.P = spec ? bwt::spec_plan(mode, spec, p.c_h, p.d)
+             : bwt::make_plan(mode, kq_bits(p), mix_bits(p), p.c_q, p.c_k, p.c_h, p.d);
+  const size_t bytes = (size_t)a.P.lds_floats * sizeof(float);
+  return bytes <= LDS_LIMIT ? bytes : 0;
 }
 
 __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {

@@ -63,6 +63,7 @@ struct Geo {
 
 struct Plan {
   int cq, ck, a1, h1, a2, h2;  // reach of the convolution before (1) / after (2) softmax, 0 if absent
+  int tq;                      // query rows of a tile step: PASS_K tq <= TB rows, PASS_D TB
   int pre, post, premix, postmix;
   Reg rZ, rP, rdC, rdE;        // regions: Z (with a convolution before softmax), P, dC, dE
   Reg mS, mA;                  // MFMA regions (16 x 16 blocks) covering Z or P, and dE
@@ -105,7 +106,7 @@ __host__ __device__ constexpr Reg grow(const Reg& R, int up, int down, int side)
 // the core tile; P there and where the convolution after softmax reads for the core; Z around
 // P; dE around dC. PASS_D: P and dP on the core tile, Z and dE around them.
 __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q, int c_k, int ch, int d,
-                                             int resident = 2) {
+                                             int resident = 2, int tq = TB) {
   Plan p{};
   p.pre = (kq & 1) != 0;
   p.post = (kq & 2) != 0;
@@ -117,12 +118,13 @@ __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q,
   p.h1 = p.pre ? (c_k - 1) / 2 : 0;
   p.a2 = p.post ? c_q - 1 : 0;
   p.h2 = p.post ? (c_k - 1) / 2 : 0;
-  const Reg core{0, 0, TB, TB};
   const bool K = mode == PASS_K;
-  p.rdC = K ? Reg{0, -p.h1, TB + p.a1, r4c(TB + 2 * p.h1)} : core;
+  p.tq = K ? tq : TB;
+  const Reg core{0, 0, p.tq, TB};
+  p.rdC = K ? Reg{0, -p.h1, p.tq + p.a1, r4c(TB + 2 * p.h1)} : core;
   if (K) {
     const int hc = imax(p.h1, p.h2);
-    p.rP = Reg{-p.a2, -hc, TB + p.a1 + p.a2, r4c(TB + 2 * hc)};
+    p.rP = Reg{-p.a2, -hc, p.tq + p.a1 + p.a2, r4c(TB + 2 * hc)};
   } else {
     p.rP = core;
   }
@@ -166,7 +168,8 @@ __host__ __device__ constexpr Plan make_plan(int mode, int kq, int mix, int c_q,
   p.lds_floats = r4c(pool);
   // what does not fit the 160 KiB of a CU is read from global memory: first Y (fewer MFMA operand
   // reads: the dA map is the smaller one), then X
-  if (resident > 0 && p.lds_floats * 4 > 160 * 1024) return make_plan(mode, kq, mix, c_q, c_k, ch, d, resident - 1);
+  if (resident > 0 && p.lds_floats * 4 > 160 * 1024)
+    return make_plan(mode, kq, mix, c_q, c_k, ch, d, resident - 1, tq);
   return p;
 }
 
@@ -184,6 +187,16 @@ __host__ __device__ constexpr SpecShape spec_shape(int spec) {
 }
 constexpr int NSPEC = 5;
 
+// Query rows per PASS_K step of a specialised shape: TB, or 13 for the convolution after softmax
+// alone, where the 3 rows before the step's rows (P) and after them (dE) then make every map of
+// the step exactly one 16-row MFMA block instead of two.
+__host__ __device__ constexpr int spec_tq(int spec) { return spec == 1 ? TB - 3 : TB; }
+// The plan of a specialised kernel (the host sizes its LDS from the same function).
+__host__ __device__ constexpr Plan spec_plan(int mode, int spec, int ch, int d) {
+  const SpecShape sh = spec_shape(spec);
+  return make_plan(mode, sh.kq, sh.mix, sh.cq, sh.ck, ch, d, 2, mode == PASS_K ? spec_tq(spec) : TB);
+}
+
 // Threads per workgroup: 256 when two workgroups fit the LDS of a CU (their barriers then
 // overlap), else 512.
 __host__ __device__ constexpr int threads_for(const Plan& p) { return p.lds_floats * 4 <= 80 * 1024 ? 256 : 512; }
@@ -192,14 +205,14 @@ __host__ __device__ constexpr int threads_for(const Plan& p) { return p.lds_floa
 // waves that would otherwise idle a share of the products, and the mixing, which needs every
 // head of a position, then runs as a pointwise pass of its own after them. Chosen per
 // specialised PASS_K shape by measurement of the whole fused backward (the halved tasks must
-// still give every wave at most one): used with mixing after softmax and 4 x 9 kernels (before
-// softmax, T=4096: 28.5 -> 27.2 ms; both sides, T=4096: 42.0 -> 37.1 ms); not with mixing before
-// softmax only (4 x 9 after softmax, T=4096: 19.5 -> 21.5 ms) nor with 6 x 11 kernels before
-// softmax and four-head groups (T=16384: 126 -> 133 ms).
+// still give every wave at most one): used with 4 x 9 kernels (before softmax with mixing
+// after, T=4096: 28.5 -> 27.2 ms; both sides, T=4096: 42.0 -> 37.1 ms; after softmax with
+// 13-row steps, whose single 16-row block per map leaves two tasks: 21.3 -> 18.8 ms, against
+// 19.8-20.8 ms with 16-row steps and whole-group tasks), not with 6 x 11 kernels before softmax
+// and four-head groups (T=16384: 126 -> 133 ms).
 __host__ __device__ constexpr int head_split(int mode, int spec, int ch, int d, int nt) {
-  if (!(spec == 2 || spec == 3) || mode != PASS_K || ch % 2 != 0) return 1;
-  const SpecShape sh = spec_shape(spec);
-  const Plan p = make_plan(mode, sh.kq, sh.mix, sh.cq, sh.ck, ch, d);
+  if (!(spec >= 1 && spec <= 3) || mode != PASS_K || ch % 2 != 0) return 1;
+  const Plan p = spec_plan(mode, spec, ch, d);
   return 2 * (p.mS.nr / 16 + p.mA.nr / 16) <= nt / 64 ? 2 : 1;
 }
 
@@ -284,7 +297,7 @@ __device__ __forceinline__ void conv_region(float* lds, const Geo& src, const Re
 // X per row (rows rq, rq + nrq, ...; nrq row groups keep the tasks within one round).
 template <int CH, int NT>
 __device__ __forceinline__ void dtheta_tasks(float* lds, const Geo& gG, const Geo& gX, int cq, int ck, int h, int nrq,
-                                             float (&acc)[EB]) {
+                                             int rows, float (&acc)[EB]) {
   const int neb = (ck + EB - 1) / EB;
   const int t = threadIdx.x;
   if (t < CH * cq * neb * nrq) {
@@ -296,7 +309,7 @@ __device__ __forceinline__ void dtheta_tasks(float* lds, const Geo& gG, const Ge
     // window slot k holds column k + h - e0 - (EB - 1); tap e0 + j reads slot c + EB - 1 - j.
     // Slots left of column -h serve only taps beyond ck and are not read.
     const int kmin = e0 + EB - 1 - 2 * h;
-    for (int r = rq; r < TB; r += nrq) {
+    for (int r = rq; r < rows; r += nrq) {
       const float* gr = at(lds, gG, u, r, 0);
       const float* xr = at(lds, gX, u, r - a, h - e0 - (EB - 1));
       float xw[TB + EB - 1];
@@ -325,8 +338,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   // LDS offsets fold away
   Plan P;
   if constexpr (SPEC != 0) {
-    constexpr SpecShape sh = spec_shape(SPEC);
-    constexpr Plan KP = make_plan(MODE, sh.kq, sh.mix, sh.cq, sh.ck, CH, D);
+    constexpr Plan KP = spec_plan(MODE, SPEC, CH, D);
     P = KP;
   } else {
     P = A.P;
@@ -341,7 +353,10 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   constexpr int CPC = SPEC == 2 ? 2 : 4;
   constexpr int HS = head_split(MODE, SPEC, CH, D, NT);
   constexpr int CHT = CH / HS;  // heads per stage-1 task
-  const int nrq = imax(1, min(TB, NT / (CH * P.cq * ((P.ck + EB - 1) / EB))));  // dtheta row groups
+  // query rows per step (a compile-time constant in the specialised kernels)
+  constexpr int TQS = SPEC != 0 ? spec_plan(MODE, SPEC, CH, D).tq : TB;
+  const int tq = SPEC != 0 ? TQS : P.tq;
+  const int nrq = imax(1, min(tq, NT / (CH * P.cq * ((P.ck + EB - 1) / EB))));  // dtheta row groups
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
   const int T = A.T, M = A.M;
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
   const int tile = MODE == PASS_D ? A.n_tiles - 1 - tile_rank : tile_rank;
   const bool pre = P.pre, post = P.post;
   const size_t bT = (size_t)b * T;
-  const Reg core{0, 0, TB, TB};
+  const Reg core{0, 0, tq, TB};  // the step's core tile: tq query rows x TB keys
 
   float* th_s = lds + P.off_th;  // [2][CH][cq][ck]: before softmax, then after
   const int thn = CH * P.cq * P.ck;
@@ -440,6 +455,20 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
       if (t < CH * NB) kfrag[x] = tr_read(kc + (t / NB) * kstride * P.ldk, 4 * lg, (t % NB) * 16, P.ldk, lane);
     }
     if (P.resident == 0) __syncthreads();  // Qc is rewritten by the first step
+    if (tq < TB) {
+      // rows of the bf16 staging past the step's tq rows: zero, so that the 16-row products of
+      // stage 6 add nothing for them (the steps write only rows below tq of Qc, dSb and Ab)
+      for (int x = tid; x < CH * (TB - tq) * P.ldk; x += NT) {
+        const int u = x / ((TB - tq) * P.ldk), rem = x % ((TB - tq) * P.ldk);
+        Qc[(u * TB + tq) * P.ldk + rem] = (__bf16)0.0f;
+        Oc[(u * TB + tq) * P.ldk + rem] = (__bf16)0.0f;
+      }
+      for (int x = tid; x < CH * (TB - tq) * LDT; x += NT) {
+        const int u = x / ((TB - tq) * LDT), rem = x % ((TB - tq) * LDT);
+        dSb[(u * TB + tq) * LDT + rem] = (__bf16)0.0f;
+        Ab[(u * TB + tq) * LDT + rem] = (__bf16)0.0f;
+      }
+    }
   } else {
     i0 = tile * TB;
     j0 = 0;
@@ -499,7 +528,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
         for (int x = 0; x < 4; ++x) {
           const int r = rb + 4 * lg + x, cc = cb + lq;
           const bool ok = valid(r, cc);
-          const bool in_core = r >= 0 && r < TB && cc >= 0 && cc < TB;
+          const bool in_core = r >= 0 && r < tq && cc >= 0 && cc < TB;
           float v[CHT];
 #pragma unroll
           for (int u = 0; u < CHT; ++u) v[u] = isS ? c[u][x] * A.scale : c[u][x];
@@ -572,7 +601,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
         if (MODE == PASS_K) {
           // the core rows of Q (S rows) and dO (dA rows), for the step's dK and dV products
           const int row = R.r0 + 16 * blk + lq;
-          if (row >= 0 && row < TB) {
+          if (row >= 0 && row < tq) {
             __bf16* dst = isS ? Qc : Oc;
 #pragma unroll
             for (int u = 0; u < CHT; ++u)
@@ -613,7 +642,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
           epilogue(isS, rb, cb, u0, c);
         }
         if (prefetch) {  // the next step's operand, in flight through the stages that follow
-          if (MODE == PASS_K ? i0 + TB < T : j0 + TB <= i0) load_global(t, MODE == PASS_K ? i0 + TB : i0,
+          if (MODE == PASS_K ? i0 + tq < T : j0 + TB <= i0) load_global(t, MODE == PASS_K ? i0 + tq : i0,
                                                                         MODE == PASS_K ? j0 : j0 + TB, fg);
         }
       }
@@ -715,7 +744,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
                           [&](int u, int r, int c, float ev) BWT_INLINE { *at(lds, P.gE, u, r, c) = valid(r, c) ? ev : 0.0f; });
       conv_region<CH, NT, CPC>(lds, P.gdE, P.rdC, th_s + thn, P.cq, P.ck, P.h2, true,
                           [&](int u, int r, int c, float dp) BWT_INLINE { *at(lds, P.gdC, u, r, c) = dC_of(u, r, c, dp); });
-      dtheta_tasks<CH, NT>(lds, P.gdE, P.gP, P.cq, P.ck, P.h2, nrq, acc_thpost);
+      dtheta_tasks<CH, NT>(lds, P.gdE, P.gP, P.cq, P.ck, P.h2, nrq, tq, acc_thpost);
     } else if (!pre) {
       for (int t = tid; t < CH * P.rdC.nr * P.rdC.nc; t += NT) {
         const int u = t / (P.rdC.nr * P.rdC.nc), rem = t % (P.rdC.nr * P.rdC.nc);
@@ -730,12 +759,12 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
     if (pre) {
       conv_region<CH, NT, CPC>(lds, P.gdC, core, th_s, P.cq, P.ck, P.h1, true,
                           [&](int u, int r, int c, float lv) BWT_INLINE { *at(lds, P.gdL, u, r, c) = valid(r, c) ? lv : 0.0f; });
-      dtheta_tasks<CH, NT>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, nrq, acc_thpre);
+      dtheta_tasks<CH, NT>(lds, P.gdC, P.gZ, P.cq, P.ck, P.h1, nrq, tq, acc_thpre);
       __syncthreads();
     }
     // ---- (5) dS = mix_pre^T(dL) and A = mix_post(E) on the core as bf16 tiles; the mixing
     // gradients' partials; the next step's row statistics
-    for (int x = tid; x < TB * TB; x += NT) {
+    for (int x = tid; x < tq * TB; x += NT) {
       const int r = x / TB, c = x % TB;
       float dl[CH], e[CH];
 #pragma unroll
@@ -760,7 +789,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
         Ab[(w * TB + r) * LDT + c] = (__bf16)av;
       }
     }
-    if (wtask) {
+    if (wtask && wr < tq) {
       if (P.premix) {  // dw_pre: the core row of dL_u S_v
         const float* pl = at(lds, P.gdL, wu, wr, 0);
         const float* ps = at(lds, P.gSc, wv, wr, 0);
@@ -778,7 +807,7 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
         acc_wpost += s;
       }
     }
-    if (i0 + TB < T) load_stats(i0 + TB, buf ^ 1);
+    if (i0 + tq < T) load_stats(i0 + tq, buf ^ 1);
     __syncthreads();
     // ---- (6) dK += dS^T Q, dV += A^T dO (registers); dQ += dS K (atomics). The next step's
     // first stage writes none of what this one reads, so no barrier follows.
@@ -802,11 +831,11 @@ __global__ __launch_bounds__(NT) void bwd_tile_kernel(BwArgs A) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = i0 + 4 * lg + x;
-          if (i < T) unsafeAtomicAdd(A.dq_acc + ((bT + i) * M + g * CH + u) * D + nb * 16 + lq, c[x]);
+          if (4 * lg + x < tq && i < T) unsafeAtomicAdd(A.dq_acc + ((bT + i) * M + g * CH + u) * D + nb * 16 + lq, c[x]);
         }
       }
     }
-    i0 += TB;
+    i0 += tq;
   }
 
   if (MODE == PASS_D) {
@@ -898,8 +927,7 @@ __host__ __device__ constexpr bool spec_built(int spec, int ch, int d) {
 template <int D, int CH, int MODE, int SPEC>
 hipError_t launch_nt(const BwArgs& a, size_t lds, unsigned grid, hipStream_t st) {
   if constexpr (SPEC != 0) {
-    constexpr SpecShape sh = spec_shape(SPEC);
-    constexpr int NT = threads_for(make_plan(MODE, sh.kq, sh.mix, sh.cq, sh.ck, CH, D));
+    constexpr int NT = threads_for(spec_plan(MODE, SPEC, CH, D));
     return launch_one<D, CH, MODE, SPEC, NT>(a, lds, grid, st);
   } else {
     return launch_one<D, CH, MODE, 0, 512>(a, lds, grid, st);
