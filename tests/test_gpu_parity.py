@@ -398,17 +398,51 @@ def test_mixing_both_sides_fp32_fused(kq, c_h):
     compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"fp32 {kq}/both")
 
 
-def test_both_sides_fp32_materialized_and_fused_refusal():
-    """fp32 tensors: the materialized chain takes every placement; the fp32 fused kernel
-    implements one side per convolution and reports convolutions on both sides unsupported."""
-    cfg = mta_inputs.MTAConfig("dual_fp32", 1, 64, 4, 16, 3, 5, 2, "both", "both", True, "fp32", 0.1, 0.1, 1.0,
+@pytest.mark.parametrize("c_q,c_k", [(1, 1), (2, 3), (3, 5), (4, 9), (8, 17), (5, 1)])
+@pytest.mark.parametrize("mix,c_h", [(None, 1), ("both", 4), ("post", 2), ("pre", 4), ("both", 2), ("post", 1)])
+def test_both_sides_fp32(c_q, c_k, mix, c_h):
+    """fp32 tensors with convolutions on both sides: the fp32 fused kernel (its both-sides
+    schedule: statistics of the convolved logits, then logits over both key halos -> weights
+    ring -> second convolution) and the materialized chain, against the oracle at the fp32 bar."""
+    cfg = mta_inputs.MTAConfig("dual_fp32", 1, 70, 4, 16, c_q, c_k, c_h, "both", mix, True, "fp32", 0.2, 0.2, 1.0,
                                0.0, 0.8, seed=26)
     inp = case(cfg)
     d = dev_inputs(cfg, inp)
-    compare(cfg, run("materialized", cfg, d, inp["lam"]), oracle_full(cfg), what="materialized fp32 both")
-    with pytest.raises(ta.MTAError) as e:
-        run("fused", cfg, d, inp["lam"])
-    assert e.value.status == ta.mta.ERR_UNSUPPORTED
+    want = oracle_full(cfg)
+    for path in ("fused", "materialized"):
+        compare(cfg, run(path, cfg, d, inp["lam"]), want, what=f"{path} fp32 both {c_q}x{c_k} mix={mix}/{c_h}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 17, 33, 100])
+@pytest.mark.parametrize("d,c_h", [(16, 4), (32, 2), (64, 4), (64, 1)])
+def test_both_sides_fp32_ragged_lengths_and_head_sizes(T, d, c_h):
+    """Both sides in fp32 at every fp32 head size (the d = 64, four-head tile is the largest
+    LDS footprint of the schedule), lengths below, at and across one 16-key tile and one row
+    tile (32 rows minus a halo of 2 (c_q - 1))."""
+    cfg = mta_inputs.MTAConfig("dual_fp32_T", 2, T, 4, d, 4, 9, c_h, "both", "both" if c_h > 1 else None, True,
+                               "fp32", 0.2, 0.2, 1.0, 0.0, 0.8, seed=28)
+    inp = case(cfg)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"fp32 both T={T} d={d}")
+
+
+@pytest.mark.parametrize("row_begin", [0, 1, 37, 90])
+def test_both_sides_fp32_row_range_equals_full_forward(row_begin):
+    """mta_forward_rows of fp32 tensors on both sides writes exactly rows row_begin.. of
+    mta_forward (bit for bit) and leaves the rows before it untouched."""
+    cfg = mta_inputs.MTAConfig("dual_fp32_rows", 2, 100, 8, 32, 4, 9, 4, "both", "both", True, "fp32", 0.1, 0.1, 1.0,
+                               0.0, 0.8, seed=29)
+    inp = case(cfg)
+    dv = dev_inputs(cfg, inp)
+    kw = dict(c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=cfg.kq, mix=cfg.mix, gn=cfg.gn)
+    args = (dv["q"], dv["k"], dv["v"], dv["theta"], dv["w"], dv["gamma"], dv["beta"], inp["lam"])
+    full = ta.forward(*args, **kw)
+    part = torch.full_like(full, 7.0)
+    ta.forward_rows(*args, row_begin=row_begin, out=part, **kw)
+    torch.cuda.synchronize()
+    f, p = full.float().cpu(), part.float().cpu()
+    assert torch.equal(p[:, row_begin:], f[:, row_begin:])
+    assert bool((p[:, :row_begin] == 7.0).all())
+    compare(cfg, f.numpy().astype(np.float64), oracle_full(cfg), what="fp32 both full")
 
 
 @pytest.mark.parametrize("row_begin", [0, 1, 97, 299])

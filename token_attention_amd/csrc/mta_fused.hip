@@ -28,7 +28,7 @@ bool fused_supported(const Problem& p) {
   const int ch = p.mix ? p.c_h : 1;
   if (ch != 1 && ch != 2 && ch != 4) return false;
   if (p.kq && (p.c_q < 1 || p.c_q > 8 || p.c_k < 1 || p.c_k > 17 || p.c_k % 2 == 0)) return false;
-  if (p.fp32 && (p.kq == KQ_BOTH || p.split_mode)) return false;
+  if (p.fp32 && p.split_mode) return false;
   if (p.fp32) return p.d == 16 || p.d == 32 || p.d == 64;
   return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
 }

@@ -12,7 +12,7 @@
 // are the query halo that the convolution reads (recomputed, never output). Each
 // wave owns one head of the group and a slab of WR rows.
 //
-// Two schedules, chosen at compile time:
+// Three schedules, chosen at compile time:
 //  * one pass (no convolution, or convolution before softmax). Per key tile:
 //      logits of the tile plus a 16-column key halo (fp32 MFMA)
 //      -> [mix before softmax, through LDS] -> Mask_0 -> fp32 in LDS
@@ -26,6 +26,13 @@
 //    normalisers): phase 1 computes exact (max, sum) of every tile row (halo
 //    included); phase 2 recomputes the logits with the key halo, forms the exact
 //    softmax weights, convolves them (Toeplitz MFMA), applies Mask_0 and does AV.
+//  * both sides (a convolution before and one after softmax, each head with its own two
+//    kernels): phase 1 as the one-pass front (logits with the key halo -> Mask_0 ->
+//    convolution -> Mask_-inf) for the exact (max, sum) of the softmax inputs; phase 2
+//    computes the logits with twice the key halo, convolves them into softmax inputs over
+//    the keys the second convolution reads, turns those into exact weights in a second
+//    ring, convolves that and does AV. An output row then reads 2 (c_q - 1) query rows
+//    before it, the tile's query halo.
 // Epilogue: per-(row, head) GroupNorm over d, affine, gate; store in the input dtype.
 //
 // Exponentials use exp2 with log2(e) folded into the logit scale (the convolutions
@@ -47,7 +54,8 @@ struct FusedArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* theta;
+  const float* theta;   // convolution kernels [M, c_q, c_k] (the one before softmax on both sides)
+  const float* theta2;  // both sides: the kernels after softmax
   const float* w_pre;   // mixing before softmax [M/c_h, c_h, c_h]
   const float* w_post;  // mixing after softmax
   const float* gamma;
@@ -65,16 +73,20 @@ struct FusedArgs {
   int xcd_remap;   // 1: keep all tiles of a (b, group) on one XCD (needs B*n_groups % 8 == 0)
 };
 
-template <typename Tin, int D_, int CH_, int WR_, int BK_, bool TWO_, bool PAIRS_>
+template <typename Tin, int D_, int CH_, int WR_, int BK_, bool TWO_, bool PAIRS_, bool DUAL_ = false>
 struct Cfg {
   typedef Tin T;
   typedef typename std::conditional<std::is_same<Tin, float>::value, float, _Float16>::type Tc;
   static constexpr int D = D_, CH = CH_, WR = WR_, BK = BK_;
-  static constexpr bool TWO = TWO_, PAIRS = PAIRS_;
+  static constexpr bool TWO = TWO_, PAIRS = PAIRS_, DUAL = DUAL_;
+  static_assert(!DUAL || TWO, "both sides use the two-phase schedule");
   static constexpr int WPH = NWAVE / CH;      // waves per head
   static constexpr int R = WR * WPH;          // computed rows per tile
   static constexpr int RB = WR / 16;          // 16-row blocks per wave
-  static constexpr int KWMAX = BK + HALO_COLS;
+  static constexpr int KW1 = BK + HALO_COLS;  // logit columns of one convolution's key halo
+  static constexpr int NB1 = KW1 / 16;
+  // staged K rows and logit columns: both sides need the halo of both convolutions
+  static constexpr int KWMAX = DUAL ? BK + 2 * HALO_COLS : KW1;
   static constexpr int KWB = KWMAX / 16;      // logit column blocks (with key halo)
   static constexpr int OB = BK / 16;          // output column blocks per key tile
   static constexpr int NB = D / 16;           // output channel blocks
@@ -88,6 +100,7 @@ struct Cfg {
   static constexpr int LDV = BK + PAD_T;    // V^T tile row stride
   static constexpr int LDP = BK + PAD_T;    // softmax-weight tile row stride
   static constexpr int LDZ = KWMAX + PAD_C; // convolution input row stride
+  static constexpr int LDW = KW1 + PAD_C;   // both sides: softmax-weight ring row stride
   static constexpr int LDX = KWMAX + 4;     // fp32 exchange tile row stride (mixing)
   static constexpr int ZROWS = ZPRE + R;
   static constexpr size_t KS_BYTES = (size_t)CH * KWMAX * LDK * sizeof(Tin);
@@ -95,12 +108,14 @@ struct Cfg {
   static constexpr size_t U_BYTES = KS_BYTES > SX_BYTES ? KS_BYTES : SX_BYTES;
   static constexpr size_t VT_BYTES = (size_t)CH * D * LDV * sizeof(Tin);
   static constexpr size_t ZB_BYTES = (size_t)CH * ZROWS * LDZ * sizeof(Tc);
+  static constexpr size_t ZW_BYTES = DUAL ? (size_t)CH * ZROWS * LDW * sizeof(Tc) : 0;
   static constexpr size_t PB_BYTES = (size_t)CH * R * LDP * sizeof(Tin);
   static constexpr size_t ST_BYTES = (size_t)CH * R * 2 * sizeof(float);
   static constexpr size_t OFF_U = 0;
   static constexpr size_t OFF_VT = OFF_U + U_BYTES;
   static constexpr size_t OFF_ZB = OFF_VT + VT_BYTES;
-  static constexpr size_t OFF_PB = OFF_ZB + ZB_BYTES;
+  static constexpr size_t OFF_ZW = OFF_ZB + ZB_BYTES;
+  static constexpr size_t OFF_PB = OFF_ZW + ZW_BYTES;
   static constexpr size_t OFF_ST = OFF_PB + PB_BYTES;
   static constexpr size_t LDS_BYTES = OFF_ST + ST_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget exceeded");
@@ -169,6 +184,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
   float* Sx = reinterpret_cast<float*>(smem + C::OFF_U);  // aliases Ks (mixing before softmax)
   T* Vt = reinterpret_cast<T*>(smem + C::OFF_VT);
   Tc* Zb = reinterpret_cast<Tc*>(smem + C::OFF_ZB);
+  Tc* Zw = reinterpret_cast<Tc*>(smem + C::OFF_ZW);  // both sides: the softmax weights
   T* Pb = reinterpret_cast<T*>(smem + C::OFF_PB);
   float* St_a = reinterpret_cast<float*>(smem + C::OFF_ST);  // [CH][R] rescale factors
   float* St_l = St_a + C::CH * C::R;                         // [CH][R] final row sums
@@ -200,9 +216,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
   const int T_ = A.T, M = A.M;
   const int kq = A.kq;
   const int cq1 = kq ? A.c_q - 1 : 0;
+  const int halo = C::DUAL ? 2 * cq1 : cq1;  // query halo rows of the tile
   const int h0 = kq ? (A.c_k - 1) / 2 : 0;
   const int i0 = A.row_begin + qt * A.r_out;
-  const int row0 = i0 - cq1;  // global row of tile row 0
+  const int row0 = i0 - halo;  // global row of tile row 0
   const int last_row = min(i0 + A.r_out, T_) - 1;
   const int n_kt = last_row / C::BK + 1;
   const int m_head = g * C::CH + hu;
@@ -230,9 +247,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
   // ---- banded Toeplitz operands of the c_q x c_k kernel ------------------------------
   // Output column n of a 16-column block reads input columns k of a 32-column window
   // that starts h0 keys left of the block: tap e = n - k + 2*h0.
-  typename MC::frag tz[CQ_MAX][C::KC];
-  if (kq) {
-    const float* th = A.theta + (size_t)m_head * A.c_q * A.c_k;
+  typedef typename MC::frag TzOps[CQ_MAX][C::KC];
+  auto toeplitz = [&](TzOps& dst, const float* theta) __attribute__((always_inline)) {
+    const float* th = theta + (size_t)m_head * A.c_q * A.c_k;
 #pragma unroll
     for (int a = 0; a < CQ_MAX; ++a) {
 #pragma unroll
@@ -246,14 +263,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
           if (a < A.c_q && e >= 0 && e < A.c_k) t = th[a * A.c_k + e];
           vals[e8] = Tc(t);
         }
-        tz[a][kc] = *reinterpret_cast<typename MC::frag*>(vals);
+        dst[a][kc] = *reinterpret_cast<typename MC::frag*>(vals);
       }
     }
+  };
+  TzOps tz, tz2;  // tz2: both sides, the kernel after softmax
+  if (kq) {
+    toeplitz(tz, A.theta);
+    if constexpr (C::DUAL) toeplitz(tz2, A.theta2);
     // zero the rows above the tile that halo outputs may read
     for (int x = tid; x < C::CH * ZPRE * C::LDZ; x += NTHREADS) {
       const int u = x / (ZPRE * C::LDZ);
       const int rem = x - u * ZPRE * C::LDZ;
       Zb[(size_t)u * C::ZROWS * C::LDZ + rem] = Tc(0.0f);
+    }
+    if constexpr (C::DUAL) {
+      for (int x = tid; x < C::CH * ZPRE * C::LDW; x += NTHREADS) {
+        const int u = x / (ZPRE * C::LDW);
+        const int rem = x - u * ZPRE * C::LDW;
+        Zw[(size_t)u * C::ZROWS * C::LDW + rem] = Tc(0.0f);
+      }
     }
   }
 
@@ -331,29 +360,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
     }
   };
 
-  // convolution of the fp16 tile in Zb (rows shifted by the query lag a) -> cv
+  // convolution of a ring of ld columns (rows shifted by the query lag a): output block ob
+  // reads ring columns 16 ob .. 16 ob + 31 -> dst[rb][ob], NOB blocks
   f32x4 cv[C::RB][C::OB];
-  auto convolve = [&]() {
+  auto convolve_ring = [&](const Tc* ring, int ld, const TzOps& tzs, auto& dst, auto nobc) __attribute__((always_inline)) {
+    constexpr int NOB = decltype(nobc)::value;
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
-      for (int ob = 0; ob < C::OB; ++ob) cv[rb][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ob = 0; ob < NOB; ++ob) dst[rb][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int a = 0; a < CQ_MAX; ++a) {
       if (a < A.c_q) {
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) {
-          const Tc* zrow = Zb + ((size_t)hu * C::ZROWS + ZPRE + ws * C::WR + rb * 16 + lr - a) * C::LDZ;
+          const Tc* zrow = ring + ((size_t)hu * C::ZROWS + ZPRE + ws * C::WR + rb * 16 + lr - a) * ld;
 #pragma unroll
-          for (int ob = 0; ob < C::OB; ++ob)
+          for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc) {
               const typename MC::frag af = MC::load(zrow + ob * 16 + kc * MC::K + lg * MC::KPL);
-              cv[rb][ob] = MC::mma(af, tz[a][kc], cv[rb][ob]);
+              dst[rb][ob] = MC::mma(af, tzs[a][kc], dst[rb][ob]);
             }
         }
       }
     }
+  };
+  // the convolution of the logits in Zb -> cv (output keys of the tile)
+  auto convolve = [&]() __attribute__((always_inline)) {
+    convolve_ring(Zb, C::LDZ, tz, cv, std::integral_constant<int, C::OB>{});
   };
 
   // AV on the weights in Pb: acc[p] += P_{head p} V_{hu}
@@ -465,6 +500,120 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
       for (int i = 0; i < 4; ++i)
         if (lr == 0) St_l[hu * C::R + ws * C::WR + rb * 16 + 4 * lg + i] = l_run[rb][i];
     __syncthreads();
+  } else if constexpr (C::DUAL) {
+    // ===================== both sides: convolutions before and after softmax ========
+    // phase 1: exact (max, sum) of the softmax inputs C = conv_pre(Mask_0(L)) of tile rows
+    // t >= c_q - 1 (the rows above them have no complete convolution; their weights are
+    // zero in phase 2, and only non-output rows read them)
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int j0 = kt * C::BK;
+      const int kbase = j0 - h0;
+      __syncthreads();
+      stage_k<C>(Ks, kb, g, M, T_, kbase, C::KW1);
+      __syncthreads();
+      logits(C::NB1);
+      // Mask_0 -> Zb, column c holding key kbase + c
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < C::NB1; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = ws * C::WR + rb * 16 + 4 * lg + i;
+            const int gr = row0 + t;
+            const int j = kbase + cb * 16 + lr;
+            const bool keep = gr >= 0 && j >= 0 && j < T_ && j <= gr;
+            Zb[((size_t)hu * C::ZROWS + ZPRE + t) * C::LDZ + cb * 16 + lr] = Tc(keep ? s[rb][cb][i] : 0.0f);
+          }
+      __syncthreads();
+      convolve();
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = ws * C::WR + rb * 16 + 4 * lg + i;
+          const int gr = row0 + t;
+          const bool row_ok = t >= cq1 && gr >= 0 && gr < T_;
+          float mx = NEG_INF;
+          float x[C::OB];
+#pragma unroll
+          for (int ob = 0; ob < C::OB; ++ob) {
+            const int j = j0 + ob * 16 + lr;
+            x[ob] = (row_ok && j <= gr) ? cv[rb][ob][i] : NEG_INF;
+            mx = fmaxf(mx, x[ob]);
+          }
+          mx = row16_max(mx);
+          const float m_new = fmaxf(m_run[rb][i], mx);
+          float sum = 0.0f;
+#pragma unroll
+          for (int ob = 0; ob < C::OB; ++ob) sum += fast_exp2(x[ob] - m_new);
+          sum = row16_sum(sum);
+          l_run[rb][i] = l_run[rb][i] * fast_exp2(m_run[rb][i] - m_new) + sum;
+          m_run[rb][i] = m_new;
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run[rb][i] = l_run[rb][i] > 0.0f ? 1.0f / l_run[rb][i] : 0.0f;
+
+    // phase 2: logits over keys j0 - 2 h0 .. (both key halos) -> Mask_0 -> convolution into
+    // the softmax inputs of keys j0 - h0 .. j0 + BK + h0 - 1 -> exact weights (Mask_-inf as
+    // zero) in Zw -> convolution -> Mask_0 -> AV
+    f32x4 cvp[C::RB][C::NB1];
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int j0 = kt * C::BK;
+      const int kbase = j0 - 2 * h0;
+      __syncthreads();
+      stage_k<C>(Ks, kb, g, M, T_, kbase, C::KWMAX);
+      stage_vt<C>(Vt, vb, g, M, T_, j0);
+      __syncthreads();
+      logits(C::KWB);
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < C::KWB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = ws * C::WR + rb * 16 + 4 * lg + i;
+            const int gr = row0 + t;
+            const int j = kbase + cb * 16 + lr;
+            const bool keep = gr >= 0 && j >= 0 && j < T_ && j <= gr;
+            Zb[((size_t)hu * C::ZROWS + ZPRE + t) * C::LDZ + cb * 16 + lr] = Tc(keep ? s[rb][cb][i] : 0.0f);
+          }
+      __syncthreads();
+      convolve_ring(Zb, C::LDZ, tz, cvp, std::integral_constant<int, C::NB1>{});
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < C::NB1; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = ws * C::WR + rb * 16 + 4 * lg + i;
+            const int gr = row0 + t;
+            const int j = j0 - h0 + cb * 16 + lr;
+            const bool keep = t >= cq1 && gr >= 0 && gr < T_ && j >= 0 && j <= gr;
+            const float pv = keep ? fast_exp2(cvp[rb][cb][i] - m_run[rb][i]) * l_run[rb][i] : 0.0f;
+            Zw[((size_t)hu * C::ZROWS + ZPRE + t) * C::LDW + cb * 16 + lr] = Tc(pv);
+          }
+      __syncthreads();
+      convolve_ring(Zw, C::LDW, tz2, cv, std::integral_constant<int, C::OB>{});
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int ob = 0; ob < C::OB; ++ob)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = ws * C::WR + rb * 16 + 4 * lg + i;
+            const int gr = row0 + t;
+            const int j = j0 + ob * 16 + lr;
+            const bool keep = t >= halo && gr < T_ && j <= gr;
+            Pb[((size_t)hu * C::R + t) * C::LDP + ob * 16 + lr] = to_elem<T>(keep ? cv[rb][ob][i] : 0.0f);
+          }
+      __syncthreads();
+      av();
+    }
   } else {
     // ===================== two phase: convolution after softmax =====================
     // phase 1: exact (max, sum) of every tile row, halo rows included
@@ -602,7 +751,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void mta_fused_kernel(FusedArgs A) {
         const float var = row16_sum(sq) * (1.0f / C::D);
         inv = 1.0f / sqrtf(var + 1e-5f);
       }
-      if (t >= cq1 && gr < T_) {
+      if (t >= halo && gr < T_) {
         T* dst = ob_ + ((size_t)gr * M + m_head) * C::D;
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
@@ -623,7 +772,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.q = p.q;
   a.k = p.k;
   a.v = p.v;
-  a.theta = p.kq == KQ_PRE ? p.theta_pre : p.theta_post;
+  a.theta = (p.kq & KQ_PRE) ? p.theta_pre : p.theta_post;
+  a.theta2 = p.theta_post;
   a.w_pre = p.w_pre;
   a.w_post = p.w_post;
   a.gamma = p.gamma;
@@ -638,7 +788,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
   a.gn = p.gn;
   a.c_q = p.kq ? p.c_q : 1;
   a.c_k = p.kq ? p.c_k : 1;
-  a.r_out = C::R - (a.c_q - 1);
+  a.r_out = C::R - (C::DUAL ? 2 : 1) * (a.c_q - 1);
   a.row_begin = p.row_begin;
   a.n_tiles = (p.T - p.row_begin + a.r_out - 1) / a.r_out;
   a.n_groups = p.M / C::CH;
@@ -652,19 +802,25 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 }
 
 // Tile shapes per (dtype, d, c_h, schedule, pairs). Per-pair accumulators cost
-// c_h * WR * d fp32 registers per wave, which caps WR at 32 when mixing after softmax.
-template <typename T, int D, int CH, bool TWO, bool PAIRS>
+// c_h * WR * d fp32 registers per wave, which caps WR at 32 when mixing after softmax. Both
+// sides take 16-key tiles: their staged K rows, logits ring and weights ring of fp32 values
+// then fit the LDS at d = 64 with four heads.
+template <typename T, int D, int CH, bool TWO, bool PAIRS, bool DUAL = false>
 hipError_t launch_shape(const Problem& p, hipStream_t stream) {
   constexpr bool F32 = std::is_same<T, float>::value;
-  constexpr int BK = (CH == 4 || F32) ? 32 : 64;
+  constexpr int BK = DUAL ? 16 : (CH == 4 || F32) ? 32 : 64;
   constexpr int WR = (CH == 4 && !PAIRS && !F32) ? 64 : 32;
-  return launch<Cfg<T, D, CH, WR, BK, TWO, PAIRS>>(p, stream);
+  return launch<Cfg<T, D, CH, WR, BK, TWO, PAIRS, DUAL>>(p, stream);
 }
 
 template <typename T, int D, int CH>
 hipError_t launch_ch(const Problem& p, hipStream_t stream) {
   const bool two = p.kq == KQ_POST;
   const bool pairs = (p.mix & MIX_POST) && CH > 1;
+  if (p.kq == KQ_BOTH) {
+    if (pairs) return launch_shape<T, D, CH, true, true, true>(p, stream);
+    return launch_shape<T, D, CH, true, false, true>(p, stream);
+  }
   if (two) {
     if (pairs) return launch_shape<T, D, CH, true, true>(p, stream);
     return launch_shape<T, D, CH, true, false>(p, stream);
