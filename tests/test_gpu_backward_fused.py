@@ -269,3 +269,45 @@ def test_backward_fused_largest_kernels_on_both_sides():
     inp, dout = grads_case(cfg)
     check(cfg, fused_grads(cfg, inp, dout), oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"],
           what="fused 8x17 both sides")
+
+
+@pytest.mark.parametrize("kq,mix,gn", [("post", "pre", True), ("pre", "post", True), ("both", "both", True),
+                                       (None, None, False)])
+def test_autograd_layer_gradients(kq, mix, gn):
+    """mta_layer under torch autograd: out equals forward_train's, the gradients that
+    loss.backward() leaves on q, k, v, theta, w, gamma, beta and a gate tensor equal those of
+    backward_fused called directly (fixed-order reductions bit for bit; dq, summed with atomics,
+    within fp32 reordering), and they match the oracle at the backward bar."""
+    cfg = mta_inputs.MTAConfig("autograd", 2, 70, 8, 64, 4, 9, 4, kq, mix, gn, "bf16", 0.2, 0.3, 1.0, 0.0, 0.9,
+                               seed=43)
+    inp, dout = grads_case(cfg)
+    d, p = to_gpu(cfg, inp)
+    leaves = {n: t.clone().requires_grad_(True) for n, t in {**d, **p}.items()}
+    lam_t = torch.tensor(float(inp["lam"]), device="cuda", requires_grad=True)
+    out = ta.mta_layer(leaves["q"], leaves["k"], leaves["v"], leaves["theta"] if kq else None,
+                       leaves["w"] if mix else None, leaves["gamma"] if gn else None, leaves["beta"] if gn else None,
+                       lam_t, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=kq, mix=mix, gn=gn)
+    dout_t = torch.from_numpy(dout).cuda().to(torch.bfloat16)
+    (out.float() * dout_t.float()).sum().backward()
+    ref_out, lse, opre = train_forward(cfg, d, p, inp["lam"])
+    ref = ta.backward_fused(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], inp["lam"],
+                            dout=dout_t, lse=lse, out_pre_gn=opre, c_q=cfg.c_q, c_k=cfg.c_k, c_h=cfg.c_h, kq=kq,
+                            mix=mix, gn=gn)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    got = {"dq": leaves["q"].grad, "dk": leaves["k"].grad, "dv": leaves["v"].grad,
+           "dtheta": leaves["theta"].grad if kq else None, "dw": leaves["w"].grad if mix else None,
+           "dgamma": leaves["gamma"].grad if gn else None, "dbeta": leaves["beta"].grad if gn else None,
+           "dlambda": lam_t.grad.reshape(1) if gn else None}
+    for n, want in ref.items():
+        if want is None:
+            assert got[n] is None, n
+            continue
+        if n == "dq":
+            assert torch.allclose(got[n].float(), want.float(), rtol=2e-2, atol=1e-3 * float(want.float().abs().max()))
+        else:
+            assert torch.equal(got[n], want), n
+    if not gn:
+        assert float(lam_t.grad) == 0.0
+    check(cfg, {n: (None if t is None else t.float().cpu().numpy().astype(np.float64)) for n, t in got.items()},
+          oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"], what=f"autograd {kq}/{mix}")

@@ -410,3 +410,47 @@ def check_args(q_ptr, k_ptr, v_ptr, theta_ptr, w_ptr, gamma_ptr, beta_ptr, out_p
 
 def last_error() -> str:
     return lib().mta_last_error().decode()
+
+
+class _MTATrainFn(torch.autograd.Function):
+    """Autograd node of the layer: ``forward_train`` in the forward, ``backward_fused`` in the
+    backward (bf16 tensors). The gate value enters as a float; its gradient is returned for
+    a ``lam`` tensor only."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, theta, w, gamma, beta, lam_t, lam, cfg):
+        c_q, c_k, c_h, kq, mix, gn = cfg
+        out, lse, o32 = forward_train(q, k, v, theta, w, gamma, beta, lam, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq,
+                                      mix=mix, gn=gn)
+        ctx.save_for_backward(q, k, v, theta, w, gamma, beta, lse, o32)
+        ctx.lam, ctx.cfg = lam, cfg
+        ctx.lam_shape = lam_t.shape if lam_t is not None else None
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, theta, w, gamma, beta, lse, o32 = ctx.saved_tensors
+        c_q, c_k, c_h, kq, mix, gn = ctx.cfg
+        g = backward_fused(q, k, v, theta, w, gamma, beta, ctx.lam, dout=dout.contiguous(), lse=lse,
+                           out_pre_gn=o32, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn)
+        dlam = None
+        if ctx.lam_shape is not None:
+            dlam = g["dlambda"].reshape(ctx.lam_shape) if gn else torch.zeros(ctx.lam_shape, device=q.device)
+        return (g["dq"], g["dk"], g["dv"], g["dtheta"], g["dw"], g["dgamma"], g["dbeta"], dlam, None, None)
+
+
+def mta_layer(q, k, v, theta=None, w=None, gamma=None, beta=None, lam=1.0, *, c_q: int = 1, c_k: int = 1,
+              c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None,
+              gn: bool = False) -> torch.Tensor:
+    """The layer as a differentiable torch operation (bf16 q, k, v on the GPU): the fused
+    training forward, and the fused backward when autograd asks for gradients of q, k, v,
+    theta, w, gamma, beta and, if ``lam`` is a tensor, of the gate value (read once with
+    ``.item()``, which waits for the device). Parameters are fp32 tensors in the shapes
+    ``forward`` takes."""
+    if q.dtype != torch.bfloat16:
+        raise ValueError("mta_layer trains bf16 tensors (the fused backward is built for bf16)")
+    lam_t = lam if isinstance(lam, torch.Tensor) else None
+    lam_f = float(lam_t.detach().item()) if lam_t is not None else float(lam)
+    cfg = (c_q, c_k, c_h, kq, mix, gn)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    return _MTATrainFn.apply(q, k, v, theta, w, gamma, beta, lam_t, lam_f, cfg)
