@@ -311,3 +311,30 @@ def test_autograd_layer_gradients(kq, mix, gn):
         assert float(lam_t.grad) == 0.0
     check(cfg, {n: (None if t is None else t.float().cpu().numpy().astype(np.float64)) for n, t in got.items()},
           oracle_grads(cfg, inp, dout), dout=dout, lam=inp["lam"], what=f"autograd {kq}/{mix}")
+
+
+@pytest.mark.parametrize("kq,mix,c_h", [("pre", "post", 2), ("both", "both", 4)])
+def test_autograd_layer_fp32(kq, mix, c_h):
+    """mta_layer with fp32 tensors: the fused fp32 forward and the unfused backward; the
+    gradients equal a direct backward_materialized call and match the gradient oracle."""
+    cfg = mta_inputs.MTAConfig("autograd32", 1, 40, 4, 32, 3, 5, c_h, kq, mix, True, "fp32", 0.2, 0.3, 1.0, 0.0, 0.9,
+                               seed=44)
+    inp, dout = grads_case(cfg)
+    d = {n: torch.from_numpy(np.ascontiguousarray(inp[n], np.float32)).cuda() for n in ("q", "k", "v")}
+    p = {n: torch.from_numpy(np.ascontiguousarray(inp[n], np.float32)).cuda() for n in ("theta", "w", "gamma", "beta")}
+    leaves = {n: t.clone().requires_grad_(True) for n, t in {**d, **p}.items()}
+    lam_t = torch.tensor(float(inp["lam"]), device="cuda", requires_grad=True)
+    out = ta.mta_layer(leaves["q"], leaves["k"], leaves["v"], leaves["theta"], leaves["w"], leaves["gamma"],
+                       leaves["beta"], lam_t, c_q=cfg.c_q, c_k=cfg.c_k, c_h=c_h, kq=kq, mix=mix, gn=True)
+    dout_t = torch.from_numpy(dout).cuda()
+    (out * dout_t).sum().backward()
+    ref = ta.backward_materialized(d["q"], d["k"], d["v"], p["theta"], p["w"], p["gamma"], p["beta"], inp["lam"],
+                                   dout=dout_t, c_q=cfg.c_q, c_k=cfg.c_k, c_h=c_h, kq=kq, mix=mix, gn=True)
+    torch.cuda.synchronize()
+    got = {"dq": leaves["q"].grad, "dk": leaves["k"].grad, "dv": leaves["v"].grad, "dtheta": leaves["theta"].grad,
+           "dw": leaves["w"].grad, "dgamma": leaves["gamma"].grad, "dbeta": leaves["beta"].grad,
+           "dlambda": lam_t.grad.reshape(1)}
+    for n, want in ref.items():
+        assert torch.allclose(got[n], want, rtol=1e-5, atol=1e-6 * float(want.abs().max())), n
+    check(cfg, {n: t.double().cpu().numpy() for n, t in got.items()}, oracle_grads(cfg, inp, dout), dout=dout,
+          lam=inp["lam"], what=f"autograd fp32 {kq}/{mix}")

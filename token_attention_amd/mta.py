@@ -413,15 +413,20 @@ def last_error() -> str:
 
 
 class _MTATrainFn(torch.autograd.Function):
-    """Autograd node of the layer: ``forward_train`` in the forward, ``backward_fused`` in the
-    backward (bf16 tensors). The gate value enters as a float; its gradient is returned for
-    a ``lam`` tensor only."""
+    """Autograd node of the layer. bf16: ``forward_train`` in the forward and ``backward_fused``
+    in the backward, or ``backward_materialized`` for the placements whose fused tiles do not fit
+    the LDS (the library reports them unsupported); fp32: ``forward`` and
+    ``backward_materialized``. The gate value enters as a float; its gradient is returned for a
+    ``lam`` tensor only."""
 
     @staticmethod
     def forward(ctx, q, k, v, theta, w, gamma, beta, lam_t, lam, cfg):
         c_q, c_k, c_h, kq, mix, gn = cfg
-        out, lse, o32 = forward_train(q, k, v, theta, w, gamma, beta, lam, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq,
-                                      mix=mix, gn=gn)
+        kw = dict(c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn)
+        if q.dtype == torch.float32:
+            out, lse, o32 = forward(q, k, v, theta, w, gamma, beta, lam, **kw), None, None
+        else:
+            out, lse, o32 = forward_train(q, k, v, theta, w, gamma, beta, lam, **kw)
         ctx.save_for_backward(q, k, v, theta, w, gamma, beta, lse, o32)
         ctx.lam, ctx.cfg = lam, cfg
         ctx.lam_shape = lam_t.shape if lam_t is not None else None
@@ -431,8 +436,17 @@ class _MTATrainFn(torch.autograd.Function):
     def backward(ctx, dout):
         q, k, v, theta, w, gamma, beta, lse, o32 = ctx.saved_tensors
         c_q, c_k, c_h, kq, mix, gn = ctx.cfg
-        g = backward_fused(q, k, v, theta, w, gamma, beta, ctx.lam, dout=dout.contiguous(), lse=lse,
-                           out_pre_gn=o32, c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn)
+        kw = dict(c_q=c_q, c_k=c_k, c_h=c_h, kq=kq, mix=mix, gn=gn)
+        dout = dout.contiguous()
+        g = None
+        if lse is not None:
+            try:
+                g = backward_fused(q, k, v, theta, w, gamma, beta, ctx.lam, dout=dout, lse=lse, out_pre_gn=o32, **kw)
+            except MTAError as e:
+                if e.status != ERR_UNSUPPORTED:
+                    raise
+        if g is None:
+            g = backward_materialized(q, k, v, theta, w, gamma, beta, ctx.lam, dout=dout, **kw)
         dlam = None
         if ctx.lam_shape is not None:
             dlam = g["dlambda"].reshape(ctx.lam_shape) if gn else torch.zeros(ctx.lam_shape, device=q.device)
@@ -442,13 +456,12 @@ class _MTATrainFn(torch.autograd.Function):
 def mta_layer(q, k, v, theta=None, w=None, gamma=None, beta=None, lam=1.0, *, c_q: int = 1, c_k: int = 1,
               c_h: int = 1, kq: Optional[str] = None, mix: Optional[str] = None,
               gn: bool = False) -> torch.Tensor:
-    """The layer as a differentiable torch operation (bf16 q, k, v on the GPU): the fused
-    training forward, and the fused backward when autograd asks for gradients of q, k, v,
-    theta, w, gamma, beta and, if ``lam`` is a tensor, of the gate value (read once with
-    ``.item()``, which waits for the device). Parameters are fp32 tensors in the shapes
-    ``forward`` takes."""
-    if q.dtype != torch.bfloat16:
-        raise ValueError("mta_layer trains bf16 tensors (the fused backward is built for bf16)")
+    """The layer as a differentiable torch operation (bf16 or fp32 q, k, v on the GPU): the
+    fused forward, and on ``loss.backward()`` the gradients of q, k, v, theta, w, gamma, beta
+    and, if ``lam`` is a tensor, of the gate value (read once with ``.item()``, which waits for
+    the device). bf16 takes the fused backward (the unfused one where the fused tiles do not
+    fit), fp32 the unfused backward. Parameters are fp32 tensors in the shapes ``forward``
+    takes."""
     lam_t = lam if isinstance(lam, torch.Tensor) else None
     lam_f = float(lam_t.detach().item()) if lam_t is not None else float(lam)
     cfg = (c_q, c_k, c_h, kq, mix, gn)
