@@ -250,8 +250,8 @@ int mta_forward_train(const void* q, const void* k, const void* v, const float* 
  * dq is accumulated with floating-point atomics, so its last bits may differ between calls;
  * dk, dv and the parameter gradients are reduced in a fixed order. Errors as for
  * mta_backward_materialized; MTA_ERR_UNSUPPORTED for MTA_FP32 and for placements whose tiles
- * do not fit in the 160 KiB of LDS (the largest kernels on both sides with c_h = 4).
- * Allocates nothing.
+ * would not fit in the 160 KiB of LDS (where the resident K/V rows do not fit they are read from
+ * global memory instead; with that, every shape of the supported range fits). Allocates nothing.
  */
 int mta_backward_fused(const void* q, const void* k, const void* v, const float* theta_kq,
                        const float* w_mix, const float* gn_gamma, const float* gn_beta, float lambda,
