@@ -1748,14 +1748,17 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
 // Query halo rows of a tile: c_q - 1 per convolution.
 inline int tile_halo(const Problem& p) { return p.kq ? ((p.kq == KQ_BOTH) ? 2 : 1) * (p.c_q - 1) : 0; }
 // Rows per tile of the launched shape. A split key range whose output rows fit one 16-row tile
-// (a decode step) takes tiles of 16 rows with one wave per head of the group; everything else
-// takes 8 waves of 32 rows. The key-split plan uses the same figure.
+// (a decode step) takes tiles of 16 rows with one wave per head of the group; the unsplit
+// per-pair schedule of two-head groups at d = 96 takes 12 waves of 16 rows (see launch_shape);
+// everything else takes 8 waves of 32 rows. The key-split plan uses the same figure.
 constexpr int SMALL_R = 16;
 inline bool short_rows(const Problem& p) { return p.T - p.row_begin <= SMALL_R - tile_halo(p); }
 inline bool small_tiles(const Problem& p) { return p.split_mode != 0 && short_rows(p); }
 inline int tile_rows(const Problem& p, bool split) {
   const int ch = p.mix ? p.c_h : 1;
-  return (split && short_rows(p)) ? SMALL_R : 32 * (8 / ch);
+  if (split && short_rows(p)) return SMALL_R;
+  if (!split && !p.fp32 && p.d == 96 && ch == 2 && p.kq == KQ_PRE && p.mix == MIX_POST) return 16 * 6;
+  return 32 * (8 / ch);
 }
 
 // Tile shapes: 8 waves of 32 query rows (two waves per SIMD, so one wave's MFMA work
@@ -1775,6 +1778,11 @@ hipError_t launch_shape(const Problem& p, hipStream_t stream) {
         return launch<Cfg<D, CH, QW, (CH > 1 ? 32 : BK), KQ, TWO, false, CQM, true, NW, false, SPLIT>>(p, stream);
     } else {
       if (p.mix == MIX_BOTH) return launch<Cfg<D, CH, QW, BK, KQ, TWO, true, CQM, true, NW, false, SPLIT>>(p, stream);
+    }
+    // per-pair accumulators for two-head groups at d = 96 (the 880M-model layer): 12 waves of 16
+    // rows, three per SIMD (161 registers, 86 KB of LDS; 0.249 -> 0.242 ms against 8 waves of 32)
+    if constexpr (!SPLIT && KQ && !TWO && MIXPOST && CH == 2 && D == 96 && QW == 32) {
+      if (p.mix == MIX_POST) return launch<Cfg<D, CH, 16, BK, KQ, TWO, true, CQM, false, 12, false, SPLIT>>(p, stream);
     }
     return launch<Cfg<D, CH, QW, BK, KQ, TWO, MIXPOST, CQM, false, NW, false, SPLIT>>(p, stream);
   };
