@@ -75,9 +75,12 @@ def oracle_full(cfg):
 
 def output_rows_per_tile(cfg):
     """Output rows of one row tile of the fused bf16 kernel for this workload: 8 waves of 32 rows,
-    8/c_h waves per head of the group, less the query halo of c_q - 1 rows per convolution."""
+    8/c_h waves per head of the group (12 waves of 16 rows for the per-pair schedule of two-head
+    groups at d = 96), less the query halo of c_q - 1 rows per convolution."""
     c_h = cfg.c_h if cfg.mix else 1
     halo = (cfg.c_q - 1) * {None: 0, "pre": 1, "post": 1, "both": 2}[cfg.kq]
+    if cfg.d == 96 and c_h == 2 and cfg.kq == "pre" and cfg.mix == "post":
+        return 16 * 6 - halo
     return 32 * (8 // c_h) - halo
 
 
@@ -423,6 +426,15 @@ def test_both_sides_fp32_ragged_lengths_and_head_sizes(T, d, c_h):
                                "fp32", 0.2, 0.2, 1.0, 0.0, 0.8, seed=28)
     inp = case(cfg)
     compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what=f"fp32 both T={T} d={d}")
+
+
+def test_both_sides_fp32_largest_tile():
+    """Both sides in fp32 at the schedule's largest LDS footprint and query halo: d = 64, four-head
+    groups mixed on both sides, 8 x 17 kernels (a 14-row halo of a 32-row tile)."""
+    cfg = mta_inputs.MTAConfig("dual_fp32_big", 1, 100, 8, 64, 8, 17, 4, "both", "both", True, "fp32", 0.1, 0.1,
+                               1.0, 0.0, 0.8, seed=30)
+    inp = case(cfg)
+    compare(cfg, run("fused", cfg, dev_inputs(cfg, inp), inp["lam"]), oracle_full(cfg), what="fp32 both 8x17 d=64")
 
 
 @pytest.mark.parametrize("row_begin", [0, 1, 37, 90])
